@@ -1,0 +1,15 @@
+"""CPU oracle for exact multi-head self-attention — TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import or call this package. The GPU library never does, and nothing here is
+shared with it.
+
+See ``oracle.attention`` for the definitions and their citations.
+"""
+from .attention import (  # noqa: F401
+    attention_probs,
+    attention_fwd,
+    attention_bwd,
+    brute_attention_fwd,
+    brute_attention_grads_fd,
+)
