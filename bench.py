@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Throughput of the fused attention path on one MI355X.
+
+One step = the whole hot path over one batch of synthetic input: the fused
+forward (attn_fwd) followed by the recompute-based backward (attn_bwd, three
+launches), on the long-sequence workload B=8, H=16, N=4096, d_k=64, bf16
+(inputs seeded, already resident in device memory when timing starts).
+
+    python bench.py [--steps K] [--warmup W] [--workload 2|3|5] [--no-cpu-baseline]
+
+Prints ONE JSON line on stdout; progress goes to stderr. FLOPs are
+algorithmic: forward 4*B*H*N^2*d (Q K^T and P V), backward 10*B*H*N^2*d
+(the Q K^T recompute, dP = dO V^T, dV = P^T dO, dK = dS^T Q, dQ = dS K).
+
+The "roofline" object describes the kernel that takes the most time per
+step, timed on its own with HIP events over back-to-back launches on the
+stream it runs on. "cpu_baseline" is the fp64 CPU oracle, timed on a bounded
+sample of whole heads of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s fwd+bwd (4·B·H·N²·d fwd) and % of MI355X bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def fwd_flops(B, H, N, d):
+    return 4.0 * B * H * N * N * d
+
+
+def bwd_flops(B, H, N, d):
+    return 10.0 * B * H * N * N * d
+
+
+def time_launches(fn, reps: int) -> float:
+    """Average milliseconds per call of ``fn`` over ``reps`` back-to-back calls (HIP events on the current stream)."""
+    import torch
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def cpu_baseline(wid: int, seed: int, budget_s: float) -> dict:
+    """The fp64 oracle (forward + backward) on whole heads of the workload, for about ``budget_s`` seconds."""
+    import numpy as np
+    from attn_inputs import WORKLOADS, make_inputs
+    from oracle import attention_bwd, attention_fwd
+    w = WORKLOADS[wid]
+    x = make_inputs(wid, seed=seed)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS uses the affinity set
+        cores = len(os.sched_getaffinity(0))
+    heads, elapsed = 0, 0.0
+    order = [(b, h) for b in range(w.B) for h in range(w.H)]
+    while heads < len(order) and (heads == 0 or elapsed * (heads + 1) / heads <= budget_s):
+        b, h = order[heads]
+        Q, K, V, DO = (x.f64(n, (b, h)) for n in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        attention_fwd(Q, K, V, x.scale)
+        if "bwd" in w.passes:
+            attention_bwd(Q, K, V, DO, x.scale)
+        elapsed += time.perf_counter() - t0
+        heads += 1
+    flops = (fwd_flops(1, heads, w.N, w.d) + (bwd_flops(1, heads, w.N, w.d) if "bwd" in w.passes else 0.0))
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads of the same workload (fwd+bwd, fp64, full N x N per head), "
+                      f"{elapsed:.1f} s", "seconds": round(elapsed, 3)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, choices=(2, 3, 5),
+                    help="workload with a backward pass (3 = long sequence, the headline)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--kernel-reps", type=int, default=20, help="launches per kernel for the roofline timing")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this attention library has no multi-GPU path "
+              "(heads shard across GPUs with no communication; see the design notes). Use --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from attn_inputs import WORKLOADS, make_inputs
+    from tiled_attention_08_amd import _lib as attn
+
+    w = WORKLOADS[args.workload]
+    B, H, N, d = w.B, w.H, w.N, w.d
+    log(f"[bench] workload {w.wid} {w.name}: B={B} H={H} N={N} d={d} bf16, seed {args.seed}")
+    x = make_inputs(args.workload, seed=args.seed)
+
+    def up(name):
+        return torch.from_numpy(np.ascontiguousarray(x.raw[name]).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v, do = up("q"), up("k"), up("v"), up("do")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = attn.workspace_for(q)
+    scale = x.scale
+    stream = torch.cuda.current_stream()
+
+    def step():
+        attn.attn_fwd(q, k, v, o, lse, scale, stream)
+        attn.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    for t in (o, lse, dq, dk, dv):
+        if not torch.isfinite(t.float()).all():
+            log("[bench] non-finite output")
+            return 1
+    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for _ in range(args.steps):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+    flops = fwd_flops(B, H, N, d) + bwd_flops(B, H, N, d)
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {ms:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    # Per-kernel timing (each kernel alone, back-to-back launches on the same stream).
+    reps = args.kernel_reps
+    kernels = {
+        "fwd": time_launches(lambda: attn.attn_fwd(q, k, v, o, lse, scale, stream), reps),
+        "bwd_prep": time_launches(lambda: attn.attn_bwd_stage(0, q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream),
+                                  reps),
+        "bwd_main": time_launches(lambda: attn.attn_bwd_stage(1, q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream),
+                                  reps),
+        "bwd_dq": time_launches(lambda: attn.attn_bwd_stage(2, q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream),
+                                reps),
+    }
+    log("[bench] kernel ms: " + ", ".join(f"{kname} {t:.4f}" for kname, t in kernels.items()))
+    kflops = {"fwd": fwd_flops(B, H, N, d), "bwd_main": bwd_flops(B, H, N, d)}
+    dominant = max(kernels, key=kernels.get)
+    if dominant in kflops:
+        achieved = kflops[dominant] / (kernels[dominant] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "kernel": {"fwd": "fwd_bf16_kernel", "bwd_main": "bwd_main_kernel"}[dominant],
+                    "avg_ms": round(kernels[dominant], 5)}
+    else:  # an HBM-bound helper dominates (small workloads)
+        rows = B * H * N
+        nbytes = {"bwd_prep": rows * d * 2 * 2 + rows * 4 + rows * d * 4,
+                  "bwd_dq": rows * d * 4 + rows * d * 2}[dominant]
+        achieved = nbytes / (kernels[dominant] * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dominant,
+                    "avg_ms": round(kernels[dominant], 5)}
+
+    record = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d_k": d, "passes": "fwd+bwd",
+                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
+        "frac_of_bf16_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "kernel_ms": {kname: round(t, 5) for kname, t in kernels.items()},
+        "fwd_tflops": round(fwd_flops(B, H, N, d) / (kernels["fwd"] * 1e-3) / 1e12, 2),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        record["cpu_baseline"] = cpu_baseline(args.workload, args.seed, args.cpu_seconds)
+    print(json.dumps(record), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,129 @@
+/*
+ * attn.h - C ABI of the fused tiled self-attention library for AMD Instinct
+ * MI355X (CDNA4, gfx950): libattn.so.
+ *
+ * The operation. Article "Selbstaufmerksamkeit, CUDA-Kernel und FlashAttention"
+ * (German edition of the self-attention / Triton / FlashAttention article,
+ * itimpress.au, 2026-11-15):
+ *   - §1, "Scores" and "Attention" formulas: for every (batch b, head h)
+ *       O = softmax(scale * Q K^T) V,  softmax taken row by row (each row of
+ *       probabilities sums to 1); the formula's scale is 1/sqrt(d_k).
+ *   - §1, last paragraph: heads are independent copies of this computation.
+ *   - §3, tiling bullet: Q, K, V are processed in on-chip tiles and only the
+ *       final output goes back to device memory; the N x N score matrix is
+ *       never stored.
+ *   - §3, online-softmax bullet: a running row maximum and normaliser rescale
+ *       the partial outputs tile by tile.
+ *   - §3, recompute bullet: the forward pass keeps only small per-row
+ *       normalisation statistics; the backward pass rebuilds the attention
+ *       tiles from them.
+ *
+ * Conventions shared by every entry point.
+ *   Layout.   Q, K, V, O, dO, dQ, dK, dV are [B, H, N, d_k] contiguous,
+ *             row-major (one head is an N x d_k block, rows d_k elements
+ *             apart). lse is [B, H, N] contiguous float32.
+ *   Statistic. lse[b,h,i] = log(sum_j exp(scale * <q_i, k_j>)), natural log:
+ *             the one per-row statistic the forward keeps for the backward.
+ *   Memory.   Every pointer is a device pointer owned by the caller and must
+ *             be 16-byte aligned. The library allocates no device memory and
+ *             keeps no pointer after a call returns.
+ *   Streams.  `stream` is a hipStream_t (NULL = the default stream). Work is
+ *             enqueued asynchronously; outputs are valid once the caller has
+ *             synchronised the stream, and inputs must stay unchanged until
+ *             then. Faults inside a kernel surface at that synchronisation,
+ *             not in the return code.
+ *   Errors.   Arguments are validated before anything is launched; on any
+ *             error nothing is launched and nothing is written. Return codes
+ *             are attn_status_t values.
+ *   Threads.  The library holds no state: calls from several host threads
+ *             are safe (ordering between them is the streams' business).
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, B/H/N < 1, non-finite scale, aliasing */
+  ATTN_ERR_UNSUPPORTED = -2,  /* d_k not in {64, 128}, or sizes beyond the int32 index range */
+  ATTN_ERR_WORKSPACE = -3,    /* workspace missing or smaller than attn_bwd_workspace_bytes() */
+  ATTN_ERR_HIP = -4           /* the HIP runtime rejected a launch */
+} attn_status_t;
+
+/*
+ * Forward, bfloat16 storage with float32 accumulation (the §3 fused method).
+ *   q, k, v  in : bf16 [B,H,N,d_k]
+ *   o        out: bf16 [B,H,N,d_k], O = softmax(scale Q K^T) V, rounded to
+ *                 nearest-even
+ *   lse      out: float32 [B,H,N] natural-log row logsumexp of scale Q K^T
+ *   d_k      64 or 128; scale any finite float (1/sqrt(d_k) in the formula).
+ * o and lse must not overlap each other or any input.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int N, int d_k, float scale, void* stream);
+
+/*
+ * Forward, float32 storage and float32 arithmetic throughout; same contract
+ * as attn_fwd otherwise.
+ */
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                 int B, int H, int N, int d_k, float scale, void* stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs for this shape: the per-row
+ * D_i = <dO_i, O_i> (float32 [B,H,N]) and a float32 [B,H,N,d_k] dQ
+ * accumulator. Returns 0 for arguments attn_bwd would reject.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d_k);
+
+/*
+ * Backward, bfloat16 storage with float32 accumulation (the §3 recompute
+ * bullet): rebuilds each probability tile P = exp(scale Q K^T - lse) from the
+ * saved lse, and returns the gradients of a scalar loss L given dO = dL/dO:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
+ *   dQ = scale dS K,  dK = scale dS^T Q.
+ *   q, k, v, o, dO in : bf16 [B,H,N,d_k]  (o as returned by attn_fwd)
+ *   lse            in : float32 [B,H,N]    (as returned by attn_fwd)
+ *   dq, dk, dv     out: bf16 [B,H,N,d_k]
+ *   workspace          device scratch of at least attn_bwd_workspace_bytes()
+ *                      bytes, owned by the caller; its contents on entry are
+ *                      ignored and on return are unspecified.
+ * dq, dk, dv and the workspace must be distinct and overlap no input.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dO, void* dq, void* dk, void* dv,
+             int B, int H, int N, int d_k, float scale,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One stage of attn_bwd, same arguments plus `stage`; attn_bwd is exactly
+ * stages 0, 1, 2 in order on `stream`. For callers that schedule or time the
+ * stages separately:
+ *   stage 0  prep:  workspace <- (delta_i = <dO_i, O_i> in float32, zeroed
+ *                   float32 dQ accumulator); reads o, dO.
+ *   stage 1  main:  recomputes P from q, k, lse; writes dk and dv; adds
+ *                   dS K into the workspace's dQ accumulator (float atomics,
+ *                   so the summation order, not the result's accuracy, varies
+ *                   run to run); needs stage 0's workspace.
+ *   stage 2  dq:    dq <- bf16(scale * accumulator).
+ * Every check of attn_bwd applies to every stage (all pointers are
+ * required). Returns ATTN_ERR_INVALID_ARG for a stage outside 0..2.
+ */
+int attn_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d_k, float scale,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

@@ -1,0 +1,46 @@
+"""Shared plumbing for the GPU tests: upload seeded inputs, read results back, compare."""
+from __future__ import annotations
+
+import numpy as np
+
+from attn_inputs import Inputs, bf16_bits_to_f64
+
+# Tolerances. fp32 path: max-abs 1e-5 on O; bf16 inputs with fp32 accumulation:
+# max-abs 2e-2 on O against the fp64 oracle run on the same bf16-rounded
+# inputs; gradients: relative L2 error 5e-2 per tensor. lse (the saved row
+# statistic): 1e-5 absolute for fp32, 1e-3 * max(1, |lse|) for bf16 inputs.
+TOL_F32_O = 1e-5
+TOL_F32_LSE = 1e-5
+TOL_BF16_O = 2e-2
+TOL_BF16_LSE_REL = 1e-3
+TOL_GRAD_RELL2 = 5e-2
+
+
+def to_device(x: Inputs, name: str):
+    import torch
+    a = x.raw[name]
+    if x.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def to_f64(t) -> np.ndarray:
+    import torch
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return bf16_bits_to_f64(t.view(torch.int16).cpu().numpy().view(np.uint16))
+    return t.cpu().numpy().astype(np.float64)
+
+
+def max_abs(a: np.ndarray, b: np.ndarray) -> float:
+    return float(np.max(np.abs(a - b))) if a.size else 0.0
+
+
+def rel_l2(a: np.ndarray, b: np.ndarray) -> float:
+    den = float(np.linalg.norm(b))
+    return float(np.linalg.norm(a - b)) / (den if den > 0 else 1.0)
+
+
+def lse_err(gpu: np.ndarray, ref: np.ndarray) -> float:
+    """Largest |gpu - ref| / max(1, |ref|)."""
+    return float(np.max(np.abs(gpu - ref) / np.maximum(1.0, np.abs(ref)))) if gpu.size else 0.0

@@ -1,0 +1,120 @@
+"""The C ABI on the host: the library loads, exports what include/attn.h declares, and
+rejects bad arguments before launching anything.
+
+No call here reaches a kernel launch: every call below fails exactly one
+validation check, and the checks run on the host before any HIP call, so these
+tests need no GPU. The fake device addresses are never dereferenced.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from tiled_attention_08_amd import _lib
+    return _lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "attn_bwd", "attn_bwd_stage",
+                                           "attn_bwd_workspace_bytes", "attn_status_string"])
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in declared_functions():
+        assert hasattr(L.lib, name), name
+    assert sorted(L.EXPORTS) == declared_functions()
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (attn_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4):
+        assert L.attn_status_string(code) and L.attn_status_string(code) != "unknown status"
+    assert L.attn_status_string(7) == "unknown status"
+
+
+# Distinct, 16-byte aligned fake device addresses, far apart (no overlaps).
+A = [0x10_0000_0000 * (i + 1) for i in range(12)]
+
+
+def fwd(L, *, q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, H=1, N=8, d=64, scale=0.125):
+    return L.lib.attn_fwd(q, k, v, o, lse, B, H, N, d, scale, None)
+
+
+def fwd32(L, **kw):
+    args = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, H=1, N=8, d=64, scale=0.125)
+    args.update(kw)
+    return L.lib.attn_fwd_f32(args["q"], args["k"], args["v"], args["o"], args["lse"], args["B"], args["H"],
+                              args["N"], args["d"], args["scale"], None)
+
+
+def bwd(L, stage=None, **kw):
+    a = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], do=A[5], dq=A[6], dk=A[7], dv=A[8], B=1, H=1, N=8, d=64,
+             scale=0.125, ws=A[9], ws_bytes=None)
+    a.update(kw)
+    if a["ws_bytes"] is None:
+        a["ws_bytes"] = L.attn_bwd_workspace_bytes(a["B"], a["H"], a["N"], a["d"])
+    args = (a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["B"], a["H"], a["N"],
+            a["d"], a["scale"], a["ws"], a["ws_bytes"], None)
+    if stage is None:
+        return L.lib.attn_bwd(*args)
+    return L.lib.attn_bwd_stage(stage, *args)
+
+
+def test_forward_rejections(L):
+    INV, UNS = L.ATTN_ERR_INVALID_ARG, L.ATTN_ERR_UNSUPPORTED
+    for f in (fwd, fwd32):
+        assert f(L, q=None) == INV
+        assert f(L, lse=None) == INV
+        assert f(L, v=A[2] + 8) == INV                    # misaligned
+        assert f(L, B=0) == INV and f(L, H=-1) == INV and f(L, N=0) == INV
+        assert f(L, scale=float("nan")) == INV and f(L, scale=float("inf")) == INV
+        assert f(L, d=96) == UNS and f(L, d=32) == UNS and f(L, d=256) == UNS
+        assert f(L, o=A[0]) == INV                        # output aliases an input
+        assert f(L, o=A[0] + 16) == INV                   # partial overlap
+        assert f(L, lse=A[3] + 64) == INV                 # lse inside o
+        assert f(L, N=1 << 30) == UNS                     # beyond 32-bit per-head indexing
+
+
+def test_backward_rejections(L):
+    INV, UNS, WS = L.ATTN_ERR_INVALID_ARG, L.ATTN_ERR_UNSUPPORTED, L.ATTN_ERR_WORKSPACE
+    for stage in (None, 0, 1, 2):
+        assert bwd(L, stage, dq=None) == INV
+        assert bwd(L, stage, do=A[5] + 4) == INV
+        assert bwd(L, stage, d=80) == UNS
+        assert bwd(L, stage, ws=None) == WS
+        assert bwd(L, stage, ws_bytes=16) == WS
+        assert bwd(L, stage, ws=A[9] + 8) == INV          # misaligned workspace
+        assert bwd(L, stage, dk=A[6]) == INV              # dk == dq
+        assert bwd(L, stage, dv=A[0]) == INV              # output aliases q
+        assert bwd(L, stage, ws=A[8]) == INV              # workspace overlaps dv
+        assert bwd(L, stage, scale=float("-inf")) == INV
+    assert bwd(L, 3) == INV and bwd(L, -1) == INV
+
+
+def test_workspace_size(L):
+    assert L.attn_bwd_workspace_bytes(8, 16, 4096, 64) >= 8 * 16 * 4096 * (64 + 1) * 4
+    assert L.attn_bwd_workspace_bytes(1, 1, 1, 64) >= 4 + 64 * 4
+    assert L.attn_bwd_workspace_bytes(1, 1, 8, 96) == 0
+    assert L.attn_bwd_workspace_bytes(0, 1, 8, 64) == 0
+
+
+def test_binding_has_no_cpu_path():
+    """The binding module contains no compute: it only marshals arguments into libattn.so."""
+    src = open(os.path.join(ROOT, "tiled_attention_08_amd", "_lib.py")).read()
+    for banned in ("oracle", "softmax", "matmul", "einsum", " @ ", "torch.exp"):
+        assert banned not in src, banned

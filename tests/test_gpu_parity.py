@@ -1,0 +1,273 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on the same seeded inputs.
+
+Small and ragged shapes are compared element by element over whole tensors;
+the five workloads run at full size in the launch configuration the benchmark
+uses, with whole sampled heads (or sampled query rows) compared against the
+oracle. All tests need an MI355X.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from attn_inputs import WORKLOADS, make_case, make_inputs
+from gpu_helpers import (TOL_BF16_LSE_REL, TOL_BF16_O, TOL_F32_LSE, TOL_F32_O, TOL_GRAD_RELL2, lse_err, max_abs,
+                         rel_l2, to_device, to_f64)
+from oracle import attention_bwd, attention_fwd
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# ------------------------------------------------------------------ fp32 forward
+
+@pytest.mark.parametrize("N,d", [(196, 64), (1, 64), (7, 64), (63, 64), (64, 64), (65, 64), (333, 64),
+                                 (1, 128), (129, 128), (200, 128)])
+def test_fwd_f32_parity(gpu_lib, N, d):
+    import torch
+    x = make_case(2 if N < 300 else 1, 2, N, d, "f32", seed=N + d, with_grad=False)
+    _say(f"fwd_f32 B={x.B} H={x.H} N={N} d={d}")
+    o, lse = gpu_lib.forward(to_device(x, "q"), to_device(x, "k"), to_device(x, "v"), x.scale)
+    torch.cuda.synchronize()
+    ro, rl = attention_fwd(x.f64("q"), x.f64("k"), x.f64("v"), x.scale)
+    assert max_abs(to_f64(o), ro) <= TOL_F32_O
+    assert max_abs(to_f64(lse), rl) <= TOL_F32_LSE
+
+
+def test_fwd_f32_workload1(gpu_lib):
+    """Single-head fp32 workload (B=H=1, N=196, d=64) in full."""
+    import torch
+    x = make_inputs(1)
+    o, lse = gpu_lib.forward(to_device(x, "q"), to_device(x, "k"), to_device(x, "v"), x.scale)
+    torch.cuda.synchronize()
+    ro, rl = attention_fwd(x.f64("q"), x.f64("k"), x.f64("v"), x.scale)
+    err = max_abs(to_f64(o), ro)
+    _say(f"workload 1 fp32 max-abs O {err:.3e}")
+    assert err <= TOL_F32_O
+    assert max_abs(to_f64(lse), rl) <= TOL_F32_LSE
+
+
+# ------------------------------------------------------------------ bf16 forward + backward, small shapes
+
+SMALL = [(1, 1, 1, 64), (1, 2, 7, 64), (2, 3, 65, 64), (2, 2, 196, 64), (2, 3, 333, 64), (1, 1, 1000, 64),
+         (1, 1, 1, 128), (1, 2, 129, 128), (2, 2, 196, 128), (1, 2, 517, 128)]
+
+
+@pytest.mark.parametrize("B,H,N,d", SMALL)
+def test_bf16_fwd_bwd_parity(gpu_lib, B, H, N, d):
+    import torch
+    x = make_case(B, H, N, d, "bf16", seed=1000 + N + d)
+    _say(f"bf16 fwd/bwd B={B} H={H} N={N} d={d}")
+    q, k, v, do = (to_device(x, n) for n in ("q", "k", "v", "do"))
+    o, lse = gpu_lib.forward(q, k, v, x.scale)
+    dq, dk, dv = gpu_lib.backward(q, k, v, o, lse, do, x.scale)
+    torch.cuda.synchronize()
+    Q, K, V, DO = x.f64("q"), x.f64("k"), x.f64("v"), x.f64("do")
+    ro, rl = attention_fwd(Q, K, V, x.scale)
+    assert max_abs(to_f64(o), ro) <= TOL_BF16_O
+    assert lse_err(to_f64(lse), rl) <= TOL_BF16_LSE_REL
+    rdq, rdk, rdv = attention_bwd(Q, K, V, DO, x.scale)
+    for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        e = rel_l2(to_f64(got), ref)
+        _say(f"  {name} rel-L2 {e:.3e}")
+        assert e <= TOL_GRAD_RELL2, name
+
+
+def test_bf16_negative_and_zero_scale(gpu_lib):
+    """Scale is a free argument: negative (folded into Q by the kernel) and zero (uniform weights)."""
+    import torch
+    x = make_case(1, 2, 150, 64, "bf16", seed=77)
+    q, k, v, do = (to_device(x, n) for n in ("q", "k", "v", "do"))
+    Q, K, V, DO = x.f64("q"), x.f64("k"), x.f64("v"), x.f64("do")
+    for scale in (-0.125, 0.0):
+        o, lse = gpu_lib.forward(q, k, v, scale)
+        dq, dk, dv = gpu_lib.backward(q, k, v, o, lse, do, scale)
+        torch.cuda.synchronize()
+        ro, rl = attention_fwd(Q, K, V, scale)
+        assert max_abs(to_f64(o), ro) <= TOL_BF16_O
+        assert lse_err(to_f64(lse), rl) <= TOL_BF16_LSE_REL
+        if scale == 0.0:
+            np.testing.assert_allclose(to_f64(o), np.broadcast_to(V.mean(axis=2, keepdims=True), V.shape), atol=1e-2)
+            np.testing.assert_allclose(to_f64(lse), math.log(150), atol=1e-3)
+        rdq, rdk, rdv = attention_bwd(Q, K, V, DO, scale)
+        assert rel_l2(to_f64(dv), rdv) <= TOL_GRAD_RELL2
+        if scale != 0.0:
+            assert rel_l2(to_f64(dq), rdq) <= TOL_GRAD_RELL2
+            assert rel_l2(to_f64(dk), rdk) <= TOL_GRAD_RELL2
+        else:
+            # scale 0: dQ = dK = 0 exactly (the kernel multiplies by the scale).
+            assert np.all(to_f64(dq) == 0) and np.all(to_f64(dk) == 0)
+
+
+# ------------------------------------------------------------------ invariants on the GPU
+
+def test_values_all_one_give_ones(gpu_lib):
+    """Rows of P sum to 1: V == 1 gives O == 1 (exactly representable), at a ragged N."""
+    import torch
+    x = make_case(2, 2, 333, 64, "bf16", seed=5, with_grad=False)
+    q, k = to_device(x, "q"), to_device(x, "k")
+    v = torch.ones_like(q)
+    o, _ = gpu_lib.forward(q, k, v, x.scale)
+    torch.cuda.synchronize()
+    assert max_abs(to_f64(o), np.ones(o.shape)) <= 4e-3
+
+
+def test_identity_values_expose_probabilities(gpu_lib):
+    """N <= d_k and V = I (padded): O = P, so each row of O is a probability row summing to 1."""
+    import torch
+    N, d = 50, 64
+    x = make_case(1, 1, N, d, "bf16", seed=6, with_grad=False)
+    q, k = to_device(x, "q"), to_device(x, "k")
+    v = torch.zeros((1, 1, N, d), dtype=torch.bfloat16, device="cuda")
+    v[0, 0, :, :N] = torch.eye(N, dtype=torch.bfloat16, device="cuda")
+    o, _ = gpu_lib.forward(q, k, v, x.scale)
+    torch.cuda.synchronize()
+    p = to_f64(o)[0, 0]
+    np.testing.assert_allclose(p[:, :N].sum(axis=1), 1.0, atol=2e-2)
+    assert np.all(p[:, N:] == 0)
+    from oracle import attention_probs
+    assert max_abs(p[:, :N], attention_probs(x.f64("q")[0, 0], x.f64("k")[0, 0], x.scale)) <= 5e-3
+
+
+def test_identical_keys_give_mean(gpu_lib):
+    import torch
+    x = make_case(1, 2, 196, 64, "bf16", seed=8, with_grad=False)
+    q, v = to_device(x, "q"), to_device(x, "v")
+    k = to_device(x, "k")[:, :, :1, :].expand(-1, -1, 196, -1).contiguous()
+    o, lse = gpu_lib.forward(q, k, v, x.scale)
+    torch.cuda.synchronize()
+    V = x.f64("v")
+    assert max_abs(to_f64(o), np.broadcast_to(V.mean(axis=2, keepdims=True), V.shape)) <= 1e-2
+    s0 = x.scale * np.einsum("bhnd,bhd->bhn", x.f64("q"), to_f64(k)[:, :, 0, :])
+    assert lse_err(to_f64(lse), s0 + math.log(196)) <= TOL_BF16_LSE_REL
+
+
+def test_key_value_permutation_invariance(gpu_lib):
+    import torch
+    x = make_case(1, 2, 300, 64, "bf16", seed=9, with_grad=False)
+    q, k, v = (to_device(x, n) for n in ("q", "k", "v"))
+    perm = torch.randperm(300, generator=torch.Generator().manual_seed(0)).cuda()
+    o1, l1 = gpu_lib.forward(q, k, v, x.scale)
+    o2, l2 = gpu_lib.forward(q, k[:, :, perm].contiguous(), v[:, :, perm].contiguous(), x.scale)
+    torch.cuda.synchronize()
+    assert max_abs(to_f64(o1), to_f64(o2)) <= 2e-2
+    assert lse_err(to_f64(l1), to_f64(l2)) <= 1e-3
+
+
+def test_forward_is_deterministic(gpu_lib):
+    import torch
+    x = make_case(2, 3, 700, 64, "bf16", seed=10, with_grad=False)
+    q, k, v = (to_device(x, n) for n in ("q", "k", "v"))
+    o1, l1 = gpu_lib.forward(q, k, v, x.scale)
+    o2, l2 = gpu_lib.forward(q, k, v, x.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_no_writes_outside_outputs(gpu_lib):
+    """Guard bands (NaN-filled) around every output stay untouched."""
+    import torch
+    B, H, N, d = 1, 2, 197, 64
+    x = make_case(B, H, N, d, "bf16", seed=11)
+    q, k, v, do = (to_device(x, n) for n in ("q", "k", "v", "do"))
+    E, G = B * H * N * d, 4096
+
+    def guarded(n, dtype):
+        buf = torch.full((n + 2 * G,), float("nan"), dtype=dtype, device="cuda")
+        return buf, buf[G:G + n]
+
+    ob, o = guarded(E, torch.bfloat16)
+    lb, lse = guarded(B * H * N, torch.float32)
+    gpu_lib.attn_fwd(q, k, v, o.view(B, H, N, d), lse.view(B, H, N), x.scale)
+    grads = [guarded(E, torch.bfloat16) for _ in range(3)]
+    ws_n = gpu_lib.attn_bwd_workspace_bytes(B, H, N, d)
+    wb = torch.full((ws_n + 2 * G,), 0x7F, dtype=torch.uint8, device="cuda")
+    gpu_lib.attn_bwd(q, k, v, o.view(B, H, N, d), lse.view(B, H, N), do, *(g[1].view(B, H, N, d) for g in grads),
+                     x.scale, wb[G:G + ws_n])
+    torch.cuda.synchronize()
+    for buf in [ob, lb] + [g[0] for g in grads]:
+        assert torch.isnan(buf[:G].float()).all() and torch.isnan(buf[-G:].float()).all()
+    assert (wb[:G] == 0x7F).all() and (wb[-G:] == 0x7F).all()
+    assert not torch.isnan(o.float()).any() and not torch.isnan(lse).any()
+
+
+# ------------------------------------------------------------------ the five workloads at full size
+
+def _sample_heads(B, H, n, seed):
+    rng = np.random.default_rng(seed)
+    flat = rng.choice(B * H, size=min(n, B * H), replace=False)
+    return [(int(f) // H, int(f) % H) for f in flat]
+
+
+@pytest.mark.parametrize("wid", [2, 3, 5])
+def test_workload_fwd_bwd(gpu_lib, wid):
+    """Workloads with a backward: full-size launch, whole sampled heads compared with the oracle."""
+    import torch
+    w = WORKLOADS[wid]
+    x = make_inputs(wid)
+    _say(f"workload {wid} {w.name} B={w.B} H={w.H} N={w.N} d={w.d}")
+    q, k, v, do = (to_device(x, n) for n in ("q", "k", "v", "do"))
+    o, lse = gpu_lib.forward(q, k, v, x.scale)
+    dq, dk, dv = gpu_lib.backward(q, k, v, o, lse, do, x.scale)
+    torch.cuda.synchronize()
+    heads = _sample_heads(w.B, w.H, {2: 24, 3: 2, 5: 3}[wid], seed=wid)
+    for b, h in heads:
+        Q, K, V, DO = (x.f64(n, (b, h)) for n in ("q", "k", "v", "do"))
+        ro, rl = attention_fwd(Q, K, V, x.scale)
+        eo = max_abs(to_f64(o[b, h]), ro)
+        el = lse_err(to_f64(lse[b, h]), rl)
+        rdq, rdk, rdv = attention_bwd(Q, K, V, DO, x.scale)
+        eg = [rel_l2(to_f64(g[b, h]), r) for g, r in ((dq, rdq), (dk, rdk), (dv, rdv))]
+        _say(f"  head ({b},{h}) O max-abs {eo:.3e} lse {el:.2e} dq/dk/dv rel-L2 {eg[0]:.2e} {eg[1]:.2e} {eg[2]:.2e}")
+        assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE_REL
+        assert max(eg) <= TOL_GRAD_RELL2
+    for t in (o, lse, dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
+    if wid == 5:
+        # Planted rows: one key dominates by a margin of >= 20, so O_i equals that V row
+        # up to bf16 output rounding.
+        O = to_f64(o)
+        for b in range(w.B):
+            for h in range(w.H):
+                rows, keys = x.planted[b, h, :, 0], x.planted[b, h, :, 1]
+                V = x.f64("v", (b, h))
+                assert max_abs(O[b, h, rows], V[keys]) <= 4e-3
+
+
+def test_workload4_fwd_rows_and_memory(gpu_lib):
+    """N = 16384, d = 128 forward: sampled query rows against the oracle, and the device memory
+    the call allocates is zero (the N x N matrix, 17 GB in bf16, is never stored)."""
+    import torch
+    w = WORKLOADS[4]
+    x = make_inputs(4)
+    _say(f"workload 4 {w.name}")
+    q, k, v = (to_device(x, n) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    free0, _ = torch.cuda.mem_get_info()
+    gpu_lib.attn_fwd(q, k, v, o, lse, x.scale)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert torch.cuda.max_memory_allocated() == base
+    assert free0 - free1 < (64 << 20)
+    rng = np.random.default_rng(4)
+    for b, h in _sample_heads(w.B, w.H, 3, seed=40):
+        rows = np.sort(rng.choice(w.N, size=256, replace=False))
+        rows[-1] = w.N - 1
+        Q = x.f64("q", (b, h))[rows]
+        ro, rl = attention_fwd(Q, x.f64("k", (b, h)), x.f64("v", (b, h)), x.scale)
+        eo = max_abs(to_f64(o[b, h])[rows], ro)
+        el = lse_err(to_f64(lse[b, h])[rows], rl)
+        _say(f"  head ({b},{h}) 256 rows: O max-abs {eo:.3e} lse {el:.2e}")
+        assert eo <= TOL_BF16_O and el <= TOL_BF16_LSE_REL
+    assert torch.isfinite(o.float()).all()

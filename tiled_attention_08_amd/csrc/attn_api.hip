@@ -1,0 +1,150 @@
+// attn_api.hip - the extern "C" entry points of libattn.so (declared in
+// include/attn.h): argument validation, head-dim dispatch and launch. Every
+// check runs on the host before anything is enqueued, so a rejected call
+// launches nothing and writes nothing.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+#include "attn_kernels.h"
+
+namespace {
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+Range span(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Shared shape checks. Returns ATTN_OK and the element counts, or an error code.
+int check_shape(int B, int H, int N, int d, float scale, size_t* elems, size_t* rows) {
+  if (B < 1 || H < 1 || N < 1) return ATTN_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  // Kernels index within a head with 32-bit ints and launch one workgroup per
+  // (head, row block) on a 1-D grid.
+  const int64_t per_head = (int64_t)N * d;
+  const int64_t heads = (int64_t)B * H;
+  if (per_head > INT32_MAX / 2) return ATTN_ERR_UNSUPPORTED;
+  if (heads * ((N + 31) / 32) > INT32_MAX / 2) return ATTN_ERR_UNSUPPORTED;
+  *rows = (size_t)heads * (size_t)N;
+  *elems = *rows * (size_t)d;
+  return ATTN_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, B/H/N < 1, non-finite scale, or overlapping buffers)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported shape (d_k must be 64 or 128; sizes must fit 32-bit per-head indexing)";
+    case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than attn_bwd_workspace_bytes()";
+    case ATTN_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d_k,
+             float scale, void* stream) {
+  size_t E = 0, R = 0;
+  const int st = check_shape(B, H, N, d_k, scale, &E, &R);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
+  const Range rq = span(q, E * 2), rk = span(k, E * 2), rv = span(v, E * 2), ro = span(o, E * 2), rl = span(lse, R * 4);
+  if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(ro, rl)) return ATTN_ERR_INVALID_ARG;
+  if (overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv)) return ATTN_ERR_INVALID_ARG;
+  return from_hip(attn::launch_fwd_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, B, H, N, d_k,
+                                        scale, static_cast<hipStream_t>(stream)));
+}
+
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d_k,
+                 float scale, void* stream) {
+  size_t E = 0, R = 0;
+  const int st = check_shape(B, H, N, d_k, scale, &E, &R);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
+  const Range rq = span(q, E * 4), rk = span(k, E * 4), rv = span(v, E * 4), ro = span(o, E * 4), rl = span(lse, R * 4);
+  if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(ro, rl)) return ATTN_ERR_INVALID_ARG;
+  if (overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv)) return ATTN_ERR_INVALID_ARG;
+  return from_hip(attn::launch_fwd_f32(q, k, v, o, lse, B, H, N, d_k, scale, static_cast<hipStream_t>(stream)));
+}
+
+size_t attn_bwd_workspace_bytes(int B, int H, int N, int d_k) {
+  size_t E = 0, R = 0;
+  if (check_shape(B, H, N, d_k, 1.0f, &E, &R) != ATTN_OK) return 0;
+  return attn::bwd_workspace_bytes(B, H, N, d_k);
+}
+
+namespace {
+
+int bwd_checks(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+               void* dk, void* dv, int B, int H, int N, int d_k, float scale, void* workspace,
+               size_t workspace_bytes) {
+  size_t E = 0, R = 0;
+  const int st = check_shape(B, H, N, d_k, scale, &E, &R);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(dO) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn::bwd_workspace_bytes(B, H, N, d_k);
+  if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
+  const Range ins[6] = {span(q, E * 2), span(k, E * 2), span(v, E * 2), span(o, E * 2), span(dO, E * 2),
+                        span(lse, R * 4)};
+  const Range outs[4] = {span(dq, E * 2), span(dk, E * 2), span(dv, E * 2), span(workspace, need)};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 6; ++b)
+      if (overlap(outs[a], ins[b])) return ATTN_ERR_INVALID_ARG;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlap(outs[a], outs[b])) return ATTN_ERR_INVALID_ARG;
+  }
+  return ATTN_OK;
+}
+
+int bwd_launch(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k, float scale,
+               void* workspace, void* stream) {
+  return from_hip(attn::launch_bwd_bf16_stage(
+      stage, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+      static_cast<const uint16_t*>(o), lse, static_cast<const uint16_t*>(dO), static_cast<uint16_t*>(dq),
+      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B, H, N, d_k, scale, workspace,
+      static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+             void* dk, void* dv, int B, int H, int N, int d_k, float scale, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  const int st = bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  for (int stage = 0; stage < 3; ++stage) {
+    const int r = bwd_launch(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, workspace, stream);
+    if (r != ATTN_OK) return r;
+  }
+  return ATTN_OK;
+}
+
+int attn_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k, float scale,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (stage < 0 || stage > 2) return ATTN_ERR_INVALID_ARG;
+  const int st = bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, workspace, workspace_bytes);
+  if (st != ATTN_OK) return st;
+  return bwd_launch(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, workspace, stream);
+}
+
+}  // extern "C"

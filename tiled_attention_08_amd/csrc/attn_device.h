@@ -1,0 +1,132 @@
+// attn_device.h - device-side building blocks shared by the attention kernels
+// (gfx950 / CDNA4, wave64).
+//
+// Matrix-core conventions used throughout (v_mfma_f32_32x32x16_bf16, checked
+// on the hardware with an in-bounds lane-layout probe):
+//   A (32 x 16, M x K): lane l supplies A[l % 32][8 * (l / 32) + s], s = 0..7
+//   B (16 x 32, K x N): lane l supplies B[8 * (l / 32) + s][l % 32]
+//   D (32 x 32):        lane l holds D[8 * j + 4 * (l / 32) + i][l % 32] in acc[4 * j + i]
+// The contraction index K may be permuted freely as long as A and B use the
+// same permutation; the kernels use the one that makes an accumulator tile
+// feed the next MFMA's B operand directly from registers: within a 16-wide
+// k-chunk, half h = l / 32 holds k = 4h + {0..3} in slots 0..3 and
+// k = 8 + 4h + {0..3} in slots 4..7.
+//
+// Transposing LDS read (ds_read_b64_tr_b16, also probed): within each group
+// of 16 lanes, lane i receives element (i % 4) of the 8-byte rows addressed by
+// lanes 4e + i / 4, for e = 0..3. If lane 4e + q of the group addresses
+// row (r0 + e), columns (c0 + 4q .. c0 + 4q + 3) of a row-major bf16 tile,
+// lane i ends up with column c0 + i of rows r0 .. r0 + 3: a transposed
+// operand read straight from a row-major tile.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x2& lo, const u32x2& hi) {
+  u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// lo.x + hi.x accumulated in fp32 (v_dot2_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float sum_bf16_pair(uint32_t pk, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Value held by the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ float other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const int lane = __lane_id();
+  return __uint_as_float(lane < 32 ? r[1] : r[0]);
+}
+
+// max / sum of x over lanes l and l ^ 32.
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// LDS tile swizzle. Tiles are row-major bf16 with 16-byte chunks (8 elements);
+// chunk c of row r is stored at chunk position c ^ swz(r). The XOR pattern
+// (r & 3) << 1 | (r >> 2) & 1 keeps both access patterns the kernels use
+// free of bank conflicts:
+//   * 16-byte row reads, 8 consecutive rows at one chunk: 8 distinct positions;
+//   * transposing 8-byte reads, rows r0..r0+3 (r0 % 4 == 0) x chunks c, c+1
+//     (c even): 8 distinct positions.
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// Byte offset of element (row, col) in a swizzled tile with `rowbytes` bytes per row.
+__device__ __forceinline__ int tile_off(int row, int col, int rowbytes) {
+  const int chunk = col >> 3;
+  return row * rowbytes + ((chunk ^ swz(row)) << 4) + ((col & 7) << 1);
+}
+
+__device__ __forceinline__ u32x4 lds_read_b128(const unsigned char* base, int off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+
+__device__ __forceinline__ void lds_write_b128(unsigned char* base, int off, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(base + off) = v;
+}
+
+__device__ __forceinline__ u32x2 lds_read_tr16_b64(const unsigned char* base, int off) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Asynchronous 16-byte copy global -> LDS (global_load_lds_dwordx4): lane l of
+// the wave writes the 16 bytes at `src` to LDS address lds_base + 16 * l.
+// `lds_base` must be wave-uniform. Completion is tracked by vmcnt.
+__device__ __forceinline__ void dma16(const void* src, unsigned char* lds_base) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// Wait until every outstanding global load of this wave (including LDS DMA) has landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Work-item index for a 1-D grid, grouping consecutive work items on one XCD.
+// Workgroups are handed to the 8 XCDs round-robin by launch index; this
+// bijection gives XCD x a contiguous block of work items (the same heads, so
+// the same K/V stay in that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int id, int total) {
+  const int x = id & 7, slot = id >> 3, per = total >> 3, rem = total & 7;
+  return x * per + (x < rem ? x : rem) + slot;
+}
+
+}  // namespace attn

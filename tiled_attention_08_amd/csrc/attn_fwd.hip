@@ -1,0 +1,368 @@
+// attn_fwd.hip - fused tiled attention forward for gfx950.
+//
+// Article "Selbstaufmerksamkeit, CUDA-Kernel und FlashAttention" (German
+// edition of the self-attention / Triton / FlashAttention article,
+// itimpress.au, 2026-11-15):
+//   §1 "Scores"/"Attention" formulas  O = softmax(scale Q K^T) V, row-wise softmax;
+//   §3 tiling bullet                  Q, K, V in on-chip tiles, only O written back;
+//   §3 online-softmax bullet          running row max and normaliser rescale the
+//                                     partial output as each K/V tile arrives;
+//   §3 recompute bullet               the row statistic (here lse) is kept for the backward.
+//
+// bf16 kernel, one workgroup = 4 waves; wave w owns 32*QB query rows.
+// Everything is computed transposed, S^T = K Q^T and O^T = V^T P^T, so that a
+// query is a lane column of every accumulator: row statistics (max, sum,
+// rescale factor) are per-lane scalars, and the S^T accumulator converts to
+// the B operand of the P*V product without leaving registers.
+//   S^T  : A = K tile rows (LDS, 16-byte reads), B = Q fragment (registers)
+//   O^T  : A = V^T (LDS, transposing 8-byte reads of the row-major V tile),
+//          B = P^T (registers, bf16)
+// K/V tiles of 64 keys are double-buffered in LDS and filled by direct
+// global->LDS DMA (no staging registers): tile j+1 is in flight while tile j
+// is computed.
+#include "attn_device.h"
+#include "attn_kernels.h"
+
+namespace attn {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kBC = 64;               // keys per K/V tile
+constexpr float kRescaleSlack = 8.0f; // log2 units a row max may grow before O, l are rescaled
+
+#ifndef FWD_WAVES_PER_EU
+#define FWD_WAVES_PER_EU 2  // two waves per SIMD: one wave's softmax overlaps the other's MFMAs
+#endif
+#ifndef FWD_QB64
+#define FWD_QB64 2          // 32-query blocks per wave at d_k = 64
+#endif
+#ifndef FWD_QB128
+#define FWD_QB128 1         // 32-query blocks per wave at d_k = 128
+#endif
+
+template <int D, int QB>
+struct FwdShape {
+  static constexpr int BR = kWaves * 32 * QB;         // query rows per workgroup
+  static constexpr int ROWB = D * 2;                  // bytes per K/V row
+  static constexpr int TILEB = kBC * ROWB;            // bytes per K or V tile
+  static constexpr int DMA_PER_WAVE = kBC * D / 8 / kThreads;  // 16-byte DMA instructions per wave per tile
+  static constexpr int LDSB = 4 * TILEB;              // K and V, two buffers each
+};
+
+template <int D, int QB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WAVES_PER_EU, FWD_WAVES_PER_EU))) void fwd_bf16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qblk, int total, float c,
+    uint32_t qsign) {
+  using S = FwdShape<D, QB>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int work = xcd_remap(blockIdx.x, total);
+  const int bh = work / n_qblk, qblk = work - bh * n_qblk;
+  const size_t head = (size_t)bh * N * D;
+  const uint16_t* Qh = Q + head;
+  const uint16_t* Kh = K + head;
+  const uint16_t* Vh = V + head;
+  const int qw0 = qblk * S::BR + wave * 32 * QB;
+
+  // Q fragments: B operand of S^T = K Q^T (lane: query l32, dims 16cc + 8h + 0..7).
+  // A negative scale is folded into Q (exact sign flip) so that c >= 0.
+  bf16x8 qf[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int q = qw0 + qb * 32 + l32;
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (q < N) v = *reinterpret_cast<const u32x4*>(Qh + (size_t)q * D + cc * 16 + h * 8);
+      v ^= qsign;
+      qf[qb][cc] = as_bf16x8(v);
+    }
+  }
+
+  f32x16 oacc[QB][D / 32];
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
+  }
+
+  const int ntiles = (N + kBC - 1) / kBC;
+
+  // K/V tile j -> LDS buffer `buf` by DMA. Wave w fills a contiguous run of
+  // 16-byte LDS slots; the lane writing slot (row, s) fetches global chunk
+  // s ^ swz(row), which yields the swizzled layout of tile_off(). Rows past
+  // N re-read row N-1 (finite data; their scores are masked below).
+  auto dma_tile = [&](int j, int buf) {
+    unsigned char* Ks = smem + buf * 2 * S::TILEB;
+    unsigned char* Vs = Ks + S::TILEB;
+#pragma unroll
+    for (int r = 0; r < S::DMA_PER_WAVE; ++r) {
+      const int slot0 = (wave * S::DMA_PER_WAVE + r) * 64;
+      const int p = slot0 + lane;
+      const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz(row);
+      const int key = min(j * kBC + row, N - 1);
+      dma16(Kh + (size_t)key * D + chunk * 8, Ks + slot0 * 16);
+      dma16(Vh + (size_t)key * D + chunk * 8, Vs + slot0 * 16);
+    }
+  };
+
+  dma_tile(0, 0);
+  wait_vmem();
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < ntiles) dma_tile(j + 1, buf ^ 1);
+    const unsigned char* Ks = smem + buf * 2 * S::TILEB;
+    const unsigned char* Vs = Ks + S::TILEB;
+
+    // ---- S^T tile: 64 keys x (32*QB) queries, fp32 accumulate.
+    f32x16 sacc[QB][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc) {
+        const bf16x8 a = as_bf16x8(lds_read_b128(Ks, tile_off(kb * 32 + l32, cc * 16 + h * 8, S::ROWB)));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = mfma32x32x16(a, qf[qb][cc], sacc[qb][kb]);
+      }
+    }
+
+    // ---- keys past N (last tile only) take no part in the row max.
+    const int kvalid = N - j * kBC;
+    const bool tail = kvalid < kBC;
+    if (tail) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (key >= kvalid)
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) sacc[qb][kb][e] = -INFINITY;
+        }
+    }
+
+    // ---- online softmax: running max in log2 units of the scaled score.
+    // The reference point m_run only moves when the tile max exceeds it by
+    // more than kRescaleSlack; any reference point gives the same softmax
+    // (it cancels between O and l), so skipping small moves only bounds the
+    // probabilities by 2^kRescaleSlack and saves the O rescale.
+    float mnew[QB];
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = fmaxf(sacc[qb][0][0], sacc[qb][1][0]);
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(sacc[qb][0][e], sacc[qb][1][e]));
+      mx = halves_max(mx) * c;
+      mnew[qb] = fmaxf(m_run[qb], mx);
+      need |= mnew[qb] > m_run[qb] + kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew[qb]);
+        m_run[qb] = mnew[qb];
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
+      }
+    }
+
+    // ---- probabilities (bf16) and their row sums.
+    uint32_t pk[QB][2][8];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float nm = -m_run[qb];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][e], c, nm));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][e + 1], c, nm));
+          if (tail) {
+            const int key = kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (key >= kvalid) p0 = 0.f;
+            if (key + 1 >= kvalid) p1 = 0.f;
+          }
+          pk[qb][kb][e >> 1] = pack_bf16(p0, p1);
+          l_run[qb] = sum_bf16_pair(pk[qb][kb][e >> 1], l_run[qb]);
+        }
+    }
+
+    // ---- O^T += V^T P^T.
+    const int g = lane >> 4, gi = lane & 15;
+    const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int row0 = kb * 32 + c2 * 16 + 4 * h + er;
+          const int col = db * 32 + dsub * 16 + 4 * qq;
+          const u32x2 lo = lds_read_tr16_b64(Vs, tile_off(row0, col, S::ROWB));
+          const u32x2 hi = lds_read_tr16_b64(Vs, tile_off(row0 + 8, col, S::ROWB));
+          const bf16x8 a = as_bf16x8(lo, hi);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const u32x4 bv = {pk[qb][kb][4 * c2], pk[qb][kb][4 * c2 + 1], pk[qb][kb][4 * c2 + 2],
+                              pk[qb][kb][4 * c2 + 3]};
+            oacc[qb][db] = mfma32x32x16(a, as_bf16x8(bv), oacc[qb][db]);
+          }
+        }
+
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O^T / l (bf16, RNE), lse = ln 2 * (m + log2 l).
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = halves_sum(l_run[qb]);
+    const float inv = 1.0f / lt;
+    const int q = qw0 + qb * 32 + l32;
+    if (q < N) {
+      uint16_t* orow = O + head + (size_t)q * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x16& a = oacc[qb][db];
+          u32x2 w = {pack_bf16(a[4 * jj] * inv, a[4 * jj + 1] * inv), pack_bf16(a[4 * jj + 2] * inv, a[4 * jj + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * jj + 4 * h) = w;
+        }
+      if (h == 0) LSE[(size_t)bh * N + q] = (m_run[qb] + log2f(lt)) * kLn2;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// fp32 forward: same method in fp32 storage and fp32 arithmetic (vector
+// ALU). One workgroup = 256 threads for 32 query rows; thread (r, t) with
+// r = tid / 8, t = tid % 8 scores keys t, t+8, ... of each 64-key tile for
+// query row r and owns output columns [t*D/8, (t+1)*D/8).
+// ------------------------------------------------------------------------
+constexpr int kF32BR = 32;
+
+template <int D>
+__global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                      const float* __restrict__ V, float* __restrict__ O,
+                                                      float* __restrict__ LSE, int N, int n_qblk, float scale) {
+  __shared__ float Ks[kBC][D + 1];
+  __shared__ float Vs[kBC][D];
+  __shared__ float Ps[kF32BR][kBC + 1];
+
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x / n_qblk, qblk = blockIdx.x - bh * n_qblk;
+  const size_t head = (size_t)bh * N * D;
+  const int r = tid >> 3, t = tid & 7;
+  const int q = qblk * kF32BR + r;
+  constexpr int DC = D / 8;
+
+  float qv[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) qv[i] = (q < N) ? Q[head + (size_t)q * D + i] : 0.f;
+
+  float acc[DC];
+#pragma unroll
+  for (int i = 0; i < DC; ++i) acc[i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  for (int j0 = 0; j0 < N; j0 += kBC) {
+    __syncthreads();
+    for (int idx = tid; idx < kBC * D; idx += 256) {
+      const int kr = idx / D, cc = idx - kr * D;
+      const bool ok = j0 + kr < N;
+      Ks[kr][cc] = ok ? K[head + (size_t)(j0 + kr) * D + cc] : 0.f;
+      Vs[kr][cc] = ok ? V[head + (size_t)(j0 + kr) * D + cc] : 0.f;
+    }
+    __syncthreads();
+
+    float s[kBC / 8];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kBC / 8; ++u) {
+      const int kr = t + 8 * u;
+      float dot = 0.f;
+#pragma unroll
+      for (int i = 0; i < D; ++i) dot = fmaf(qv[i], Ks[kr][i], dot);
+      s[u] = (j0 + kr < N) ? dot * scale : -INFINITY;
+      mx = fmaxf(mx, s[u]);
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float mnew = fmaxf(m, mx);
+    const float alpha = expf(m - mnew);
+    float rs = 0.f;
+#pragma unroll
+    for (int u = 0; u < kBC / 8; ++u) {
+      const float p = (j0 + t + 8 * u < N) ? expf(s[u] - mnew) : 0.f;
+      rs += p;
+      Ps[r][t + 8 * u] = p;
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) rs += __shfl_xor(rs, o);
+    l = l * alpha + rs;
+    m = mnew;
+#pragma unroll
+    for (int i = 0; i < DC; ++i) acc[i] *= alpha;
+    __syncthreads();
+    for (int kr = 0; kr < kBC; ++kr) {
+      const float p = Ps[r][kr];
+#pragma unroll
+      for (int i = 0; i < DC; ++i) acc[i] = fmaf(p, Vs[kr][t * DC + i], acc[i]);
+    }
+  }
+  if (q < N) {
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int i = 0; i < DC; ++i) O[head + (size_t)q * D + t * DC + i] = acc[i] * inv;
+    if (t == 0) LSE[(size_t)bh * N + q] = m + logf(l);
+  }
+}
+
+}  // namespace
+
+template <int D, int QB>
+static hipError_t launch_fwd_bf16_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+                                    float* lse, int B, int H, int N, float scale, hipStream_t stream) {
+  using S = FwdShape<D, QB>;
+  const int n_qblk = (N + S::BR - 1) / S::BR;
+  const int total = n_qblk * B * H;
+  const float c = fabsf(scale) * kLog2e;
+  const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, o, lse, N, n_qblk,
+                     total, c, qsign);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int B,
+                           int H, int N, int d, float scale, hipStream_t stream) {
+  if (d == 64) return launch_fwd_bf16_t<64, FWD_QB64>(q, k, v, o, lse, B, H, N, scale, stream);
+  return launch_fwd_bf16_t<128, FWD_QB128>(q, k, v, o, lse, B, H, N, scale, stream);
+}
+
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
+                          int d, float scale, hipStream_t stream) {
+  const int n_qblk = (N + kF32BR - 1) / kF32BR;
+  const int total = n_qblk * B * H;
+  if (d == 64)
+    hipLaunchKernelGGL((fwd_f32_kernel<64>), dim3(total), dim3(256), 0, stream, q, k, v, o, lse, N, n_qblk, scale);
+  else
+    hipLaunchKernelGGL((fwd_f32_kernel<128>), dim3(total), dim3(256), 0, stream, q, k, v, o, lse, N, n_qblk, scale);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,32 @@
+// attn_kernels.h - launchers of the attention kernels (internal to libattn.so).
+// Each launcher assumes validated arguments (see attn_api.cpp) and only
+// enqueues work on `stream`; it returns hipGetLastError() of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Rows of a head handled by one backward workgroup (keys) and per inner step (queries).
+constexpr int kBwdKeysPerBlock = 128;
+constexpr int kBwdQueriesPerStep = 64;
+
+hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int B,
+                           int H, int N, int d, float scale, hipStream_t stream);
+
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
+                          int d, float scale, hipStream_t stream);
+
+// Workspace layout: delta [B*H*N] fp32, then (256-byte aligned) dq_acc [B*H*N*d] fp32.
+size_t bwd_workspace_bytes(int B, int H, int N, int d);
+
+// One backward stage: 0 = delta + zeroed dQ accumulator, 1 = main (dK, dV, dQ
+// accumulation), 2 = dQ conversion.
+hipError_t launch_bwd_bf16_stage(int stage, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq, uint16_t* dk,
+                                 uint16_t* dv, int B, int H, int N, int d, float scale, void* workspace,
+                                 hipStream_t stream);
+
+}  // namespace attn
