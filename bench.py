@@ -2,15 +2,17 @@
 """Throughput of the fused attention path on one MI355X.
 
 One step = the whole hot path over one batch of synthetic input: the fused
-forward (attn_fwd) followed by the recompute-based backward (attn_bwd, three
-launches), on the long-sequence workload B=8, H=16, N=4096, d_k=64, bf16
+forward (attn_fwd) followed by the recompute-based backward (attn_bwd: delta, dK/dV
+and dQ launches), on the long-sequence workload B=8, H=16, N=4096, d_k=64, bf16
 (inputs seeded, already resident in device memory when timing starts).
 
     python bench.py [--steps K] [--warmup W] [--workload 2|3|5] [--no-cpu-baseline]
 
 Prints ONE JSON line on stdout; progress goes to stderr. FLOPs are
 algorithmic: forward 4*B*H*N^2*d (Q K^T and P V), backward 10*B*H*N^2*d
-(the Q K^T recompute, dP = dO V^T, dV = P^T dO, dK = dS^T Q, dQ = dS K).
+(the Q K^T recompute, dP = dO V^T, dV = P^T dO, dK = dS^T Q, dQ = dS K); work
+the implementation repeats (the dQ kernel's second Q K^T and dO V^T) is not
+counted.
 
 The "roofline" object describes the kernel that takes the most time per
 step, timed on its own with HIP events over back-to-back launches on the
@@ -100,7 +102,20 @@ def main(argv=None) -> int:
     ap.add_argument("--kernel-reps", type=int, default=20, help="launches per kernel for the roofline timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (three times) and exit: the "
+                         "known-size reference for scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args(argv)
+    if args.copy_calibration_mib:
+        import torch
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.copy_calibration_mib} MiB x 3")
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -158,31 +173,36 @@ def main(argv=None) -> int:
 
     # Per-kernel timing (each kernel alone, back-to-back launches on the same stream).
     reps = args.kernel_reps
+    def stage(i):
+        return lambda: attn.attn_bwd_stage(i, q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream)
+
     kernels = {
         "fwd": time_launches(lambda: attn.attn_fwd(q, k, v, o, lse, scale, stream), reps),
-        "bwd_prep": time_launches(lambda: attn.attn_bwd_stage(0, q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream),
-                                  reps),
-        "bwd_main": time_launches(lambda: attn.attn_bwd_stage(1, q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream),
-                                  reps),
-        "bwd_dq": time_launches(lambda: attn.attn_bwd_stage(2, q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream),
-                                reps),
+        "bwd_prep": time_launches(stage(0), reps),
+        "bwd_dkdv": time_launches(stage(1), reps),
+        "bwd_dq": time_launches(stage(2), reps),
     }
     log("[bench] kernel ms: " + ", ".join(f"{kname} {t:.4f}" for kname, t in kernels.items()))
-    kflops = {"fwd": fwd_flops(B, H, N, d), "bwd_main": bwd_flops(B, H, N, d)}
+    # Algorithmic FLOPs per launch. The dK/dV kernel performs the S recompute,
+    # dP, dV and dK products (8 B H N^2 d). The dQ kernel repeats S and dP to
+    # avoid a cross-workgroup reduction; only its dQ product (2 B H N^2 d) is
+    # algorithmic work, so its roofline fraction counts that alone.
+    kflops = {"fwd": fwd_flops(B, H, N, d), "bwd_dkdv": 0.8 * bwd_flops(B, H, N, d),
+              "bwd_dq": 0.2 * bwd_flops(B, H, N, d)}
+    kname_full = {"fwd": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel",
+                  "bwd_prep": "bwd_prep_kernel"}
     dominant = max(kernels, key=kernels.get)
     if dominant in kflops:
         achieved = kflops[dominant] / (kernels[dominant] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                    "kernel": {"fwd": "fwd_bf16_kernel", "bwd_main": "bwd_main_kernel"}[dominant],
-                    "avg_ms": round(kernels[dominant], 5)}
-    else:  # an HBM-bound helper dominates (small workloads)
+                    "kernel": kname_full[dominant], "avg_ms": round(kernels[dominant], 5)}
+    else:  # the HBM-bound delta kernel dominates (tiny workloads only)
         rows = B * H * N
-        nbytes = {"bwd_prep": rows * d * 2 * 2 + rows * 4 + rows * d * 4,
-                  "bwd_dq": rows * d * 4 + rows * d * 2}[dominant]
+        nbytes = rows * d * 2 * 2 + rows * 4
         achieved = nbytes / (kernels[dominant] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": dominant,
+                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": kname_full[dominant],
                     "avg_ms": round(kernels[dominant], 5)}
 
     record = {

@@ -76,8 +76,8 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
 
 /*
  * Bytes of device workspace attn_bwd needs for this shape: the per-row
- * D_i = <dO_i, O_i> (float32 [B,H,N]) and a float32 [B,H,N,d_k] dQ
- * accumulator. Returns 0 for arguments attn_bwd would reject.
+ * delta_i = <dO_i, O_i> in float32 ([B,H,N], rounded up to 256 bytes).
+ * Returns 0 for arguments attn_bwd would reject.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d_k);
 
@@ -104,13 +104,12 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  * One stage of attn_bwd, same arguments plus `stage`; attn_bwd is exactly
  * stages 0, 1, 2 in order on `stream`. For callers that schedule or time the
  * stages separately:
- *   stage 0  prep:  workspace <- (delta_i = <dO_i, O_i> in float32, zeroed
- *                   float32 dQ accumulator); reads o, dO.
- *   stage 1  main:  recomputes P from q, k, lse; writes dk and dv; adds
- *                   dS K into the workspace's dQ accumulator (float atomics,
- *                   so the summation order, not the result's accuracy, varies
- *                   run to run); needs stage 0's workspace.
- *   stage 2  dq:    dq <- bf16(scale * accumulator).
+ *   stage 0  prep:  workspace <- delta_i = <dO_i, O_i> (float32); reads o, dO.
+ *   stage 1  dK/dV: rebuilds P from q, k, lse and writes dk, dv; needs the
+ *                   workspace of stage 0.
+ *   stage 2  dQ:    rebuilds P from q, k, lse and writes dq; needs the
+ *                   workspace of stage 0 (stages 1 and 2 are independent).
+ * All stages are deterministic: no atomics, bitwise-repeatable results.
  * Every check of attn_bwd applies to every stage (all pointers are
  * required). Returns ATTN_ERR_INVALID_ARG for a stage outside 0..2.
  */

@@ -171,6 +171,24 @@ def test_forward_is_deterministic(gpu_lib):
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
 
 
+def test_backward_is_deterministic_and_staged(gpu_lib):
+    """The backward uses no atomics: reruns are bitwise equal, and attn_bwd equals stages 0, 1, 2."""
+    import torch
+    x = make_case(2, 2, 450, 64, "bf16", seed=12)
+    q, k, v, do = (to_device(x, n) for n in ("q", "k", "v", "do"))
+    o, lse = gpu_lib.forward(q, k, v, x.scale)
+    g1 = gpu_lib.backward(q, k, v, o, lse, do, x.scale)
+    g2 = gpu_lib.backward(q, k, v, o, lse, do, x.scale)
+    ws = gpu_lib.workspace_for(q)
+    g3 = [torch.empty_like(q) for _ in range(3)]
+    for st in (0, 1, 2):
+        gpu_lib.attn_bwd_stage(st, q, k, v, o, lse, do, *g3, x.scale, ws)
+    torch.cuda.synchronize()
+    for a, b, c in zip(g1, g2, g3):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+
+
 def test_no_writes_outside_outputs(gpu_lib):
     """Guard bands (NaN-filled) around every output stay untouched."""
     import torch

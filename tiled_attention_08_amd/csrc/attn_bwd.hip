@@ -11,19 +11,23 @@
 //   delta_i = <dO_i, O_i> (= sum_j P_ij dP_ij),  dS = P * (dP - delta),
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
-// Three launches on one stream:
-//   1. bwd_prep_kernel    delta = rowsum(dO * O) (fp32), zero the fp32 dQ accumulator;
-//   2. bwd_main_kernel    one workgroup per (head, block of 128 keys); loops over
-//                         64-query steps, recomputes S and P, accumulates dK and dV
-//                         in registers and adds each step's dQ share into the
-//                         fp32 accumulator with float atomics;
-//   3. bwd_dq_kernel      dQ = bf16(scale * accumulator).
-// In the main kernel a key is a lane column (S = Q K^T, m = query, n = key),
-// so dV^T = dO^T P and dK^T = Q^T dS take P and dS straight from registers;
-// dO^T and Q^T come from transposing LDS reads of the row-major tiles. dQ
-// needs dS with the key as contraction index, so dS makes one round trip
-// through LDS (written as [key][query], read back transposed) and dQ = dS K
-// is accumulated with queries as accumulator rows.
+// Three launches on one stream, deterministic (no atomics):
+//   stage 0  bwd_prep_kernel   delta = rowsum(dO * O) in fp32 (the workspace);
+//   stage 1  bwd_dkdv_kernel   one workgroup per (head, 128 keys), looping over
+//                              64-query steps: rebuilds S and P, accumulates
+//                              dV and dK in registers. A key is a lane column
+//                              (S = Q K^T, m = query, n = key), so dV^T = dO^T P
+//                              and dK^T = Q^T dS take P and dS straight from
+//                              registers; dO^T and Q^T come from transposing
+//                              LDS reads of the row-major tiles;
+//   stage 2  bwd_dq_kernel     one workgroup per (head, query block), looping
+//                              over 32-key steps: rebuilds S^T and P^T with a
+//                              query per lane column (lse and delta are then
+//                              per-lane scalars) and accumulates dQ^T = K^T dS^T
+//                              with dS^T straight from registers.
+// The dQ kernel repeats the Q K^T and dO V^T products of the dK/dV kernel: 14
+// instead of 10 units of N^2 d work, in exchange for no cross-workgroup
+// reduction and no dS round trip through memory.
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -32,17 +36,19 @@ namespace attn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int BCK = kBwdKeysPerBlock;    // keys per workgroup (32 per wave)
-constexpr int BRQ = kBwdQueriesPerStep;  // queries per step
+constexpr int BCK = kBwdKeysPerBlock;    // dK/dV kernel: keys per workgroup (32 per wave)
+constexpr int BRQ = kBwdQueriesPerStep;  // dK/dV kernel: queries per step
+constexpr int BCQ = 32;                  // dQ kernel: keys per step
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+#ifndef BWD_WAVES_PER_EU
+#define BWD_WAVES_PER_EU 2
+#endif
 
-// ---------------------------------------------------------------- 1. prep
+// ---------------------------------------------------------------- stage 0: delta
 // 8 lanes per row; each lane covers D/8 consecutive elements.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
-                                                       float* __restrict__ delta, float* __restrict__ dq_acc,
-                                                       long rows) {
+                                                       float* __restrict__ delta, long rows) {
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
   const long row = gid >> 3;
   const int part = (int)(gid & 7);
@@ -61,9 +67,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
         s = fmaf(__uint_as_float(a[w] & 0xffff0000u), __uint_as_float(b[w] & 0xffff0000u), s);
       }
     }
-    float* z = dq_acc + row * D + part * PER;
-#pragma unroll
-    for (int c = 0; c < PER; c += 4) *reinterpret_cast<float4*>(z + c) = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   s += __shfl_xor(s, 1);
   s += __shfl_xor(s, 2);
@@ -71,44 +74,47 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
   if (row < rows && part == 0) delta[row] = s;
 }
 
-// ---------------------------------------------------------------- 3. dq convert
-__global__ __launch_bounds__(256) void bwd_dq_kernel(const float* __restrict__ acc, uint16_t* __restrict__ dq,
-                                                     long n8, float scale) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const float4 a = reinterpret_cast<const float4*>(acc)[2 * i];
-  const float4 b = reinterpret_cast<const float4*>(acc)[2 * i + 1];
-  const u32x4 w = {pack_bf16(a.x * scale, a.y * scale), pack_bf16(a.z * scale, a.w * scale),
-                   pack_bf16(b.x * scale, b.y * scale), pack_bf16(b.z * scale, b.w * scale)};
-  reinterpret_cast<u32x4*>(dq)[i] = w;
+// DMA a row-major [rows x D] block (rows row0.., clamped to N-1) into a
+// swizzled LDS tile. Wave `wave` fills `per_lane` runs of 64 consecutive
+// 16-byte slots; the lane writing slot (row, s) fetches global chunk
+// s ^ swz(row), which yields the layout tile_off() addresses. Rows past N
+// re-read row N-1 (finite data); every use of such a row is masked.
+template <int D>
+__device__ __forceinline__ void dma_rows(const uint16_t* head_src, int row0, int N, unsigned char* dst, int wave,
+                                         int lane, int per_lane) {
+  constexpr int ROWB = D * 2;
+  for (int r = 0; r < per_lane; ++r) {
+    const int slot0 = (wave * per_lane + r) * 64;
+    const int p = slot0 + lane;
+    const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz<ROWB>(row);
+    const int gr = min(row0 + row, N - 1);
+    dma16(head_src + (size_t)gr * D + chunk * 8, dst + slot0 * 16);
+  }
 }
 
-// ---------------------------------------------------------------- 2. main
+// ---------------------------------------------------------------- stage 1: dK, dV
 template <int D>
-struct BwdShape {
+struct DkdvShape {
   static constexpr int ROWB = D * 2;
-  static constexpr int KTILEB = BCK * ROWB;             // resident K block
   static constexpr int QTILEB = BRQ * ROWB;             // one Q or dO step tile
-  static constexpr int DSROWB = BRQ * 2;                // dS^T row: 64 queries
-  static constexpr int DSB = BCK * DSROWB;              // dS^T tile
-  static constexpr int KCPT = BCK * D / 8 / kThreads;   // 16-byte chunks per thread, K block
-  static constexpr int QCPT = BRQ * D / 8 / kThreads;   // 16-byte chunks per thread, Q/dO tile
-  static constexpr int OFF_K = 0;
-  static constexpr int OFF_Q = OFF_K + KTILEB;
+  static constexpr int QDMA = BRQ * D / 8 / kThreads;   // 16-byte DMAs per lane per Q or dO tile
+  static constexpr int OFF_Q = 0;
   static constexpr int OFF_DO = OFF_Q + 2 * QTILEB;
-  static constexpr int OFF_L = OFF_DO + 2 * QTILEB;     // lse * log2(e), two buffers
+  static constexpr int OFF_L = OFF_DO + 2 * QTILEB;     // lse, two buffers
   static constexpr int OFF_DL = OFF_L + 2 * BRQ * 4;    // delta, two buffers
-  static constexpr int OFF_DS = OFF_DL + 2 * BRQ * 4;
-  static constexpr int LDSB = OFF_DS + DSB;
+  static constexpr int LDSB = OFF_DL + 2 * BRQ * 4;
 };
 
+// d_k = 128 needs more than 256 registers per lane (its dK and dV
+// accumulators alone take 128): one wave per SIMD there.
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_main_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
-    float* __restrict__ dq_acc, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk, int total,
-    float c, float scale) {
-  using S = BwdShape<D>;
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(D == 64 ? BWD_WAVES_PER_EU : 1, D == 64 ? BWD_WAVES_PER_EU : 1)))
+void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+                     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk, int total, float c,
+                     float scale) {
+  using S = DkdvShape<D>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -119,11 +125,9 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(
   const int bh = work / n_kblk, kblk = work - bh * n_kblk;
   const size_t head = (size_t)bh * N * D;
   const size_t hrow = (size_t)bh * N;
-  const int k0 = kblk * BCK;
-  const int krow = wave * 32 + l32;  // this lane's key within the block
-  const int key = k0 + krow;
+  const int key = kblk * BCK + wave * 32 + l32;  // this lane's key
   const bool key_ok = key < N;
-  const bool key_tail = k0 + BCK > N;
+  const bool key_tail = kblk * BCK + BCK > N;
 
   // K and V fragments of this lane's key: B operands of S = Q K^T and dP = dO V^T.
   bf16x8 kf[D / 16], vf[D / 16];
@@ -137,16 +141,15 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(
     kf[cc] = as_bf16x8(a);
     vf[cc] = as_bf16x8(b);
   }
-  // The whole K block in LDS: B operand (transposing reads) of dQ = dS K.
-  unsigned char* Ks = smem + S::OFF_K;
-#pragma unroll
-  for (int r = 0; r < S::KCPT; ++r) {
-    const int id = tid + r * kThreads;
-    const int row = id / (D / 8), ch = id - row * (D / 8);
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (k0 + row < N) v = *reinterpret_cast<const u32x4*>(K + head + (size_t)(k0 + row) * D + ch * 8);
-    lds_write_b128(Ks, tile_off(row, ch * 8, S::ROWB), v);
-  }
+
+  auto dma_step = [&](int i, int buf) {
+    const int q0 = i * BRQ;
+    dma_rows<D>(Q + head, q0, N, smem + S::OFF_Q + buf * S::QTILEB, wave, lane, S::QDMA);
+    dma_rows<D>(dO + head, q0, N, smem + S::OFF_DO + buf * S::QTILEB, wave, lane, S::QDMA);
+    const size_t r = hrow + min(q0 + lane, N - 1);
+    if (wave == 0) dma4(LSE + r, smem + S::OFF_L + buf * BRQ * 4);
+    if (wave == 1) dma4(delta + r, smem + S::OFF_DL + buf * BRQ * 4);
+  };
 
   f32x16 dvacc[D / 32], dkacc[D / 32];
 #pragma unroll
@@ -156,58 +159,21 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(
   }
 
   const int nq = (N + BRQ - 1) / BRQ;
-  u32x4 qst[S::QCPT], dost[S::QCPT];
-  float lst = 0.f, dst = 0.f;
-
-  auto gload = [&](int i) {
-    const int q0 = i * BRQ;
-#pragma unroll
-    for (int r = 0; r < S::QCPT; ++r) {
-      const int id = tid + r * kThreads;
-      const int row = id / (D / 8), ch = id - row * (D / 8);
-      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (q0 + row < N) {
-        a = *reinterpret_cast<const u32x4*>(Q + head + (size_t)(q0 + row) * D + ch * 8);
-        b = *reinterpret_cast<const u32x4*>(dO + head + (size_t)(q0 + row) * D + ch * 8);
-      }
-      qst[r] = a;
-      dost[r] = b;
-    }
-    if (tid < BRQ) {
-      const int q = q0 + tid;
-      lst = q < N ? LSE[hrow + q] * kLog2e : 0.f;
-      dst = q < N ? delta[hrow + q] : 0.f;
-    }
-  };
-  auto lstore = [&](int buf) {
-    unsigned char* Qs = smem + S::OFF_Q + buf * S::QTILEB;
-    unsigned char* dOs = smem + S::OFF_DO + buf * S::QTILEB;
-#pragma unroll
-    for (int r = 0; r < S::QCPT; ++r) {
-      const int id = tid + r * kThreads;
-      const int row = id / (D / 8), ch = id - row * (D / 8);
-      const int off = tile_off(row, ch * 8, S::ROWB);
-      lds_write_b128(Qs, off, qst[r]);
-      lds_write_b128(dOs, off, dost[r]);
-    }
-    if (tid < BRQ) {
-      reinterpret_cast<float*>(smem + S::OFF_L + buf * BRQ * 4)[tid] = lst;
-      reinterpret_cast<float*>(smem + S::OFF_DL + buf * BRQ * 4)[tid] = dst;
-    }
-  };
-
-  gload(0);
-  lstore(0);
+  dma_step(0, 0);
+  wait_vmem();
   __syncthreads();
 
-  unsigned char* dSt = smem + S::OFF_DS;
-
-  for (int i = 0; i < nq; ++i) {
+  // One 64-query step. MASKED (the last step when N % 64 != 0, and every step
+  // of the last key block when N % 128 != 0) gives probability 0 to queries
+  // and keys past N; other steps carry no masking code.
+  auto step = [&](int i, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int buf = i & 1;
-    if (i + 1 < nq) gload(i + 1);
+    const int q0 = i * BRQ;
+    if (i + 1 < nq) dma_step(i + 1, buf ^ 1);
     const unsigned char* Qs = smem + S::OFF_Q + buf * S::QTILEB;
     const unsigned char* dOs = smem + S::OFF_DO + buf * S::QTILEB;
-    const float* L2 = reinterpret_cast<const float*>(smem + S::OFF_L + buf * BRQ * 4);
+    const float* L = reinterpret_cast<const float*>(smem + S::OFF_L + buf * BRQ * 4);
     const float* DL = reinterpret_cast<const float*>(smem + S::OFF_DL + buf * BRQ * 4);
 
     // ---- S = Q K^T and dP = dO V^T for 64 queries x this lane's key.
@@ -218,38 +184,36 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(
       pacc[mb] = f32x16{};
 #pragma unroll
       for (int cc = 0; cc < D / 16; ++cc) {
-        const int off = tile_off(mb * 32 + l32, cc * 16 + h * 8, S::ROWB);
-        const bf16x8 aq = as_bf16x8(lds_read_b128(Qs, off));
-        const bf16x8 ad = as_bf16x8(lds_read_b128(dOs, off));
-        sacc[mb] = mfma32x32x16(aq, kf[cc], sacc[mb]);
-        pacc[mb] = mfma32x32x16(ad, vf[cc], pacc[mb]);
+        const int off = tile_off<S::ROWB>(mb * 32 + l32, cc * 16 + h * 8);
+        sacc[mb] = mfma32x32x16(as_bf16x8(lds_read_b128(Qs, off)), kf[cc], sacc[mb]);
+        pacc[mb] = mfma32x32x16(as_bf16x8(lds_read_b128(dOs, off)), vf[cc], pacc[mb]);
       }
     }
 
     // ---- P = exp2(S * scale * log2 e - lse * log2 e), dS = P * (dP - delta).
-    uint32_t ppk[2][8], dspk[2][8];
+    // pp[mb][c2] / dsb[mb][c2]: B operands (bf16 P and dS) for queries mb*32 + 16*c2 + (0..15).
+    u32x4 pp[2][2], dsb[2][2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const float4 l4 = *reinterpret_cast<const float4*>(L2 + mb * 32 + 8 * jj + 4 * h);
-        const float4 d4 = *reinterpret_cast<const float4*>(DL + mb * 32 + 8 * jj + 4 * h);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const int r0 = mb * 32 + 8 * jj + 4 * h;
+        const float4 l4 = *reinterpret_cast<const float4*>(L + r0);
+        const float4 d4 = *reinterpret_cast<const float4*>(DL + r0);
+        const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
         const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
         float p[4], ds[4];
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           p[ii] = __builtin_amdgcn_exp2f(fmaf(sacc[mb][4 * jj + ii], c, -lv[ii]));
-          if (key_tail && !key_ok) p[ii] = 0.f;
+          if (MASKED && (!key_ok || q0 + r0 + ii >= N)) p[ii] = 0.f;
           ds[ii] = p[ii] * (pacc[mb][4 * jj + ii] - dv[ii]);
         }
-        ppk[mb][2 * jj] = pack_bf16(p[0], p[1]);
-        ppk[mb][2 * jj + 1] = pack_bf16(p[2], p[3]);
-        dspk[mb][2 * jj] = pack_bf16(ds[0], ds[1]);
-        dspk[mb][2 * jj + 1] = pack_bf16(ds[2], ds[3]);
-        // dS^T row of this key: queries mb*32 + 8jj + 4h .. +3.
-        const u32x2 w = {dspk[mb][2 * jj], dspk[mb][2 * jj + 1]};
-        *reinterpret_cast<u32x2*>(dSt + tile_off(krow, mb * 32 + 8 * jj + 4 * h, S::DSROWB)) = w;
+        const int c2 = jj >> 1, w0 = 2 * (jj & 1);
+        pp[mb][c2][w0] = pack_bf16(p[0], p[1]);
+        pp[mb][c2][w0 + 1] = pack_bf16(p[2], p[3]);
+        dsb[mb][c2][w0] = pack_bf16(ds[0], ds[1]);
+        dsb[mb][c2][w0 + 1] = pack_bf16(ds[2], ds[3]);
       }
 
     // ---- dV^T += dO^T P and dK^T += Q^T dS (m = dim, n = key, k = query).
@@ -257,59 +221,28 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
-        const u32x4 bp = {ppk[mb][4 * c2], ppk[mb][4 * c2 + 1], ppk[mb][4 * c2 + 2], ppk[mb][4 * c2 + 3]};
-        const u32x4 bs = {dspk[mb][4 * c2], dspk[mb][4 * c2 + 1], dspk[mb][4 * c2 + 2], dspk[mb][4 * c2 + 3]};
         const int row0 = mb * 32 + c2 * 16 + 4 * h + er;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           const int col = db * 32 + dsub * 16 + 4 * qq;
-          const int o0 = tile_off(row0, col, S::ROWB), o1 = tile_off(row0 + 8, col, S::ROWB);
+          const int o0 = tile_off<S::ROWB>(row0, col), o1 = tile_off<S::ROWB>(row0 + 8, col);
           const bf16x8 adot = as_bf16x8(lds_read_tr16_b64(dOs, o0), lds_read_tr16_b64(dOs, o1));
           const bf16x8 aqt = as_bf16x8(lds_read_tr16_b64(Qs, o0), lds_read_tr16_b64(Qs, o1));
-          dvacc[db] = mfma32x32x16(adot, as_bf16x8(bp), dvacc[db]);
-          dkacc[db] = mfma32x32x16(aqt, as_bf16x8(bs), dkacc[db]);
+          dvacc[db] = mfma32x32x16(adot, as_bf16x8(pp[mb][c2]), dvacc[db]);
+          dkacc[db] = mfma32x32x16(aqt, as_bf16x8(dsb[mb][c2]), dkacc[db]);
         }
       }
 
-    __syncthreads();  // dS^T tile complete
+    wait_vmem();
+    __syncthreads();  // next step's tiles visible to all waves; this step's buffers free
+  };
 
-    // ---- dQ share of this key block, dQ = dS K: (D/32) x 2 output tiles of
-    // 32 queries x 32 dims split over the 4 waves; contraction over the 128
-    // keys. A = dS (rows = queries) and B = K (columns = dims) both come from
-    // transposing reads of key-major tiles. The accumulator holds 32
-    // consecutive dims per row in a lane column, so each atomic instruction
-    // updates two contiguous 128-byte row segments.
-#pragma unroll
-    for (int blk = wave; blk < (D / 32) * 2; blk += 4) {
-      const int db = blk >> 1, nb = blk & 1;
-      f32x16 qacc = f32x16{};
-#pragma unroll
-      for (int kc = 0; kc < BCK / 16; ++kc) {
-        const int row0 = kc * 16 + 4 * h + er;
-        const int sa = tile_off(row0, nb * 32 + dsub * 16 + 4 * qq, S::DSROWB);
-        const int sb = tile_off(row0 + 8, nb * 32 + dsub * 16 + 4 * qq, S::DSROWB);
-        const int ka = tile_off(row0, db * 32 + dsub * 16 + 4 * qq, S::ROWB);
-        const int kb8 = tile_off(row0 + 8, db * 32 + dsub * 16 + 4 * qq, S::ROWB);
-        const bf16x8 a = as_bf16x8(lds_read_tr16_b64(dSt, sa), lds_read_tr16_b64(dSt, sb));
-        const bf16x8 b = as_bf16x8(lds_read_tr16_b64(Ks, ka), lds_read_tr16_b64(Ks, kb8));
-        qacc = mfma32x32x16(a, b, qacc);
-      }
-      // Lane: dim db*32 + l32; rows: queries nb*32 + 8jj + 4h + ii.
-      float* col = dq_acc + head + db * 32 + l32;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int q = i * BRQ + nb * 32 + 8 * jj + 4 * h + ii;
-          if (q < N) unsafeAtomicAdd(col + (size_t)q * D, qacc[4 * jj + ii]);
-        }
-    }
+  // Steps that need no mask form one single-path loop; the rest follow.
+  const int nq_full = key_tail ? 0 : N / BRQ;
+  for (int i = 0; i < nq_full; ++i) step(i, BoolC<false>{});
+  for (int i = nq_full; i < nq; ++i) step(i, BoolC<true>{});
 
-    if (i + 1 < nq) lstore(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: dV = dV^T^T, dK = scale * dK^T^T (bf16, RNE). Lane: key, dims db*32 + 8jj + 4h + 0..3.
+  // ---- epilogue: dV = (dV^T)^T, dK = scale (dK^T)^T, bf16 RNE. Lane: key, dims db*32 + 8jj + 4h + 0..3.
   if (key_ok) {
     uint16_t* dvrow = dV + head + (size_t)key * D;
     uint16_t* dkrow = dK + head + (size_t)key * D;
@@ -328,11 +261,167 @@ __global__ __launch_bounds__(kThreads) void bwd_main_kernel(
   }
 }
 
+// ---------------------------------------------------------------- stage 2: dQ
+template <int D, int QB>
+struct DqShape {
+  static constexpr int BR = 4 * 32 * QB;                // queries per workgroup
+  static constexpr int ROWB = D * 2;
+  static constexpr int TILEB = BCQ * ROWB;              // one K or V step tile
+  static constexpr int KDMA = BCQ * D / 8 / kThreads;   // 16-byte DMAs per lane per K or V tile
+  static constexpr int LDSB = 4 * TILEB;                // K and V, two buffers each
+};
+
+template <int D, int QB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BWD_WAVES_PER_EU, BWD_WAVES_PER_EU)))
+void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                   const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+                   uint16_t* __restrict__ dQ, int N, int n_qblk, int total, float c, float scale) {
+  using S = DqShape<D, QB>;
+  static_assert(S::KDMA >= 1, "K/V step tile must cover every lane");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 4, gi = lane & 15;
+  const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
+  const int work = xcd_remap(blockIdx.x, total);
+  const int bh = work / n_qblk, qblk = work - bh * n_qblk;
+  const size_t head = (size_t)bh * N * D;
+  const size_t hrow = (size_t)bh * N;
+  const int qw0 = qblk * S::BR + wave * 32 * QB;
+
+  // Per query (lane column l32 of block qb): Q and dO fragments (B operands of
+  // S^T = K Q^T and dP^T = V dO^T), lse in log2 units and delta.
+  bf16x8 qf[QB][D / 16], df[QB][D / 16];
+  float lse2[QB], dl[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int q = qw0 + qb * 32 + l32;
+    const bool ok = q < N;
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      if (ok) {
+        a = *reinterpret_cast<const u32x4*>(Q + head + (size_t)q * D + cc * 16 + h * 8);
+        b = *reinterpret_cast<const u32x4*>(dO + head + (size_t)q * D + cc * 16 + h * 8);
+      }
+      qf[qb][cc] = as_bf16x8(a);
+      df[qb][cc] = as_bf16x8(b);
+    }
+    lse2[qb] = ok ? LSE[hrow + q] * kLog2e : 0.f;
+    dl[qb] = ok ? delta[hrow + q] : 0.f;
+  }
+
+  f32x16 dqacc[QB][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) dqacc[qb][db] = f32x16{};
+
+  auto dma_step = [&](int j, int buf) {
+    dma_rows<D>(K + head, j * BCQ, N, smem + buf * 2 * S::TILEB, wave, lane, S::KDMA);
+    dma_rows<D>(V + head, j * BCQ, N, smem + buf * 2 * S::TILEB + S::TILEB, wave, lane, S::KDMA);
+  };
+
+  const int ntiles = (N + BCQ - 1) / BCQ;
+  dma_step(0, 0);
+  wait_vmem();
+  __syncthreads();
+
+  // One 32-key step; MASKED (the last step when N % 32 != 0) gives keys past N probability 0.
+  auto step = [&](int j, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const int buf = j & 1;
+    if (j + 1 < ntiles) dma_step(j + 1, buf ^ 1);
+    const unsigned char* Ks = smem + buf * 2 * S::TILEB;
+    const unsigned char* Vs = Ks + S::TILEB;
+    const int kvalid = N - j * BCQ;
+
+    // ---- S^T = K Q^T and dP^T = V dO^T: 32 keys x (32*QB) queries.
+    f32x16 sacc[QB], pacc[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      sacc[qb] = f32x16{};
+      pacc[qb] = f32x16{};
+    }
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+      const int off = tile_off<S::ROWB>(l32, cc * 16 + h * 8);
+      const bf16x8 ak = as_bf16x8(lds_read_b128(Ks, off));
+      const bf16x8 av = as_bf16x8(lds_read_b128(Vs, off));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        sacc[qb] = mfma32x32x16(ak, qf[qb][cc], sacc[qb]);
+        pacc[qb] = mfma32x32x16(av, df[qb][cc], pacc[qb]);
+      }
+    }
+
+    // ---- dS^T = P^T * (dP^T - delta), P^T = exp2(S^T c - lse2); packed as the
+    // B operand of dQ^T = K^T dS^T for keys 16*c2 + (0..15).
+    u32x4 dsb[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][e], c, -lse2[qb]));
+        float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][e + 1], c, -lse2[qb]));
+        if (MASKED) {
+          const int key = 8 * (e >> 2) + 4 * h + (e & 3);
+          if (key >= kvalid) p0 = 0.f;
+          if (key + 1 >= kvalid) p1 = 0.f;
+        }
+        dsb[qb][e >> 3][(e >> 1) & 3] = pack_bf16(p0 * (pacc[qb][e] - dl[qb]), p1 * (pacc[qb][e + 1] - dl[qb]));
+      }
+
+    // ---- dQ^T += K^T dS^T (m = dim, n = query, k = key); K^T by transposing reads.
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      const int row0 = c2 * 16 + 4 * h + er;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int col = db * 32 + dsub * 16 + 4 * qq;
+        const bf16x8 a = as_bf16x8(lds_read_tr16_b64(Ks, tile_off<S::ROWB>(row0, col)),
+                                   lds_read_tr16_b64(Ks, tile_off<S::ROWB>(row0 + 8, col)));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) dqacc[qb][db] = mfma32x32x16(a, as_bf16x8(dsb[qb][c2]), dqacc[qb][db]);
+      }
+    }
+  };
+
+  const int nfull = N / BCQ;
+  for (int j = 0; j < nfull; ++j) {
+    step(j, BoolC<false>{});
+    wait_vmem();
+    __syncthreads();
+  }
+  if (nfull < ntiles) step(nfull, BoolC<true>{});
+
+  // ---- epilogue: dQ = scale (dQ^T)^T, bf16 RNE. Lane: query, dims db*32 + 8jj + 4h + 0..3.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int q = qw0 + qb * 32 + l32;
+    if (q < N) {
+      uint16_t* row = dQ + head + (size_t)q * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x16& a = dqacc[qb][db];
+          const u32x2 w = {pack_bf16(a[4 * jj] * scale, a[4 * jj + 1] * scale),
+                           pack_bf16(a[4 * jj + 2] * scale, a[4 * jj + 3] * scale)};
+          *reinterpret_cast<u32x2*>(row + db * 32 + 8 * jj + 4 * h) = w;
+        }
+    }
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 }  // namespace
 
 size_t bwd_workspace_bytes(int B, int H, int N, int d) {
-  const size_t rows = (size_t)B * H * N;
-  return align256(rows * 4) + align256(rows * (size_t)d * 4);
+  (void)d;
+  return align256((size_t)B * H * N * 4);
 }
 
 template <int D>
@@ -342,20 +431,22 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
                                      hipStream_t stream) {
   const long rows = (long)B * H * N;
   float* delta = reinterpret_cast<float*>(workspace);
-  float* dq_acc = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(workspace) + align256(rows * 4));
+  const float c = scale * kLog2e;
   if (stage == 0) {
-    const long prep_threads = rows * 8;
-    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, stream, o,
-                       dO, delta, dq_acc, rows);
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, stream, o, dO,
+                       delta, rows);
   } else if (stage == 1) {
     const int n_kblk = (N + BCK - 1) / BCK;
     const int total = n_kblk * B * H;
-    hipLaunchKernelGGL((bwd_main_kernel<D>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse, delta, dq_acc,
-                       dk, dv, N, n_kblk, total, scale * kLog2e, scale);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse, delta, dk, dv,
+                       N, n_kblk, total, c, scale);
   } else {
-    const long n8 = rows * D / 8;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, dq_acc, dq, n8,
-                       scale);
+    constexpr int QB = D == 64 ? 2 : 1;
+    constexpr int BR = DqShape<D, QB>::BR;
+    const int n_qblk = (N + BR - 1) / BR;
+    const int total = n_qblk * B * H;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, QB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse, delta, dq,
+                       N, n_qblk, total, c, scale);
   }
   return hipGetLastError();
 }

@@ -31,6 +31,12 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Compile-time boolean tag for code paths specialised on a flag.
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -63,6 +69,13 @@ __device__ __forceinline__ float sum_bf16_pair(uint32_t pk, float acc) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// NaN-propagating maxima (v_maximum3_f32 on gfx950). Unlike fmaxf they need
+// no canonicalising copy of each operand.
+__device__ __forceinline__ float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float fmax3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
+}
+
 // Value held by the lane 32 positions away (the other half of the wave).
 __device__ __forceinline__ float other_half(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -73,26 +86,34 @@ __device__ __forceinline__ float other_half(float x) {
 // max / sum of x over lanes l and l ^ 32.
 __device__ __forceinline__ float halves_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float halves_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// LDS tile swizzle. Tiles are row-major bf16 with 16-byte chunks (8 elements);
-// chunk c of row r is stored at chunk position c ^ swz(r). The XOR pattern
-// (r & 3) << 1 | (r >> 2) & 1 keeps both access patterns the kernels use
-// free of bank conflicts:
-//   * 16-byte row reads, 8 consecutive rows at one chunk: 8 distinct positions;
-//   * transposing 8-byte reads, rows r0..r0+3 (r0 % 4 == 0) x chunks c, c+1
-//     (c even): 8 distinct positions.
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// LDS tile swizzle. Tiles are row-major bf16 with 16-byte chunks (8
+// elements); chunk c of row r is stored at chunk position c ^ swz(r). gfx950
+// serves a 16-lane quarter of a ds_read_b128 from one 256-byte window of its
+// banks, so the 16 lanes of an operand read (16 consecutive rows, same
+// logical chunk) must land on 16 distinct 16-byte slots of that window:
+//   128-byte rows (two rows per window): swz(r) = (r >> 1) & 7 makes the
+//     8 rows of each parity take 8 different slots;
+//   256-byte rows (one row per window):  swz(r) = r & 15.
+// Transposing 8-byte reads (4 rows x 2 chunks per 16 lanes) stay
+// conflict-free under either pattern (measured).
+template <int ROWB>
+__device__ __forceinline__ int swz(int row) {
+  static_assert(ROWB == 128 || ROWB == 256, "tiles have 128- or 256-byte rows");
+  return ROWB == 128 ? ((row >> 1) & 7) : (row & 15);
+}
 
-// Byte offset of element (row, col) in a swizzled tile with `rowbytes` bytes per row.
-__device__ __forceinline__ int tile_off(int row, int col, int rowbytes) {
+// Byte offset of element (row, col) in a swizzled tile with ROWB bytes per row.
+template <int ROWB>
+__device__ __forceinline__ int tile_off(int row, int col) {
   const int chunk = col >> 3;
-  return row * rowbytes + ((chunk ^ swz(row)) << 4) + ((col & 7) << 1);
+  return row * ROWB + ((chunk ^ swz<ROWB>(row)) << 4) + ((col & 7) << 1);
 }
 
 __device__ __forceinline__ u32x4 lds_read_b128(const unsigned char* base, int off) {
@@ -115,6 +136,12 @@ __device__ __forceinline__ u32x2 lds_read_tr16_b64(const unsigned char* base, in
 __device__ __forceinline__ void dma16(const void* src, unsigned char* lds_base) {
   typedef __attribute__((address_space(3))) void lds_void;
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// Same with 4 bytes per lane (global_load_lds_dword): lane l writes lds_base + 4 * l.
+__device__ __forceinline__ void dma4(const void* src, unsigned char* lds_base) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 4, 0, 0);
 }
 
 // Wait until every outstanding global load of this wave (including LDS DMA) has landed.

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WA
 
   // K/V tile j -> LDS buffer `buf` by DMA. Wave w fills a contiguous run of
   // 16-byte LDS slots; the lane writing slot (row, s) fetches global chunk
-  // s ^ swz(row), which yields the swizzled layout of tile_off(). Rows past
+  // s ^ swz<S::ROWB>(row), which yields the swizzled layout of tile_off(). Rows past
   // N re-read row N-1 (finite data; their scores are masked below).
   auto dma_tile = [&](int j, int buf) {
     unsigned char* Ks = smem + buf * 2 * S::TILEB;
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WA
     for (int r = 0; r < S::DMA_PER_WAVE; ++r) {
       const int slot0 = (wave * S::DMA_PER_WAVE + r) * 64;
       const int p = slot0 + lane;
-      const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz(row);
+      const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz<S::ROWB>(row);
       const int key = min(j * kBC + row, N - 1);
       dma16(Kh + (size_t)key * D + chunk * 8, Ks + slot0 * 16);
       dma16(Vh + (size_t)key * D + chunk * 8, Vs + slot0 * 16);
@@ -118,11 +118,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WA
   wait_vmem();
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
+  // One K/V tile. MASKED (the last tile when N % 64 != 0 only) drops keys
+  // past N from the row max and gives them probability 0; full tiles carry no
+  // masking code at all.
+  auto tile = [&](int j, auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
     const int buf = j & 1;
-    if (j + 1 < ntiles) dma_tile(j + 1, buf ^ 1);
     const unsigned char* Ks = smem + buf * 2 * S::TILEB;
     const unsigned char* Vs = Ks + S::TILEB;
+    const int kvalid = N - j * kBC;
 
     // ---- S^T tile: 64 keys x (32*QB) queries, fp32 accumulate.
     f32x16 sacc[QB][2];
@@ -132,16 +136,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WA
       for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = f32x16{};
 #pragma unroll
       for (int cc = 0; cc < D / 16; ++cc) {
-        const bf16x8 a = as_bf16x8(lds_read_b128(Ks, tile_off(kb * 32 + l32, cc * 16 + h * 8, S::ROWB)));
+        const bf16x8 a = as_bf16x8(lds_read_b128(Ks, tile_off<S::ROWB>(kb * 32 + l32, cc * 16 + h * 8)));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = mfma32x32x16(a, qf[qb][cc], sacc[qb][kb]);
       }
     }
 
-    // ---- keys past N (last tile only) take no part in the row max.
-    const int kvalid = N - j * kBC;
-    const bool tail = kvalid < kBC;
-    if (tail) {
+    if (MASKED) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -162,9 +163,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WA
     bool need = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = fmaxf(sacc[qb][0][0], sacc[qb][1][0]);
+      // NaN-propagating maximum (v_maximum3_f32): no canonicalisation of the
+      // MFMA results is needed, unlike fmaxf.
+      float mx = fmax2(sacc[qb][0][0], sacc[qb][1][0]);
 #pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(sacc[qb][0][e], sacc[qb][1][e]));
+      for (int e = 1; e < 16; ++e) mx = fmax3(mx, sacc[qb][0][e], sacc[qb][1][e]);
       mx = halves_max(mx) * c;
       mnew[qb] = fmaxf(m_run[qb], mx);
       need |= mnew[qb] > m_run[qb] + kRescaleSlack;
@@ -180,8 +183,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WA
       }
     }
 
-    // ---- probabilities (bf16) and their row sums.
-    uint32_t pk[QB][2][8];
+    // ---- probabilities (bf16) and their row sums. pb[qb][kb][c2] is directly
+    // the B operand of the P V product for keys kb*32 + 16*c2 + (0..15).
+    u32x4 pb[QB][2][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float nm = -m_run[qb];
@@ -191,13 +195,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WA
         for (int e = 0; e < 16; e += 2) {
           float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][e], c, nm));
           float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][e + 1], c, nm));
-          if (tail) {
+          if (MASKED) {
             const int key = kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
             if (key >= kvalid) p0 = 0.f;
             if (key + 1 >= kvalid) p1 = 0.f;
           }
-          pk[qb][kb][e >> 1] = pack_bf16(p0, p1);
-          l_run[qb] = sum_bf16_pair(pk[qb][kb][e >> 1], l_run[qb]);
+          const uint32_t w = pack_bf16(p0, p1);
+          pb[qb][kb][e >> 3][(e >> 1) & 3] = w;
+          l_run[qb] = sum_bf16_pair(w, l_run[qb]);
         }
     }
 
@@ -212,20 +217,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WA
         for (int db = 0; db < D / 32; ++db) {
           const int row0 = kb * 32 + c2 * 16 + 4 * h + er;
           const int col = db * 32 + dsub * 16 + 4 * qq;
-          const u32x2 lo = lds_read_tr16_b64(Vs, tile_off(row0, col, S::ROWB));
-          const u32x2 hi = lds_read_tr16_b64(Vs, tile_off(row0 + 8, col, S::ROWB));
+          const u32x2 lo = lds_read_tr16_b64(Vs, tile_off<S::ROWB>(row0, col));
+          const u32x2 hi = lds_read_tr16_b64(Vs, tile_off<S::ROWB>(row0 + 8, col));
           const bf16x8 a = as_bf16x8(lo, hi);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const u32x4 bv = {pk[qb][kb][4 * c2], pk[qb][kb][4 * c2 + 1], pk[qb][kb][4 * c2 + 2],
-                              pk[qb][kb][4 * c2 + 3]};
-            oacc[qb][db] = mfma32x32x16(a, as_bf16x8(bv), oacc[qb][db]);
-          }
+          for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32x32x16(a, as_bf16x8(pb[qb][kb][c2]), oacc[qb][db]);
         }
+  };
 
+  // Full tiles in one single-path loop, then the partial last tile (if any).
+  const int nfull = N / kBC;  // tiles whose 64 keys are all < N
+  for (int j = 0; j < nfull; ++j) {
+    if (j + 1 < ntiles) dma_tile(j + 1, (j & 1) ^ 1);
+    tile(j, BoolC<false>{});
     wait_vmem();
     __syncthreads();
   }
+  if (nfull < ntiles) tile(nfull, BoolC<true>{});
 
   // ---- epilogue: O = O^T / l (bf16, RNE), lse = ln 2 * (m + log2 l).
 #pragma unroll
