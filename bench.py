@@ -62,6 +62,33 @@ def time_launches(fn, reps: int) -> float:
     return start.elapsed_time(end) / reps
 
 
+def sources_sha256() -> str:
+    """sha256 over the library's kernel sources (csrc/*.hip and *.h, sorted by path)."""
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "tiled_attention_08_amd", "csrc")
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of ``kernel`` from the committed FETCH_SIZE / WRITE_SIZE record, or None
+    if there is none for this workload or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_sha256():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else int(k["traffic_bytes"])
+
+
 def cpu_baseline(wid: int, seed: int, budget_s: float) -> dict:
     """The fp64 oracle (forward + backward) on whole heads of the workload, for about ``budget_s`` seconds."""
     import numpy as np
@@ -195,15 +222,16 @@ def main(argv=None) -> int:
     if dominant in kflops:
         achieved = kflops[dominant] / (kernels[dominant] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": measured_traffic(w.name, kname_full[dominant]),
                     "kernel": kname_full[dominant], "avg_ms": round(kernels[dominant], 5)}
     else:  # the HBM-bound delta kernel dominates (tiny workloads only)
         rows = B * H * N
         nbytes = rows * d * 2 * 2 + rows * 4
         achieved = nbytes / (kernels[dominant] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "kernel": kname_full[dominant],
-                    "avg_ms": round(kernels[dominant], 5)}
+                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name, kname_full[dominant]),
+                    "kernel": kname_full[dominant], "avg_ms": round(kernels[dominant], 5)}
 
     record = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
