@@ -105,16 +105,16 @@ def cpu_baseline(wid: int, seed: int, budget_s: float) -> dict:
     order = [(b, h) for b in range(w.B) for h in range(w.H)]
     while heads < len(order) and (heads == 0 or elapsed * (heads + 1) / heads <= budget_s):
         b, h = order[heads]
-        Q, K, V, DO = (x.f64(n, (b, h)) for n in ("q", "k", "v", "do"))
+        Q, K, V = (x.f64(n, (b, h)) for n in ("q", "k", "v"))
         t0 = time.perf_counter()
         attention_fwd(Q, K, V, x.scale)
         if "bwd" in w.passes:
-            attention_bwd(Q, K, V, DO, x.scale)
+            attention_bwd(Q, K, V, x.f64("do", (b, h)), x.scale)
         elapsed += time.perf_counter() - t0
         heads += 1
     flops = (fwd_flops(1, heads, w.N, w.d) + (bwd_flops(1, heads, w.N, w.d) if "bwd" in w.passes else 0.0))
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.H} heads of the same workload (fwd+bwd, fp64, full N x N per head), "
+            "sample": f"{heads} of {w.B * w.H} heads of the same workload ({'+'.join(w.passes)}, fp64, full N x N per head), "
                       f"{elapsed:.1f} s", "seconds": round(elapsed, 3)}
 
 
@@ -123,8 +123,8 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=3, choices=(2, 3, 5),
-                    help="workload with a backward pass (3 = long sequence, the headline)")
+    ap.add_argument("--workload", type=int, default=3, choices=(2, 3, 4, 5),
+                    help="3 = long sequence, the headline; 4 runs the forward only (its workload has no backward)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--kernel-reps", type=int, default=20, help="launches per kernel for the roofline timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -164,22 +164,26 @@ def main(argv=None) -> int:
     def up(name):
         return torch.from_numpy(np.ascontiguousarray(x.raw[name]).view(np.int16)).view(torch.bfloat16).cuda()
 
-    q, k, v, do = up("q"), up("k"), up("v"), up("do")
+    with_bwd = "bwd" in w.passes
+    q, k, v = up("q"), up("k"), up("v")
+    do = up("do") if with_bwd else None
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = attn.workspace_for(q)
+    if with_bwd:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = attn.workspace_for(q)
     scale = x.scale
     stream = torch.cuda.current_stream()
 
     def step():
         attn.attn_fwd(q, k, v, o, lse, scale, stream)
-        attn.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream)
+        if with_bwd:
+            attn.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    for t in (o, lse, dq, dk, dv):
+    for t in (o, lse) + ((dq, dk, dv) if with_bwd else ()):
         if not torch.isfinite(t.float()).all():
             log("[bench] non-finite output")
             return 1
@@ -194,7 +198,7 @@ def main(argv=None) -> int:
     t_end.record(stream)
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
-    flops = fwd_flops(B, H, N, d) + bwd_flops(B, H, N, d)
+    flops = fwd_flops(B, H, N, d) + (bwd_flops(B, H, N, d) if with_bwd else 0.0)
     value = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {ms:.3f} ms/step, {value:.1f} TFLOP/s")
 
@@ -203,12 +207,10 @@ def main(argv=None) -> int:
     def stage(i):
         return lambda: attn.attn_bwd_stage(i, q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream)
 
-    kernels = {
-        "fwd": time_launches(lambda: attn.attn_fwd(q, k, v, o, lse, scale, stream), reps),
-        "bwd_prep": time_launches(stage(0), reps),
-        "bwd_dkdv": time_launches(stage(1), reps),
-        "bwd_dq": time_launches(stage(2), reps),
-    }
+    kernels = {"fwd": time_launches(lambda: attn.attn_fwd(q, k, v, o, lse, scale, stream), reps)}
+    if with_bwd:
+        kernels.update({"bwd_prep": time_launches(stage(0), reps), "bwd_dkdv": time_launches(stage(1), reps),
+                        "bwd_dq": time_launches(stage(2), reps)})
     log("[bench] kernel ms: " + ", ".join(f"{kname} {t:.4f}" for kname, t in kernels.items()))
     # Algorithmic FLOPs per launch. The dK/dV kernel performs the S recompute,
     # dP, dV and dK products (8 B H N^2 d). The dQ kernel repeats S and dP to
@@ -237,7 +239,7 @@ def main(argv=None) -> int:
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d_k": d, "passes": "fwd+bwd",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d_k": d, "passes": "+".join(w.passes),
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "frac_of_bf16_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "kernel_ms": {kname: round(t, 5) for kname, t in kernels.items()},

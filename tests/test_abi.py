@@ -107,9 +107,9 @@ def test_backward_rejections(L):
 
 
 def test_workspace_size(L):
-    assert L.attn_bwd_workspace_bytes(8, 16, 4096, 64) == 8 * 16 * 4096 * 4
-    assert L.attn_bwd_workspace_bytes(1, 1, 1, 64) == 256
-    assert L.attn_bwd_workspace_bytes(1, 3, 100, 128) == 1280
+    assert L.attn_bwd_workspace_bytes(8, 16, 4096, 64) == 2 * 8 * 16 * 4096 * 4
+    assert L.attn_bwd_workspace_bytes(1, 1, 1, 64) == 512
+    assert L.attn_bwd_workspace_bytes(1, 3, 100, 128) == 2560
     assert L.attn_bwd_workspace_bytes(1, 1, 8, 96) == 0
     assert L.attn_bwd_workspace_bytes(0, 1, 8, 64) == 0
 

@@ -12,7 +12,7 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Three launches on one stream, deterministic (no atomics):
-//   stage 0  bwd_prep_kernel   delta = rowsum(dO * O) in fp32 (the workspace);
+//   stage 0  bwd_prep_kernel   workspace <- lse * log2(e) and delta = rowsum(dO * O), fp32;
 //   stage 1  bwd_dkdv_kernel   one workgroup per (head, 128 keys), looping over
 //                              64-query steps: rebuilds S and P, accumulates
 //                              dV and dK in registers. A key is a lane column
@@ -48,6 +48,7 @@ constexpr int BCQ = 32;                  // dQ kernel: keys per step
 // 8 lanes per row; each lane covers D/8 consecutive elements.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
+                                                       const float* __restrict__ LSE, float* __restrict__ lse2,
                                                        float* __restrict__ delta, long rows) {
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
   const long row = gid >> 3;
@@ -71,7 +72,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
   s += __shfl_xor(s, 1);
   s += __shfl_xor(s, 2);
   s += __shfl_xor(s, 4);
-  if (row < rows && part == 0) delta[row] = s;
+  if (row < rows && part == 0) {
+    delta[row] = s;
+    lse2[row] = LSE[row] * kLog2e;
+  }
 }
 
 // DMA a row-major [rows x D] block (rows row0.., clamped to N-1) into a
@@ -100,7 +104,7 @@ struct DkdvShape {
   static constexpr int QDMA = BRQ * D / 8 / kThreads;   // 16-byte DMAs per lane per Q or dO tile
   static constexpr int OFF_Q = 0;
   static constexpr int OFF_DO = OFF_Q + 2 * QTILEB;
-  static constexpr int OFF_L = OFF_DO + 2 * QTILEB;     // lse, two buffers
+  static constexpr int OFF_L = OFF_DO + 2 * QTILEB;     // lse * log2(e), two buffers
   static constexpr int OFF_DL = OFF_L + 2 * BRQ * 4;    // delta, two buffers
   static constexpr int LDSB = OFF_DL + 2 * BRQ * 4;
 };
@@ -111,7 +115,7 @@ template <int D>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? BWD_WAVES_PER_EU : 1, D == 64 ? BWD_WAVES_PER_EU : 1)))
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+                     const uint16_t* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ delta,
                      uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk, int total, float c,
                      float scale) {
   using S = DkdvShape<D>;
@@ -147,7 +151,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     dma_rows<D>(Q + head, q0, N, smem + S::OFF_Q + buf * S::QTILEB, wave, lane, S::QDMA);
     dma_rows<D>(dO + head, q0, N, smem + S::OFF_DO + buf * S::QTILEB, wave, lane, S::QDMA);
     const size_t r = hrow + min(q0 + lane, N - 1);
-    if (wave == 0) dma4(LSE + r, smem + S::OFF_L + buf * BRQ * 4);
+    if (wave == 0) dma4(lse2 + r, smem + S::OFF_L + buf * BRQ * 4);
     if (wave == 1) dma4(delta + r, smem + S::OFF_DL + buf * BRQ * 4);
   };
 
@@ -166,9 +170,11 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // One 64-query step. MASKED (the last step when N % 64 != 0, and every step
   // of the last key block when N % 128 != 0) gives probability 0 to queries
   // and keys past N; other steps carry no masking code.
-  auto step = [&](int i, auto masked) {
+  // The buffer index is a compile-time constant (BUF == i % 2) so that every
+  // LDS offset in the step folds into an immediate.
+  auto step = [&](int i, auto masked, auto bufc) {
     constexpr bool MASKED = decltype(masked)::value;
-    const int buf = i & 1;
+    constexpr int buf = decltype(bufc)::value;
     const int q0 = i * BRQ;
     if (i + 1 < nq) dma_step(i + 1, buf ^ 1);
     const unsigned char* Qs = smem + S::OFF_Q + buf * S::QTILEB;
@@ -200,7 +206,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         const int r0 = mb * 32 + 8 * jj + 4 * h;
         const float4 l4 = *reinterpret_cast<const float4*>(L + r0);
         const float4 d4 = *reinterpret_cast<const float4*>(DL + r0);
-        const float lv[4] = {l4.x * kLog2e, l4.y * kLog2e, l4.z * kLog2e, l4.w * kLog2e};
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
         float p[4], ds[4];
 #pragma unroll
@@ -239,8 +245,21 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
   // Steps that need no mask form one single-path loop; the rest follow.
   const int nq_full = key_tail ? 0 : N / BRQ;
-  for (int i = 0; i < nq_full; ++i) step(i, BoolC<false>{});
-  for (int i = nq_full; i < nq; ++i) step(i, BoolC<true>{});
+  int i = 0;
+  for (; i + 1 < nq_full; i += 2) {
+    step(i, BoolC<false>{}, IntC<0>{});
+    step(i + 1, BoolC<false>{}, IntC<1>{});
+  }
+  if (i < nq_full) {
+    step(i, BoolC<false>{}, IntC<0>{});
+    ++i;
+  }
+  for (; i < nq; ++i) {
+    if (i & 1)
+      step(i, BoolC<true>{}, IntC<1>{});
+    else
+      step(i, BoolC<true>{}, IntC<0>{});
+  }
 
   // ---- epilogue: dV = (dV^T)^T, dK = scale (dK^T)^T, bf16 RNE. Lane: key, dims db*32 + 8jj + 4h + 0..3.
   if (key_ok) {
@@ -274,7 +293,7 @@ struct DqShape {
 template <int D, int QB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BWD_WAVES_PER_EU, BWD_WAVES_PER_EU)))
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                   const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+                   const uint16_t* __restrict__ dO, const float* __restrict__ lse2_in, const float* __restrict__ delta,
                    uint16_t* __restrict__ dQ, int N, int n_qblk, int total, float c, float scale) {
   using S = DqShape<D, QB>;
   static_assert(S::KDMA >= 1, "K/V step tile must cover every lane");
@@ -308,7 +327,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       qf[qb][cc] = as_bf16x8(a);
       df[qb][cc] = as_bf16x8(b);
     }
-    lse2[qb] = ok ? LSE[hrow + q] * kLog2e : 0.f;
+    lse2[qb] = ok ? lse2_in[hrow + q] : 0.f;
     dl[qb] = ok ? delta[hrow + q] : 0.f;
   }
 
@@ -419,9 +438,10 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+// Workspace: lse * log2(e), then delta; fp32 [B*H*N] each, 256-byte aligned.
 size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   (void)d;
-  return align256((size_t)B * H * N * 4);
+  return 2 * align256((size_t)B * H * N * 4);
 }
 
 template <int D>
@@ -430,22 +450,23 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
                                      uint16_t* dk, uint16_t* dv, int B, int H, int N, float scale, void* workspace,
                                      hipStream_t stream) {
   const long rows = (long)B * H * N;
-  float* delta = reinterpret_cast<float*>(workspace);
+  float* lse2 = reinterpret_cast<float*>(workspace);
+  float* delta = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(workspace) + align256(rows * 4));
   const float c = scale * kLog2e;
   if (stage == 0) {
     hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, stream, o, dO,
-                       delta, rows);
+                       lse, lse2, delta, rows);
   } else if (stage == 1) {
     const int n_kblk = (N + BCK - 1) / BCK;
     const int total = n_kblk * B * H;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse, delta, dk, dv,
-                       N, n_kblk, total, c, scale);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, delta, dk,
+                       dv, N, n_kblk, total, c, scale);
   } else {
     constexpr int QB = D == 64 ? 2 : 1;
     constexpr int BR = DqShape<D, QB>::BR;
     const int n_qblk = (N + BR - 1) / BR;
     const int total = n_qblk * B * H;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, QB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse, delta, dq,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, QB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, delta, dq,
                        N, n_qblk, total, c, scale);
   }
   return hipGetLastError();

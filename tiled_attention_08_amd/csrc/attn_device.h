@@ -37,6 +37,11 @@ struct BoolC {
   static constexpr bool value = B;
 };
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
