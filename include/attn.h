@@ -76,7 +76,7 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
 
 /*
  * Bytes of device workspace attn_bwd needs for this shape: lse * log2(e) and
- * delta_i = <dO_i, O_i>, float32 [B,H,N] each (each rounded up to 256 bytes).
+ * -delta_i = -<dO_i, O_i>, float32 [B,H,N] each (each rounded up to 256 bytes).
  * Returns 0 for arguments attn_bwd would reject.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int N, int d_k);
@@ -104,7 +104,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  * One stage of attn_bwd, same arguments plus `stage`; attn_bwd is exactly
  * stages 0, 1, 2 in order on `stream`. For callers that schedule or time the
  * stages separately:
- *   stage 0  prep:  workspace <- lse * log2(e) and delta_i = <dO_i, O_i>
+ *   stage 0  prep:  workspace <- lse * log2(e) and -delta_i = -<dO_i, O_i>
  *                   (float32); reads o, dO, lse.
  *   stage 1  dK/dV: rebuilds P from q, k, lse and writes dk, dv; needs the
  *                   workspace of stage 0.

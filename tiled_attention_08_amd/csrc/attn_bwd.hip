@@ -12,7 +12,7 @@
 //   dQ = scale dS K,  dK = scale dS^T Q.
 //
 // Three launches on one stream, deterministic (no atomics):
-//   stage 0  bwd_prep_kernel   workspace <- lse * log2(e) and delta = rowsum(dO * O), fp32;
+//   stage 0  bwd_prep_kernel   workspace <- lse * log2(e) and -delta = -rowsum(dO * O), fp32;
 //   stage 1  bwd_dkdv_kernel   one workgroup per (head, 128 keys), looping over
 //                              64-query steps: rebuilds S and P, accumulates
 //                              dV and dK in registers. A key is a lane column
@@ -37,7 +37,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int BCK = kBwdKeysPerBlock;    // dK/dV kernel: keys per workgroup (32 per wave)
-constexpr int BRQ = kBwdQueriesPerStep;  // dK/dV kernel: queries per step
+#ifndef BWD_MB
+#define BWD_MB 2  // dK/dV kernel: 32-query blocks per step
+#endif
 constexpr int BCQ = 32;                  // dQ kernel: keys per step
 
 #ifndef BWD_WAVES_PER_EU
@@ -49,7 +51,7 @@ constexpr int BCQ = 32;                  // dQ kernel: keys per step
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
                                                        const float* __restrict__ LSE, float* __restrict__ lse2,
-                                                       float* __restrict__ delta, long rows) {
+                                                       float* __restrict__ ndelta, long rows) {
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
   const long row = gid >> 3;
   const int part = (int)(gid & 7);
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
   s += __shfl_xor(s, 2);
   s += __shfl_xor(s, 4);
   if (row < rows && part == 0) {
-    delta[row] = s;
+    ndelta[row] = -s;
     lse2[row] = LSE[row] * kLog2e;
   }
 }
@@ -97,28 +99,31 @@ __device__ __forceinline__ void dma_rows(const uint16_t* head_src, int row0, int
 }
 
 // ---------------------------------------------------------------- stage 1: dK, dV
-template <int D>
+template <int D, int MB>
 struct DkdvShape {
+  static constexpr int BRQ = 32 * MB;                   // queries per step
+  static constexpr int LROWS = BRQ < 64 ? 64 : BRQ;     // lse / -delta entries per buffer (one per DMA lane)
   static constexpr int ROWB = D * 2;
   static constexpr int QTILEB = BRQ * ROWB;             // one Q or dO step tile
   static constexpr int QDMA = BRQ * D / 8 / kThreads;   // 16-byte DMAs per lane per Q or dO tile
   static constexpr int OFF_Q = 0;
   static constexpr int OFF_DO = OFF_Q + 2 * QTILEB;
   static constexpr int OFF_L = OFF_DO + 2 * QTILEB;     // lse * log2(e), two buffers
-  static constexpr int OFF_DL = OFF_L + 2 * BRQ * 4;    // delta, two buffers
-  static constexpr int LDSB = OFF_DL + 2 * BRQ * 4;
+  static constexpr int OFF_DL = OFF_L + 2 * LROWS * 4;  // -delta, two buffers
+  static constexpr int LDSB = OFF_DL + 2 * LROWS * 4;
 };
 
 // d_k = 128 needs more than 256 registers per lane (its dK and dV
 // accumulators alone take 128): one wave per SIMD there.
-template <int D>
+template <int D, int MB>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? BWD_WAVES_PER_EU : 1, D == 64 ? BWD_WAVES_PER_EU : 1)))
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                     const uint16_t* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ delta,
+                     const uint16_t* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ ndelta,
                      uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk, int total, float c,
                      float scale) {
-  using S = DkdvShape<D>;
+  using S = DkdvShape<D, MB>;
+  constexpr int BRQ = S::BRQ;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -151,8 +156,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     dma_rows<D>(Q + head, q0, N, smem + S::OFF_Q + buf * S::QTILEB, wave, lane, S::QDMA);
     dma_rows<D>(dO + head, q0, N, smem + S::OFF_DO + buf * S::QTILEB, wave, lane, S::QDMA);
     const size_t r = hrow + min(q0 + lane, N - 1);
-    if (wave == 0) dma4(lse2 + r, smem + S::OFF_L + buf * BRQ * 4);
-    if (wave == 1) dma4(delta + r, smem + S::OFF_DL + buf * BRQ * 4);
+    if (wave == 0) dma4(lse2 + r, smem + S::OFF_L + buf * S::LROWS * 4);
+    if (wave == 1) dma4(ndelta + r, smem + S::OFF_DL + buf * S::LROWS * 4);
   };
 
   f32x16 dvacc[D / 32], dkacc[D / 32];
@@ -179,15 +184,25 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     if (i + 1 < nq) dma_step(i + 1, buf ^ 1);
     const unsigned char* Qs = smem + S::OFF_Q + buf * S::QTILEB;
     const unsigned char* dOs = smem + S::OFF_DO + buf * S::QTILEB;
-    const float* L = reinterpret_cast<const float*>(smem + S::OFF_L + buf * BRQ * 4);
-    const float* DL = reinterpret_cast<const float*>(smem + S::OFF_DL + buf * BRQ * 4);
+    const float* L = reinterpret_cast<const float*>(smem + S::OFF_L + buf * S::LROWS * 4);
+    const float* DL = reinterpret_cast<const float*>(smem + S::OFF_DL + buf * S::LROWS * 4);
 
-    // ---- S = Q K^T and dP = dO V^T for 64 queries x this lane's key.
-    f32x16 sacc[2], pacc[2];
+    // ---- S = Q K^T and dP - delta = dO V^T - delta for BRQ queries x this
+    // lane's key. The dP accumulator starts from -delta of its rows (rows
+    // 8j + 4h + i, read as four float4 in accumulator order), so no separate
+    // subtraction is needed.
+    f32x16 sacc[MB], pacc[MB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       sacc[mb] = f32x16{};
-      pacc[mb] = f32x16{};
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float4 d4 = *reinterpret_cast<const float4*>(DL + mb * 32 + 8 * jj + 4 * h);
+        pacc[mb][4 * jj] = d4.x;
+        pacc[mb][4 * jj + 1] = d4.y;
+        pacc[mb][4 * jj + 2] = d4.z;
+        pacc[mb][4 * jj + 3] = d4.w;
+      }
 #pragma unroll
       for (int cc = 0; cc < D / 16; ++cc) {
         const int off = tile_off<S::ROWB>(mb * 32 + l32, cc * 16 + h * 8);
@@ -198,22 +213,20 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
     // ---- P = exp2(S * scale * log2 e - lse * log2 e), dS = P * (dP - delta).
     // pp[mb][c2] / dsb[mb][c2]: B operands (bf16 P and dS) for queries mb*32 + 16*c2 + (0..15).
-    u32x4 pp[2][2], dsb[2][2];
+    u32x4 pp[MB][2], dsb[MB][2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r0 = mb * 32 + 8 * jj + 4 * h;
         const float4 l4 = *reinterpret_cast<const float4*>(L + r0);
-        const float4 d4 = *reinterpret_cast<const float4*>(DL + r0);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
         float p[4], ds[4];
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           p[ii] = __builtin_amdgcn_exp2f(fmaf(sacc[mb][4 * jj + ii], c, -lv[ii]));
           if (MASKED && (!key_ok || q0 + r0 + ii >= N)) p[ii] = 0.f;
-          ds[ii] = p[ii] * (pacc[mb][4 * jj + ii] - dv[ii]);
+          ds[ii] = p[ii] * pacc[mb][4 * jj + ii];
         }
         const int c2 = jj >> 1, w0 = 2 * (jj & 1);
         pp[mb][c2][w0] = pack_bf16(p[0], p[1]);
@@ -224,7 +237,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
     // ---- dV^T += dO^T P and dK^T += Q^T dS (m = dim, n = key, k = query).
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         const int row0 = mb * 32 + c2 * 16 + 4 * h + er;
@@ -293,7 +306,7 @@ struct DqShape {
 template <int D, int QB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BWD_WAVES_PER_EU, BWD_WAVES_PER_EU)))
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                   const uint16_t* __restrict__ dO, const float* __restrict__ lse2_in, const float* __restrict__ delta,
+                   const uint16_t* __restrict__ dO, const float* __restrict__ lse2_in, const float* __restrict__ ndelta,
                    uint16_t* __restrict__ dQ, int N, int n_qblk, int total, float c, float scale) {
   using S = DqShape<D, QB>;
   static_assert(S::KDMA >= 1, "K/V step tile must cover every lane");
@@ -310,7 +323,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int qw0 = qblk * S::BR + wave * 32 * QB;
 
   // Per query (lane column l32 of block qb): Q and dO fragments (B operands of
-  // S^T = K Q^T and dP^T = V dO^T), lse in log2 units and delta.
+  // S^T = K Q^T and dP^T = V dO^T), lse in log2 units and -delta.
   bf16x8 qf[QB][D / 16], df[QB][D / 16];
   float lse2[QB], dl[QB];
 #pragma unroll
@@ -328,7 +341,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       df[qb][cc] = as_bf16x8(b);
     }
     lse2[qb] = ok ? lse2_in[hrow + q] : 0.f;
-    dl[qb] = ok ? delta[hrow + q] : 0.f;
+    dl[qb] = ok ? ndelta[hrow + q] : 0.f;
   }
 
   f32x16 dqacc[QB][D / 32];
@@ -389,7 +402,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
           if (key >= kvalid) p0 = 0.f;
           if (key + 1 >= kvalid) p1 = 0.f;
         }
-        dsb[qb][e >> 3][(e >> 1) & 3] = pack_bf16(p0 * (pacc[qb][e] - dl[qb]), p1 * (pacc[qb][e + 1] - dl[qb]));
+        dsb[qb][e >> 3][(e >> 1) & 3] = pack_bf16(p0 * (pacc[qb][e] + dl[qb]), p1 * (pacc[qb][e + 1] + dl[qb]));
       }
 
     // ---- dQ^T += K^T dS^T (m = dim, n = query, k = key); K^T by transposing reads.
@@ -438,7 +451,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-// Workspace: lse * log2(e), then delta; fp32 [B*H*N] each, 256-byte aligned.
+// Workspace: lse * log2(e), then -delta; fp32 [B*H*N] each, 256-byte aligned.
 size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   (void)d;
   return 2 * align256((size_t)B * H * N * 4);
@@ -451,22 +464,22 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
                                      hipStream_t stream) {
   const long rows = (long)B * H * N;
   float* lse2 = reinterpret_cast<float*>(workspace);
-  float* delta = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(workspace) + align256(rows * 4));
+  float* ndelta = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(workspace) + align256(rows * 4));
   const float c = scale * kLog2e;
   if (stage == 0) {
     hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, stream, o, dO,
-                       lse, lse2, delta, rows);
+                       lse, lse2, ndelta, rows);
   } else if (stage == 1) {
     const int n_kblk = (N + BCK - 1) / BCK;
     const int total = n_kblk * B * H;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, delta, dk,
-                       dv, N, n_kblk, total, c, scale);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BWD_MB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, ndelta,
+                       dk, dv, N, n_kblk, total, c, scale);
   } else {
     constexpr int QB = D == 64 ? 2 : 1;
     constexpr int BR = DqShape<D, QB>::BR;
     const int n_qblk = (N + BR - 1) / BR;
     const int total = n_qblk * B * H;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, QB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, delta, dq,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, QB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, ndelta, dq,
                        N, n_qblk, total, c, scale);
   }
   return hipGetLastError();

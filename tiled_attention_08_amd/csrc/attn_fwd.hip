@@ -17,9 +17,8 @@
 //   S^T  : A = K tile rows (LDS, 16-byte reads), B = Q fragment (registers)
 //   O^T  : A = V^T (LDS, transposing 8-byte reads of the row-major V tile),
 //          B = P^T (registers, bf16)
-// K/V tiles of 64 keys are double-buffered in LDS and filled by direct
-// global->LDS DMA (no staging registers): tile j+1 is in flight while tile j
-// is computed.
+// K/V tiles go HBM -> LDS by direct DMA (no staging registers) into a ring
+// of NS slots, so the next NS-1 tiles are in flight while one is computed.
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -29,38 +28,64 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBC = 64;               // keys per K/V tile
-constexpr float kRescaleSlack = 8.0f; // log2 units a row max may grow before O, l are rescaled
+constexpr float kRescaleSlack = 8.0f;  // log2 units a row max may grow before O, l are rescaled
 
+// Launch shape per head dim: 32-query blocks per wave (QB), 32-key blocks per
+// K/V tile (KB) and K/V tiles in flight (NS, the LDS ring depth). Two waves
+// share each SIMD (at most 256 registers per lane).
 #ifndef FWD_WAVES_PER_EU
-#define FWD_WAVES_PER_EU 2  // two waves per SIMD: one wave's softmax overlaps the other's MFMAs
+#define FWD_WAVES_PER_EU 2
 #endif
 #ifndef FWD_QB64
-#define FWD_QB64 2          // 32-query blocks per wave at d_k = 64
+#define FWD_QB64 2
+#endif
+#ifndef FWD_KB64
+#define FWD_KB64 2
+#endif
+#ifndef FWD_NS64
+#define FWD_NS64 2
 #endif
 #ifndef FWD_QB128
-#define FWD_QB128 1         // 32-query blocks per wave at d_k = 128
+#define FWD_QB128 1
+#endif
+#ifndef FWD_KB128
+#define FWD_KB128 2
+#endif
+#ifndef FWD_NS128
+#define FWD_NS128 2
 #endif
 
-template <int D, int QB>
+template <int D, int QB, int KB, int NS>
 struct FwdShape {
-  static constexpr int BR = kWaves * 32 * QB;         // query rows per workgroup
-  static constexpr int ROWB = D * 2;                  // bytes per K/V row
-  static constexpr int TILEB = kBC * ROWB;            // bytes per K or V tile
-  static constexpr int DMA_PER_WAVE = kBC * D / 8 / kThreads;  // 16-byte DMA instructions per wave per tile
-  static constexpr int LDSB = 4 * TILEB;              // K and V, two buffers each
+  static constexpr int BR = kWaves * 32 * QB;                 // query rows per workgroup
+  static constexpr int BC = 32 * KB;                          // keys per K/V tile
+  static constexpr int ROWB = D * 2;                          // bytes per K/V row
+  static constexpr int TILEB = BC * ROWB;                     // bytes per K or V tile
+  static constexpr int DMA_PER_WAVE = BC * D / 8 / kThreads;  // 16-byte DMA instructions per wave per tensor
+  static constexpr int LDSB = NS * 2 * TILEB;                 // ring of NS (K, V) tile pairs
+  static_assert(DMA_PER_WAVE >= 1, "every lane takes part in each tile DMA");
 };
 
-template <int D, int QB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WAVES_PER_EU, FWD_WAVES_PER_EU))) void fwd_bf16_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qblk, int total, float c,
-    uint32_t qsign) {
-  using S = FwdShape<D, QB>;
+// s_waitcnt encoding (gfx9): wait until at most N vector-memory operations of
+// this wave are outstanding; LGKM and export counters are left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmem_below() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+template <int D, int QB, int KB, int NS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WAVES_PER_EU, FWD_WAVES_PER_EU)))
+void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                     uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qblk, int total, float c,
+                     uint32_t qsign) {
+  using S = FwdShape<D, QB, KB, NS>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 4, gi = lane & 15;
+  const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
   const int work = xcd_remap(blockIdx.x, total);
   const int bh = work / n_qblk, qblk = work - bh * n_qblk;
   const size_t head = (size_t)bh * N * D;
@@ -94,44 +119,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WA
     for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
   }
 
-  const int ntiles = (N + kBC - 1) / kBC;
+  const int ntiles = (N + S::BC - 1) / S::BC;
 
-  // K/V tile j -> LDS buffer `buf` by DMA. Wave w fills a contiguous run of
+  // K/V tile j -> ring slot j % NS by DMA. Wave w fills a contiguous run of
   // 16-byte LDS slots; the lane writing slot (row, s) fetches global chunk
-  // s ^ swz<S::ROWB>(row), which yields the swizzled layout of tile_off(). Rows past
-  // N re-read row N-1 (finite data; their scores are masked below).
-  auto dma_tile = [&](int j, int buf) {
-    unsigned char* Ks = smem + buf * 2 * S::TILEB;
+  // s ^ swz(row), which yields the swizzled layout tile_off() addresses.
+  // Rows past N re-read row N-1 (finite data; their scores are masked below).
+  auto dma_tile = [&](int j) {
+    unsigned char* Ks = smem + (j % NS) * 2 * S::TILEB;
     unsigned char* Vs = Ks + S::TILEB;
 #pragma unroll
     for (int r = 0; r < S::DMA_PER_WAVE; ++r) {
       const int slot0 = (wave * S::DMA_PER_WAVE + r) * 64;
       const int p = slot0 + lane;
       const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz<S::ROWB>(row);
-      const int key = min(j * kBC + row, N - 1);
+      const int key = min(j * S::BC + row, N - 1);
       dma16(Kh + (size_t)key * D + chunk * 8, Ks + slot0 * 16);
       dma16(Vh + (size_t)key * D + chunk * 8, Vs + slot0 * 16);
     }
   };
+  // Wait until tile j has landed, given that tiles up to min(j + NS - 2, ntiles - 1)
+  // have been issued after it (each tile is 2 * DMA_PER_WAVE instructions per wave).
+  auto wait_tile = [&](int j) {
+    constexpr int PER = 2 * S::DMA_PER_WAVE;
+    const int after = min(j + NS - 2, ntiles - 1) - j;
+    if (NS >= 4 && after >= 2)
+      wait_vmem_below<(NS >= 4 ? 2 * PER : 0)>();
+    else if (NS >= 3 && after >= 1)
+      wait_vmem_below<(NS >= 3 ? PER : 0)>();
+    else
+      wait_vmem_below<0>();
+  };
 
-  dma_tile(0, 0);
-  wait_vmem();
+  for (int j = 0; j < NS - 1 && j < ntiles; ++j) dma_tile(j);
+  wait_tile(0);
   __syncthreads();
 
-  // One K/V tile. MASKED (the last tile when N % 64 != 0 only) drops keys
-  // past N from the row max and gives them probability 0; full tiles carry no
-  // masking code at all.
+  // One K/V tile. MASKED (the last tile when N is not a multiple of the tile)
+  // drops keys past N from the row max and gives them probability 0; full
+  // tiles carry no masking code at all.
   auto tile = [&](int j, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
-    const int buf = j & 1;
-    const unsigned char* Ks = smem + buf * 2 * S::TILEB;
+    const unsigned char* Ks = smem + (j % NS) * 2 * S::TILEB;
     const unsigned char* Vs = Ks + S::TILEB;
-    const int kvalid = N - j * kBC;
+    const int kvalid = N - j * S::BC;
 
-    // ---- S^T tile: 64 keys x (32*QB) queries, fp32 accumulate.
-    f32x16 sacc[QB][2];
+    // ---- S^T tile: BC keys x (32*QB) queries, fp32 accumulate.
+    f32x16 sacc[QB][KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = f32x16{};
 #pragma unroll
@@ -144,7 +180,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WA
 
     if (MASKED) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
@@ -165,9 +201,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WA
     for (int qb = 0; qb < QB; ++qb) {
       // NaN-propagating maximum (v_maximum3_f32): no canonicalisation of the
       // MFMA results is needed, unlike fmaxf.
-      float mx = fmax2(sacc[qb][0][0], sacc[qb][1][0]);
+      float mx = sacc[qb][0][0];
 #pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmax3(mx, sacc[qb][0][e], sacc[qb][1][e]);
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int e = (kb == 0 ? 1 : 0); e < 16; e += 2)
+          mx = (e + 1 < 16) ? fmax3(mx, sacc[qb][kb][e], sacc[qb][kb][e + 1]) : fmax2(mx, sacc[qb][kb][e]);
       mx = halves_max(mx) * c;
       mnew[qb] = fmaxf(m_run[qb], mx);
       need |= mnew[qb] > m_run[qb] + kRescaleSlack;
@@ -185,12 +224,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WA
 
     // ---- probabilities (bf16) and their row sums. pb[qb][kb][c2] is directly
     // the B operand of the P V product for keys kb*32 + 16*c2 + (0..15).
-    u32x4 pb[QB][2][2];
+    u32x4 pb[QB][KB][2];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const float nm = -m_run[qb];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
           float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][e], c, nm));
@@ -207,10 +246,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WA
     }
 
     // ---- O^T += V^T P^T.
-    const int g = lane >> 4, gi = lane & 15;
-    const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
@@ -226,11 +263,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WA
   };
 
   // Full tiles in one single-path loop, then the partial last tile (if any).
-  const int nfull = N / kBC;  // tiles whose 64 keys are all < N
+  const int nfull = N / S::BC;  // tiles whose keys are all < N
   for (int j = 0; j < nfull; ++j) {
-    if (j + 1 < ntiles) dma_tile(j + 1, (j & 1) ^ 1);
+    if (j + NS - 1 < ntiles) dma_tile(j + NS - 1);
     tile(j, BoolC<false>{});
-    wait_vmem();
+    if (j + 1 < ntiles) wait_tile(j + 1);
     __syncthreads();
   }
   if (nfull < ntiles) tile(nfull, BoolC<true>{});
@@ -263,6 +300,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WA
 // query row r and owns output columns [t*D/8, (t+1)*D/8).
 // ------------------------------------------------------------------------
 constexpr int kF32BR = 32;
+constexpr int kBC = 64;  // keys per K/V tile of the fp32 kernel
 
 template <int D>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
@@ -343,23 +381,23 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 
 }  // namespace
 
-template <int D, int QB>
+template <int D, int QB, int KB, int NS>
 static hipError_t launch_fwd_bf16_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                                     float* lse, int B, int H, int N, float scale, hipStream_t stream) {
-  using S = FwdShape<D, QB>;
+  using S = FwdShape<D, QB, KB, NS>;
   const int n_qblk = (N + S::BR - 1) / S::BR;
   const int total = n_qblk * B * H;
   const float c = fabsf(scale) * kLog2e;
   const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, o, lse, N, n_qblk,
-                     total, c, qsign);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, KB, NS>), dim3(total), dim3(kThreads), 0, stream, q, k, v, o, lse, N,
+                     n_qblk, total, c, qsign);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int B,
                            int H, int N, int d, float scale, hipStream_t stream) {
-  if (d == 64) return launch_fwd_bf16_t<64, FWD_QB64>(q, k, v, o, lse, B, H, N, scale, stream);
-  return launch_fwd_bf16_t<128, FWD_QB128>(q, k, v, o, lse, B, H, N, scale, stream);
+  if (d == 64) return launch_fwd_bf16_t<64, FWD_QB64, FWD_KB64, FWD_NS64>(q, k, v, o, lse, B, H, N, scale, stream);
+  return launch_fwd_bf16_t<128, FWD_QB128, FWD_KB128, FWD_NS128>(q, k, v, o, lse, B, H, N, scale, stream);
 }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,

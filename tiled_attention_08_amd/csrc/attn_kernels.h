@@ -9,9 +9,8 @@
 
 namespace attn {
 
-// Rows of a head handled by one backward workgroup (keys) and per inner step (queries).
+// Keys of a head handled by one dK/dV workgroup (32 per wave).
 constexpr int kBwdKeysPerBlock = 128;
-constexpr int kBwdQueriesPerStep = 64;
 
 hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int B,
                            int H, int N, int d, float scale, hipStream_t stream);
