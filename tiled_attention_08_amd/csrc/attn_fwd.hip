@@ -9,7 +9,7 @@
 //                                     partial output as each K/V tile arrives;
 //   §3 recompute bullet               the row statistic (here lse) is kept for the backward.
 //
-// bf16 kernel, one workgroup = 4 waves; wave w owns 32*QB query rows.
+// bf16 kernel: one workgroup = 4 or 8 waves; wave w owns 32*QB query rows.
 // Everything is computed transposed, S^T = K Q^T and O^T = V^T P^T, so that a
 // query is a lane column of every accumulator: row statistics (max, sum,
 // rescale factor) are per-lane scalars, and the S^T accumulator converts to
@@ -26,8 +26,6 @@ namespace attn {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr float kRescaleSlack = 8.0f;  // log2 units a row max may grow before O, l are rescaled
 
 // Launch shape per head dim: 32-query blocks per wave (QB), 32-key blocks per
@@ -35,6 +33,15 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units a row max may grow before O
 // share each SIMD (at most 256 registers per lane).
 #ifndef FWD_WAVES_PER_EU
 #define FWD_WAVES_PER_EU 2
+#endif
+// Long sequences use 8-wave workgroups (one per CU, two waves per SIMD, one
+// K/V ring shared by all 8); short ones 4-wave workgroups so that the row
+// block does not overshoot N by much.
+#ifndef FWD_WAVES_LONG
+#define FWD_WAVES_LONG 8
+#endif
+#ifndef FWD_LONG_N
+#define FWD_LONG_N 1024
 #endif
 #ifndef FWD_QB64
 #define FWD_QB64 2
@@ -55,13 +62,14 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units a row max may grow before O
 #define FWD_NS128 2
 #endif
 
-template <int D, int QB, int KB, int NS>
+template <int D, int QB, int KB, int NS, int WAVES>
 struct FwdShape {
-  static constexpr int BR = kWaves * 32 * QB;                 // query rows per workgroup
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int BR = WAVES * 32 * QB;                  // query rows per workgroup
   static constexpr int BC = 32 * KB;                          // keys per K/V tile
   static constexpr int ROWB = D * 2;                          // bytes per K/V row
   static constexpr int TILEB = BC * ROWB;                     // bytes per K or V tile
-  static constexpr int DMA_PER_WAVE = BC * D / 8 / kThreads;  // 16-byte DMA instructions per wave per tensor
+  static constexpr int DMA_PER_WAVE = BC * D / 8 / THREADS;   // 16-byte DMA instructions per wave per tensor
   static constexpr int LDSB = NS * 2 * TILEB;                 // ring of NS (K, V) tile pairs
   static_assert(DMA_PER_WAVE >= 1, "every lane takes part in each tile DMA");
 };
@@ -74,12 +82,12 @@ __device__ __forceinline__ void wait_vmem_below() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-template <int D, int QB, int KB, int NS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(FWD_WAVES_PER_EU, FWD_WAVES_PER_EU)))
+template <int D, int QB, int KB, int NS, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(FWD_WAVES_PER_EU, FWD_WAVES_PER_EU)))
 void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                      uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qblk, int total, float c,
                      uint32_t qsign) {
-  using S = FwdShape<D, QB, KB, NS>;
+  using S = FwdShape<D, QB, KB, NS, WAVES>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -381,23 +389,29 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 
 }  // namespace
 
-template <int D, int QB, int KB, int NS>
+template <int D, int QB, int KB, int NS, int WAVES>
 static hipError_t launch_fwd_bf16_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                                     float* lse, int B, int H, int N, float scale, hipStream_t stream) {
-  using S = FwdShape<D, QB, KB, NS>;
+  using S = FwdShape<D, QB, KB, NS, WAVES>;
   const int n_qblk = (N + S::BR - 1) / S::BR;
   const int total = n_qblk * B * H;
   const float c = fabsf(scale) * kLog2e;
   const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, KB, NS>), dim3(total), dim3(kThreads), 0, stream, q, k, v, o, lse, N,
-                     n_qblk, total, c, qsign);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, KB, NS, WAVES>), dim3(total), dim3(S::THREADS), 0, stream, q, k, v, o,
+                     lse, N, n_qblk, total, c, qsign);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int B,
                            int H, int N, int d, float scale, hipStream_t stream) {
-  if (d == 64) return launch_fwd_bf16_t<64, FWD_QB64, FWD_KB64, FWD_NS64>(q, k, v, o, lse, B, H, N, scale, stream);
-  return launch_fwd_bf16_t<128, FWD_QB128, FWD_KB128, FWD_NS128>(q, k, v, o, lse, B, H, N, scale, stream);
+  const bool lng = N >= FWD_LONG_N;
+  if (d == 64)
+    return lng ? launch_fwd_bf16_t<64, FWD_QB64, FWD_KB64, FWD_NS64, FWD_WAVES_LONG>(q, k, v, o, lse, B, H, N, scale,
+                                                                                    stream)
+               : launch_fwd_bf16_t<64, FWD_QB64, FWD_KB64, FWD_NS64, 4>(q, k, v, o, lse, B, H, N, scale, stream);
+  return lng ? launch_fwd_bf16_t<128, FWD_QB128, FWD_KB128, FWD_NS128, FWD_WAVES_LONG>(q, k, v, o, lse, B, H, N, scale,
+                                                                                      stream)
+             : launch_fwd_bf16_t<128, FWD_QB128, FWD_KB128, FWD_NS128, 4>(q, k, v, o, lse, B, H, N, scale, stream);
 }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
