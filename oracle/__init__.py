@@ -4,7 +4,8 @@ Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import or call this package. The GPU library never does, and nothing here is
 shared with it.
 
-See ``oracle.attention`` for the definitions and their citations.
+See ``oracle.attention`` (the definition) and ``oracle.masked`` (key-padding and
+causal masks) for the definitions and their citations.
 """
 from .attention import (  # noqa: F401
     attention_probs,
@@ -13,3 +14,4 @@ from .attention import (  # noqa: F401
     brute_attention_fwd,
     brute_attention_grads_fd,
 )
+from .masked import masked_attention_bwd, masked_attention_fwd, visible_keys  # noqa: F401

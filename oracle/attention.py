@@ -147,28 +147,37 @@ def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
 # sharing nothing with the vectorised oracle above.
 # ----------------------------------------------------------------------------
 
-def brute_attention_fwd(q, k, v, scale: float):
+def brute_attention_fwd(q, k, v, scale: float, allowed=None):
     """One head, pure Python: o_i = sum_j e^{s_ij} v_j / sum_j e^{s_ij}, s_ij = scale * <q_i, k_j>.
 
     No max subtraction (inputs must keep scale*<q,k> small); sums use math.fsum.
     q: M x d, k: N x d, v: N x dv as nested sequences. Returns (o, lse) as lists.
+    ``allowed`` (optional M x N booleans) drops the pairs it marks False from
+    the sums; a row with no allowed pair gives o_i = 0 and lse_i = -inf.
     """
     q = [[float(x) for x in row] for row in q]
     k = [[float(x) for x in row] for row in k]
     v = [[float(x) for x in row] for row in v]
     o, lse = [], []
-    for qi in q:
+    for i, qi in enumerate(q):
         w = []
-        for kj in k:
+        for j, kj in enumerate(k):
+            if allowed is not None and not allowed[i][j]:
+                w.append(0.0)
+                continue
             s = scale * math.fsum(a * b for a, b in zip(qi, kj))
             w.append(math.exp(s))
         z = math.fsum(w)
+        if z == 0.0:
+            o.append([0.0] * len(v[0]))
+            lse.append(-math.inf)
+            continue
         o.append([math.fsum(w[j] * v[j][c] for j in range(len(k))) / z for c in range(len(v[0]))])
         lse.append(math.log(z))
     return o, lse
 
 
-def brute_attention_grads_fd(q, k, v, do, scale: float, h: float = 1e-6):
+def brute_attention_grads_fd(q, k, v, do, scale: float, h: float = 1e-6, allowed=None):
     """Central finite differences of L = sum_ic O_ic * dO_ic through ``brute_attention_fwd``.
 
     Returns (dq, dk, dv) as float64 arrays. Only for tiny shapes.
@@ -179,7 +188,7 @@ def brute_attention_grads_fd(q, k, v, do, scale: float, h: float = 1e-6):
     do = np.array(do, dtype=np.float64)
 
     def loss(qq, kk, vv):
-        o, _ = brute_attention_fwd(qq.tolist(), kk.tolist(), vv.tolist(), scale)
+        o, _ = brute_attention_fwd(qq.tolist(), kk.tolist(), vv.tolist(), scale, allowed)
         return math.fsum(o[i][c] * do[i, c] for i in range(len(o)) for c in range(len(o[0])))
 
     grads = []
