@@ -208,7 +208,7 @@ def main(argv=None) -> int:
     # Per-kernel timing (each kernel alone, back-to-back launches on the same stream).
     reps = args.kernel_reps
     def stage(i):
-        return lambda: attn.attn_bwd_stage(i, q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream)
+        return lambda: attn.attn_bwd_stage(i, q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream=stream)
 
     kernels = {"fwd": time_launches(lambda: attn.attn_fwd(q, k, v, o, lse, scale, stream), reps)}
     if with_bwd:

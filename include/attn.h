@@ -49,8 +49,10 @@ extern "C" {
 
 typedef enum {
   ATTN_OK = 0,
-  ATTN_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, B/H/N < 1, non-finite scale, aliasing */
-  ATTN_ERR_UNSUPPORTED = -2,  /* d_k not in {64, 128}, or sizes beyond the int32 index range */
+  ATTN_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, B/H/N < 1, non-finite scale, aliasing,
+                                 causal not 0 or 1 */
+  ATTN_ERR_UNSUPPORTED = -2,  /* d_k not in {64, 128}, dtype unknown, or sizes beyond the int32
+                                 index range */
   ATTN_ERR_WORKSPACE = -3,    /* workspace missing or smaller than attn_bwd_workspace_bytes() */
   ATTN_ERR_HIP = -4           /* the HIP runtime rejected a launch */
 } attn_status_t;
@@ -101,9 +103,46 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * One stage of attn_bwd, same arguments plus `stage`; attn_bwd is exactly
- * stages 0, 1, 2 in order on `stream`. For callers that schedule or time the
- * stages separately:
+ * Extended entry points: element type and masks.
+ *
+ * The article defines unmasked attention (§1 "Attention" formula). §3 opens
+ * with long text sequences as the case where the N x N score matrix becomes
+ * the limit; for text, two masks are standard, and these entry points take
+ * them (the article prints neither, so the definition below is a reading):
+ *   key padding  kv_len: device pointer to B int32 (4-byte aligned), or NULL
+ *                for "all N keys". Keys j >= kv_len[b] are hidden from every
+ *                query of batch entry b. Values outside [0, N] are clamped to
+ *                it on the device (no error can be reported from there).
+ *   causal       0 or 1. With 1, query i sees keys j <= i only (positions in
+ *                the same sequence, counted from 0).
+ * A hidden pair has score -inf, i.e. probability 0; each row's softmax runs
+ * over its visible keys. A row with no visible key (kv_len[b] = 0) gets
+ * O = 0 and lse = -inf, and passes no gradient: its dQ row is 0, and keys no
+ * query sees get dK = dV = 0.
+ *
+ * dtype is an attn_dtype_t. ATTN_DTYPE_BF16: Q, K, V, O, dO, dQ, dK, dV are
+ * bfloat16; attn_fwd_ex(ATTN_DTYPE_BF16, ..., 0, NULL, stream) is attn_fwd.
+ * Any other value returns ATTN_ERR_UNSUPPORTED.
+ */
+typedef enum { ATTN_DTYPE_BF16 = 0 } attn_dtype_t;
+
+int attn_fwd_ex(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int N, int d_k, float scale, int causal, const int* kv_len, void* stream);
+
+/*
+ * Backward with masks: the gradients of attn_fwd_ex's output for the same
+ * dtype, causal and kv_len (which must be the values the forward used). The
+ * workspace contract is attn_bwd's; kv_len must not overlap an output.
+ */
+int attn_bwd_ex(int dtype, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dO, void* dq, void* dk, void* dv,
+                int B, int H, int N, int d_k, float scale, int causal, const int* kv_len,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One stage of attn_bwd_ex, same arguments plus `stage`; attn_bwd_ex is
+ * exactly stages 0, 1, 2 in order on `stream`. For callers that schedule or
+ * time the stages separately:
  *   stage 0  prep:  workspace <- lse * log2(e) and -delta_i = -<dO_i, O_i>
  *                   (float32); reads o, dO, lse.
  *   stage 1  dK/dV: rebuilds P from q, k, lse and writes dk, dv; needs the
@@ -111,12 +150,12 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  *   stage 2  dQ:    rebuilds P from q, k, lse and writes dq; needs the
  *                   workspace of stage 0 (stages 1 and 2 are independent).
  * All stages are deterministic: no atomics, bitwise-repeatable results.
- * Every check of attn_bwd applies to every stage (all pointers are
+ * Every check of attn_bwd_ex applies to every stage (all pointers are
  * required). Returns ATTN_ERR_INVALID_ARG for a stage outside 0..2.
  */
-int attn_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
-                   const void* dO, void* dq, void* dk, void* dv,
-                   int B, int H, int N, int d_k, float scale,
+int attn_bwd_stage(int stage, int dtype, const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d_k, float scale, int causal, const int* kv_len,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable text for a status code (never NULL). */

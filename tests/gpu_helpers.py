@@ -8,11 +8,16 @@ from attn_inputs import Inputs, bf16_bits_to_f64
 # Tolerances. fp32 path: max-abs 1e-5 on O; bf16 inputs with fp32 accumulation:
 # max-abs 2e-2 on O against the fp64 oracle run on the same bf16-rounded
 # inputs; gradients: relative L2 error 5e-2 per tensor. lse (the saved row
-# statistic): 1e-5 absolute for fp32, 1e-3 * max(1, |lse|) for bf16 inputs.
+# statistic): 1e-5 absolute for fp32; for bf16 inputs 4e-3 * max(1, |lse|):
+# the kernels normalise by the sum of the bf16-rounded weights (the weights the
+# P V product uses), each off by at most 2^-8 relative (round to nearest, 8
+# significant bits), so l is off by at most 2^-8 relative and lse = m + ln l by
+# at most 2^-8 ~ 3.9e-3 absolute; rows with few visible keys (causal mask)
+# come close to that bound because their rounding errors do not average out.
 TOL_F32_O = 1e-5
 TOL_F32_LSE = 1e-5
 TOL_BF16_O = 2e-2
-TOL_BF16_LSE_REL = 1e-3
+TOL_BF16_LSE_REL = 4e-3
 TOL_GRAD_RELL2 = 5e-2
 
 

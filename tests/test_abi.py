@@ -28,8 +28,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "attn_bwd", "attn_bwd_stage",
-                                           "attn_bwd_workspace_bytes", "attn_status_string"])
+    assert declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_bwd", "attn_bwd_ex",
+                                           "attn_bwd_stage", "attn_bwd_workspace_bytes", "attn_status_string"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -55,6 +55,13 @@ def fwd(L, *, q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, H=1, N=8, d=64, sca
     return L.lib.attn_fwd(q, k, v, o, lse, B, H, N, d, scale, None)
 
 
+def fwd_ex(L, *, dtype=0, causal=0, kv_len=None, **kw):
+    a = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, H=1, N=8, d=64, scale=0.125)
+    a.update(kw)
+    return L.lib.attn_fwd_ex(dtype, a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                             a["scale"], causal, kv_len, None)
+
+
 def fwd32(L, **kw):
     args = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, H=1, N=8, d=64, scale=0.125)
     args.update(kw)
@@ -62,17 +69,20 @@ def fwd32(L, **kw):
                               args["N"], args["d"], args["scale"], None)
 
 
-def bwd(L, stage=None, **kw):
+def bwd(L, stage=None, ex=False, dtype=0, causal=0, kv_len=None, **kw):
     a = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], do=A[5], dq=A[6], dk=A[7], dv=A[8], B=1, H=1, N=8, d=64,
              scale=0.125, ws=A[9], ws_bytes=None)
     a.update(kw)
     if a["ws_bytes"] is None:
         a["ws_bytes"] = L.attn_bwd_workspace_bytes(a["B"], a["H"], a["N"], a["d"])
-    args = (a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["B"], a["H"], a["N"],
-            a["d"], a["scale"], a["ws"], a["ws_bytes"], None)
+    head = (a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"], a["B"], a["H"], a["N"],
+            a["d"], a["scale"])
+    tail = (a["ws"], a["ws_bytes"], None)
+    if stage is None and not ex:
+        return L.lib.attn_bwd(*head, *tail)
     if stage is None:
-        return L.lib.attn_bwd(*args)
-    return L.lib.attn_bwd_stage(stage, *args)
+        return L.lib.attn_bwd_ex(dtype, *head, causal, kv_len, *tail)
+    return L.lib.attn_bwd_stage(stage, dtype, *head, causal, kv_len, *tail)
 
 
 def test_forward_rejections(L):
@@ -90,6 +100,17 @@ def test_forward_rejections(L):
         assert f(L, N=1 << 30) == UNS                     # beyond 32-bit per-head indexing
 
 
+def test_extended_forward_rejections(L):
+    INV, UNS = L.ATTN_ERR_INVALID_ARG, L.ATTN_ERR_UNSUPPORTED
+    assert fwd_ex(L, dtype=1) == UNS and fwd_ex(L, dtype=-1) == UNS
+    assert fwd_ex(L, causal=2) == INV and fwd_ex(L, causal=-1) == INV
+    assert fwd_ex(L, kv_len=A[10] + 2) == INV               # kv_len not 4-byte aligned
+    assert fwd_ex(L, kv_len=A[3] + 4) == INV                # kv_len inside o
+    assert fwd_ex(L, kv_len=A[4]) == INV                    # kv_len on lse
+    assert fwd_ex(L, q=None, causal=1) == INV
+    assert fwd_ex(L, d=96, causal=1) == UNS
+
+
 def test_backward_rejections(L):
     INV, UNS, WS = L.ATTN_ERR_INVALID_ARG, L.ATTN_ERR_UNSUPPORTED, L.ATTN_ERR_WORKSPACE
     for stage in (None, 0, 1, 2):
@@ -104,6 +125,12 @@ def test_backward_rejections(L):
         assert bwd(L, stage, ws=A[8]) == INV              # workspace overlaps dv
         assert bwd(L, stage, scale=float("-inf")) == INV
     assert bwd(L, 3) == INV and bwd(L, -1) == INV
+    for stage in (None, 0, 1, 2):
+        assert bwd(L, stage, ex=True, dtype=3) == UNS
+        assert bwd(L, stage, ex=True, causal=5) == INV
+        assert bwd(L, stage, ex=True, kv_len=A[10] + 1) == INV
+        assert bwd(L, stage, ex=True, kv_len=A[7]) == INV     # kv_len inside dk
+        assert bwd(L, stage, ex=True, kv_len=A[9] + 8) == INV  # kv_len inside the workspace
 
 
 def test_workspace_size(L):

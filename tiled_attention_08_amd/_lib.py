@@ -19,10 +19,11 @@ ATTN_ERR_INVALID_ARG = -1
 ATTN_ERR_UNSUPPORTED = -2
 ATTN_ERR_WORKSPACE = -3
 ATTN_ERR_HIP = -4
+ATTN_DTYPE_BF16 = 0
 
 # Every symbol include/attn.h declares.
-EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_bwd", "attn_bwd_stage", "attn_bwd_workspace_bytes",
-           "attn_status_string")
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_bwd_stage",
+           "attn_bwd_workspace_bytes", "attn_status_string")
 
 
 def _load() -> ctypes.CDLL:
@@ -38,7 +39,11 @@ def _load() -> ctypes.CDLL:
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, vp, sz, vp]
     lib.attn_bwd.restype = i
-    lib.attn_bwd_stage.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, vp, sz, vp]
+    lib.attn_fwd_ex.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
+    lib.attn_fwd_ex.restype = i
+    lib.attn_bwd_ex.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
+    lib.attn_bwd_ex.restype = i
+    lib.attn_bwd_stage.argtypes = [i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
     lib.attn_bwd_stage.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
@@ -96,6 +101,21 @@ def _check_lse(lse, B, H, N):
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
 
 
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ATTN_DTYPE_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _check_kv_len(kv_len, B):
+    import torch
+    if kv_len is None:
+        return
+    if kv_len.dtype != torch.int32 or tuple(kv_len.shape) != (B,) or not kv_len.is_contiguous() or not kv_len.is_cuda:
+        raise ValueError("kv_len must be a contiguous int32 device tensor of shape [B]")
+
+
 def attn_fwd(q, k, v, o, lse, scale: float, stream=None) -> None:
     """bf16 forward into caller-provided ``o`` (bf16 [B,H,N,d]) and ``lse`` (float32 [B,H,N])."""
     import torch
@@ -104,6 +124,15 @@ def attn_fwd(q, k, v, o, lse, scale: float, stream=None) -> None:
         raise ValueError("attn_fwd takes bfloat16 tensors")
     _check_lse(lse, B, H, N)
     _check(lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale), _stream(stream)))
+
+
+def attn_fwd_ex(q, k, v, o, lse, scale: float, causal: bool = False, kv_len=None, stream=None) -> None:
+    """Forward with masks: ``causal`` (query i sees keys j <= i) and ``kv_len`` (int32 [B] device tensor of valid keys)."""
+    B, H, N, d = _shape(q, k, v, o)
+    _check_lse(lse, B, H, N)
+    _check_kv_len(kv_len, B)
+    _check(lib.attn_fwd_ex(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
+                           int(bool(causal)), _ptr(kv_len), _stream(stream)))
 
 
 def attn_fwd_f32(q, k, v, o, lse, scale: float, stream=None) -> None:
@@ -133,17 +162,28 @@ def attn_bwd(q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, stream=No
                         B, H, N, d, float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
-def attn_bwd_stage(stage: int, q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, stream=None) -> None:
-    """One stage (0 prep, 1 main, 2 dq) of attn_bwd; same arguments."""
-    import torch
+def attn_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, causal: bool = False, kv_len=None,
+                stream=None) -> None:
+    """Backward with the masks of attn_fwd_ex (which must match the forward's)."""
     B, H, N, d = _shape(q, k, v, o, do, dq, dk, dv)
-    if q.dtype != torch.bfloat16:
-        raise ValueError("attn_bwd_stage takes bfloat16 tensors")
     _check_lse(lse, B, H, N)
+    _check_kv_len(kv_len, B)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.attn_bwd_stage(int(stage), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
-                              _ptr(dk), _ptr(dv), B, H, N, d, float(scale), _ptr(workspace), ws_bytes,
-                              _stream(stream)))
+    _check(lib.attn_bwd_ex(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                           _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(kv_len),
+                           _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def attn_bwd_stage(stage: int, q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, causal: bool = False,
+                   kv_len=None, stream=None) -> None:
+    """One stage (0 prep, 1 dK/dV, 2 dQ) of attn_bwd_ex; same arguments."""
+    B, H, N, d = _shape(q, k, v, o, do, dq, dk, dv)
+    _check_lse(lse, B, H, N)
+    _check_kv_len(kv_len, B)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.attn_bwd_stage(int(stage), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                              _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
+                              _ptr(kv_len), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 # ---------------------------------------------------------------- allocating conveniences

@@ -48,26 +48,38 @@ extern "C" {
 const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
-    case ATTN_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, B/H/N < 1, non-finite scale, or overlapping buffers)";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported shape (d_k must be 64 or 128; sizes must fit 32-bit per-head indexing)";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, B/H/N < 1, non-finite scale, causal not 0 or 1, or overlapping buffers)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported (d_k must be 64 or 128, dtype must be known, sizes must fit 32-bit per-head indexing)";
     case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than attn_bwd_workspace_bytes()";
     case ATTN_ERR_HIP: return "HIP runtime error at launch";
     default: return "unknown status";
   }
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d_k,
-             float scale, void* stream) {
+int attn_fwd_ex(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                int d_k, float scale, int causal, const int* kv_len, void* stream) {
   size_t E = 0, R = 0;
   const int st = check_shape(B, H, N, d_k, scale, &E, &R);
   if (st != ATTN_OK) return st;
+  if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
+  if (kv_len != nullptr && (reinterpret_cast<uintptr_t>(kv_len) & 3u) != 0) return ATTN_ERR_INVALID_ARG;
   const Range rq = span(q, E * 2), rk = span(k, E * 2), rv = span(v, E * 2), ro = span(o, E * 2), rl = span(lse, R * 4);
   if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(ro, rl)) return ATTN_ERR_INVALID_ARG;
   if (overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv)) return ATTN_ERR_INVALID_ARG;
+  if (kv_len != nullptr) {
+    const Range rkv = span(kv_len, (size_t)B * 4);
+    if (overlap(rkv, ro) || overlap(rkv, rl)) return ATTN_ERR_INVALID_ARG;
+  }
   return from_hip(attn::launch_fwd_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                         static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, B, H, N, d_k,
-                                        scale, static_cast<hipStream_t>(stream)));
+                                        scale, causal, kv_len, static_cast<hipStream_t>(stream)));
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d_k,
+             float scale, void* stream) {
+  return attn_fwd_ex(ATTN_DTYPE_BF16, q, k, v, o, lse, B, H, N, d_k, scale, 0, nullptr, stream);
 }
 
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d_k,
@@ -90,12 +102,15 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d_k) {
 
 namespace {
 
-int bwd_checks(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
-               void* dk, void* dv, int B, int H, int N, int d_k, float scale, void* workspace,
-               size_t workspace_bytes) {
+int bwd_checks(int dtype, const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k, float scale, int causal,
+               const int* kv_len, void* workspace, size_t workspace_bytes) {
   size_t E = 0, R = 0;
   const int st = check_shape(B, H, N, d_k, scale, &E, &R);
   if (st != ATTN_OK) return st;
+  if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (kv_len != nullptr && (reinterpret_cast<uintptr_t>(kv_len) & 3u) != 0) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(dO) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return ATTN_ERR_INVALID_ARG;
@@ -110,41 +125,53 @@ int bwd_checks(const void* q, const void* k, const void* v, const void* o, const
       if (overlap(outs[a], ins[b])) return ATTN_ERR_INVALID_ARG;
     for (int b = a + 1; b < 4; ++b)
       if (overlap(outs[a], outs[b])) return ATTN_ERR_INVALID_ARG;
+    if (kv_len != nullptr && overlap(outs[a], span(kv_len, (size_t)B * 4))) return ATTN_ERR_INVALID_ARG;
   }
   return ATTN_OK;
 }
 
 int bwd_launch(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
-               const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k, float scale,
-               void* workspace, void* stream) {
+               const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k, float scale, int causal,
+               const int* kv_len, void* workspace, void* stream) {
   return from_hip(attn::launch_bwd_bf16_stage(
       stage, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       static_cast<const uint16_t*>(o), lse, static_cast<const uint16_t*>(dO), static_cast<uint16_t*>(dq),
-      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B, H, N, d_k, scale, workspace,
+      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B, H, N, d_k, scale, causal, kv_len, workspace,
       static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
-             void* dk, void* dv, int B, int H, int N, int d_k, float scale, void* workspace, size_t workspace_bytes,
-             void* stream) {
-  const int st = bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, workspace, workspace_bytes);
+int attn_bwd_ex(int dtype, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k, float scale, int causal,
+                const int* kv_len, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = bwd_checks(dtype, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, workspace,
+                            workspace_bytes);
   if (st != ATTN_OK) return st;
   for (int stage = 0; stage < 3; ++stage) {
-    const int r = bwd_launch(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, workspace, stream);
+    const int r = bwd_launch(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, workspace,
+                             stream);
     if (r != ATTN_OK) return r;
   }
   return ATTN_OK;
 }
 
-int attn_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
-                   const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k, float scale,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+             void* dk, void* dv, int B, int H, int N, int d_k, float scale, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  return attn_bwd_ex(ATTN_DTYPE_BF16, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, 0, nullptr, workspace,
+                     workspace_bytes, stream);
+}
+
+int attn_bwd_stage(int stage, int dtype, const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k,
+                   float scale, int causal, const int* kv_len, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   if (stage < 0 || stage > 2) return ATTN_ERR_INVALID_ARG;
-  const int st = bwd_checks(q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, workspace, workspace_bytes);
+  const int st = bwd_checks(dtype, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, workspace,
+                            workspace_bytes);
   if (st != ATTN_OK) return st;
-  return bwd_launch(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, workspace, stream);
+  return bwd_launch(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, workspace, stream);
 }
 
 }  // extern "C"

@@ -121,7 +121,7 @@ __attribute__((amdgpu_waves_per_eu(D == 64 ? BWD_WAVES_PER_EU : 1, D == 64 ? BWD
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                      const uint16_t* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ ndelta,
                      uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk, int total, float c,
-                     float scale) {
+                     float scale, const int* __restrict__ kv_len, int H, int causal) {
   using S = DkdvShape<D, MB>;
   constexpr int BRQ = S::BRQ;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
@@ -134,9 +134,24 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int bh = work / n_kblk, kblk = work - bh * n_kblk;
   const size_t head = (size_t)bh * N * D;
   const size_t hrow = (size_t)bh * N;
-  const int key = kblk * BCK + wave * 32 + l32;  // this lane's key
+  const int k0 = kblk * BCK;
+  const int key = k0 + wave * 32 + l32;  // this lane's key
   const bool key_ok = key < N;
-  const bool key_tail = kblk * BCK + BCK > N;
+  // Query i sees key j iff j < kv and (not causal or j <= i); kv = valid keys
+  // of this batch entry.
+  const int kv = kv_len ? min(max(kv_len[bh / H], 0), N) : N;
+
+  if (k0 >= kv) {  // no query sees any key of this block: zero gradients
+    if (key_ok) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int c8 = 0; c8 < D / 8; ++c8) {
+        *reinterpret_cast<u32x4*>(dK + head + (size_t)key * D + c8 * 8) = z;
+        *reinterpret_cast<u32x4*>(dV + head + (size_t)key * D + c8 * 8) = z;
+      }
+    }
+    return;
+  }
 
   // K and V fragments of this lane's key: B operands of S = Q K^T and dP = dO V^T.
   bf16x8 kf[D / 16], vf[D / 16];
@@ -167,16 +182,22 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     dkacc[db] = f32x16{};
   }
 
+  // Steps [i_beg, nq) hold a query that sees a key of this block (under the
+  // causal mask queries before k0 see none). Steps [u_beg, u_end) need no
+  // mask: all their queries exist and see all 128 keys.
   const int nq = (N + BRQ - 1) / BRQ;
-  dma_step(0, 0);
+  const int i_beg = causal ? k0 / BRQ : 0;
+  const int u_beg = causal ? (k0 + BCK - 1 + BRQ - 1) / BRQ : 0;
+  const int u_end = k0 + BCK <= kv ? N / BRQ : 0;
+  dma_step(i_beg, 0);
   wait_vmem();
   __syncthreads();
 
-  // One 64-query step. MASKED (the last step when N % 64 != 0, and every step
-  // of the last key block when N % 128 != 0) gives probability 0 to queries
-  // and keys past N; other steps carry no masking code.
-  // The buffer index is a compile-time constant (BUF == i % 2) so that every
-  // LDS offset in the step folds into an immediate.
+  // One 64-query step. MASKED steps give probability 0 to every pair the
+  // masks hide (queries or keys past N, keys past kv, keys after the query
+  // under the causal mask); other steps carry no masking code.
+  // The buffer index is a compile-time constant (BUF == (i - i_beg) % 2) so
+  // that every LDS offset in the step folds into an immediate.
   auto step = [&](int i, auto masked, auto bufc) {
     constexpr bool MASKED = decltype(masked)::value;
     constexpr int buf = decltype(bufc)::value;
@@ -225,7 +246,10 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           p[ii] = __builtin_amdgcn_exp2f(fmaf(sacc[mb][4 * jj + ii], c, -lv[ii]));
-          if (MASKED && (!key_ok || q0 + r0 + ii >= N)) p[ii] = 0.f;
+          if (MASKED) {
+            const int qi = q0 + r0 + ii;
+            if (key >= kv || qi >= N || (causal && key > qi)) p[ii] = 0.f;
+          }
           ds[ii] = p[ii] * pacc[mb][4 * jj + ii];
         }
         const int c2 = jj >> 1, w0 = 2 * (jj & 1);
@@ -256,22 +280,40 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     __syncthreads();  // next step's tiles visible to all waves; this step's buffers free
   };
 
-  // Steps that need no mask form one single-path loop; the rest follow.
-  const int nq_full = key_tail ? 0 : N / BRQ;
-  int i = 0;
-  for (; i + 1 < nq_full; i += 2) {
-    step(i, BoolC<false>{}, IntC<0>{});
-    step(i + 1, BoolC<false>{}, IntC<1>{});
+  // Masked steps before the unmasked range (the causal diagonal), the
+  // unmasked range as one single-path loop unrolled by buffer, then the
+  // masked steps after it (query tail, or every step when a key of this block
+  // is hidden by kv).
+  const bool has_u = u_beg < u_end;
+  const int m1_end = has_u ? u_beg : nq;
+  int i = i_beg;
+  for (; i + 1 < m1_end; i += 2) {
+    step(i, BoolC<true>{}, IntC<0>{});
+    step(i + 1, BoolC<true>{}, IntC<1>{});
   }
-  if (i < nq_full) {
-    step(i, BoolC<false>{}, IntC<0>{});
+  if (i < m1_end) {
+    step(i, BoolC<true>{}, IntC<0>{});
     ++i;
   }
-  for (; i < nq; ++i) {
-    if (i & 1)
-      step(i, BoolC<true>{}, IntC<1>{});
-    else
-      step(i, BoolC<true>{}, IntC<0>{});
+  if (has_u) {
+    if (i < u_end && ((i - i_beg) & 1)) {
+      step(i, BoolC<false>{}, IntC<1>{});
+      ++i;
+    }
+    for (; i + 1 < u_end; i += 2) {
+      step(i, BoolC<false>{}, IntC<0>{});
+      step(i + 1, BoolC<false>{}, IntC<1>{});
+    }
+    if (i < u_end) {
+      step(i, BoolC<false>{}, IntC<0>{});
+      ++i;
+    }
+    for (; i < nq; ++i) {
+      if ((i - i_beg) & 1)
+        step(i, BoolC<true>{}, IntC<1>{});
+      else
+        step(i, BoolC<true>{}, IntC<0>{});
+    }
   }
 
   // ---- epilogue: dV = (dV^T)^T, dK = scale (dK^T)^T, bf16 RNE. Lane: key, dims db*32 + 8jj + 4h + 0..3.
@@ -307,7 +349,8 @@ template <int D, int QB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BWD_WAVES_PER_EU, BWD_WAVES_PER_EU)))
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                    const uint16_t* __restrict__ dO, const float* __restrict__ lse2_in, const float* __restrict__ ndelta,
-                   uint16_t* __restrict__ dQ, int N, int n_qblk, int total, float c, float scale) {
+                   uint16_t* __restrict__ dQ, int N, int n_qblk, int total, float c, float scale,
+                   const int* __restrict__ kv_len, int H, int causal) {
   using S = DqShape<D, QB>;
   static_assert(S::KDMA >= 1, "K/V step tile must cover every lane");
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
@@ -317,10 +360,24 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int g = lane >> 4, gi = lane & 15;
   const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
   const int work = xcd_remap(blockIdx.x, total);
-  const int bh = work / n_qblk, qblk = work - bh * n_qblk;
+  const int bh = work / n_qblk;
+  // Causal: the last row blocks have the most keys; they are handed out first.
+  const int qblk = causal ? n_qblk - 1 - (work - bh * n_qblk) : work - bh * n_qblk;
   const size_t head = (size_t)bh * N * D;
   const size_t hrow = (size_t)bh * N;
   const int qw0 = qblk * S::BR + wave * 32 * QB;
+
+  // Visible keys of query q: j < klim(q) = min(kv, q + 1) (causal) or kv.
+  const int kv = kv_len ? min(max(kv_len[bh / H], 0), N) : N;
+  auto klim = [&](int q) { return causal ? min(kv, q + 1) : kv; };
+  int klq[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) klq[qb] = klim(qw0 + qb * 32 + l32);
+  // Key steps this workgroup reads, steps all its queries see in full, and
+  // the steps this wave has any visible key in.
+  const int ntiles = (klim(qblk * S::BR + S::BR - 1) + BCQ - 1) / BCQ;
+  const int nfull = klim(qblk * S::BR) / BCQ;
+  const int nvis_w = (klim(qw0 + 32 * QB - 1) + BCQ - 1) / BCQ;
 
   // Per query (lane column l32 of block qb): Q and dO fragments (B operands of
   // S^T = K Q^T and dP^T = V dO^T), lse in log2 units and -delta.
@@ -355,19 +412,23 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     dma_rows<D>(V + head, j * BCQ, N, smem + buf * 2 * S::TILEB + S::TILEB, wave, lane, S::KDMA);
   };
 
-  const int ntiles = (N + BCQ - 1) / BCQ;
-  dma_step(0, 0);
-  wait_vmem();
+  if (ntiles > 0) {
+    dma_step(0, 0);
+    wait_vmem();
+  }
   __syncthreads();
 
-  // One 32-key step; MASKED (the last step when N % 32 != 0) gives keys past N probability 0.
-  auto step = [&](int j, auto masked) {
+  // One 32-key step. MASKED steps give probability 0 to each lane's keys at
+  // or beyond klim(query) (keys past N or kv, keys after the query under the
+  // causal mask). COMPUTE false: this wave sees no key of the step and only
+  // takes part in the DMA.
+  auto step = [&](int j, auto masked, bool compute) {
     constexpr bool MASKED = decltype(masked)::value;
     const int buf = j & 1;
     if (j + 1 < ntiles) dma_step(j + 1, buf ^ 1);
+    if (!compute) return;
     const unsigned char* Ks = smem + buf * 2 * S::TILEB;
     const unsigned char* Vs = Ks + S::TILEB;
-    const int kvalid = N - j * BCQ;
 
     // ---- S^T = K Q^T and dP^T = V dO^T: 32 keys x (32*QB) queries.
     f32x16 sacc[QB], pacc[QB];
@@ -398,9 +459,9 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][e], c, -lse2[qb]));
         float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][e + 1], c, -lse2[qb]));
         if (MASKED) {
-          const int key = 8 * (e >> 2) + 4 * h + (e & 3);
-          if (key >= kvalid) p0 = 0.f;
-          if (key + 1 >= kvalid) p1 = 0.f;
+          const int key = j * BCQ + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (key >= klq[qb]) p0 = 0.f;
+          if (key + 1 >= klq[qb]) p1 = 0.f;
         }
         dsb[qb][e >> 3][(e >> 1) & 3] = pack_bf16(p0 * (pacc[qb][e] + dl[qb]), p1 * (pacc[qb][e + 1] + dl[qb]));
       }
@@ -420,13 +481,19 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     }
   };
 
-  const int nfull = N / BCQ;
-  for (int j = 0; j < nfull; ++j) {
-    step(j, BoolC<false>{});
+  int j = 0;
+  for (; j < nfull; ++j) {
+    step(j, BoolC<false>{}, true);
     wait_vmem();
     __syncthreads();
   }
-  if (nfull < ntiles) step(nfull, BoolC<true>{});
+  for (; j < ntiles; ++j) {
+    step(j, BoolC<true>{}, j < nvis_w);
+    if (j + 1 < ntiles) {
+      wait_vmem();
+      __syncthreads();
+    }
+  }
 
   // ---- epilogue: dQ = scale (dQ^T)^T, bf16 RNE. Lane: query, dims db*32 + 8jj + 4h + 0..3.
 #pragma unroll
@@ -460,8 +527,8 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d) {
 template <int D>
 static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq,
-                                     uint16_t* dk, uint16_t* dv, int B, int H, int N, float scale, void* workspace,
-                                     hipStream_t stream) {
+                                     uint16_t* dk, uint16_t* dv, int B, int H, int N, float scale, int causal,
+                                     const int* kv_len, void* workspace, hipStream_t stream) {
   const long rows = (long)B * H * N;
   float* lse2 = reinterpret_cast<float*>(workspace);
   float* ndelta = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(workspace) + align256(rows * 4));
@@ -473,24 +540,27 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
     const int n_kblk = (N + BCK - 1) / BCK;
     const int total = n_kblk * B * H;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, BWD_MB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, ndelta,
-                       dk, dv, N, n_kblk, total, c, scale);
+                       dk, dv, N, n_kblk, total, c, scale, kv_len, H, causal);
   } else {
     constexpr int QB = D == 64 ? 2 : 1;
     constexpr int BR = DqShape<D, QB>::BR;
     const int n_qblk = (N + BR - 1) / BR;
     const int total = n_qblk * B * H;
     hipLaunchKernelGGL((bwd_dq_kernel<D, QB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, ndelta, dq,
-                       N, n_qblk, total, c, scale);
+                       N, n_qblk, total, c, scale, kv_len, H, causal);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_bf16_stage(int stage, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq, uint16_t* dk,
-                                 uint16_t* dv, int B, int H, int N, int d, float scale, void* workspace,
-                                 hipStream_t stream) {
-  if (d == 64) return launch_bwd_stage_t<64>(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, workspace, stream);
-  return launch_bwd_stage_t<128>(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, workspace, stream);
+                                 uint16_t* dv, int B, int H, int N, int d, float scale, int causal,
+                                 const int* kv_len, void* workspace, hipStream_t stream) {
+  if (d == 64)
+    return launch_bwd_stage_t<64>(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, causal, kv_len, workspace,
+                                  stream);
+  return launch_bwd_stage_t<128>(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, causal, kv_len, workspace,
+                                 stream);
 }
 
 }  // namespace attn

@@ -86,7 +86,7 @@ template <int D, int QB, int KB, int NS, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(FWD_WAVES_PER_EU, FWD_WAVES_PER_EU)))
 void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                      uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qblk, int total, float c,
-                     uint32_t qsign) {
+                     uint32_t qsign, const int* __restrict__ kv_len, int H, int causal) {
   using S = FwdShape<D, QB, KB, NS, WAVES>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
 
@@ -95,12 +95,22 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int g = lane >> 4, gi = lane & 15;
   const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
   const int work = xcd_remap(blockIdx.x, total);
-  const int bh = work / n_qblk, qblk = work - bh * n_qblk;
+  const int bh = work / n_qblk;
+  // Causal: the last row blocks have the most keys; they are handed out first.
+  const int qblk = causal ? n_qblk - 1 - (work - bh * n_qblk) : work - bh * n_qblk;
   const size_t head = (size_t)bh * N * D;
   const uint16_t* Qh = Q + head;
   const uint16_t* Kh = K + head;
   const uint16_t* Vh = V + head;
   const int qw0 = qblk * S::BR + wave * 32 * QB;
+
+  // Visible keys of query q: j < klim(q) with klim(q) = min(kv, q + 1) under
+  // the causal mask and kv otherwise (kv = valid keys of this batch entry).
+  const int kv = kv_len ? min(max(kv_len[bh / H], 0), N) : N;
+  auto klim = [&](int q) { return causal ? min(kv, q + 1) : kv; };
+  int klq[QB];  // per lane and row block
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) klq[qb] = klim(qw0 + qb * 32 + l32);
 
   // Q fragments: B operand of S^T = K Q^T (lane: query l32, dims 16cc + 8h + 0..7).
   // A negative scale is folded into Q (exact sign flip) so that c >= 0.
@@ -127,7 +137,12 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
   }
 
-  const int ntiles = (N + S::BC - 1) / S::BC;
+  // Tiles this workgroup reads, tiles every query of the workgroup sees in
+  // full (no mask), and per wave the same two bounds.
+  const int ntiles = (klim(qblk * S::BR + S::BR - 1) + S::BC - 1) / S::BC;
+  const int nfull_wg = klim(qblk * S::BR) / S::BC;
+  const int nfull_w = klim(qw0) / S::BC;
+  const int nvis_w = (klim(qw0 + 32 * QB - 1) + S::BC - 1) / S::BC;
 
   // K/V tile j -> ring slot j % NS by DMA. Wave w fills a contiguous run of
   // 16-byte LDS slots; the lane writing slot (row, s) fetches global chunk
@@ -160,17 +175,19 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   };
 
   for (int j = 0; j < NS - 1 && j < ntiles; ++j) dma_tile(j);
-  wait_tile(0);
+  if (ntiles > 0) wait_tile(0);
   __syncthreads();
 
-  // One K/V tile. MASKED (the last tile when N is not a multiple of the tile)
-  // drops keys past N from the row max and gives them probability 0; full
-  // tiles carry no masking code at all.
+  // One K/V tile. MASKED tiles (the partial last tile, key padding, the
+  // causal diagonal) drop each lane's invisible keys from the row max and give
+  // them probability 0; fully visible tiles carry no masking code at all.
   auto tile = [&](int j, auto masked) {
     constexpr bool MASKED = decltype(masked)::value;
     const unsigned char* Ks = smem + (j % NS) * 2 * S::TILEB;
     const unsigned char* Vs = Ks + S::TILEB;
-    const int kvalid = N - j * S::BC;
+    int kvalid[QB];  // visible keys of this tile, per row block (MASKED only)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) kvalid[qb] = klq[qb] - j * S::BC;
 
     // ---- S^T tile: BC keys x (32*QB) queries, fp32 accumulate.
     f32x16 sacc[QB][KB];
@@ -192,9 +209,9 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-          if (key >= kvalid)
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) sacc[qb][kb][e] = -INFINITY;
+          for (int qb = 0; qb < QB; ++qb)
+            if (key >= kvalid[qb]) sacc[qb][kb][e] = -INFINITY;
         }
     }
 
@@ -222,7 +239,8 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - mnew[qb]);
+        // A lane that has seen no visible key yet keeps max -inf (alpha = 1).
+        const float alpha = mnew[qb] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - mnew[qb]);
         m_run[qb] = mnew[qb];
         l_run[qb] *= alpha;
 #pragma unroll
@@ -244,8 +262,8 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
           float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][e + 1], c, nm));
           if (MASKED) {
             const int key = kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-            if (key >= kvalid) p0 = 0.f;
-            if (key + 1 >= kvalid) p1 = 0.f;
+            if (key >= kvalid[qb]) p0 = 0.f;
+            if (key + 1 >= kvalid[qb]) p1 = 0.f;
           }
           const uint32_t w = pack_bf16(p0, p1);
           pb[qb][kb][e >> 3][(e >> 1) & 3] = w;
@@ -270,21 +288,34 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         }
   };
 
-  // Full tiles in one single-path loop, then the partial last tile (if any).
-  const int nfull = N / S::BC;  // tiles whose keys are all < N
-  for (int j = 0; j < nfull; ++j) {
+  // Tiles every query of the workgroup sees in full run one single-path
+  // loop. In the rest each wave picks unmasked, masked or nothing for its own
+  // rows; all waves still take part in every DMA and barrier.
+  int j = 0;
+  for (; j < nfull_wg; ++j) {
     if (j + NS - 1 < ntiles) dma_tile(j + NS - 1);
     tile(j, BoolC<false>{});
     if (j + 1 < ntiles) wait_tile(j + 1);
     __syncthreads();
   }
-  if (nfull < ntiles) tile(nfull, BoolC<true>{});
+  for (; j < ntiles; ++j) {
+    if (j + NS - 1 < ntiles) dma_tile(j + NS - 1);
+    if (j < nfull_w)
+      tile(j, BoolC<false>{});
+    else if (j < nvis_w)
+      tile(j, BoolC<true>{});
+    if (j + 1 < ntiles) {
+      wait_tile(j + 1);
+      __syncthreads();
+    }
+  }
 
-  // ---- epilogue: O = O^T / l (bf16, RNE), lse = ln 2 * (m + log2 l).
+  // ---- epilogue: O = O^T / l (bf16, RNE), lse = ln 2 * (m + log2 l). A row
+  // with no visible key (l = 0) gets O = 0 and lse = -inf.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = halves_sum(l_run[qb]);
-    const float inv = 1.0f / lt;
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     const int q = qw0 + qb * 32 + l32;
     if (q < N) {
       uint16_t* orow = O + head + (size_t)q * D;
@@ -296,7 +327,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
           u32x2 w = {pack_bf16(a[4 * jj] * inv, a[4 * jj + 1] * inv), pack_bf16(a[4 * jj + 2] * inv, a[4 * jj + 3] * inv)};
           *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * jj + 4 * h) = w;
         }
-      if (h == 0) LSE[(size_t)bh * N + q] = (m_run[qb] + log2f(lt)) * kLn2;
+      if (h == 0) LSE[(size_t)bh * N + q] = lt > 0.f ? (m_run[qb] + log2f(lt)) * kLn2 : -INFINITY;
     }
   }
 }
@@ -391,27 +422,30 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 
 template <int D, int QB, int KB, int NS, int WAVES>
 static hipError_t launch_fwd_bf16_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
-                                    float* lse, int B, int H, int N, float scale, hipStream_t stream) {
+                                    float* lse, int B, int H, int N, float scale, int causal, const int* kv_len,
+                                    hipStream_t stream) {
   using S = FwdShape<D, QB, KB, NS, WAVES>;
   const int n_qblk = (N + S::BR - 1) / S::BR;
   const int total = n_qblk * B * H;
   const float c = fabsf(scale) * kLog2e;
   const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, KB, NS, WAVES>), dim3(total), dim3(S::THREADS), 0, stream, q, k, v, o,
-                     lse, N, n_qblk, total, c, qsign);
+                     lse, N, n_qblk, total, c, qsign, kv_len, H, causal);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int B,
-                           int H, int N, int d, float scale, hipStream_t stream) {
+                           int H, int N, int d, float scale, int causal, const int* kv_len, hipStream_t stream) {
   const bool lng = N >= FWD_LONG_N;
   if (d == 64)
     return lng ? launch_fwd_bf16_t<64, FWD_QB64, FWD_KB64, FWD_NS64, FWD_WAVES_LONG>(q, k, v, o, lse, B, H, N, scale,
-                                                                                    stream)
-               : launch_fwd_bf16_t<64, FWD_QB64, FWD_KB64, FWD_NS64, 4>(q, k, v, o, lse, B, H, N, scale, stream);
+                                                                                    causal, kv_len, stream)
+               : launch_fwd_bf16_t<64, FWD_QB64, FWD_KB64, FWD_NS64, 4>(q, k, v, o, lse, B, H, N, scale, causal,
+                                                                       kv_len, stream);
   return lng ? launch_fwd_bf16_t<128, FWD_QB128, FWD_KB128, FWD_NS128, FWD_WAVES_LONG>(q, k, v, o, lse, B, H, N, scale,
-                                                                                      stream)
-             : launch_fwd_bf16_t<128, FWD_QB128, FWD_KB128, FWD_NS128, 4>(q, k, v, o, lse, B, H, N, scale, stream);
+                                                                                      causal, kv_len, stream)
+             : launch_fwd_bf16_t<128, FWD_QB128, FWD_KB128, FWD_NS128, 4>(q, k, v, o, lse, B, H, N, scale, causal,
+                                                                         kv_len, stream);
 }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,

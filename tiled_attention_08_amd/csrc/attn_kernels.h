@@ -1,5 +1,5 @@
 // attn_kernels.h - launchers of the attention kernels (internal to libattn.so).
-// Each launcher assumes validated arguments (see attn_api.cpp) and only
+// Each launcher assumes validated arguments (see attn_api.hip) and only
 // enqueues work on `stream`; it returns hipGetLastError() of the launch.
 #pragma once
 
@@ -12,20 +12,23 @@ namespace attn {
 // Keys of a head handled by one dK/dV workgroup (32 per wave).
 constexpr int kBwdKeysPerBlock = 128;
 
+// causal != 0: query i sees keys j <= i. kv_len (device, B ints, or null):
+// keys j >= kv_len[b] are hidden from every query of batch entry b (values are
+// clamped to [0, N] on the device).
 hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int B,
-                           int H, int N, int d, float scale, hipStream_t stream);
+                           int H, int N, int d, float scale, int causal, const int* kv_len, hipStream_t stream);
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
                           int d, float scale, hipStream_t stream);
 
-// Workspace layout: delta [B*H*N] fp32, then (256-byte aligned) dq_acc [B*H*N*d] fp32.
+// Workspace layout: lse * log2(e) [B*H*N] fp32, then (256-byte aligned) -delta [B*H*N] fp32.
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
 
-// One backward stage: 0 = delta + zeroed dQ accumulator, 1 = main (dK, dV, dQ
-// accumulation), 2 = dQ conversion.
+// One backward stage: 0 = lse * log2(e) and -delta, 1 = dK and dV, 2 = dQ.
+// Masks as for launch_fwd_bf16.
 hipError_t launch_bwd_bf16_stage(int stage, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq, uint16_t* dk,
-                                 uint16_t* dv, int B, int H, int N, int d, float scale, void* workspace,
-                                 hipStream_t stream);
+                                 uint16_t* dv, int B, int H, int N, int d, float scale, int causal,
+                                 const int* kv_len, void* workspace, hipStream_t stream);
 
 }  // namespace attn
