@@ -6,7 +6,7 @@ forward (attn_fwd) followed by the recompute-based backward (attn_bwd: delta, dK
 and dQ launches), on the long-sequence workload B=8, H=16, N=4096, d_k=64, bf16
 (inputs seeded, already resident in device memory when timing starts).
 
-    python bench.py [--steps K] [--warmup W] [--workload 2|3|5] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload 2|3|4|5] [--causal] [--no-cpu-baseline]
 
 Prints ONE JSON line on stdout; progress goes to stderr. FLOPs are
 algorithmic: forward 4*B*H*N^2*d (Q K^T and P V), backward 10*B*H*N^2*d
@@ -40,12 +40,17 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def fwd_flops(B, H, N, d):
-    return 4.0 * B * H * N * N * d
+def pairs(N, causal=False):
+    """Query-key pairs of one head the method computes: N^2, or N(N+1)/2 under the causal mask."""
+    return N * (N + 1) / 2.0 if causal else float(N) * N
 
 
-def bwd_flops(B, H, N, d):
-    return 10.0 * B * H * N * N * d
+def fwd_flops(B, H, N, d, causal=False):
+    return 4.0 * B * H * pairs(N, causal) * d
+
+
+def bwd_flops(B, H, N, d, causal=False):
+    return 10.0 * B * H * pairs(N, causal) * d
 
 
 def time_launches(fn, reps: int) -> float:
@@ -89,11 +94,11 @@ def measured_traffic(workload: str, kernel: str):
     return None if k is None else int(k["traffic_bytes"])
 
 
-def cpu_baseline(wid: int, seed: int, budget_s: float) -> dict:
+def cpu_baseline(wid: int, seed: int, budget_s: float, causal: bool = False) -> dict:
     """The fp64 oracle (forward + backward) on whole heads of the workload, for about ``budget_s`` seconds."""
     import numpy as np
     from attn_inputs import WORKLOADS, make_inputs
-    from oracle import attention_bwd, attention_fwd
+    from oracle import attention_bwd, attention_fwd, masked_attention_bwd, masked_attention_fwd
     w = WORKLOADS[wid]
     x = make_inputs(wid, seed=seed)
     try:
@@ -107,14 +112,20 @@ def cpu_baseline(wid: int, seed: int, budget_s: float) -> dict:
         b, h = order[heads]
         Q, K, V = (x.f64(n, (b, h)) for n in ("q", "k", "v"))
         t0 = time.perf_counter()
-        attention_fwd(Q, K, V, x.scale)
-        if "bwd" in w.passes:
-            attention_bwd(Q, K, V, x.f64("do", (b, h)), x.scale)
+        if causal:
+            Q, K, V = Q[None, None], K[None, None], V[None, None]
+            masked_attention_fwd(Q, K, V, x.scale, causal=True)
+            if "bwd" in w.passes:
+                masked_attention_bwd(Q, K, V, x.f64("do", (b, h))[None, None], x.scale, causal=True)
+        else:
+            attention_fwd(Q, K, V, x.scale)
+            if "bwd" in w.passes:
+                attention_bwd(Q, K, V, x.f64("do", (b, h)), x.scale)
         elapsed += time.perf_counter() - t0
         heads += 1
-    flops = (fwd_flops(1, heads, w.N, w.d) + (bwd_flops(1, heads, w.N, w.d) if "bwd" in w.passes else 0.0))
+    flops = (fwd_flops(1, heads, w.N, w.d, causal) + (bwd_flops(1, heads, w.N, w.d, causal) if "bwd" in w.passes else 0.0))
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.H} heads of the same workload ({'+'.join(w.passes)}, fp64, full N x N per head), "
+            "sample": f"{heads} of {w.B * w.H} heads of the same workload ({'+'.join(w.passes)}{', causal' if causal else ''}, fp64, full N x N per head), "
                       f"{elapsed:.1f} s", "seconds": round(elapsed, 3)}
 
 
@@ -129,6 +140,9 @@ def main(argv=None) -> int:
     ap.add_argument("--kernel-reps", type=int, default=20, help="launches per kernel for the roofline timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--causal", action="store_true",
+                    help="time the causal-mask path (attn_fwd_ex / attn_bwd_ex); FLOPs count the N(N+1)/2 visible "
+                         "query-key pairs of each head")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (three times) and exit: the "
                          "known-size reference for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -176,6 +190,11 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream()
 
     def step():
+        if args.causal:
+            attn.attn_fwd_ex(q, k, v, o, lse, scale, causal=True, stream=stream)
+            if with_bwd:
+                attn.attn_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale, ws, causal=True, stream=stream)
+            return
         attn.attn_fwd(q, k, v, o, lse, scale, stream)
         if with_bwd:
             attn.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream)
@@ -201,16 +220,17 @@ def main(argv=None) -> int:
     t_end.record(stream)
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
-    flops = fwd_flops(B, H, N, d) + (bwd_flops(B, H, N, d) if with_bwd else 0.0)
+    cz = args.causal
+    flops = fwd_flops(B, H, N, d, cz) + (bwd_flops(B, H, N, d, cz) if with_bwd else 0.0)
     value = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {ms:.3f} ms/step, {value:.1f} TFLOP/s")
 
     # Per-kernel timing (each kernel alone, back-to-back launches on the same stream).
     reps = args.kernel_reps
     def stage(i):
-        return lambda: attn.attn_bwd_stage(i, q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream=stream)
+        return lambda: attn.attn_bwd_stage(i, q, k, v, o, lse, do, dq, dk, dv, scale, ws, causal=cz, stream=stream)
 
-    kernels = {"fwd": time_launches(lambda: attn.attn_fwd(q, k, v, o, lse, scale, stream), reps)}
+    kernels = {"fwd": time_launches(lambda: attn.attn_fwd_ex(q, k, v, o, lse, scale, causal=cz, stream=stream), reps)}
     if with_bwd:
         kernels.update({"bwd_prep": time_launches(stage(0), reps), "bwd_dkdv": time_launches(stage(1), reps),
                         "bwd_dq": time_launches(stage(2), reps)})
@@ -219,8 +239,8 @@ def main(argv=None) -> int:
     # dP, dV and dK products (8 B H N^2 d). The dQ kernel repeats S and dP to
     # avoid a cross-workgroup reduction; only its dQ product (2 B H N^2 d) is
     # algorithmic work, so its roofline fraction counts that alone.
-    kflops = {"fwd": fwd_flops(B, H, N, d), "bwd_dkdv": 0.8 * bwd_flops(B, H, N, d),
-              "bwd_dq": 0.2 * bwd_flops(B, H, N, d)}
+    kflops = {"fwd": fwd_flops(B, H, N, d, cz), "bwd_dkdv": 0.8 * bwd_flops(B, H, N, d, cz),
+              "bwd_dq": 0.2 * bwd_flops(B, H, N, d, cz)}
     kname_full = {"fwd": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel",
                   "bwd_prep": "bwd_prep_kernel"}
     dominant = max(kernels, key=kernels.get)
@@ -228,31 +248,31 @@ def main(argv=None) -> int:
         achieved = kflops[dominant] / (kernels[dominant] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": measured_traffic(w.name, kname_full[dominant]),
+                    "traffic": measured_traffic(w.name + ("_causal" if cz else ""), kname_full[dominant]),
                     "kernel": kname_full[dominant], "avg_ms": round(kernels[dominant], 5)}
     else:  # the HBM-bound delta kernel dominates (tiny workloads only)
         rows = B * H * N
         nbytes = rows * d * 2 * 2 + rows * 4
         achieved = nbytes / (kernels[dominant] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name, kname_full[dominant]),
+                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name + ("_causal" if cz else ""), kname_full[dominant]),
                     "kernel": kname_full[dominant], "avg_ms": round(kernels[dominant], 5)}
 
     record = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC if not cz else METRIC + ", causal mask (N(N+1)/2 pairs per head)", "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d_k": d, "passes": "+".join(w.passes),
+        "config": {"workload": w.name + ("_causal" if cz else ""), "B": B, "H": H, "N": N, "d_k": d, "passes": "+".join(w.passes),
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "frac_of_bf16_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "kernel_ms": {kname: round(t, 5) for kname, t in kernels.items()},
-        "fwd_tflops": round(fwd_flops(B, H, N, d) / (kernels["fwd"] * 1e-3) / 1e12, 2),
+        "fwd_tflops": round(fwd_flops(B, H, N, d, cz) / (kernels["fwd"] * 1e-3) / 1e12, 2),
         "roofline": roofline,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        record["cpu_baseline"] = cpu_baseline(args.workload, args.seed, args.cpu_seconds)
+        record["cpu_baseline"] = cpu_baseline(args.workload, args.seed, args.cpu_seconds, cz)
     print(json.dumps(record), flush=True)
     return 0
 

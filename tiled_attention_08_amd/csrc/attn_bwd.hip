@@ -131,7 +131,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int g = lane >> 4, gi = lane & 15;
   const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
   const int work = xcd_remap(blockIdx.x, total);
-  const int bh = work / n_kblk, kblk = work - bh * n_kblk;
+  int bh, kblk;  // causal: the first key blocks have the most queries and are handed out first
+  work_order(work, total, n_kblk, causal != 0, false, bh, kblk);
   const size_t head = (size_t)bh * N * D;
   const size_t hrow = (size_t)bh * N;
   const int k0 = kblk * BCK;
@@ -360,9 +361,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int g = lane >> 4, gi = lane & 15;
   const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
   const int work = xcd_remap(blockIdx.x, total);
-  const int bh = work / n_qblk;
-  // Causal: the last row blocks have the most keys; they are handed out first.
-  const int qblk = causal ? n_qblk - 1 - (work - bh * n_qblk) : work - bh * n_qblk;
+  int bh, qblk;  // causal: the last row blocks have the most keys and are handed out first
+  work_order(work, total, n_qblk, causal != 0, true, bh, qblk);
   const size_t head = (size_t)bh * N * D;
   const size_t hrow = (size_t)bh * N;
   const int qw0 = qblk * S::BR + wave * 32 * QB;

@@ -161,4 +161,26 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
   return x * per + (x < rem ? x : rem) + slot;
 }
 
+// (head, block) of work item `work` (after xcd_remap) for a grid of total =
+// heads * n_blk items. Plain order: head-major, block ascending. With
+// `causal`, blocks carry unequal work (the block with the most is n_blk - 1
+// when heavy_last, else 0) and are handed out heaviest first: when each XCD's
+// range holds whole heads, the range is ordered by block (heaviest first),
+// then head, so every XCD keeps its own heads (and their K/V in its L2) while
+// the long blocks of all of them start before any short one; otherwise blocks
+// are reversed within each head.
+__device__ __forceinline__ void work_order(int work, int total, int n_blk, bool causal, bool heavy_last, int& bh,
+                                           int& blk) {
+  bh = work / n_blk;
+  blk = work - bh * n_blk;
+  if (!causal) return;
+  const int per = total >> 3;
+  if ((total & 7) == 0 && per % n_blk == 0) {
+    const int hpx = per / n_blk, x = work / per, r = work - x * per, rank = r / hpx;
+    bh = x * hpx + (r - rank * hpx);
+    blk = rank;
+  }
+  if (heavy_last) blk = n_blk - 1 - blk;
+}
+
 }  // namespace attn

@@ -95,9 +95,8 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int g = lane >> 4, gi = lane & 15;
   const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
   const int work = xcd_remap(blockIdx.x, total);
-  const int bh = work / n_qblk;
-  // Causal: the last row blocks have the most keys; they are handed out first.
-  const int qblk = causal ? n_qblk - 1 - (work - bh * n_qblk) : work - bh * n_qblk;
+  int bh, qblk;  // causal: the last row blocks have the most keys and are handed out first
+  work_order(work, total, n_qblk, causal != 0, true, bh, qblk);
   const size_t head = (size_t)bh * N * D;
   const uint16_t* Qh = Q + head;
   const uint16_t* Kh = K + head;
@@ -107,10 +106,8 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   // Visible keys of query q: j < klim(q) with klim(q) = min(kv, q + 1) under
   // the causal mask and kv otherwise (kv = valid keys of this batch entry).
   const int kv = kv_len ? min(max(kv_len[bh / H], 0), N) : N;
-  auto klim = [&](int q) { return causal ? min(kv, q + 1) : kv; };
-  int klq[QB];  // per lane and row block
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) klq[qb] = klim(qw0 + qb * 32 + l32);
+  const int cshift = causal ? 0 : N;  // klim(q) = min(kv, q + 1 + cshift); q + 1 + N > kv for every q
+  auto klim = [&](int q) { return min(kv, q + 1 + cshift); };
 
   // Q fragments: B operand of S^T = K Q^T (lane: query l32, dims 16cc + 8h + 0..7).
   // A negative scale is folded into Q (exact sign flip) so that c >= 0.
@@ -138,10 +135,9 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
 
   // Tiles this workgroup reads, tiles every query of the workgroup sees in
-  // full (no mask), and per wave the same two bounds.
+  // full (no mask), and the tiles this wave sees any key of.
   const int ntiles = (klim(qblk * S::BR + S::BR - 1) + S::BC - 1) / S::BC;
   const int nfull_wg = klim(qblk * S::BR) / S::BC;
-  const int nfull_w = klim(qw0) / S::BC;
   const int nvis_w = (klim(qw0 + 32 * QB - 1) + S::BC - 1) / S::BC;
 
   // K/V tile j -> ring slot j % NS by DMA. Wave w fills a contiguous run of
@@ -187,7 +183,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     const unsigned char* Vs = Ks + S::TILEB;
     int kvalid[QB];  // visible keys of this tile, per row block (MASKED only)
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) kvalid[qb] = klq[qb] - j * S::BC;
+    for (int qb = 0; qb < QB; ++qb) kvalid[qb] = klim(qw0 + qb * 32 + l32) - j * S::BC;
 
     // ---- S^T tile: BC keys x (32*QB) queries, fp32 accumulate.
     f32x16 sacc[QB][KB];
@@ -289,8 +285,8 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   };
 
   // Tiles every query of the workgroup sees in full run one single-path
-  // loop. In the rest each wave picks unmasked, masked or nothing for its own
-  // rows; all waves still take part in every DMA and barrier.
+  // loop. In the rest each wave runs the masked tile or, past its last
+  // visible key, nothing; all waves still take part in every DMA and barrier.
   int j = 0;
   for (; j < nfull_wg; ++j) {
     if (j + NS - 1 < ntiles) dma_tile(j + NS - 1);
@@ -300,10 +296,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
   for (; j < ntiles; ++j) {
     if (j + NS - 1 < ntiles) dma_tile(j + NS - 1);
-    if (j < nfull_w)
-      tile(j, BoolC<false>{});
-    else if (j < nvis_w)
-      tile(j, BoolC<true>{});
+    if (j < nvis_w) tile(j, BoolC<true>{});  // masks are no-ops on the tiles this wave sees in full
     if (j + 1 < ntiles) {
       wait_tile(j + 1);
       __syncthreads();
