@@ -16,7 +16,8 @@ Generator recipe (the same for every workload):
   rng = numpy.random.Generator(PCG64(SeedSequence([seed, workload_id])))
   draw order Q, K, V, dO; each drawn in float32 as rng.standard_normal * sigma
   (or rng.uniform(-1, 1) where the workload says so), then rounded
-  round-to-nearest-even to bfloat16 for bf16 workloads. The rounded bits are
+  round-to-nearest-even to bfloat16 for bf16 cases (to IEEE binary16 for f16
+  cases, numpy's float16 conversion, also round-to-nearest-even). The rounded bits are
   uploaded unchanged, and their exact values (upcast to float64) feed the
   oracle.
 """
@@ -48,7 +49,7 @@ class Workload:
     H: int
     N: int
     d: int
-    dtype: str                 # "f32" or "bf16": storage type of Q, K, V, O, dO, dQ, dK, dV
+    dtype: str                 # "f32", "bf16" or "f16": storage type of Q, K, V, O, dO, dQ, dK, dV
     passes: Tuple[str, ...]    # ("fwd",) or ("fwd", "bwd")
     qk_sigma: float = 1.0      # Q, K ~ N(0, qk_sigma^2)
     v_dist: str = "normal"     # "normal" -> N(0,1); "uniform" -> U(-1, 1)
@@ -95,8 +96,8 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 class Inputs:
     """One seeded problem instance.
 
-    ``raw[name]`` holds what is uploaded: uint16 bfloat16 bit patterns for bf16
-    workloads, float32 for f32 ones, each of shape [B, H, N, d] contiguous.
+    ``raw[name]`` holds what is uploaded: uint16 bit patterns for bf16 and f16
+    cases, float32 for f32 ones, each of shape [B, H, N, d] contiguous.
     ``planted`` (stress workload only) is an int array [B, H, R, 2] of
     (query row, key row) pairs where K[key] was set to a copy of Q[row].
     """
@@ -114,6 +115,8 @@ class Inputs:
         a = self.raw[name][index]
         if self.dtype == "bf16":
             return bf16_bits_to_f64(a)
+        if self.dtype == "f16":
+            return np.ascontiguousarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
         return np.asarray(a, dtype=np.float64)
 
 
@@ -134,8 +137,8 @@ def make_case(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: int = 0
               qk_sigma: float = 1.0, v_dist: str = "normal", planted_frac: float = 0.0,
               with_grad: bool = True, scale: Optional[float] = None) -> Inputs:
     """Draw Q, K, V (and dO) for an arbitrary shape with the workload recipe."""
-    if dtype not in ("bf16", "f32"):
-        raise ValueError("dtype must be 'bf16' or 'f32'")
+    if dtype not in ("bf16", "f16", "f32"):
+        raise ValueError("dtype must be 'bf16', 'f16' or 'f32'")
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(wid)])))
     shape = (B, H, N, d)
     q = _draw(rng, shape, "normal", qk_sigma)
@@ -162,7 +165,12 @@ def make_case(B: int, H: int, N: int, d: int, dtype: str = "bf16", seed: int = 0
     for name, arr in (("q", q), ("k", k), ("v", v), ("do", do)):
         if arr is None:
             continue
-        raw[name] = f32_to_bf16_bits(arr).reshape(shape) if dtype == "bf16" else arr
+        if dtype == "bf16":
+            raw[name] = f32_to_bf16_bits(arr).reshape(shape)
+        elif dtype == "f16":
+            raw[name] = arr.astype(np.float16).view(np.uint16)
+        else:
+            raw[name] = arr
     sc = float(np.float32(1.0 / math.sqrt(d))) if scale is None else float(np.float32(scale))
     return Inputs(B, H, N, d, dtype, sc, raw, planted)
 

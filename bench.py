@@ -140,6 +140,8 @@ def main(argv=None) -> int:
     ap.add_argument("--kernel-reps", type=int, default=20, help="launches per kernel for the roofline timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dtype", default="bf16", choices=("bf16", "f16"),
+                    help="storage type of Q, K, V, O and the gradients (f16 runs attn_fwd_ex / attn_bwd_ex)")
     ap.add_argument("--causal", action="store_true",
                     help="time the causal-mask path (attn_fwd_ex / attn_bwd_ex); FLOPs count the N(N+1)/2 visible "
                          "query-key pairs of each head")
@@ -167,16 +169,24 @@ def main(argv=None) -> int:
 
     import numpy as np
     import torch
-    from attn_inputs import WORKLOADS, make_inputs
+    from attn_inputs import WORKLOADS, make_case, make_inputs
     from tiled_attention_08_amd import _lib as attn
 
     w = WORKLOADS[args.workload]
     B, H, N, d = w.B, w.H, w.N, w.d
-    log(f"[bench] workload {w.wid} {w.name}: B={B} H={H} N={N} d={d} bf16, seed {args.seed}")
-    x = make_inputs(args.workload, seed=args.seed)
+    cz = args.causal
+    log(f"[bench] workload {w.wid} {w.name}: B={B} H={H} N={N} d={d} {args.dtype}{' causal' if cz else ''}, seed {args.seed}")
+    if args.dtype == "bf16":
+        x = make_inputs(args.workload, seed=args.seed)
+    else:
+        x = make_case(B, H, N, d, args.dtype, seed=args.seed, wid=w.wid, qk_sigma=w.qk_sigma, v_dist=w.v_dist,
+                      planted_frac=w.planted_frac, with_grad="bwd" in w.passes)
 
     def up(name):
-        return torch.from_numpy(np.ascontiguousarray(x.raw[name]).view(np.int16)).view(torch.bfloat16).cuda()
+        a = np.ascontiguousarray(x.raw[name])
+        if args.dtype == "f16":
+            return torch.from_numpy(a.view(np.float16)).cuda()
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
 
     with_bwd = "bwd" in w.passes
     q, k, v = up("q"), up("k"), up("v")
@@ -190,10 +200,10 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream()
 
     def step():
-        if args.causal:
-            attn.attn_fwd_ex(q, k, v, o, lse, scale, causal=True, stream=stream)
+        if args.causal or args.dtype != "bf16":
+            attn.attn_fwd_ex(q, k, v, o, lse, scale, causal=cz, stream=stream)
             if with_bwd:
-                attn.attn_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale, ws, causal=True, stream=stream)
+                attn.attn_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale, ws, causal=cz, stream=stream)
             return
         attn.attn_fwd(q, k, v, o, lse, scale, stream)
         if with_bwd:
@@ -220,7 +230,6 @@ def main(argv=None) -> int:
     t_end.record(stream)
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
-    cz = args.causal
     flops = fwd_flops(B, H, N, d, cz) + (bwd_flops(B, H, N, d, cz) if with_bwd else 0.0)
     value = flops / (ms * 1e-3) / 1e12
     log(f"[bench] {ms:.3f} ms/step, {value:.1f} TFLOP/s")
@@ -241,28 +250,28 @@ def main(argv=None) -> int:
     # algorithmic work, so its roofline fraction counts that alone.
     kflops = {"fwd": fwd_flops(B, H, N, d, cz), "bwd_dkdv": 0.8 * bwd_flops(B, H, N, d, cz),
               "bwd_dq": 0.2 * bwd_flops(B, H, N, d, cz)}
-    kname_full = {"fwd": "fwd_bf16_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel",
+    kname_full = {"fwd": "fwd_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel",
                   "bwd_prep": "bwd_prep_kernel"}
     dominant = max(kernels, key=kernels.get)
     if dominant in kflops:
         achieved = kflops[dominant] / (kernels[dominant] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": measured_traffic(w.name + ("_causal" if cz else ""), kname_full[dominant]),
+                    "traffic": measured_traffic(w.name + ("_causal" if cz else "") + ("_f16" if args.dtype == "f16" else ""), kname_full[dominant]),
                     "kernel": kname_full[dominant], "avg_ms": round(kernels[dominant], 5)}
     else:  # the HBM-bound delta kernel dominates (tiny workloads only)
         rows = B * H * N
         nbytes = rows * d * 2 * 2 + rows * 4
         achieved = nbytes / (kernels[dominant] * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name + ("_causal" if cz else ""), kname_full[dominant]),
+                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name + ("_causal" if cz else "") + ("_f16" if args.dtype == "f16" else ""), kname_full[dominant]),
                     "kernel": kname_full[dominant], "avg_ms": round(kernels[dominant], 5)}
 
     record = {
         "metric": METRIC if not cz else METRIC + ", causal mask (N(N+1)/2 pairs per head)", "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name + ("_causal" if cz else ""), "B": B, "H": H, "N": N, "d_k": d, "passes": "+".join(w.passes),
+        "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
+        "config": {"workload": w.name + ("_causal" if cz else "") + ("_f16" if args.dtype == "f16" else ""), "B": B, "H": H, "N": N, "d_k": d, "passes": "+".join(w.passes),
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "frac_of_bf16_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "kernel_ms": {kname: round(t, 5) for kname, t in kernels.items()},

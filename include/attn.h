@@ -120,11 +120,15 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  * O = 0 and lse = -inf, and passes no gradient: its dQ row is 0, and keys no
  * query sees get dK = dV = 0.
  *
- * dtype is an attn_dtype_t. ATTN_DTYPE_BF16: Q, K, V, O, dO, dQ, dK, dV are
- * bfloat16; attn_fwd_ex(ATTN_DTYPE_BF16, ..., 0, NULL, stream) is attn_fwd.
- * Any other value returns ATTN_ERR_UNSUPPORTED.
+ * dtype is an attn_dtype_t, the storage type of Q, K, V, O, dO, dQ, dK, dV
+ * (lse and the workspace stay float32): ATTN_DTYPE_BF16 (bfloat16) or
+ * ATTN_DTYPE_F16 (IEEE binary16). Both use the matrix cores in that type with
+ * float32 accumulation; probabilities and dS are rounded to it (nearest even)
+ * before their products, and outputs are rounded to it.
+ * attn_fwd_ex(ATTN_DTYPE_BF16, ..., 0, NULL, stream) is attn_fwd. Any other
+ * dtype returns ATTN_ERR_UNSUPPORTED.
  */
-typedef enum { ATTN_DTYPE_BF16 = 0 } attn_dtype_t;
+typedef enum { ATTN_DTYPE_BF16 = 0, ATTN_DTYPE_F16 = 1 } attn_dtype_t;
 
 int attn_fwd_ex(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int H, int N, int d_k, float scale, int causal, const int* kv_len, void* stream);

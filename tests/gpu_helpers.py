@@ -19,6 +19,10 @@ TOL_F32_LSE = 1e-5
 TOL_BF16_O = 2e-2
 TOL_BF16_LSE_REL = 4e-3
 TOL_GRAD_RELL2 = 5e-2
+# fp16 storage: the same O and gradient bounds; the weights carry 11
+# significant bits (at most 2^-11 ~ 4.9e-4 relative rounding), so lse is held
+# to 1e-3 * max(1, |lse|).
+TOL_F16_LSE_REL = 1e-3
 
 
 def to_device(x: Inputs, name: str):
@@ -26,6 +30,8 @@ def to_device(x: Inputs, name: str):
     a = x.raw[name]
     if x.dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    if x.dtype == "f16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.float16)).cuda()
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 

@@ -102,7 +102,7 @@ def test_forward_rejections(L):
 
 def test_extended_forward_rejections(L):
     INV, UNS = L.ATTN_ERR_INVALID_ARG, L.ATTN_ERR_UNSUPPORTED
-    assert fwd_ex(L, dtype=1) == UNS and fwd_ex(L, dtype=-1) == UNS
+    assert fwd_ex(L, dtype=2) == UNS and fwd_ex(L, dtype=-1) == UNS
     assert fwd_ex(L, causal=2) == INV and fwd_ex(L, causal=-1) == INV
     assert fwd_ex(L, kv_len=A[10] + 2) == INV               # kv_len not 4-byte aligned
     assert fwd_ex(L, kv_len=A[3] + 4) == INV                # kv_len inside o

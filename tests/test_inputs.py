@@ -61,3 +61,14 @@ def test_stress_distributions_and_planting():
         rows, keys = x.planted[0, h, :, 0], x.planted[0, h, :, 1]
         assert len(set(rows.tolist())) == 20 and len(set(keys.tolist())) == 20
         np.testing.assert_array_equal(x.raw["k"][0, h, keys], x.raw["q"][0, h, rows])
+
+
+def test_f16_rounding_matches_torch():
+    """fp16 cases round with numpy's float16 conversion (nearest even), the same as torch's CPU cast."""
+    torch = pytest.importorskip("torch")
+    x = make_case(1, 2, 50, 64, "f16", seed=9)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([9, 0])))
+    q32 = rng.standard_normal(size=(1, 2, 50, 64), dtype=np.float32)
+    ref = torch.from_numpy(q32).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(x.raw["q"], ref)
+    np.testing.assert_array_equal(x.f64("q"), ref.view(np.float16).astype(np.float64))

@@ -20,6 +20,7 @@ ATTN_ERR_UNSUPPORTED = -2
 ATTN_ERR_WORKSPACE = -3
 ATTN_ERR_HIP = -4
 ATTN_DTYPE_BF16 = 0
+ATTN_DTYPE_F16 = 1
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_bwd_stage",
@@ -105,6 +106,8 @@ def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.bfloat16:
         return ATTN_DTYPE_BF16
+    if t.dtype == torch.float16:
+        return ATTN_DTYPE_F16
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
@@ -188,13 +191,20 @@ def attn_bwd_stage(stage: int, q, k, v, o, lse, do, dq, dk, dv, scale: float, wo
 
 # ---------------------------------------------------------------- allocating conveniences
 
-def forward(q, k, v, scale: float, stream=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
-    """Allocate O and lse with torch, then run the forward matching q's dtype (bf16 or float32)."""
+def forward(q, k, v, scale: float, stream=None, causal: bool = False, kv_len=None):
+    """Allocate O and lse with torch, then run the forward matching q's dtype (bf16, float16 or float32)."""
     import torch
     B, H, N, d = _shape(q, k, v)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    (attn_fwd if q.dtype == torch.bfloat16 else attn_fwd_f32)(q, k, v, o, lse, scale, stream)
+    if q.dtype == torch.float32:
+        if causal or kv_len is not None:
+            raise ValueError("the float32 forward takes no mask")
+        attn_fwd_f32(q, k, v, o, lse, scale, stream)
+    elif q.dtype == torch.bfloat16 and not causal and kv_len is None:
+        attn_fwd(q, k, v, o, lse, scale, stream)
+    else:
+        attn_fwd_ex(q, k, v, o, lse, scale, causal=causal, kv_len=kv_len, stream=stream)
     return o, lse
 
 
@@ -204,11 +214,14 @@ def workspace_for(q) -> "torch.Tensor":
     return torch.empty(attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
 
 
-def backward(q, k, v, o, lse, do, scale: float, workspace=None, stream=None):
-    """Allocate dQ, dK, dV (and the workspace unless given), then run the bf16 backward."""
+def backward(q, k, v, o, lse, do, scale: float, workspace=None, stream=None, causal: bool = False, kv_len=None):
+    """Allocate dQ, dK, dV (and the workspace unless given), then run the 16-bit backward matching q's dtype."""
     import torch
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
         workspace = workspace_for(q)
-    attn_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, workspace, stream)
+    if q.dtype == torch.bfloat16 and not causal and kv_len is None:
+        attn_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, workspace, stream)
+    else:
+        attn_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale, workspace, causal=causal, kv_len=kv_len, stream=stream)
     return dq, dk, dv

@@ -61,7 +61,7 @@ int attn_fwd_ex(int dtype, const void* q, const void* k, const void* v, void* o,
   size_t E = 0, R = 0;
   const int st = check_shape(B, H, N, d_k, scale, &E, &R);
   if (st != ATTN_OK) return st;
-  if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
   if (kv_len != nullptr && (reinterpret_cast<uintptr_t>(kv_len) & 3u) != 0) return ATTN_ERR_INVALID_ARG;
@@ -72,7 +72,7 @@ int attn_fwd_ex(int dtype, const void* q, const void* k, const void* v, void* o,
     const Range rkv = span(kv_len, (size_t)B * 4);
     if (overlap(rkv, ro) || overlap(rkv, rl)) return ATTN_ERR_INVALID_ARG;
   }
-  return from_hip(attn::launch_fwd_bf16(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+  return from_hip(attn::launch_fwd_16(dtype == ATTN_DTYPE_F16, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                         static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, B, H, N, d_k,
                                         scale, causal, kv_len, static_cast<hipStream_t>(stream)));
 }
@@ -108,7 +108,7 @@ int bwd_checks(int dtype, const void* q, const void* k, const void* v, const voi
   size_t E = 0, R = 0;
   const int st = check_shape(B, H, N, d_k, scale, &E, &R);
   if (st != ATTN_OK) return st;
-  if (dtype != ATTN_DTYPE_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
   if (kv_len != nullptr && (reinterpret_cast<uintptr_t>(kv_len) & 3u) != 0) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(dO) ||
@@ -130,11 +130,11 @@ int bwd_checks(int dtype, const void* q, const void* k, const void* v, const voi
   return ATTN_OK;
 }
 
-int bwd_launch(int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
+int bwd_launch(int dtype, int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k, float scale, int causal,
                const int* kv_len, void* workspace, void* stream) {
-  return from_hip(attn::launch_bwd_bf16_stage(
-      stage, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+  return from_hip(attn::launch_bwd_16_stage(
+      dtype == ATTN_DTYPE_F16, stage, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
       static_cast<const uint16_t*>(o), lse, static_cast<const uint16_t*>(dO), static_cast<uint16_t*>(dq),
       static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B, H, N, d_k, scale, causal, kv_len, workspace,
       static_cast<hipStream_t>(stream)));
@@ -149,7 +149,7 @@ int attn_bwd_ex(int dtype, const void* q, const void* k, const void* v, const vo
                             workspace_bytes);
   if (st != ATTN_OK) return st;
   for (int stage = 0; stage < 3; ++stage) {
-    const int r = bwd_launch(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, workspace,
+    const int r = bwd_launch(dtype, stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, workspace,
                              stream);
     if (r != ATTN_OK) return r;
   }
@@ -171,7 +171,8 @@ int attn_bwd_stage(int stage, int dtype, const void* q, const void* k, const voi
   const int st = bwd_checks(dtype, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, workspace,
                             workspace_bytes);
   if (st != ATTN_OK) return st;
-  return bwd_launch(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, workspace, stream);
+  return bwd_launch(dtype, stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, workspace,
+                    stream);
 }
 
 }  // extern "C"

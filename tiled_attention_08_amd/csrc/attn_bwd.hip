@@ -48,7 +48,7 @@ constexpr int BCQ = 32;                  // dQ kernel: keys per step
 
 // ---------------------------------------------------------------- stage 0: delta
 // 8 lanes per row; each lane covers D/8 consecutive elements.
-template <int D>
+template <class E, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
                                                        const float* __restrict__ LSE, float* __restrict__ lse2,
                                                        float* __restrict__ ndelta, long rows) {
@@ -66,8 +66,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
       const u32x4 b = *reinterpret_cast<const u32x4*>(g + c);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        s = fmaf(__uint_as_float(a[w] << 16), __uint_as_float(b[w] << 16), s);
-        s = fmaf(__uint_as_float(a[w] & 0xffff0000u), __uint_as_float(b[w] & 0xffff0000u), s);
+        s = fmaf(E::lo(a[w]), E::lo(b[w]), s);
+        s = fmaf(E::hi(a[w]), E::hi(b[w]), s);
       }
     }
   }
@@ -115,7 +115,7 @@ struct DkdvShape {
 
 // d_k = 128 needs more than 256 registers per lane (its dK and dV
 // accumulators alone take 128): one wave per SIMD there.
-template <int D, int MB>
+template <class E, int D, int MB>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(D == 64 ? BWD_WAVES_PER_EU : 1, D == 64 ? BWD_WAVES_PER_EU : 1)))
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -155,7 +155,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
 
   // K and V fragments of this lane's key: B operands of S = Q K^T and dP = dO V^T.
-  bf16x8 kf[D / 16], vf[D / 16];
+  u32x4 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int cc = 0; cc < D / 16; ++cc) {
     u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
@@ -163,8 +163,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       a = *reinterpret_cast<const u32x4*>(K + head + (size_t)key * D + cc * 16 + h * 8);
       b = *reinterpret_cast<const u32x4*>(V + head + (size_t)key * D + cc * 16 + h * 8);
     }
-    kf[cc] = as_bf16x8(a);
-    vf[cc] = as_bf16x8(b);
+    kf[cc] = a;
+    vf[cc] = b;
   }
 
   auto dma_step = [&](int i, int buf) {
@@ -228,8 +228,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
       for (int cc = 0; cc < D / 16; ++cc) {
         const int off = tile_off<S::ROWB>(mb * 32 + l32, cc * 16 + h * 8);
-        sacc[mb] = mfma32x32x16(as_bf16x8(lds_read_b128(Qs, off)), kf[cc], sacc[mb]);
-        pacc[mb] = mfma32x32x16(as_bf16x8(lds_read_b128(dOs, off)), vf[cc], pacc[mb]);
+        sacc[mb] = E::mfma(lds_read_b128(Qs, off), kf[cc], sacc[mb]);
+        pacc[mb] = E::mfma(lds_read_b128(dOs, off), vf[cc], pacc[mb]);
       }
     }
 
@@ -254,10 +254,10 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
           ds[ii] = p[ii] * pacc[mb][4 * jj + ii];
         }
         const int c2 = jj >> 1, w0 = 2 * (jj & 1);
-        pp[mb][c2][w0] = pack_bf16(p[0], p[1]);
-        pp[mb][c2][w0 + 1] = pack_bf16(p[2], p[3]);
-        dsb[mb][c2][w0] = pack_bf16(ds[0], ds[1]);
-        dsb[mb][c2][w0 + 1] = pack_bf16(ds[2], ds[3]);
+        pp[mb][c2][w0] = E::pack(p[0], p[1]);
+        pp[mb][c2][w0 + 1] = E::pack(p[2], p[3]);
+        dsb[mb][c2][w0] = E::pack(ds[0], ds[1]);
+        dsb[mb][c2][w0 + 1] = E::pack(ds[2], ds[3]);
       }
 
     // ---- dV^T += dO^T P and dK^T += Q^T dS (m = dim, n = key, k = query).
@@ -270,10 +270,10 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         for (int db = 0; db < D / 32; ++db) {
           const int col = db * 32 + dsub * 16 + 4 * qq;
           const int o0 = tile_off<S::ROWB>(row0, col), o1 = tile_off<S::ROWB>(row0 + 8, col);
-          const bf16x8 adot = as_bf16x8(lds_read_tr16_b64(dOs, o0), lds_read_tr16_b64(dOs, o1));
-          const bf16x8 aqt = as_bf16x8(lds_read_tr16_b64(Qs, o0), lds_read_tr16_b64(Qs, o1));
-          dvacc[db] = mfma32x32x16(adot, as_bf16x8(pp[mb][c2]), dvacc[db]);
-          dkacc[db] = mfma32x32x16(aqt, as_bf16x8(dsb[mb][c2]), dkacc[db]);
+          const u32x4 adot = cat(lds_read_tr16_b64(dOs, o0), lds_read_tr16_b64(dOs, o1));
+          const u32x4 aqt = cat(lds_read_tr16_b64(Qs, o0), lds_read_tr16_b64(Qs, o1));
+          dvacc[db] = E::mfma(adot, pp[mb][c2], dvacc[db]);
+          dkacc[db] = E::mfma(aqt, dsb[mb][c2], dkacc[db]);
         }
       }
 
@@ -327,9 +327,9 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       for (int jj = 0; jj < 4; ++jj) {
         const f32x16& a = dvacc[db];
         const f32x16& b = dkacc[db];
-        const u32x2 wv = {pack_bf16(a[4 * jj], a[4 * jj + 1]), pack_bf16(a[4 * jj + 2], a[4 * jj + 3])};
-        const u32x2 wk = {pack_bf16(b[4 * jj] * scale, b[4 * jj + 1] * scale),
-                          pack_bf16(b[4 * jj + 2] * scale, b[4 * jj + 3] * scale)};
+        const u32x2 wv = {E::pack(a[4 * jj], a[4 * jj + 1]), E::pack(a[4 * jj + 2], a[4 * jj + 3])};
+        const u32x2 wk = {E::pack(b[4 * jj] * scale, b[4 * jj + 1] * scale),
+                          E::pack(b[4 * jj + 2] * scale, b[4 * jj + 3] * scale)};
         *reinterpret_cast<u32x2*>(dvrow + db * 32 + 8 * jj + 4 * h) = wv;
         *reinterpret_cast<u32x2*>(dkrow + db * 32 + 8 * jj + 4 * h) = wk;
       }
@@ -346,7 +346,7 @@ struct DqShape {
   static constexpr int LDSB = 4 * TILEB;                // K and V, two buffers each
 };
 
-template <int D, int QB>
+template <class E, int D, int QB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BWD_WAVES_PER_EU, BWD_WAVES_PER_EU)))
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                    const uint16_t* __restrict__ dO, const float* __restrict__ lse2_in, const float* __restrict__ ndelta,
@@ -381,7 +381,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
   // Per query (lane column l32 of block qb): Q and dO fragments (B operands of
   // S^T = K Q^T and dP^T = V dO^T), lse in log2 units and -delta.
-  bf16x8 qf[QB][D / 16], df[QB][D / 16];
+  u32x4 qf[QB][D / 16], df[QB][D / 16];
   float lse2[QB], dl[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -394,8 +394,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         a = *reinterpret_cast<const u32x4*>(Q + head + (size_t)q * D + cc * 16 + h * 8);
         b = *reinterpret_cast<const u32x4*>(dO + head + (size_t)q * D + cc * 16 + h * 8);
       }
-      qf[qb][cc] = as_bf16x8(a);
-      df[qb][cc] = as_bf16x8(b);
+      qf[qb][cc] = a;
+      df[qb][cc] = b;
     }
     lse2[qb] = ok ? lse2_in[hrow + q] : 0.f;
     dl[qb] = ok ? ndelta[hrow + q] : 0.f;
@@ -440,12 +440,12 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
     for (int cc = 0; cc < D / 16; ++cc) {
       const int off = tile_off<S::ROWB>(l32, cc * 16 + h * 8);
-      const bf16x8 ak = as_bf16x8(lds_read_b128(Ks, off));
-      const bf16x8 av = as_bf16x8(lds_read_b128(Vs, off));
+      const u32x4 ak = lds_read_b128(Ks, off);
+      const u32x4 av = lds_read_b128(Vs, off);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        sacc[qb] = mfma32x32x16(ak, qf[qb][cc], sacc[qb]);
-        pacc[qb] = mfma32x32x16(av, df[qb][cc], pacc[qb]);
+        sacc[qb] = E::mfma(ak, qf[qb][cc], sacc[qb]);
+        pacc[qb] = E::mfma(av, df[qb][cc], pacc[qb]);
       }
     }
 
@@ -463,7 +463,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
           if (key >= klq[qb]) p0 = 0.f;
           if (key + 1 >= klq[qb]) p1 = 0.f;
         }
-        dsb[qb][e >> 3][(e >> 1) & 3] = pack_bf16(p0 * (pacc[qb][e] + dl[qb]), p1 * (pacc[qb][e + 1] + dl[qb]));
+        dsb[qb][e >> 3][(e >> 1) & 3] = E::pack(p0 * (pacc[qb][e] + dl[qb]), p1 * (pacc[qb][e + 1] + dl[qb]));
       }
 
     // ---- dQ^T += K^T dS^T (m = dim, n = query, k = key); K^T by transposing reads.
@@ -473,10 +473,10 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const int col = db * 32 + dsub * 16 + 4 * qq;
-        const bf16x8 a = as_bf16x8(lds_read_tr16_b64(Ks, tile_off<S::ROWB>(row0, col)),
-                                   lds_read_tr16_b64(Ks, tile_off<S::ROWB>(row0 + 8, col)));
+        const u32x4 a = cat(lds_read_tr16_b64(Ks, tile_off<S::ROWB>(row0, col)),
+                            lds_read_tr16_b64(Ks, tile_off<S::ROWB>(row0 + 8, col)));
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) dqacc[qb][db] = mfma32x32x16(a, as_bf16x8(dsb[qb][c2]), dqacc[qb][db]);
+        for (int qb = 0; qb < QB; ++qb) dqacc[qb][db] = E::mfma(a, dsb[qb][c2], dqacc[qb][db]);
       }
     }
   };
@@ -506,8 +506,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const f32x16& a = dqacc[qb][db];
-          const u32x2 w = {pack_bf16(a[4 * jj] * scale, a[4 * jj + 1] * scale),
-                           pack_bf16(a[4 * jj + 2] * scale, a[4 * jj + 3] * scale)};
+          const u32x2 w = {E::pack(a[4 * jj] * scale, a[4 * jj + 1] * scale),
+                           E::pack(a[4 * jj + 2] * scale, a[4 * jj + 3] * scale)};
           *reinterpret_cast<u32x2*>(row + db * 32 + 8 * jj + 4 * h) = w;
         }
     }
@@ -524,7 +524,7 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   return 2 * align256((size_t)B * H * N * 4);
 }
 
-template <int D>
+template <class E, int D>
 static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq,
                                      uint16_t* dk, uint16_t* dv, int B, int H, int N, float scale, int causal,
@@ -534,33 +534,33 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
   float* ndelta = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(workspace) + align256(rows * 4));
   const float c = scale * kLog2e;
   if (stage == 0) {
-    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, stream, o, dO,
+    hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, stream, o, dO,
                        lse, lse2, ndelta, rows);
   } else if (stage == 1) {
     const int n_kblk = (N + BCK - 1) / BCK;
     const int total = n_kblk * B * H;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, BWD_MB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, ndelta,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, BWD_MB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, ndelta,
                        dk, dv, N, n_kblk, total, c, scale, kv_len, H, causal);
   } else {
     constexpr int QB = D == 64 ? 2 : 1;
     constexpr int BR = DqShape<D, QB>::BR;
     const int n_qblk = (N + BR - 1) / BR;
     const int total = n_qblk * B * H;
-    hipLaunchKernelGGL((bwd_dq_kernel<D, QB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, ndelta, dq,
+    hipLaunchKernelGGL((bwd_dq_kernel<E, D, QB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, ndelta, dq,
                        N, n_qblk, total, c, scale, kv_len, H, causal);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_bf16_stage(int stage, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+hipError_t launch_bwd_16_stage(bool f16, int stage, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq, uint16_t* dk,
                                  uint16_t* dv, int B, int H, int N, int d, float scale, int causal,
                                  const int* kv_len, void* workspace, hipStream_t stream) {
-  if (d == 64)
-    return launch_bwd_stage_t<64>(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, causal, kv_len, workspace,
-                                  stream);
-  return launch_bwd_stage_t<128>(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, causal, kv_len, workspace,
-                                 stream);
+#define ATTN_BWD_STAGE(E, D) \
+  launch_bwd_stage_t<E, D>(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, causal, kv_len, workspace, stream)
+  if (f16) return d == 64 ? ATTN_BWD_STAGE(F16, 64) : ATTN_BWD_STAGE(F16, 128);
+  return d == 64 ? ATTN_BWD_STAGE(Bf16, 64) : ATTN_BWD_STAGE(Bf16, 128);
+#undef ATTN_BWD_STAGE
 }
 
 }  // namespace attn

@@ -74,6 +74,48 @@ __device__ __forceinline__ float sum_bf16_pair(uint32_t pk, float acc) {
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// Eight 16-bit elements from two 4-element halves.
+__device__ __forceinline__ u32x4 cat(const u32x2& lo, const u32x2& hi) { return u32x4{lo[0], lo[1], hi[0], hi[1]}; }
+
+// The 16-bit element types of storage and matrix-core operands. Fragments
+// are carried as raw 32-bit words (a u32x4 holds 8 elements, a uint32_t a
+// pair, low half first); each type supplies the 32x32x16 product with fp32
+// accumulation, round-to-nearest-even packing of two floats, the fp32 sum of
+// a packed pair (v_dot2 against (1, 1)) and the widening of each half.
+struct Bf16 {
+  __device__ static __forceinline__ f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ uint32_t pack(float lo, float hi) { return pack_bf16(lo, hi); }
+  __device__ static __forceinline__ float sum_pair(uint32_t pk, float acc) { return sum_bf16_pair(pk, acc); }
+  __device__ static __forceinline__ float lo(uint32_t w) { return __uint_as_float(w << 16); }
+  __device__ static __forceinline__ float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+};
+
+struct F16 {
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  __device__ static __forceinline__ f32x16 mfma(const u32x4& a, const u32x4& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+  // v_cvt_pk_f16_f32 (round to nearest even).
+  __device__ static __forceinline__ uint32_t pack(float lo, float hi) {
+    f16x2 v;
+    v[0] = (_Float16)lo;
+    v[1] = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static __forceinline__ float sum_pair(uint32_t pk, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pk), one, acc, false);
+  }
+  __device__ static __forceinline__ float lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)w); }
+  __device__ static __forceinline__ float hi(uint32_t w) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+  }
+};
+
 // NaN-propagating maxima (v_maximum3_f32 on gfx950). Unlike fmaxf they need
 // no canonicalising copy of each operand.
 __device__ __forceinline__ float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }

@@ -9,14 +9,16 @@
 //                                     partial output as each K/V tile arrives;
 //   §3 recompute bullet               the row statistic (here lse) is kept for the backward.
 //
-// bf16 kernel: one workgroup = 4 or 8 waves; wave w owns 32*QB query rows.
+// 16-bit kernel (bf16 or fp16 storage and matrix-core operands, fp32
+// accumulation and softmax): one workgroup = 4 or 8 waves; wave w owns 32*QB
+// query rows.
 // Everything is computed transposed, S^T = K Q^T and O^T = V^T P^T, so that a
 // query is a lane column of every accumulator: row statistics (max, sum,
 // rescale factor) are per-lane scalars, and the S^T accumulator converts to
 // the B operand of the P*V product without leaving registers.
 //   S^T  : A = K tile rows (LDS, 16-byte reads), B = Q fragment (registers)
 //   O^T  : A = V^T (LDS, transposing 8-byte reads of the row-major V tile),
-//          B = P^T (registers, bf16)
+//          B = P^T (registers, 16-bit)
 // K/V tiles go HBM -> LDS by direct DMA (no staging registers) into a ring
 // of NS slots, so the next NS-1 tiles are in flight while one is computed.
 #include "attn_device.h"
@@ -82,9 +84,9 @@ __device__ __forceinline__ void wait_vmem_below() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-template <int D, int QB, int KB, int NS, int WAVES>
+template <class E, int D, int QB, int KB, int NS, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(FWD_WAVES_PER_EU, FWD_WAVES_PER_EU)))
-void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                      uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qblk, int total, float c,
                      uint32_t qsign, const int* __restrict__ kv_len, int H, int causal) {
   using S = FwdShape<D, QB, KB, NS, WAVES>;
@@ -111,7 +113,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
   // Q fragments: B operand of S^T = K Q^T (lane: query l32, dims 16cc + 8h + 0..7).
   // A negative scale is folded into Q (exact sign flip) so that c >= 0.
-  bf16x8 qf[QB][D / 16];
+  u32x4 qf[QB][D / 16];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int q = qw0 + qb * 32 + l32;
@@ -120,7 +122,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       u32x4 v = {0u, 0u, 0u, 0u};
       if (q < N) v = *reinterpret_cast<const u32x4*>(Qh + (size_t)q * D + cc * 16 + h * 8);
       v ^= qsign;
-      qf[qb][cc] = as_bf16x8(v);
+      qf[qb][cc] = v;
     }
   }
 
@@ -193,9 +195,9 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = f32x16{};
 #pragma unroll
       for (int cc = 0; cc < D / 16; ++cc) {
-        const bf16x8 a = as_bf16x8(lds_read_b128(Ks, tile_off<S::ROWB>(kb * 32 + l32, cc * 16 + h * 8)));
+        const u32x4 a = lds_read_b128(Ks, tile_off<S::ROWB>(kb * 32 + l32, cc * 16 + h * 8));
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = mfma32x32x16(a, qf[qb][cc], sacc[qb][kb]);
+        for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = E::mfma(a, qf[qb][cc], sacc[qb][kb]);
       }
     }
 
@@ -244,7 +246,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       }
     }
 
-    // ---- probabilities (bf16) and their row sums. pb[qb][kb][c2] is directly
+    // ---- probabilities (16-bit) and their row sums. pb[qb][kb][c2] is directly
     // the B operand of the P V product for keys kb*32 + 16*c2 + (0..15).
     u32x4 pb[QB][KB][2];
 #pragma unroll
@@ -261,9 +263,9 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
             if (key >= kvalid[qb]) p0 = 0.f;
             if (key + 1 >= kvalid[qb]) p1 = 0.f;
           }
-          const uint32_t w = pack_bf16(p0, p1);
+          const uint32_t w = E::pack(p0, p1);
           pb[qb][kb][e >> 3][(e >> 1) & 3] = w;
-          l_run[qb] = sum_bf16_pair(w, l_run[qb]);
+          l_run[qb] = E::sum_pair(w, l_run[qb]);
         }
     }
 
@@ -278,9 +280,9 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
           const int col = db * 32 + dsub * 16 + 4 * qq;
           const u32x2 lo = lds_read_tr16_b64(Vs, tile_off<S::ROWB>(row0, col));
           const u32x2 hi = lds_read_tr16_b64(Vs, tile_off<S::ROWB>(row0 + 8, col));
-          const bf16x8 a = as_bf16x8(lo, hi);
+          const u32x4 a = cat(lo, hi);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32x32x16(a, as_bf16x8(pb[qb][kb][c2]), oacc[qb][db]);
+          for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mfma(a, pb[qb][kb][c2], oacc[qb][db]);
         }
   };
 
@@ -303,7 +305,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     }
   }
 
-  // ---- epilogue: O = O^T / l (bf16, RNE), lse = ln 2 * (m + log2 l). A row
+  // ---- epilogue: O = O^T / l (16-bit, RNE), lse = ln 2 * (m + log2 l). A row
   // with no visible key (l = 0) gets O = 0 and lse = -inf.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -317,7 +319,7 @@ void fwd_bf16_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const f32x16& a = oacc[qb][db];
-          u32x2 w = {pack_bf16(a[4 * jj] * inv, a[4 * jj + 1] * inv), pack_bf16(a[4 * jj + 2] * inv, a[4 * jj + 3] * inv)};
+          u32x2 w = {E::pack(a[4 * jj] * inv, a[4 * jj + 1] * inv), E::pack(a[4 * jj + 2] * inv, a[4 * jj + 3] * inv)};
           *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * jj + 4 * h) = w;
         }
       if (h == 0) LSE[(size_t)bh * N + q] = lt > 0.f ? (m_run[qb] + log2f(lt)) * kLn2 : -INFINITY;
@@ -413,8 +415,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 
 }  // namespace
 
-template <int D, int QB, int KB, int NS, int WAVES>
-static hipError_t launch_fwd_bf16_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
+template <class E, int D, int QB, int KB, int NS, int WAVES>
+static hipError_t launch_fwd_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                                     float* lse, int B, int H, int N, float scale, int causal, const int* kv_len,
                                     hipStream_t stream) {
   using S = FwdShape<D, QB, KB, NS, WAVES>;
@@ -422,23 +424,31 @@ static hipError_t launch_fwd_bf16_t(const uint16_t* q, const uint16_t* k, const 
   const int total = n_qblk * B * H;
   const float c = fabsf(scale) * kLog2e;
   const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QB, KB, NS, WAVES>), dim3(total), dim3(S::THREADS), 0, stream, q, k, v, o,
+  hipLaunchKernelGGL((fwd_kernel<E, D, QB, KB, NS, WAVES>), dim3(total), dim3(S::THREADS), 0, stream, q, k, v, o,
                      lse, N, n_qblk, total, c, qsign, kv_len, H, causal);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int B,
-                           int H, int N, int d, float scale, int causal, const int* kv_len, hipStream_t stream) {
+template <class E>
+static hipError_t launch_fwd_e(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                               int B, int H, int N, int d, float scale, int causal, const int* kv_len,
+                               hipStream_t stream) {
   const bool lng = N >= FWD_LONG_N;
   if (d == 64)
-    return lng ? launch_fwd_bf16_t<64, FWD_QB64, FWD_KB64, FWD_NS64, FWD_WAVES_LONG>(q, k, v, o, lse, B, H, N, scale,
+    return lng ? launch_fwd_t<E, 64, FWD_QB64, FWD_KB64, FWD_NS64, FWD_WAVES_LONG>(q, k, v, o, lse, B, H, N, scale,
+                                                                                  causal, kv_len, stream)
+               : launch_fwd_t<E, 64, FWD_QB64, FWD_KB64, FWD_NS64, 4>(q, k, v, o, lse, B, H, N, scale, causal, kv_len,
+                                                                     stream);
+  return lng ? launch_fwd_t<E, 128, FWD_QB128, FWD_KB128, FWD_NS128, FWD_WAVES_LONG>(q, k, v, o, lse, B, H, N, scale,
                                                                                     causal, kv_len, stream)
-               : launch_fwd_bf16_t<64, FWD_QB64, FWD_KB64, FWD_NS64, 4>(q, k, v, o, lse, B, H, N, scale, causal,
+             : launch_fwd_t<E, 128, FWD_QB128, FWD_KB128, FWD_NS128, 4>(q, k, v, o, lse, B, H, N, scale, causal,
                                                                        kv_len, stream);
-  return lng ? launch_fwd_bf16_t<128, FWD_QB128, FWD_KB128, FWD_NS128, FWD_WAVES_LONG>(q, k, v, o, lse, B, H, N, scale,
-                                                                                      causal, kv_len, stream)
-             : launch_fwd_bf16_t<128, FWD_QB128, FWD_KB128, FWD_NS128, 4>(q, k, v, o, lse, B, H, N, scale, causal,
-                                                                         kv_len, stream);
+}
+
+hipError_t launch_fwd_16(bool f16, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                         int B, int H, int N, int d, float scale, int causal, const int* kv_len, hipStream_t stream) {
+  return f16 ? launch_fwd_e<F16>(q, k, v, o, lse, B, H, N, d, scale, causal, kv_len, stream)
+             : launch_fwd_e<Bf16>(q, k, v, o, lse, B, H, N, d, scale, causal, kv_len, stream);
 }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,

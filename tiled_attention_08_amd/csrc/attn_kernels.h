@@ -15,8 +15,9 @@ constexpr int kBwdKeysPerBlock = 128;
 // causal != 0: query i sees keys j <= i. kv_len (device, B ints, or null):
 // keys j >= kv_len[b] are hidden from every query of batch entry b (values are
 // clamped to [0, N] on the device).
-hipError_t launch_fwd_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse, int B,
-                           int H, int N, int d, float scale, int causal, const int* kv_len, hipStream_t stream);
+// 16-bit storage: bf16, or fp16 when f16 is true.
+hipError_t launch_fwd_16(bool f16, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                         int B, int H, int N, int d, float scale, int causal, const int* kv_len, hipStream_t stream);
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
                           int d, float scale, hipStream_t stream);
@@ -26,7 +27,7 @@ size_t bwd_workspace_bytes(int B, int H, int N, int d);
 
 // One backward stage: 0 = lse * log2(e) and -delta, 1 = dK and dV, 2 = dQ.
 // Masks as for launch_fwd_bf16.
-hipError_t launch_bwd_bf16_stage(int stage, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+hipError_t launch_bwd_16_stage(bool f16, int stage, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq, uint16_t* dk,
                                  uint16_t* dv, int B, int H, int N, int d, float scale, int causal,
                                  const int* kv_len, void* workspace, hipStream_t stream);
