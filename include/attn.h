@@ -51,7 +51,7 @@ typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, B/H/N < 1, non-finite scale, aliasing,
                                  causal not 0 or 1 */
-  ATTN_ERR_UNSUPPORTED = -2,  /* d_k not in {64, 128}, dtype unknown, or sizes beyond the int32
+  ATTN_ERR_UNSUPPORTED = -2,  /* d_k not in {32, 64, 96, 128}, dtype unknown, or sizes beyond the int32
                                  index range */
   ATTN_ERR_WORKSPACE = -3,    /* workspace missing or smaller than attn_bwd_workspace_bytes() */
   ATTN_ERR_HIP = -4           /* the HIP runtime rejected a launch */
@@ -63,7 +63,8 @@ typedef enum {
  *   o        out: bf16 [B,H,N,d_k], O = softmax(scale Q K^T) V, rounded to
  *                 nearest-even
  *   lse      out: float32 [B,H,N] natural-log row logsumexp of scale Q K^T
- *   d_k      64 or 128; scale any finite float (1/sqrt(d_k) in the formula).
+ *   d_k      32, 64, 96 or 128 (the article's ViT heads have 64); scale any
+ *            finite float (1/sqrt(d_k) in the formula).
  * o and lse must not overlap each other or any input.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

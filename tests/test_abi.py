@@ -93,7 +93,7 @@ def test_forward_rejections(L):
         assert f(L, v=A[2] + 8) == INV                    # misaligned
         assert f(L, B=0) == INV and f(L, H=-1) == INV and f(L, N=0) == INV
         assert f(L, scale=float("nan")) == INV and f(L, scale=float("inf")) == INV
-        assert f(L, d=96) == UNS and f(L, d=32) == UNS and f(L, d=256) == UNS
+        assert f(L, d=80) == UNS and f(L, d=16) == UNS and f(L, d=256) == UNS and f(L, d=48) == UNS
         assert f(L, o=A[0]) == INV                        # output aliases an input
         assert f(L, o=A[0] + 16) == INV                   # partial overlap
         assert f(L, lse=A[3] + 64) == INV                 # lse inside o
@@ -108,7 +108,7 @@ def test_extended_forward_rejections(L):
     assert fwd_ex(L, kv_len=A[3] + 4) == INV                # kv_len inside o
     assert fwd_ex(L, kv_len=A[4]) == INV                    # kv_len on lse
     assert fwd_ex(L, q=None, causal=1) == INV
-    assert fwd_ex(L, d=96, causal=1) == UNS
+    assert fwd_ex(L, d=72, causal=1) == UNS
 
 
 def test_backward_rejections(L):
@@ -116,7 +116,7 @@ def test_backward_rejections(L):
     for stage in (None, 0, 1, 2):
         assert bwd(L, stage, dq=None) == INV
         assert bwd(L, stage, do=A[5] + 4) == INV
-        assert bwd(L, stage, d=80) == UNS
+        assert bwd(L, stage, d=80) == UNS and bwd(L, stage, d=160) == UNS
         assert bwd(L, stage, ws=None) == WS
         assert bwd(L, stage, ws_bytes=16) == WS
         assert bwd(L, stage, ws=A[9] + 8) == INV          # misaligned workspace
@@ -137,7 +137,8 @@ def test_workspace_size(L):
     assert L.attn_bwd_workspace_bytes(8, 16, 4096, 64) == 2 * 8 * 16 * 4096 * 4
     assert L.attn_bwd_workspace_bytes(1, 1, 1, 64) == 512
     assert L.attn_bwd_workspace_bytes(1, 3, 100, 128) == 2560
-    assert L.attn_bwd_workspace_bytes(1, 1, 8, 96) == 0
+    assert L.attn_bwd_workspace_bytes(1, 1, 8, 80) == 0
+    assert L.attn_bwd_workspace_bytes(1, 1, 8, 96) == 512
     assert L.attn_bwd_workspace_bytes(0, 1, 8, 64) == 0
 
 

@@ -33,6 +33,7 @@ def _kv(kv):
     (1, 1, 1, 64, False, None), (2, 3, 65, 64, False, None), (2, 2, 196, 64, False, None),
     (2, 2, 333, 64, True, [333, 120]), (1, 2, 1100, 64, False, None), (2, 1, 1100, 64, True, None),
     (1, 2, 129, 128, False, None), (2, 1, 517, 128, True, [517, 0]), (1, 1, 1030, 128, False, [700]),
+    (2, 2, 200, 32, True, None), (1, 1, 1050, 96, False, None),
 ])
 def test_f16_fwd_bwd_parity(gpu_lib, B, H, N, d, causal, kv):
     import torch

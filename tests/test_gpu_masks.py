@@ -86,6 +86,10 @@ SMALL = [
     (3, 1, 517, 128, True, [517, 300, 0]),
     (2, 1, 1030, 128, True, [1030, 640]),
     (2, 1, 1030, 128, False, [777, 1]),
+    (2, 2, 300, 32, True, [300, 45]),
+    (2, 1, 1200, 32, True, None),
+    (2, 2, 250, 96, True, [250, 0]),
+    (2, 1, 1100, 96, True, [1100, 801]),
 ]
 
 

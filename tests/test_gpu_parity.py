@@ -29,7 +29,7 @@ def _say(msg):
 # ------------------------------------------------------------------ fp32 forward
 
 @pytest.mark.parametrize("N,d", [(196, 64), (1, 64), (7, 64), (63, 64), (64, 64), (65, 64), (333, 64),
-                                 (1, 128), (129, 128), (200, 128)])
+                                 (1, 128), (129, 128), (200, 128), (77, 32), (260, 32), (1, 96), (150, 96)])
 def test_fwd_f32_parity(gpu_lib, N, d):
     import torch
     x = make_case(2 if N < 300 else 1, 2, N, d, "f32", seed=N + d, with_grad=False)
@@ -57,7 +57,8 @@ def test_fwd_f32_workload1(gpu_lib):
 # ------------------------------------------------------------------ bf16 forward + backward, small shapes
 
 SMALL = [(1, 1, 1, 64), (1, 2, 7, 64), (2, 3, 65, 64), (2, 2, 196, 64), (2, 3, 333, 64), (1, 1, 1000, 64),
-         (1, 1, 1, 128), (1, 2, 129, 128), (2, 2, 196, 128), (1, 2, 517, 128)]
+         (1, 1, 1, 128), (1, 2, 129, 128), (2, 2, 196, 128), (1, 2, 517, 128),
+         (1, 1, 1, 32), (2, 2, 100, 32), (1, 2, 1111, 32), (1, 1, 1, 96), (2, 2, 140, 96), (1, 2, 1070, 96)]
 
 
 @pytest.mark.parametrize("B,H,N,d", SMALL)

@@ -27,7 +27,7 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 int check_shape(int B, int H, int N, int d, float scale, size_t* elems, size_t* rows) {
   if (B < 1 || H < 1 || N < 1) return ATTN_ERR_INVALID_ARG;
   if (!isfinite(scale)) return ATTN_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 96 && d != 128) return ATTN_ERR_UNSUPPORTED;
   // Kernels index within a head with 32-bit ints and launch one workgroup per
   // (head, row block) on a 1-D grid.
   const int64_t per_head = (int64_t)N * d;
@@ -49,7 +49,7 @@ const char* attn_status_string(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, B/H/N < 1, non-finite scale, causal not 0 or 1, or overlapping buffers)";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported (d_k must be 64 or 128, dtype must be known, sizes must fit 32-bit per-head indexing)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported (d_k must be 32, 64, 96 or 128, dtype must be known, sizes must fit 32-bit per-head indexing)";
     case ATTN_ERR_WORKSPACE: return "workspace missing or smaller than attn_bwd_workspace_bytes()";
     case ATTN_ERR_HIP: return "HIP runtime error at launch";
     default: return "unknown status";

@@ -55,17 +55,17 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
   const long row = gid >> 3;
   const int part = (int)(gid & 7);
-  constexpr int PER = D / 8;  // elements per lane
+  constexpr int PER = D / 8;  // elements per lane: 4, 8, 12 or 16, read 4 at a time (8 bytes)
   float s = 0.f;
   if (row < rows) {
     const uint16_t* o = O + row * D + part * PER;
     const uint16_t* g = dO + row * D + part * PER;
 #pragma unroll
-    for (int c = 0; c < PER; c += 8) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(o + c);
-      const u32x4 b = *reinterpret_cast<const u32x4*>(g + c);
+    for (int c = 0; c < PER; c += 4) {
+      const u32x2 a = *reinterpret_cast<const u32x2*>(o + c);
+      const u32x2 b = *reinterpret_cast<const u32x2*>(g + c);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < 2; ++w) {
         s = fmaf(E::lo(a[w]), E::lo(b[w]), s);
         s = fmaf(E::hi(a[w]), E::hi(b[w]), s);
       }
@@ -85,11 +85,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 // 16-byte slots; the lane writing slot (row, s) fetches global chunk
 // s ^ swz(row), which yields the layout tile_off() addresses. Rows past N
 // re-read row N-1 (finite data); every use of such a row is masked.
+// `runs` (total 64-slot runs of the tile) may be below 4 * per_lane: the last
+// waves then issue fewer DMAs (callers wait for all of a wave's loads).
 template <int D>
 __device__ __forceinline__ void dma_rows(const uint16_t* head_src, int row0, int N, unsigned char* dst, int wave,
-                                         int lane, int per_lane) {
+                                         int lane, int per_lane, int runs) {
   constexpr int ROWB = D * 2;
   for (int r = 0; r < per_lane; ++r) {
+    if (wave * per_lane + r >= runs) break;
     const int slot0 = (wave * per_lane + r) * 64;
     const int p = slot0 + lane;
     const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz<ROWB>(row);
@@ -106,6 +109,7 @@ struct DkdvShape {
   static constexpr int ROWB = D * 2;
   static constexpr int QTILEB = BRQ * ROWB;             // one Q or dO step tile
   static constexpr int QDMA = BRQ * D / 8 / kThreads;   // 16-byte DMAs per lane per Q or dO tile
+  static_assert(QDMA >= 1 && (BRQ * D / 8) % kThreads == 0, "Q / dO tiles split evenly over the lanes");
   static constexpr int OFF_Q = 0;
   static constexpr int OFF_DO = OFF_Q + 2 * QTILEB;
   static constexpr int OFF_L = OFF_DO + 2 * QTILEB;     // lse * log2(e), two buffers
@@ -113,11 +117,11 @@ struct DkdvShape {
   static constexpr int LDSB = OFF_DL + 2 * LROWS * 4;
 };
 
-// d_k = 128 needs more than 256 registers per lane (its dK and dV
-// accumulators alone take 128): one wave per SIMD there.
+// d_k = 96 and 128 need more than 256 registers per lane (the dK and dV
+// accumulators alone take 96 or 128): one wave per SIMD there.
 template <class E, int D, int MB>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(D == 64 ? BWD_WAVES_PER_EU : 1, D == 64 ? BWD_WAVES_PER_EU : 1)))
+__attribute__((amdgpu_waves_per_eu(D <= 64 ? BWD_WAVES_PER_EU : 1, D <= 64 ? BWD_WAVES_PER_EU : 1)))
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                      const uint16_t* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ ndelta,
                      uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk, int total, float c,
@@ -169,8 +173,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
   auto dma_step = [&](int i, int buf) {
     const int q0 = i * BRQ;
-    dma_rows<D>(Q + head, q0, N, smem + S::OFF_Q + buf * S::QTILEB, wave, lane, S::QDMA);
-    dma_rows<D>(dO + head, q0, N, smem + S::OFF_DO + buf * S::QTILEB, wave, lane, S::QDMA);
+    dma_rows<D>(Q + head, q0, N, smem + S::OFF_Q + buf * S::QTILEB, wave, lane, S::QDMA, 4 * S::QDMA);
+    dma_rows<D>(dO + head, q0, N, smem + S::OFF_DO + buf * S::QTILEB, wave, lane, S::QDMA, 4 * S::QDMA);
     const size_t r = hrow + min(q0 + lane, N - 1);
     if (wave == 0) dma4(lse2 + r, smem + S::OFF_L + buf * S::LROWS * 4);
     if (wave == 1) dma4(ndelta + r, smem + S::OFF_DL + buf * S::LROWS * 4);
@@ -342,7 +346,8 @@ struct DqShape {
   static constexpr int BR = 4 * 32 * QB;                // queries per workgroup
   static constexpr int ROWB = D * 2;
   static constexpr int TILEB = BCQ * ROWB;              // one K or V step tile
-  static constexpr int KDMA = BCQ * D / 8 / kThreads;   // 16-byte DMAs per lane per K or V tile
+  static constexpr int KRUNS = BCQ * D / 8 / 64;        // 64-slot DMA runs per K or V tile (2 to 8)
+  static constexpr int KDMA = (KRUNS + 3) / 4;          // runs per wave (the last waves may do fewer)
   static constexpr int LDSB = 4 * TILEB;                // K and V, two buffers each
 };
 
@@ -353,7 +358,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                    uint16_t* __restrict__ dQ, int N, int n_qblk, int total, float c, float scale,
                    const int* __restrict__ kv_len, int H, int causal) {
   using S = DqShape<D, QB>;
-  static_assert(S::KDMA >= 1, "K/V step tile must cover every lane");
+  static_assert((BCQ * D / 8) % 64 == 0, "K/V step tiles are whole 64-slot runs");
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -408,8 +413,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     for (int db = 0; db < D / 32; ++db) dqacc[qb][db] = f32x16{};
 
   auto dma_step = [&](int j, int buf) {
-    dma_rows<D>(K + head, j * BCQ, N, smem + buf * 2 * S::TILEB, wave, lane, S::KDMA);
-    dma_rows<D>(V + head, j * BCQ, N, smem + buf * 2 * S::TILEB + S::TILEB, wave, lane, S::KDMA);
+    dma_rows<D>(K + head, j * BCQ, N, smem + buf * 2 * S::TILEB, wave, lane, S::KDMA, S::KRUNS);
+    dma_rows<D>(V + head, j * BCQ, N, smem + buf * 2 * S::TILEB + S::TILEB, wave, lane, S::KDMA, S::KRUNS);
   };
 
   if (ntiles > 0) {
@@ -542,7 +547,7 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
     hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, BWD_MB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, ndelta,
                        dk, dv, N, n_kblk, total, c, scale, kv_len, H, causal);
   } else {
-    constexpr int QB = D == 64 ? 2 : 1;
+    constexpr int QB = D <= 64 ? 2 : 1;
     constexpr int BR = DqShape<D, QB>::BR;
     const int n_qblk = (N + BR - 1) / BR;
     const int total = n_qblk * B * H;
@@ -558,8 +563,20 @@ hipError_t launch_bwd_16_stage(bool f16, int stage, const uint16_t* q, const uin
                                  const int* kv_len, void* workspace, hipStream_t stream) {
 #define ATTN_BWD_STAGE(E, D) \
   launch_bwd_stage_t<E, D>(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, causal, kv_len, workspace, stream)
-  if (f16) return d == 64 ? ATTN_BWD_STAGE(F16, 64) : ATTN_BWD_STAGE(F16, 128);
-  return d == 64 ? ATTN_BWD_STAGE(Bf16, 64) : ATTN_BWD_STAGE(Bf16, 128);
+  if (f16) {
+    switch (d) {
+      case 32: return ATTN_BWD_STAGE(F16, 32);
+      case 64: return ATTN_BWD_STAGE(F16, 64);
+      case 96: return ATTN_BWD_STAGE(F16, 96);
+      default: return ATTN_BWD_STAGE(F16, 128);
+    }
+  }
+  switch (d) {
+    case 32: return ATTN_BWD_STAGE(Bf16, 32);
+    case 64: return ATTN_BWD_STAGE(Bf16, 64);
+    case 96: return ATTN_BWD_STAGE(Bf16, 96);
+    default: return ATTN_BWD_STAGE(Bf16, 128);
+  }
 #undef ATTN_BWD_STAGE
 }
 

@@ -140,20 +140,25 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// LDS tile swizzle. Tiles are row-major bf16 with 16-byte chunks (8
+// LDS tile swizzle. Tiles are row-major 16-bit elements in 16-byte chunks (8
 // elements); chunk c of row r is stored at chunk position c ^ swz(r). gfx950
 // serves a 16-lane quarter of a ds_read_b128 from one 256-byte window of its
 // banks, so the 16 lanes of an operand read (16 consecutive rows, same
 // logical chunk) must land on 16 distinct 16-byte slots of that window:
 //   128-byte rows (two rows per window): swz(r) = (r >> 1) & 7 makes the
 //     8 rows of each parity take 8 different slots;
-//   256-byte rows (one row per window):  swz(r) = r & 15.
+//   256-byte rows (one row per window):  swz(r) = r & 15;
+//   64-byte rows (four rows per window) and 192-byte rows (rows start at
+//     window offsets 0, 192, 128, 64 in turn): swz(r) = (r >> 2) & 3, which
+//     spreads each group of four rows with the same window offset over four
+//     slots (and keeps the chunk index below 12 for 192-byte rows).
 // Transposing 8-byte reads (4 rows x 2 chunks per 16 lanes) stay
-// conflict-free under either pattern (measured).
+// conflict-free under these patterns (measured for 128 and 256 bytes,
+// counted bank by bank for 64 and 192).
 template <int ROWB>
 __device__ __forceinline__ int swz(int row) {
-  static_assert(ROWB == 128 || ROWB == 256, "tiles have 128- or 256-byte rows");
-  return ROWB == 128 ? ((row >> 1) & 7) : (row & 15);
+  static_assert(ROWB == 64 || ROWB == 128 || ROWB == 192 || ROWB == 256, "tiles have 64 to 256-byte rows");
+  return ROWB == 128 ? ((row >> 1) & 7) : ROWB == 256 ? (row & 15) : ((row >> 2) & 3);
 }
 
 // Byte offset of element (row, col) in a swizzled tile with ROWB bytes per row.

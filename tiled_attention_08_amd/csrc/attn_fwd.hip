@@ -73,7 +73,8 @@ struct FwdShape {
   static constexpr int TILEB = BC * ROWB;                     // bytes per K or V tile
   static constexpr int DMA_PER_WAVE = BC * D / 8 / THREADS;   // 16-byte DMA instructions per wave per tensor
   static constexpr int LDSB = NS * 2 * TILEB;                 // ring of NS (K, V) tile pairs
-  static_assert(DMA_PER_WAVE >= 1, "every lane takes part in each tile DMA");
+  static_assert(DMA_PER_WAVE >= 1 && (BC * D / 8) % THREADS == 0,
+                "every lane takes part in each tile DMA, the same number of times");
 };
 
 // s_waitcnt encoding (gfx9): wait until at most N vector-memory operations of
@@ -429,20 +430,32 @@ static hipError_t launch_fwd_t(const uint16_t* q, const uint16_t* k, const uint1
   return hipGetLastError();
 }
 
+// Launch shapes per head dim (long rows: 8-wave workgroups; short: 4-wave):
+//   d = 32:  one 32-query block per wave, 128-key tiles (long) or two blocks and 64-key tiles (short);
+//   d = 64:  FWD_QB64 / FWD_KB64 / FWD_NS64;
+//   d = 96:  one query block, 128-key tiles (192-byte rows: 64-key tiles would not split evenly over the
+//            DMA lanes);
+//   d = 128: FWD_QB128 / FWD_KB128 / FWD_NS128.
 template <class E>
 static hipError_t launch_fwd_e(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
                                int B, int H, int N, int d, float scale, int causal, const int* kv_len,
                                hipStream_t stream) {
   const bool lng = N >= FWD_LONG_N;
-  if (d == 64)
-    return lng ? launch_fwd_t<E, 64, FWD_QB64, FWD_KB64, FWD_NS64, FWD_WAVES_LONG>(q, k, v, o, lse, B, H, N, scale,
-                                                                                  causal, kv_len, stream)
-               : launch_fwd_t<E, 64, FWD_QB64, FWD_KB64, FWD_NS64, 4>(q, k, v, o, lse, B, H, N, scale, causal, kv_len,
-                                                                     stream);
-  return lng ? launch_fwd_t<E, 128, FWD_QB128, FWD_KB128, FWD_NS128, FWD_WAVES_LONG>(q, k, v, o, lse, B, H, N, scale,
-                                                                                    causal, kv_len, stream)
-             : launch_fwd_t<E, 128, FWD_QB128, FWD_KB128, FWD_NS128, 4>(q, k, v, o, lse, B, H, N, scale, causal,
-                                                                       kv_len, stream);
+#define ATTN_FWD(D, QB, KB, NS, W) \
+  launch_fwd_t<E, D, QB, KB, NS, W>(q, k, v, o, lse, B, H, N, scale, causal, kv_len, stream)
+  switch (d) {
+    case 32:
+      return lng ? ATTN_FWD(32, 1, 4, 2, FWD_WAVES_LONG) : ATTN_FWD(32, 2, 2, 2, 4);
+    case 64:
+      return lng ? ATTN_FWD(64, FWD_QB64, FWD_KB64, FWD_NS64, FWD_WAVES_LONG)
+                 : ATTN_FWD(64, FWD_QB64, FWD_KB64, FWD_NS64, 4);
+    case 96:
+      return lng ? ATTN_FWD(96, 1, 4, 2, FWD_WAVES_LONG) : ATTN_FWD(96, 1, 4, 2, 4);
+    default:
+      return lng ? ATTN_FWD(128, FWD_QB128, FWD_KB128, FWD_NS128, FWD_WAVES_LONG)
+                 : ATTN_FWD(128, FWD_QB128, FWD_KB128, FWD_NS128, 4);
+  }
+#undef ATTN_FWD
 }
 
 hipError_t launch_fwd_16(bool f16, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
@@ -455,10 +468,20 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           int d, float scale, hipStream_t stream) {
   const int n_qblk = (N + kF32BR - 1) / kF32BR;
   const int total = n_qblk * B * H;
-  if (d == 64)
-    hipLaunchKernelGGL((fwd_f32_kernel<64>), dim3(total), dim3(256), 0, stream, q, k, v, o, lse, N, n_qblk, scale);
-  else
-    hipLaunchKernelGGL((fwd_f32_kernel<128>), dim3(total), dim3(256), 0, stream, q, k, v, o, lse, N, n_qblk, scale);
+  switch (d) {
+    case 32:
+      hipLaunchKernelGGL((fwd_f32_kernel<32>), dim3(total), dim3(256), 0, stream, q, k, v, o, lse, N, n_qblk, scale);
+      break;
+    case 64:
+      hipLaunchKernelGGL((fwd_f32_kernel<64>), dim3(total), dim3(256), 0, stream, q, k, v, o, lse, N, n_qblk, scale);
+      break;
+    case 96:
+      hipLaunchKernelGGL((fwd_f32_kernel<96>), dim3(total), dim3(256), 0, stream, q, k, v, o, lse, N, n_qblk, scale);
+      break;
+    default:
+      hipLaunchKernelGGL((fwd_f32_kernel<128>), dim3(total), dim3(256), 0, stream, q, k, v, o, lse, N, n_qblk,
+                         scale);
+  }
   return hipGetLastError();
 }
 
