@@ -104,6 +104,17 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward, float32 storage and float32 arithmetic throughout (vector ALU):
+ * the gradients of attn_fwd_f32's output, same formulas, stages and
+ * workspace contract as attn_bwd (attn_bwd_workspace_bytes gives the size),
+ * with float32 [B,H,N,d_k] tensors in place of bf16 ones.
+ */
+int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse,
+                 const float* dO, float* dq, float* dk, float* dv,
+                 int B, int H, int N, int d_k, float scale,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Extended entry points: element type and masks.
  *
  * The article defines unmasked attention (§1 "Attention" formula). §3 opens

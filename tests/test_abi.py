@@ -28,8 +28,9 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_bwd", "attn_bwd_ex",
-                                           "attn_bwd_stage", "attn_bwd_workspace_bytes", "attn_status_string"])
+    assert declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_bwd", "attn_bwd_f32",
+                                           "attn_bwd_ex", "attn_bwd_stage", "attn_bwd_workspace_bytes",
+                                           "attn_status_string"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -131,6 +132,22 @@ def test_backward_rejections(L):
         assert bwd(L, stage, ex=True, kv_len=A[10] + 1) == INV
         assert bwd(L, stage, ex=True, kv_len=A[7]) == INV     # kv_len inside dk
         assert bwd(L, stage, ex=True, kv_len=A[9] + 8) == INV  # kv_len inside the workspace
+
+
+def test_f32_backward_rejections(L):
+    """attn_bwd_f32 checks float32 extents: an output 8 bytes into a 2-byte-element extent still overlaps."""
+    INV, UNS, WS = L.ATTN_ERR_INVALID_ARG, L.ATTN_ERR_UNSUPPORTED, L.ATTN_ERR_WORKSPACE
+
+    def b32(**kw):
+        a = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], do=A[5], dq=A[6], dk=A[7], dv=A[8], B=1, H=1, N=8, d=64,
+                 scale=0.125, ws=A[9])
+        a.update(kw)
+        n = L.attn_bwd_workspace_bytes(a["B"], a["H"], a["N"], a["d"])
+        return L.lib.attn_bwd_f32(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
+                                  a["B"], a["H"], a["N"], a["d"], a["scale"], a["ws"], n, None)
+    assert b32(q=None) == INV and b32(d=80) == UNS and b32(ws=None) == WS
+    assert b32(dq=A[0] + 8 * 64 * 2) == INV      # inside q's float32 extent (8 x 64 x 4 bytes), past a 2-byte one
+    assert b32(dk=A[6]) == INV
 
 
 def test_workspace_size(L):

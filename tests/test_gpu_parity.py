@@ -14,8 +14,8 @@ import numpy as np
 import pytest
 
 from attn_inputs import WORKLOADS, make_case, make_inputs
-from gpu_helpers import (TOL_BF16_LSE_REL, TOL_BF16_O, TOL_F32_LSE, TOL_F32_O, TOL_GRAD_RELL2, lse_err, max_abs,
-                         rel_l2, to_device, to_f64)
+from gpu_helpers import (TOL_BF16_LSE_REL, TOL_BF16_O, TOL_F32_GRAD_RELL2, TOL_F32_LSE, TOL_F32_O, TOL_GRAD_RELL2,
+                         lse_err, max_abs, rel_l2, to_device, to_f64)
 from oracle import attention_bwd, attention_fwd
 
 pytestmark = pytest.mark.gpu
@@ -39,6 +39,27 @@ def test_fwd_f32_parity(gpu_lib, N, d):
     ro, rl = attention_fwd(x.f64("q"), x.f64("k"), x.f64("v"), x.scale)
     assert max_abs(to_f64(o), ro) <= TOL_F32_O
     assert max_abs(to_f64(lse), rl) <= TOL_F32_LSE
+
+
+@pytest.mark.parametrize("B,H,N,d", [(1, 1, 1, 64), (2, 2, 196, 64), (1, 2, 333, 32), (1, 1, 150, 96),
+                                     (1, 2, 129, 128), (1, 1, 1000, 64)])
+def test_f32_fwd_bwd_parity(gpu_lib, B, H, N, d):
+    """fp32 forward and backward (attn_fwd_f32, attn_bwd_f32) against the oracle."""
+    import torch
+    x = make_case(B, H, N, d, "f32", seed=7000 + N + d)
+    _say(f"fwd/bwd f32 B={B} H={H} N={N} d={d}")
+    q, k, v, do = (to_device(x, n) for n in ("q", "k", "v", "do"))
+    o, lse = gpu_lib.forward(q, k, v, x.scale)
+    dq, dk, dv = gpu_lib.backward(q, k, v, o, lse, do, x.scale)
+    torch.cuda.synchronize()
+    Q, K, V, DO = x.f64("q"), x.f64("k"), x.f64("v"), x.f64("do")
+    ro, rl = attention_fwd(Q, K, V, x.scale)
+    assert max_abs(to_f64(o), ro) <= TOL_F32_O
+    assert max_abs(to_f64(lse), rl) <= TOL_F32_LSE
+    for name, got, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), attention_bwd(Q, K, V, DO, x.scale)):
+        e = rel_l2(to_f64(got), ref)
+        _say(f"  {name} rel-L2 {e:.3e} max-abs {max_abs(to_f64(got), ref):.3e}")
+        assert e <= TOL_F32_GRAD_RELL2, name
 
 
 def test_fwd_f32_workload1(gpu_lib):

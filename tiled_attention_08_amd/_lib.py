@@ -23,7 +23,7 @@ ATTN_DTYPE_BF16 = 0
 ATTN_DTYPE_F16 = 1
 
 # Every symbol include/attn.h declares.
-EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_bwd", "attn_bwd_ex", "attn_bwd_stage",
+EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_bwd", "attn_bwd_f32", "attn_bwd_ex", "attn_bwd_stage",
            "attn_bwd_workspace_bytes", "attn_status_string")
 
 
@@ -40,6 +40,8 @@ def _load() -> ctypes.CDLL:
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, vp, sz, vp]
     lib.attn_bwd.restype = i
+    lib.attn_bwd_f32.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, vp, sz, vp]
+    lib.attn_bwd_f32.restype = i
     lib.attn_fwd_ex.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
     lib.attn_fwd_ex.restype = i
     lib.attn_bwd_ex.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
@@ -165,6 +167,18 @@ def attn_bwd(q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, stream=No
                         B, H, N, d, float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def attn_bwd_f32(q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, stream=None) -> None:
+    """float32 backward into caller-provided ``dq``, ``dk``, ``dv`` (float32 [B,H,N,d])."""
+    import torch
+    B, H, N, d = _shape(q, k, v, o, do, dq, dk, dv)
+    if q.dtype != torch.float32:
+        raise ValueError("attn_bwd_f32 takes float32 tensors")
+    _check_lse(lse, B, H, N)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.attn_bwd_f32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+                            B, H, N, d, float(scale), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
 def attn_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, causal: bool = False, kv_len=None,
                 stream=None) -> None:
     """Backward with the masks of attn_fwd_ex (which must match the forward's)."""
@@ -215,12 +229,16 @@ def workspace_for(q) -> "torch.Tensor":
 
 
 def backward(q, k, v, o, lse, do, scale: float, workspace=None, stream=None, causal: bool = False, kv_len=None):
-    """Allocate dQ, dK, dV (and the workspace unless given), then run the 16-bit backward matching q's dtype."""
+    """Allocate dQ, dK, dV (and the workspace unless given), then run the backward matching q's dtype."""
     import torch
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if workspace is None:
         workspace = workspace_for(q)
-    if q.dtype == torch.bfloat16 and not causal and kv_len is None:
+    if q.dtype == torch.float32:
+        if causal or kv_len is not None:
+            raise ValueError("the float32 backward takes no mask")
+        attn_bwd_f32(q, k, v, o, lse, do, dq, dk, dv, scale, workspace, stream)
+    elif q.dtype == torch.bfloat16 and not causal and kv_len is None:
         attn_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, workspace, stream)
     else:
         attn_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale, workspace, causal=causal, kv_len=kv_len, stream=stream)

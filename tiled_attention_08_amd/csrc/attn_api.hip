@@ -102,13 +102,15 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d_k) {
 
 namespace {
 
+// dtype -1 stands for float32 storage (attn_bwd_f32).
 int bwd_checks(int dtype, const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k, float scale, int causal,
                const int* kv_len, void* workspace, size_t workspace_bytes) {
   size_t E = 0, R = 0;
   const int st = check_shape(B, H, N, d_k, scale, &E, &R);
   if (st != ATTN_OK) return st;
-  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_UNSUPPORTED;
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16 && dtype != -1) return ATTN_ERR_UNSUPPORTED;
+  E *= dtype == -1 ? 2 : 1;  // the ranges below count 2-byte elements
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
   if (kv_len != nullptr && (reinterpret_cast<uintptr_t>(kv_len) & 3u) != 0) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(dO) ||
@@ -151,6 +153,20 @@ int attn_bwd_ex(int dtype, const void* q, const void* k, const void* v, const vo
   for (int stage = 0; stage < 3; ++stage) {
     const int r = bwd_launch(dtype, stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, workspace,
                              stream);
+    if (r != ATTN_OK) return r;
+  }
+  return ATTN_OK;
+}
+
+int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse, const float* dO,
+                 float* dq, float* dk, float* dv, int B, int H, int N, int d_k, float scale, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  const int st = bwd_checks(-1, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, 0, nullptr, workspace,
+                            workspace_bytes);
+  if (st != ATTN_OK) return st;
+  for (int stage = 0; stage < 3; ++stage) {
+    const int r = from_hip(attn::launch_bwd_f32_stage(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale,
+                                                      workspace, static_cast<hipStream_t>(stream)));
     if (r != ATTN_OK) return r;
   }
   return ATTN_OK;

@@ -519,6 +519,154 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------- fp32 backward
+// fp32 storage and fp32 arithmetic throughout (vector ALU), the same three
+// deterministic stages. Four lanes share a row (a key in stage 1, a query in
+// stage 2): lane part p owns columns [p * D/4, (p+1) * D/4) of that row, dot
+// products are split over the four lanes and summed with two xor shuffles.
+constexpr int kF32Rows = 64;   // rows (keys or queries) per workgroup: 256 threads / 4
+constexpr int kF32Step = 32;   // rows of the other side staged in LDS per step
+
+__global__ __launch_bounds__(256) void bwd_prep_f32_kernel(const float* __restrict__ O, const float* __restrict__ dO,
+                                                           const float* __restrict__ LSE, float* __restrict__ lse_out,
+                                                           float* __restrict__ ndelta, long rows, int D) {
+  const long gid = (long)blockIdx.x * 256 + threadIdx.x;
+  const long row = gid >> 3;
+  const int part = (int)(gid & 7);
+  float s = 0.f;
+  if (row < rows)
+    for (int c = part; c < D; c += 8) s = fmaf(O[row * D + c], dO[row * D + c], s);
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  s += __shfl_xor(s, 4);
+  if (row < rows && part == 0) {
+    ndelta[row] = -s;
+    lse_out[row] = LSE[row];
+  }
+}
+
+__device__ __forceinline__ float sum4(float x) {
+  x += __shfl_xor(x, 1);
+  return x + __shfl_xor(x, 2);
+}
+
+// Stage 1: dV_j = sum_i P_ij dO_i, dK_j = scale * sum_i dS_ij Q_i for 64 keys j.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                           const float* __restrict__ V, const float* __restrict__ dO,
+                                                           const float* __restrict__ LSE, const float* __restrict__ ndelta,
+                                                           float* __restrict__ dK, float* __restrict__ dV, int N,
+                                                           int n_kblk, float scale) {
+  constexpr int DC = D / 4;
+  __shared__ float Qs[kF32Step][D], dOs[kF32Step][D], Ls[kF32Step], Ds[kF32Step];
+  const int tid = threadIdx.x, part = tid & 3;
+  const int bh = blockIdx.x / n_kblk, kblk = blockIdx.x - bh * n_kblk;
+  const size_t head = (size_t)bh * N * D;
+  const int key = kblk * kF32Rows + (tid >> 2);
+  const bool ok = key < N;
+  float kr[DC], vr[DC], dk[DC], dv[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    kr[c] = ok ? K[head + (size_t)key * D + part * DC + c] : 0.f;
+    vr[c] = ok ? V[head + (size_t)key * D + part * DC + c] : 0.f;
+    dk[c] = 0.f;
+    dv[c] = 0.f;
+  }
+  for (int i0 = 0; i0 < N; i0 += kF32Step) {
+    __syncthreads();
+    for (int idx = tid; idx < kF32Step * D; idx += 256) {
+      const int r = idx / D, c = idx - r * D;
+      const bool in = i0 + r < N;
+      Qs[r][c] = in ? Q[head + (size_t)(i0 + r) * D + c] : 0.f;
+      dOs[r][c] = in ? dO[head + (size_t)(i0 + r) * D + c] : 0.f;
+    }
+    if (tid < kF32Step) {
+      const bool in = i0 + tid < N;
+      Ls[tid] = in ? LSE[(size_t)bh * N + i0 + tid] : 0.f;
+      Ds[tid] = in ? ndelta[(size_t)bh * N + i0 + tid] : 0.f;
+    }
+    __syncthreads();
+    const int rows = min(kF32Step, N - i0);
+    for (int r = 0; r < rows; ++r) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        s = fmaf(Qs[r][part * DC + c], kr[c], s);
+        dp = fmaf(dOs[r][part * DC + c], vr[c], dp);
+      }
+      s = sum4(s);
+      dp = sum4(dp);
+      const float p = ok ? expf(s * scale - Ls[r]) : 0.f;
+      const float ds = p * (dp + Ds[r]);
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        dv[c] = fmaf(p, dOs[r][part * DC + c], dv[c]);
+        dk[c] = fmaf(ds, Qs[r][part * DC + c], dk[c]);
+      }
+    }
+  }
+  if (ok) {
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+      dV[head + (size_t)key * D + part * DC + c] = dv[c];
+      dK[head + (size_t)key * D + part * DC + c] = dk[c] * scale;
+    }
+  }
+}
+
+// Stage 2: dQ_i = scale * sum_j dS_ij K_j for 64 queries i.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                         const float* __restrict__ V, const float* __restrict__ dO,
+                                                         const float* __restrict__ LSE, const float* __restrict__ ndelta,
+                                                         float* __restrict__ dQ, int N, int n_qblk, float scale) {
+  constexpr int DC = D / 4;
+  __shared__ float Ks[kF32Step][D], Vs[kF32Step][D];
+  const int tid = threadIdx.x, part = tid & 3;
+  const int bh = blockIdx.x / n_qblk, qblk = blockIdx.x - bh * n_qblk;
+  const size_t head = (size_t)bh * N * D;
+  const int q = qblk * kF32Rows + (tid >> 2);
+  const bool ok = q < N;
+  float qr[DC], dor[DC], dq[DC];
+#pragma unroll
+  for (int c = 0; c < DC; ++c) {
+    qr[c] = ok ? Q[head + (size_t)q * D + part * DC + c] : 0.f;
+    dor[c] = ok ? dO[head + (size_t)q * D + part * DC + c] : 0.f;
+    dq[c] = 0.f;
+  }
+  const float l = ok ? LSE[(size_t)bh * N + q] : 0.f;
+  const float nd = ok ? ndelta[(size_t)bh * N + q] : 0.f;
+  for (int j0 = 0; j0 < N; j0 += kF32Step) {
+    __syncthreads();
+    for (int idx = tid; idx < kF32Step * D; idx += 256) {
+      const int r = idx / D, c = idx - r * D;
+      const bool in = j0 + r < N;
+      Ks[r][c] = in ? K[head + (size_t)(j0 + r) * D + c] : 0.f;
+      Vs[r][c] = in ? V[head + (size_t)(j0 + r) * D + c] : 0.f;
+    }
+    __syncthreads();
+    const int rows = min(kF32Step, N - j0);
+    for (int r = 0; r < rows; ++r) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int c = 0; c < DC; ++c) {
+        s = fmaf(qr[c], Ks[r][part * DC + c], s);
+        dp = fmaf(dor[c], Vs[r][part * DC + c], dp);
+      }
+      s = sum4(s);
+      dp = sum4(dp);
+      const float p = ok ? expf(s * scale - l) : 0.f;
+      const float ds = p * (dp + nd);
+#pragma unroll
+      for (int c = 0; c < DC; ++c) dq[c] = fmaf(ds, Ks[r][part * DC + c], dq[c]);
+    }
+  }
+  if (ok) {
+#pragma unroll
+    for (int c = 0; c < DC; ++c) dQ[head + (size_t)q * D + part * DC + c] = dq[c] * scale;
+  }
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -578,6 +726,40 @@ hipError_t launch_bwd_16_stage(bool f16, int stage, const uint16_t* q, const uin
     default: return ATTN_BWD_STAGE(Bf16, 128);
   }
 #undef ATTN_BWD_STAGE
+}
+
+template <int D>
+static void launch_f32_stage_t(int stage, dim3 grid, const float* q, const float* k, const float* v,
+                               const float* dO, const float* lse_ws, const float* ndelta, float* dq, float* dk,
+                               float* dv, int N, int nblk, float scale, hipStream_t stream) {
+  if (stage == 1)
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D>), grid, dim3(256), 0, stream, q, k, v, dO, lse_ws, ndelta, dk, dv, N,
+                       nblk, scale);
+  else
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D>), grid, dim3(256), 0, stream, q, k, v, dO, lse_ws, ndelta, dq, N, nblk,
+                       scale);
+}
+
+hipError_t launch_bwd_f32_stage(int stage, const float* q, const float* k, const float* v, const float* o,
+                                const float* lse, const float* dO, float* dq, float* dk, float* dv, int B, int H, int N,
+                                int d, float scale, void* workspace, hipStream_t stream) {
+  const long rows = (long)B * H * N;
+  float* lse_ws = reinterpret_cast<float*>(workspace);
+  float* ndelta = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(workspace) + align256(rows * 4));
+  if (stage == 0) {
+    hipLaunchKernelGGL(bwd_prep_f32_kernel, dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, stream, o, dO,
+                       lse, lse_ws, ndelta, rows, d);
+    return hipGetLastError();
+  }
+  const int nblk = (N + kF32Rows - 1) / kF32Rows;
+  const dim3 grid((unsigned)(nblk * B * H));
+  switch (d) {
+    case 32: launch_f32_stage_t<32>(stage, grid, q, k, v, dO, lse_ws, ndelta, dq, dk, dv, N, nblk, scale, stream); break;
+    case 64: launch_f32_stage_t<64>(stage, grid, q, k, v, dO, lse_ws, ndelta, dq, dk, dv, N, nblk, scale, stream); break;
+    case 96: launch_f32_stage_t<96>(stage, grid, q, k, v, dO, lse_ws, ndelta, dq, dk, dv, N, nblk, scale, stream); break;
+    default: launch_f32_stage_t<128>(stage, grid, q, k, v, dO, lse_ws, ndelta, dq, dk, dv, N, nblk, scale, stream);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace attn

@@ -32,4 +32,9 @@ hipError_t launch_bwd_16_stage(bool f16, int stage, const uint16_t* q, const uin
                                  uint16_t* dv, int B, int H, int N, int d, float scale, int causal,
                                  const int* kv_len, void* workspace, hipStream_t stream);
 
+// fp32 backward stage (vector ALU; same stages and workspace as the 16-bit one).
+hipError_t launch_bwd_f32_stage(int stage, const float* q, const float* k, const float* v, const float* o,
+                                const float* lse, const float* dO, float* dq, float* dk, float* dv, int B, int H, int N,
+                                int d, float scale, void* workspace, hipStream_t stream);
+
 }  // namespace attn
