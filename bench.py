@@ -129,19 +129,75 @@ def cpu_baseline(wid: int, seed: int, budget_s: float, causal: bool = False) -> 
                       f"{elapsed:.1f} s", "seconds": round(elapsed, 3)}
 
 
+PEAK_F32_TFLOPS = 157.3  # MI355X fp32 vector ALU
+
+
+def bench_f32(args, w) -> int:
+    """fp32 forward (attn_fwd_f32) of a forward-only fp32 workload: latency per launch and fp32 vector-ALU roofline."""
+    import numpy as np
+    import torch
+    from attn_inputs import make_inputs
+    from tiled_attention_08_amd import _lib as attn
+    B, H, N, d = w.B, w.H, w.N, w.d
+    x = make_inputs(w.wid, seed=args.seed)
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(x.raw[n])).cuda() for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        attn.attn_fwd_f32(q, k, v, o, lse, x.scale, stream)
+
+    step()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        step()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    flops = fwd_flops(B, H, N, d)
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] fp32 forward {ms * 1e3:.2f} us per launch, {value:.3f} TFLOP/s")
+    record = {
+        "metric": "attention forward latency, fp32 (us per launch)", "value": round(ms * 1e3, 3), "unit": "us",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "N": N, "d_k": d, "passes": "fwd"},
+        "tflops": round(value, 4),
+        "roofline": {"bound": "alu", "achieved": round(value, 4), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(value / PEAK_F32_TFLOPS, 5), "traffic": None, "kernel": "fwd_f32_kernel",
+                     "avg_ms": round(ms, 5),
+                     "note": "one head of 196 rows: 7 workgroups on 256 CUs, so launch latency dominates"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        record["cpu_baseline"] = cpu_baseline(w.wid, args.seed, min(args.cpu_seconds, 2.0))
+    print(json.dumps(record), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=3, choices=(2, 3, 4, 5),
-                    help="3 = long sequence, the headline; 4 runs the forward only (its workload has no backward)")
+    ap.add_argument("--workload", type=int, default=3, choices=(1, 2, 3, 4, 5),
+                    help="3 = long sequence, the headline; 1 (fp32) and 4 run the forward only (their workloads have "
+                         "no backward)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--kernel-reps", type=int, default=20, help="launches per kernel for the roofline timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dtype", default="bf16", choices=("bf16", "f16"),
                     help="storage type of Q, K, V, O and the gradients (f16 runs attn_fwd_ex / attn_bwd_ex)")
+    ap.add_argument("--cold", action="store_true",
+                    help="rotate through copies of the inputs (about 1 GiB in all) so that every launch reads its "
+                         "inputs from HBM, not from L2 or the MALL")
     ap.add_argument("--causal", action="store_true",
                     help="time the causal-mask path (attn_fwd_ex / attn_bwd_ex); FLOPs count the N(N+1)/2 visible "
                          "query-key pairs of each head")
@@ -175,6 +231,8 @@ def main(argv=None) -> int:
     w = WORKLOADS[args.workload]
     B, H, N, d = w.B, w.H, w.N, w.d
     cz = args.causal
+    if w.dtype == "f32":
+        return bench_f32(args, w)
     log(f"[bench] workload {w.wid} {w.name}: B={B} H={H} N={N} d={d} {args.dtype}{' causal' if cz else ''}, seed {args.seed}")
     if args.dtype == "bf16":
         x = make_inputs(args.workload, seed=args.seed)
@@ -189,34 +247,56 @@ def main(argv=None) -> int:
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
 
     with_bwd = "bwd" in w.passes
-    q, k, v = up("q"), up("k"), up("v")
-    do = up("do") if with_bwd else None
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
-    if with_bwd:
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = attn.workspace_for(q)
+
+    def new_set(src=None):
+        t = {n: (up(n) if src is None else src[n].clone()) for n in ("q", "k", "v") + (("do",) if with_bwd else ())}
+        t["o"] = torch.empty_like(t["q"])
+        t["lse"] = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        if with_bwd:
+            t.update(dq=torch.empty_like(t["q"]), dk=torch.empty_like(t["q"]), dv=torch.empty_like(t["q"]),
+                     ws=attn.workspace_for(t["q"]))
+        return t
+
+    sets = [new_set()]
+    set_bytes = sum(t.numel() * t.element_size() for t in sets[0].values())
+    if args.cold:
+        # Copies of the same inputs at other addresses, about 1 GiB in all (L2 4 MB per XCD, MALL 256 MB), used
+        # in turn so that no launch finds its inputs in a cache.
+        while len(sets) * set_bytes < (1 << 30) or len(sets) < 2:
+            sets.append(new_set(sets[0]))
+        log(f"[bench] cold: {len(sets)} input sets of {set_bytes / 2**20:.1f} MiB")
     scale = x.scale
     stream = torch.cuda.current_stream()
+    turn = [0]
+
+    def next_set():
+        t = sets[turn[0] % len(sets)]
+        turn[0] += 1
+        return t
 
     def step():
+        t = next_set()
         if args.causal or args.dtype != "bf16":
-            attn.attn_fwd_ex(q, k, v, o, lse, scale, causal=cz, stream=stream)
+            attn.attn_fwd_ex(t["q"], t["k"], t["v"], t["o"], t["lse"], scale, causal=cz, stream=stream)
             if with_bwd:
-                attn.attn_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale, ws, causal=cz, stream=stream)
+                attn.attn_bwd_ex(t["q"], t["k"], t["v"], t["o"], t["lse"], t["do"], t["dq"], t["dk"], t["dv"], scale,
+                                 t["ws"], causal=cz, stream=stream)
             return
-        attn.attn_fwd(q, k, v, o, lse, scale, stream)
+        attn.attn_fwd(t["q"], t["k"], t["v"], t["o"], t["lse"], scale, stream)
         if with_bwd:
-            attn.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream)
+            attn.attn_bwd(t["q"], t["k"], t["v"], t["o"], t["lse"], t["do"], t["dq"], t["dk"], t["dv"], scale,
+                          t["ws"], stream)
 
     # One checked step first, so that the host-side check does not leave the
     # GPU idle (and its clock low) between the warm-up and the timed steps.
-    step()
+    for _ in range(len(sets)):
+        step()
     torch.cuda.synchronize()
-    for t in (o, lse) + ((dq, dk, dv) if with_bwd else ()):
-        if not torch.isfinite(t.float()).all():
-            log("[bench] non-finite output")
-            return 1
+    for st in sets:
+        for n in ("o", "lse") + (("dq", "dk", "dv") if with_bwd else ()):
+            if not torch.isfinite(st[n].float()).all():
+                log("[bench] non-finite output")
+                return 1
     for _ in range(args.warmup):
         step()
     log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
@@ -237,9 +317,17 @@ def main(argv=None) -> int:
     # Per-kernel timing (each kernel alone, back-to-back launches on the same stream).
     reps = args.kernel_reps
     def stage(i):
-        return lambda: attn.attn_bwd_stage(i, q, k, v, o, lse, do, dq, dk, dv, scale, ws, causal=cz, stream=stream)
+        def run():
+            t = next_set()
+            attn.attn_bwd_stage(i, t["q"], t["k"], t["v"], t["o"], t["lse"], t["do"], t["dq"], t["dk"], t["dv"], scale,
+                                t["ws"], causal=cz, stream=stream)
+        return run
 
-    kernels = {"fwd": time_launches(lambda: attn.attn_fwd_ex(q, k, v, o, lse, scale, causal=cz, stream=stream), reps)}
+    def fwd_only():
+        t = next_set()
+        attn.attn_fwd_ex(t["q"], t["k"], t["v"], t["o"], t["lse"], scale, causal=cz, stream=stream)
+
+    kernels = {"fwd": time_launches(fwd_only, reps)}
     if with_bwd:
         kernels.update({"bwd_prep": time_launches(stage(0), reps), "bwd_dkdv": time_launches(stage(1), reps),
                         "bwd_dq": time_launches(stage(2), reps)})
@@ -249,29 +337,39 @@ def main(argv=None) -> int:
     # avoid a cross-workgroup reduction; only its dQ product (2 B H N^2 d) is
     # algorithmic work, so its roofline fraction counts that alone.
     kflops = {"fwd": fwd_flops(B, H, N, d, cz), "bwd_dkdv": 0.8 * bwd_flops(B, H, N, d, cz),
-              "bwd_dq": 0.2 * bwd_flops(B, H, N, d, cz)}
+              "bwd_dq": 0.2 * bwd_flops(B, H, N, d, cz), "bwd_prep": 0.0}
+    # Algorithmic HBM bytes per launch: every tensor read or written once (E elements of s bytes per [B,H,N,d]
+    # tensor, R fp32 rows per statistic).
+    E, R, sz = B * H * N * d, B * H * N, 2
+    kbytes = {"fwd": 4 * E * sz + 4 * R, "bwd_prep": 2 * E * sz + 12 * R, "bwd_dkdv": 6 * E * sz + 8 * R,
+              "bwd_dq": 5 * E * sz + 8 * R}
     kname_full = {"fwd": "fwd_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel",
                   "bwd_prep": "bwd_prep_kernel"}
     dominant = max(kernels, key=kernels.get)
-    if dominant in kflops:
-        achieved = kflops[dominant] / (kernels[dominant] * 1e-3) / 1e12
+    wkey = w.name + ("_causal" if cz else "") + ("_f16" if args.dtype == "f16" else "")
+    # The kernel's bound: matrix cores when its algorithmic FLOP per HBM byte reaches the machine balance
+    # (2516.6 TFLOP/s / 8 TB/s = 315), HBM below it.
+    intensity = kflops[dominant] / kbytes[dominant]
+    t_s = kernels[dominant] * 1e-3
+    if intensity >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = kflops[dominant] / t_s / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                    "traffic": measured_traffic(w.name + ("_causal" if cz else "") + ("_f16" if args.dtype == "f16" else ""), kname_full[dominant]),
-                    "kernel": kname_full[dominant], "avg_ms": round(kernels[dominant], 5)}
-    else:  # the HBM-bound delta kernel dominates (tiny workloads only)
-        rows = B * H * N
-        nbytes = rows * d * 2 * 2 + rows * 4
-        achieved = nbytes / (kernels[dominant] * 1e-3) / 1e9
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = kbytes[dominant] / t_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": measured_traffic(w.name + ("_causal" if cz else "") + ("_f16" if args.dtype == "f16" else ""), kname_full[dominant]),
-                    "kernel": kname_full[dominant], "avg_ms": round(kernels[dominant], 5)}
+                    "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roofline.update({"traffic": measured_traffic(wkey, kname_full[dominant]), "kernel": kname_full[dominant],
+                     "avg_ms": round(kernels[dominant], 5), "algorithmic_bytes": kbytes[dominant],
+                     "flop_per_byte": round(intensity, 1)})
+    if args.cold:
+        roofline["inputs"] = f"rotating {len(sets)} input sets ({set_bytes * len(sets) / 2**30:.2f} GiB, beyond L2 and MALL)"
 
     record = {
         "metric": METRIC if not cz else METRIC + ", causal mask (N(N+1)/2 pairs per head)", "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
-        "config": {"workload": w.name + ("_causal" if cz else "") + ("_f16" if args.dtype == "f16" else ""), "B": B, "H": H, "N": N, "d_k": d, "passes": "+".join(w.passes),
+        "config": {"workload": wkey + ("_cold" if args.cold else ""), "B": B, "H": H, "N": N, "d_k": d, "passes": "+".join(w.passes),
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "frac_of_bf16_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "kernel_ms": {kname: round(t, 5) for kname, t in kernels.items()},

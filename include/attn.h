@@ -115,7 +115,7 @@ int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Extended entry points: element type and masks.
+ * Extended entry points: element type, memory layout and masks.
  *
  * The article defines unmasked attention (§1 "Attention" formula). §3 opens
  * with long text sequences as the case where the N x N score matrix becomes
@@ -137,20 +137,39 @@ int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
  * ATTN_DTYPE_F16 (IEEE binary16). Both use the matrix cores in that type with
  * float32 accumulation; probabilities and dS are rounded to it (nearest even)
  * before their products, and outputs are rounded to it.
- * attn_fwd_ex(ATTN_DTYPE_BF16, ..., 0, NULL, stream) is attn_fwd. Any other
- * dtype returns ATTN_ERR_UNSUPPORTED.
+ * attn_fwd_ex(ATTN_DTYPE_BF16, ATTN_LAYOUT_BHND, ..., 0, NULL, stream) is
+ * attn_fwd. Any other dtype returns ATTN_ERR_UNSUPPORTED.
  */
 typedef enum { ATTN_DTYPE_BF16 = 0, ATTN_DTYPE_F16 = 1 } attn_dtype_t;
 
-int attn_fwd_ex(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+/*
+ * layout is an attn_layout_t: where the rows of head (b, h) sit. In every
+ * layout the d_k elements of a row are contiguous and lse stays [B, H, N].
+ *   ATTN_LAYOUT_BHND        every tensor [B, H, N, d_k] contiguous (as for
+ *                           attn_fwd / attn_bwd).
+ *   ATTN_LAYOUT_BNHD        every tensor [B, N, H, d_k] contiguous: the
+ *                           token-major layout a row-wise projection X W
+ *                           produces, read and written with no transpose.
+ *   ATTN_LAYOUT_QKV_PACKED  q, k, v point into one [B, N, 3, H, d_k] buffer
+ *                           (the output of one fused Q/K/V projection):
+ *                           k = q + H d_k and v = q + 2 H d_k elements;
+ *                           dq, dk, dv likewise into one gradient buffer of
+ *                           that shape; o and dO are [B, N, H, d_k].
+ *                           Otherwise ATTN_ERR_INVALID_ARG.
+ * An unknown layout returns ATTN_ERR_UNSUPPORTED.
+ */
+typedef enum { ATTN_LAYOUT_BHND = 0, ATTN_LAYOUT_BNHD = 1, ATTN_LAYOUT_QKV_PACKED = 2 } attn_layout_t;
+
+int attn_fwd_ex(int dtype, int layout, const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int H, int N, int d_k, float scale, int causal, const int* kv_len, void* stream);
 
 /*
  * Backward with masks: the gradients of attn_fwd_ex's output for the same
- * dtype, causal and kv_len (which must be the values the forward used). The
- * workspace contract is attn_bwd's; kv_len must not overlap an output.
+ * dtype, layout, causal and kv_len (which must be the values the forward
+ * used); dq, dk, dv come back in that layout. The workspace contract is
+ * attn_bwd's; kv_len must not overlap an output.
  */
-int attn_bwd_ex(int dtype, const void* q, const void* k, const void* v, const void* o, const float* lse,
+int attn_bwd_ex(int dtype, int layout, const void* q, const void* k, const void* v, const void* o, const float* lse,
                 const void* dO, void* dq, void* dk, void* dv,
                 int B, int H, int N, int d_k, float scale, int causal, const int* kv_len,
                 void* workspace, size_t workspace_bytes, void* stream);
@@ -169,7 +188,7 @@ int attn_bwd_ex(int dtype, const void* q, const void* k, const void* v, const vo
  * Every check of attn_bwd_ex applies to every stage (all pointers are
  * required). Returns ATTN_ERR_INVALID_ARG for a stage outside 0..2.
  */
-int attn_bwd_stage(int stage, int dtype, const void* q, const void* k, const void* v, const void* o,
+int attn_bwd_stage(int stage, int dtype, int layout, const void* q, const void* k, const void* v, const void* o,
                    const float* lse, const void* dO, void* dq, void* dk, void* dv,
                    int B, int H, int N, int d_k, float scale, int causal, const int* kv_len,
                    void* workspace, size_t workspace_bytes, void* stream);

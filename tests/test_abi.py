@@ -36,6 +36,7 @@ def test_header_declares_the_boundary():
 def test_library_exports_every_declared_symbol(L):
     for name in declared_functions():
         assert hasattr(L.lib, name), name
+        assert callable(getattr(L, name, None)), f"no Python wrapper for {name}"
     assert sorted(L.EXPORTS) == declared_functions()
     out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (attn_\w+)", out))
@@ -56,10 +57,10 @@ def fwd(L, *, q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, H=1, N=8, d=64, sca
     return L.lib.attn_fwd(q, k, v, o, lse, B, H, N, d, scale, None)
 
 
-def fwd_ex(L, *, dtype=0, causal=0, kv_len=None, **kw):
+def fwd_ex(L, *, dtype=0, layout=0, causal=0, kv_len=None, **kw):
     a = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], B=1, H=1, N=8, d=64, scale=0.125)
     a.update(kw)
-    return L.lib.attn_fwd_ex(dtype, a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+    return L.lib.attn_fwd_ex(dtype, layout, a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
                              a["scale"], causal, kv_len, None)
 
 
@@ -70,7 +71,7 @@ def fwd32(L, **kw):
                               args["N"], args["d"], args["scale"], None)
 
 
-def bwd(L, stage=None, ex=False, dtype=0, causal=0, kv_len=None, **kw):
+def bwd(L, stage=None, ex=False, dtype=0, layout=0, causal=0, kv_len=None, **kw):
     a = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], do=A[5], dq=A[6], dk=A[7], dv=A[8], B=1, H=1, N=8, d=64,
              scale=0.125, ws=A[9], ws_bytes=None)
     a.update(kw)
@@ -82,8 +83,8 @@ def bwd(L, stage=None, ex=False, dtype=0, causal=0, kv_len=None, **kw):
     if stage is None and not ex:
         return L.lib.attn_bwd(*head, *tail)
     if stage is None:
-        return L.lib.attn_bwd_ex(dtype, *head, causal, kv_len, *tail)
-    return L.lib.attn_bwd_stage(stage, dtype, *head, causal, kv_len, *tail)
+        return L.lib.attn_bwd_ex(dtype, layout, *head, causal, kv_len, *tail)
+    return L.lib.attn_bwd_stage(stage, dtype, layout, *head, causal, kv_len, *tail)
 
 
 def test_forward_rejections(L):
@@ -110,6 +111,25 @@ def test_extended_forward_rejections(L):
     assert fwd_ex(L, kv_len=A[4]) == INV                    # kv_len on lse
     assert fwd_ex(L, q=None, causal=1) == INV
     assert fwd_ex(L, d=72, causal=1) == UNS
+    assert fwd_ex(L, layout=3) == UNS and fwd_ex(L, layout=-1) == UNS
+
+
+def test_layout_rejections(L):
+    """Packed Q/K/V: k and v must sit H*d and 2*H*d elements after q; outputs may not touch the packed buffer."""
+    INV = L.ATTN_ERR_INVALID_ARG
+    B, H, N, d = 1, 2, 8, 64
+    hd = H * d * 2                         # bytes between q, k and v inside one packed row
+    qkv_bytes = 3 * B * N * H * d * 2
+    good = dict(q=A[0], k=A[0] + hd, v=A[0] + 2 * hd, B=B, H=H, N=N, d=d)
+    assert fwd_ex(L, layout=2, **dict(good, k=A[1])) == INV                    # k not inside q's packed row
+    assert fwd_ex(L, layout=2, **dict(good, v=A[0] + hd)) == INV               # v == k
+    assert fwd_ex(L, layout=2, **dict(good, o=A[0] + qkv_bytes - 256)) == INV  # o inside the packed buffer
+    assert fwd_ex(L, layout=2, **dict(good, lse=A[0] + 2 * hd + 64)) == INV    # lse inside the packed buffer
+    for stage in (None, 1):
+        gq = dict(dq=A[6], dk=A[6] + hd, dv=A[6] + 2 * hd)
+        assert bwd(L, stage, ex=True, layout=2, **dict(good, **dict(gq, dk=A[7]))) == INV    # dk not packed
+        assert bwd(L, stage, ex=True, layout=2, **dict(good, **dict(gq, dq=A[0] + 16 * hd, dk=A[0] + 17 * hd,
+                                                                       dv=A[0] + 18 * hd))) == INV  # grads on inputs
 
 
 def test_backward_rejections(L):

@@ -21,6 +21,7 @@ ATTN_ERR_WORKSPACE = -3
 ATTN_ERR_HIP = -4
 ATTN_DTYPE_BF16 = 0
 ATTN_DTYPE_F16 = 1
+LAYOUTS = {"bhnd": 0, "bnhd": 1, "qkv_packed": 2}
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_bwd", "attn_bwd_f32", "attn_bwd_ex", "attn_bwd_stage",
@@ -42,11 +43,11 @@ def _load() -> ctypes.CDLL:
     lib.attn_bwd.restype = i
     lib.attn_bwd_f32.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, vp, sz, vp]
     lib.attn_bwd_f32.restype = i
-    lib.attn_fwd_ex.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
+    lib.attn_fwd_ex.argtypes = [i, i, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
     lib.attn_fwd_ex.restype = i
-    lib.attn_bwd_ex.argtypes = [i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
+    lib.attn_bwd_ex.argtypes = [i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
     lib.attn_bwd_ex.restype = i
-    lib.attn_bwd_stage.argtypes = [i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
+    lib.attn_bwd_stage.argtypes = [i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
     lib.attn_bwd_stage.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
@@ -98,6 +99,40 @@ def _shape(q, *others):
     return tuple(int(x) for x in q.shape)
 
 
+def _dims(layout: str, qkv, others=()):
+    """(B, H, N, d) from tensors in ``layout``; checks every row is contiguous and each tensor has its layout's strides.
+
+    qkv: the q, k, v (or dq, dk, dv) tensors; others: o / dO. In "bhnd" all are [B, H, N, d] contiguous; in
+    "bnhd" all are [B, N, H, d] contiguous; in "qkv_packed" q, k, v are the [B, N, H, d] slices 0, 1, 2 of one
+    [B, N, 3, H, d] tensor and the others [B, N, H, d] contiguous.
+    """
+    if layout not in LAYOUTS:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}")
+    t0 = qkv[0]
+    if t0.dim() != 4:
+        raise ValueError("tensors must be 4-D")
+    if layout == "bhnd":
+        B, H, N, d = (int(x) for x in t0.shape)
+    else:
+        B, N, H, d = (int(x) for x in t0.shape)
+    for t in tuple(qkv) + tuple(others):
+        if tuple(t.shape) != tuple(t0.shape) or t.dtype != t0.dtype:
+            raise ValueError("all tensors must share one shape and dtype")
+    for t in others:
+        if not t.is_contiguous():
+            raise ValueError("o / dO must be contiguous")
+    if layout == "qkv_packed":
+        want = (N * 3 * H * d, 3 * H * d, d, 1)
+        for t in qkv:
+            if tuple(t.stride()) != want:
+                raise ValueError("qkv_packed: q, k, v must be slices [:, :, 0/1/2] of one contiguous [B, N, 3, H, d]")
+    else:
+        for t in qkv:
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+    return B, H, N, d
+
+
 def _check_lse(lse, B, H, N):
     import torch
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
@@ -131,13 +166,15 @@ def attn_fwd(q, k, v, o, lse, scale: float, stream=None) -> None:
     _check(lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale), _stream(stream)))
 
 
-def attn_fwd_ex(q, k, v, o, lse, scale: float, causal: bool = False, kv_len=None, stream=None) -> None:
-    """Forward with masks: ``causal`` (query i sees keys j <= i) and ``kv_len`` (int32 [B] device tensor of valid keys)."""
-    B, H, N, d = _shape(q, k, v, o)
+def attn_fwd_ex(q, k, v, o, lse, scale: float, causal: bool = False, kv_len=None, stream=None,
+                layout: str = "bhnd") -> None:
+    """Forward with masks and layouts: ``causal`` (query i sees keys j <= i), ``kv_len`` (int32 [B] device tensor
+    of valid keys), ``layout`` "bhnd", "bnhd" or "qkv_packed" (see ``_dims``)."""
+    B, H, N, d = _dims(layout, (q, k, v), (o,))
     _check_lse(lse, B, H, N)
     _check_kv_len(kv_len, B)
-    _check(lib.attn_fwd_ex(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, float(scale),
-                           int(bool(causal)), _ptr(kv_len), _stream(stream)))
+    _check(lib.attn_fwd_ex(_dtype_code(q), LAYOUTS[layout], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N,
+                           d, float(scale), int(bool(causal)), _ptr(kv_len), _stream(stream)))
 
 
 def attn_fwd_f32(q, k, v, o, lse, scale: float, stream=None) -> None:
@@ -180,27 +217,29 @@ def attn_bwd_f32(q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, strea
 
 
 def attn_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, causal: bool = False, kv_len=None,
-                stream=None) -> None:
-    """Backward with the masks of attn_fwd_ex (which must match the forward's)."""
-    B, H, N, d = _shape(q, k, v, o, do, dq, dk, dv)
+                stream=None, layout: str = "bhnd") -> None:
+    """Backward with the masks and layout of attn_fwd_ex (which must match the forward's)."""
+    B, H, N, d = _dims(layout, (q, k, v), (o, do))
+    _dims(layout, (dq, dk, dv))
     _check_lse(lse, B, H, N)
     _check_kv_len(kv_len, B)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.attn_bwd_ex(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
-                           _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(kv_len),
+    _check(lib.attn_bwd_ex(_dtype_code(q), LAYOUTS[layout], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
+                           _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(kv_len),
                            _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def attn_bwd_stage(stage: int, q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, causal: bool = False,
-                   kv_len=None, stream=None) -> None:
+                   kv_len=None, stream=None, layout: str = "bhnd") -> None:
     """One stage (0 prep, 1 dK/dV, 2 dQ) of attn_bwd_ex; same arguments."""
-    B, H, N, d = _shape(q, k, v, o, do, dq, dk, dv)
+    B, H, N, d = _dims(layout, (q, k, v), (o, do))
+    _dims(layout, (dq, dk, dv))
     _check_lse(lse, B, H, N)
     _check_kv_len(kv_len, B)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.attn_bwd_stage(int(stage), _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
-                              _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)),
-                              _ptr(kv_len), _ptr(workspace), ws_bytes, _stream(stream)))
+    _check(lib.attn_bwd_stage(int(stage), _dtype_code(q), LAYOUTS[layout], _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                              _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
+                              int(bool(causal)), _ptr(kv_len), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 # ---------------------------------------------------------------- allocating conveniences

@@ -41,6 +41,46 @@ int check_shape(int B, int H, int N, int d, float scale, size_t* elems, size_t* 
 
 int from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
 
+// Strides of the tensor groups (q, k, v), (o, dO) and (dq, dk, dv) for a layout.
+struct Layout {
+  attn::Strides qkv, o, grad;
+  bool packed;  // q, k, v (and dq, dk, dv) interleaved in one [B, N, 3, H, d] buffer
+};
+
+int make_layout(int layout, int B, int H, int N, int d, Layout* L) {
+  const long long hd = (long long)H * d, nd = (long long)N * d;
+  (void)B;
+  switch (layout) {
+    case ATTN_LAYOUT_BHND:
+      L->qkv = attn::Strides{H * nd, nd, d};
+      L->o = L->grad = L->qkv;
+      L->packed = false;
+      break;
+    case ATTN_LAYOUT_BNHD:
+      L->qkv = attn::Strides{N * hd, d, (int)hd};
+      L->o = L->grad = L->qkv;
+      L->packed = false;
+      break;
+    case ATTN_LAYOUT_QKV_PACKED:
+      L->qkv = attn::Strides{3 * N * hd, d, (int)(3 * hd)};
+      L->o = attn::Strides{N * hd, d, (int)hd};
+      L->grad = L->qkv;
+      L->packed = true;
+      break;
+    default:
+      return ATTN_ERR_UNSUPPORTED;
+  }
+  // Rows of a head are addressed with 32-bit element offsets.
+  if ((long long)N * L->qkv.n > INT32_MAX / 2) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+// For the packed layout: the second and third tensor sit H * d and 2 H * d elements after the first.
+bool packed_trio(const void* a, const void* b, const void* c, size_t hd_bytes) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a);
+  return reinterpret_cast<uintptr_t>(b) == x + hd_bytes && reinterpret_cast<uintptr_t>(c) == x + 2 * hd_bytes;
+}
+
 }  // namespace
 
 extern "C" {
@@ -56,30 +96,37 @@ const char* attn_status_string(int status) {
   }
 }
 
-int attn_fwd_ex(int dtype, const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
-                int d_k, float scale, int causal, const int* kv_len, void* stream) {
+int attn_fwd_ex(int dtype, int layout, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                int H, int N, int d_k, float scale, int causal, const int* kv_len, void* stream) {
   size_t E = 0, R = 0;
-  const int st = check_shape(B, H, N, d_k, scale, &E, &R);
+  int st = check_shape(B, H, N, d_k, scale, &E, &R);
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_UNSUPPORTED;
+  Layout L;
+  if ((st = make_layout(layout, B, H, N, d_k, &L)) != ATTN_OK) return st;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
   if (kv_len != nullptr && (reinterpret_cast<uintptr_t>(kv_len) & 3u) != 0) return ATTN_ERR_INVALID_ARG;
-  const Range rq = span(q, E * 2), rk = span(k, E * 2), rv = span(v, E * 2), ro = span(o, E * 2), rl = span(lse, R * 4);
+  if (L.packed && !packed_trio(q, k, v, (size_t)H * d_k * 2)) return ATTN_ERR_INVALID_ARG;
+  // Extents: a packed q, k, v buffer is one 3 E element range starting at q.
+  const Range rq = L.packed ? span(q, 3 * E * 2) : span(q, E * 2);
+  const Range rk = L.packed ? rq : span(k, E * 2), rv = L.packed ? rq : span(v, E * 2);
+  const Range ro = span(o, E * 2), rl = span(lse, R * 4);
   if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(ro, rl)) return ATTN_ERR_INVALID_ARG;
   if (overlap(rl, rq) || overlap(rl, rk) || overlap(rl, rv)) return ATTN_ERR_INVALID_ARG;
   if (kv_len != nullptr) {
     const Range rkv = span(kv_len, (size_t)B * 4);
     if (overlap(rkv, ro) || overlap(rkv, rl)) return ATTN_ERR_INVALID_ARG;
   }
-  return from_hip(attn::launch_fwd_16(dtype == ATTN_DTYPE_F16, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                        static_cast<const uint16_t*>(v), static_cast<uint16_t*>(o), lse, B, H, N, d_k,
-                                        scale, causal, kv_len, static_cast<hipStream_t>(stream)));
+  return from_hip(attn::launch_fwd_16(dtype == ATTN_DTYPE_F16, static_cast<const uint16_t*>(q),
+                                      static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                                      static_cast<uint16_t*>(o), lse, B, H, N, d_k, scale, causal, kv_len, L.qkv, L.o,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d_k,
              float scale, void* stream) {
-  return attn_fwd_ex(ATTN_DTYPE_BF16, q, k, v, o, lse, B, H, N, d_k, scale, 0, nullptr, stream);
+  return attn_fwd_ex(ATTN_DTYPE_BF16, ATTN_LAYOUT_BHND, q, k, v, o, lse, B, H, N, d_k, scale, 0, nullptr, stream);
 }
 
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N, int d_k,
@@ -102,31 +149,37 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d_k) {
 
 namespace {
 
-// dtype -1 stands for float32 storage (attn_bwd_f32).
-int bwd_checks(int dtype, const void* q, const void* k, const void* v, const void* o, const float* lse,
+// dtype -1 stands for float32 storage (attn_bwd_f32, contiguous layout only).
+int bwd_checks(int dtype, int layout, const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k, float scale, int causal,
-               const int* kv_len, void* workspace, size_t workspace_bytes) {
+               const int* kv_len, void* workspace, size_t workspace_bytes, Layout* L) {
   size_t E = 0, R = 0;
-  const int st = check_shape(B, H, N, d_k, scale, &E, &R);
+  int st = check_shape(B, H, N, d_k, scale, &E, &R);
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16 && dtype != -1) return ATTN_ERR_UNSUPPORTED;
-  E *= dtype == -1 ? 2 : 1;  // the ranges below count 2-byte elements
+  if ((st = make_layout(layout, B, H, N, d_k, L)) != ATTN_OK) return st;
+  const size_t esz = dtype == -1 ? 4 : 2;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
   if (kv_len != nullptr && (reinterpret_cast<uintptr_t>(kv_len) & 3u) != 0) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse) || !aligned16(dO) ||
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return ATTN_ERR_INVALID_ARG;
+  const size_t hd_bytes = (size_t)H * d_k * esz;
+  if (L->packed && (!packed_trio(q, k, v, hd_bytes) || !packed_trio(dq, dk, dv, hd_bytes))) return ATTN_ERR_INVALID_ARG;
   const size_t need = attn::bwd_workspace_bytes(B, H, N, d_k);
   if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
-  const Range ins[6] = {span(q, E * 2), span(k, E * 2), span(v, E * 2), span(o, E * 2), span(dO, E * 2),
-                        span(lse, R * 4)};
-  const Range outs[4] = {span(dq, E * 2), span(dk, E * 2), span(dv, E * 2), span(workspace, need)};
+  // Extents: packed q, k, v (and dq, dk, dv) are one 3 E element buffer each.
+  const size_t tb = E * esz, pb = L->packed ? 3 * tb : tb;
+  const Range ins[6] = {span(q, pb), L->packed ? span(q, pb) : span(k, tb), L->packed ? span(q, pb) : span(v, tb),
+                        span(o, tb), span(dO, tb), span(lse, R * 4)};
+  const Range outs[4] = {span(dq, pb), L->packed ? span(dq, pb) : span(dk, tb), L->packed ? span(dq, pb) : span(dv, tb),
+                         span(workspace, need)};
   for (int a = 0; a < 4; ++a) {
     for (int b = 0; b < 6; ++b)
       if (overlap(outs[a], ins[b])) return ATTN_ERR_INVALID_ARG;
-    for (int b = a + 1; b < 4; ++b)
-      if (overlap(outs[a], outs[b])) return ATTN_ERR_INVALID_ARG;
+    for (int b = a + 1; b < 4; ++b)  // packed dq, dk, dv interleave by construction
+      if (!(L->packed && b < 3) && overlap(outs[a], outs[b])) return ATTN_ERR_INVALID_ARG;
     if (kv_len != nullptr && overlap(outs[a], span(kv_len, (size_t)B * 4))) return ATTN_ERR_INVALID_ARG;
   }
   return ATTN_OK;
@@ -134,35 +187,23 @@ int bwd_checks(int dtype, const void* q, const void* k, const void* v, const voi
 
 int bwd_launch(int dtype, int stage, const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k, float scale, int causal,
-               const int* kv_len, void* workspace, void* stream) {
+               const int* kv_len, const Layout& L, void* workspace, void* stream) {
+  const attn::Strides st[4] = {L.qkv, L.o, L.o, L.grad};
   return from_hip(attn::launch_bwd_16_stage(
-      dtype == ATTN_DTYPE_F16, stage, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-      static_cast<const uint16_t*>(o), lse, static_cast<const uint16_t*>(dO), static_cast<uint16_t*>(dq),
-      static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B, H, N, d_k, scale, causal, kv_len, workspace,
-      static_cast<hipStream_t>(stream)));
+      dtype == ATTN_DTYPE_F16, stage, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o), lse, static_cast<const uint16_t*>(dO),
+      static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B, H, N, d_k, scale, causal,
+      kv_len, st, workspace, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
 
-int attn_bwd_ex(int dtype, const void* q, const void* k, const void* v, const void* o, const float* lse,
-                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k, float scale, int causal,
-                const int* kv_len, void* workspace, size_t workspace_bytes, void* stream) {
-  const int st = bwd_checks(dtype, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, workspace,
-                            workspace_bytes);
-  if (st != ATTN_OK) return st;
-  for (int stage = 0; stage < 3; ++stage) {
-    const int r = bwd_launch(dtype, stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, workspace,
-                             stream);
-    if (r != ATTN_OK) return r;
-  }
-  return ATTN_OK;
-}
-
 int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o, const float* lse, const float* dO,
                  float* dq, float* dk, float* dv, int B, int H, int N, int d_k, float scale, void* workspace,
                  size_t workspace_bytes, void* stream) {
-  const int st = bwd_checks(-1, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, 0, nullptr, workspace,
-                            workspace_bytes);
+  Layout L;
+  const int st = bwd_checks(-1, ATTN_LAYOUT_BHND, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, 0, nullptr,
+                            workspace, workspace_bytes, &L);
   if (st != ATTN_OK) return st;
   for (int stage = 0; stage < 3; ++stage) {
     const int r = from_hip(attn::launch_bwd_f32_stage(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale,
@@ -172,22 +213,38 @@ int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
   return ATTN_OK;
 }
 
+int attn_bwd_ex(int dtype, int layout, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k, float scale, int causal,
+                const int* kv_len, void* workspace, size_t workspace_bytes, void* stream) {
+  Layout L;
+  const int st = bwd_checks(dtype, layout, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len,
+                            workspace, workspace_bytes, &L);
+  if (st != ATTN_OK) return st;
+  for (int stage = 0; stage < 3; ++stage) {
+    const int r = bwd_launch(dtype, stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, L,
+                             workspace, stream);
+    if (r != ATTN_OK) return r;
+  }
+  return ATTN_OK;
+}
+
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
              void* dk, void* dv, int B, int H, int N, int d_k, float scale, void* workspace, size_t workspace_bytes,
              void* stream) {
-  return attn_bwd_ex(ATTN_DTYPE_BF16, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, 0, nullptr, workspace,
-                     workspace_bytes, stream);
+  return attn_bwd_ex(ATTN_DTYPE_BF16, ATTN_LAYOUT_BHND, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, 0,
+                     nullptr, workspace, workspace_bytes, stream);
 }
 
-int attn_bwd_stage(int stage, int dtype, const void* q, const void* k, const void* v, const void* o,
+int attn_bwd_stage(int stage, int dtype, int layout, const void* q, const void* k, const void* v, const void* o,
                    const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k,
                    float scale, int causal, const int* kv_len, void* workspace, size_t workspace_bytes,
                    void* stream) {
   if (stage < 0 || stage > 2) return ATTN_ERR_INVALID_ARG;
-  const int st = bwd_checks(dtype, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, workspace,
-                            workspace_bytes);
+  Layout L;
+  const int st = bwd_checks(dtype, layout, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len,
+                            workspace, workspace_bytes, &L);
   if (st != ATTN_OK) return st;
-  return bwd_launch(dtype, stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, workspace,
+  return bwd_launch(dtype, stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, L, workspace,
                     stream);
 }
 

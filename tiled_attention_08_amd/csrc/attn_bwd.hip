@@ -51,15 +51,17 @@ constexpr int BCQ = 32;                  // dQ kernel: keys per step
 template <class E, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ O, const uint16_t* __restrict__ dO,
                                                        const float* __restrict__ LSE, float* __restrict__ lse2,
-                                                       float* __restrict__ ndelta, long rows) {
+                                                       float* __restrict__ ndelta, long rows, int N, int H, Strides so,
+                                                       Strides sd) {
   const long gid = (long)blockIdx.x * 256 + threadIdx.x;
   const long row = gid >> 3;
   const int part = (int)(gid & 7);
   constexpr int PER = D / 8;  // elements per lane: 4, 8, 12 or 16, read 4 at a time (8 bytes)
   float s = 0.f;
   if (row < rows) {
-    const uint16_t* o = O + row * D + part * PER;
-    const uint16_t* g = dO + row * D + part * PER;
+    const int bh = (int)(row / N), n = (int)(row - (long)bh * N);
+    const uint16_t* o = O + head_off(so, bh, H) + n * so.n + part * PER;
+    const uint16_t* g = dO + head_off(sd, bh, H) + n * sd.n + part * PER;
 #pragma unroll
     for (int c = 0; c < PER; c += 4) {
       const u32x2 a = *reinterpret_cast<const u32x2*>(o + c);
@@ -88,8 +90,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 // `runs` (total 64-slot runs of the tile) may be below 4 * per_lane: the last
 // waves then issue fewer DMAs (callers wait for all of a wave's loads).
 template <int D>
-__device__ __forceinline__ void dma_rows(const uint16_t* head_src, int row0, int N, unsigned char* dst, int wave,
-                                         int lane, int per_lane, int runs) {
+__device__ __forceinline__ void dma_rows(const uint16_t* head_src, int row_stride, int row0, int N,
+                                         unsigned char* dst, int wave, int lane, int per_lane, int runs) {
   constexpr int ROWB = D * 2;
   for (int r = 0; r < per_lane; ++r) {
     if (wave * per_lane + r >= runs) break;
@@ -97,7 +99,7 @@ __device__ __forceinline__ void dma_rows(const uint16_t* head_src, int row0, int
     const int p = slot0 + lane;
     const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz<ROWB>(row);
     const int gr = min(row0 + row, N - 1);
-    dma16(head_src + (size_t)gr * D + chunk * 8, dst + slot0 * 16);
+    dma16(head_src + gr * row_stride + chunk * 8, dst + slot0 * 16);
   }
 }
 
@@ -125,7 +127,8 @@ __attribute__((amdgpu_waves_per_eu(D <= 64 ? BWD_WAVES_PER_EU : 1, D <= 64 ? BWD
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                      const uint16_t* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ ndelta,
                      uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk, int total, float c,
-                     float scale, const int* __restrict__ kv_len, int H, int causal) {
+                     float scale, const int* __restrict__ kv_len, int H, int causal, Strides sq, Strides sd,
+                     Strides sg) {
   using S = DkdvShape<D, MB>;
   constexpr int BRQ = S::BRQ;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
@@ -137,7 +140,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const int work = xcd_remap(blockIdx.x, total);
   int bh, kblk;  // causal: the first key blocks have the most queries and are handed out first
   work_order(work, total, n_kblk, causal != 0, false, bh, kblk);
-  const size_t head = (size_t)bh * N * D;
+  const size_t hq = head_off(sq, bh, H), hd = head_off(sd, bh, H), hg = head_off(sg, bh, H);
   const size_t hrow = (size_t)bh * N;
   const int k0 = kblk * BCK;
   const int key = k0 + wave * 32 + l32;  // this lane's key
@@ -151,8 +154,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
       const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int c8 = 0; c8 < D / 8; ++c8) {
-        *reinterpret_cast<u32x4*>(dK + head + (size_t)key * D + c8 * 8) = z;
-        *reinterpret_cast<u32x4*>(dV + head + (size_t)key * D + c8 * 8) = z;
+        *reinterpret_cast<u32x4*>(dK + hg + key * sg.n + c8 * 8) = z;
+        *reinterpret_cast<u32x4*>(dV + hg + key * sg.n + c8 * 8) = z;
       }
     }
     return;
@@ -164,8 +167,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   for (int cc = 0; cc < D / 16; ++cc) {
     u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
     if (key_ok) {
-      a = *reinterpret_cast<const u32x4*>(K + head + (size_t)key * D + cc * 16 + h * 8);
-      b = *reinterpret_cast<const u32x4*>(V + head + (size_t)key * D + cc * 16 + h * 8);
+      a = *reinterpret_cast<const u32x4*>(K + hq + key * sq.n + cc * 16 + h * 8);
+      b = *reinterpret_cast<const u32x4*>(V + hq + key * sq.n + cc * 16 + h * 8);
     }
     kf[cc] = a;
     vf[cc] = b;
@@ -173,8 +176,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
   auto dma_step = [&](int i, int buf) {
     const int q0 = i * BRQ;
-    dma_rows<D>(Q + head, q0, N, smem + S::OFF_Q + buf * S::QTILEB, wave, lane, S::QDMA, 4 * S::QDMA);
-    dma_rows<D>(dO + head, q0, N, smem + S::OFF_DO + buf * S::QTILEB, wave, lane, S::QDMA, 4 * S::QDMA);
+    dma_rows<D>(Q + hq, sq.n, q0, N, smem + S::OFF_Q + buf * S::QTILEB, wave, lane, S::QDMA, 4 * S::QDMA);
+    dma_rows<D>(dO + hd, sd.n, q0, N, smem + S::OFF_DO + buf * S::QTILEB, wave, lane, S::QDMA, 4 * S::QDMA);
     const size_t r = hrow + min(q0 + lane, N - 1);
     if (wave == 0) dma4(lse2 + r, smem + S::OFF_L + buf * S::LROWS * 4);
     if (wave == 1) dma4(ndelta + r, smem + S::OFF_DL + buf * S::LROWS * 4);
@@ -323,8 +326,8 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 
   // ---- epilogue: dV = (dV^T)^T, dK = scale (dK^T)^T, bf16 RNE. Lane: key, dims db*32 + 8jj + 4h + 0..3.
   if (key_ok) {
-    uint16_t* dvrow = dV + head + (size_t)key * D;
-    uint16_t* dkrow = dK + head + (size_t)key * D;
+    uint16_t* dvrow = dV + hg + key * sg.n;
+    uint16_t* dkrow = dK + hg + key * sg.n;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -356,7 +359,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BWD_WA
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                    const uint16_t* __restrict__ dO, const float* __restrict__ lse2_in, const float* __restrict__ ndelta,
                    uint16_t* __restrict__ dQ, int N, int n_qblk, int total, float c, float scale,
-                   const int* __restrict__ kv_len, int H, int causal) {
+                   const int* __restrict__ kv_len, int H, int causal, Strides sq, Strides sd, Strides sg) {
   using S = DqShape<D, QB>;
   static_assert((BCQ * D / 8) % 64 == 0, "K/V step tiles are whole 64-slot runs");
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
@@ -368,7 +371,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int work = xcd_remap(blockIdx.x, total);
   int bh, qblk;  // causal: the last row blocks have the most keys and are handed out first
   work_order(work, total, n_qblk, causal != 0, true, bh, qblk);
-  const size_t head = (size_t)bh * N * D;
+  const size_t hq = head_off(sq, bh, H), hd = head_off(sd, bh, H);
   const size_t hrow = (size_t)bh * N;
   const int qw0 = qblk * S::BR + wave * 32 * QB;
 
@@ -396,8 +399,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     for (int cc = 0; cc < D / 16; ++cc) {
       u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
       if (ok) {
-        a = *reinterpret_cast<const u32x4*>(Q + head + (size_t)q * D + cc * 16 + h * 8);
-        b = *reinterpret_cast<const u32x4*>(dO + head + (size_t)q * D + cc * 16 + h * 8);
+        a = *reinterpret_cast<const u32x4*>(Q + hq + q * sq.n + cc * 16 + h * 8);
+        b = *reinterpret_cast<const u32x4*>(dO + hd + q * sd.n + cc * 16 + h * 8);
       }
       qf[qb][cc] = a;
       df[qb][cc] = b;
@@ -413,8 +416,8 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     for (int db = 0; db < D / 32; ++db) dqacc[qb][db] = f32x16{};
 
   auto dma_step = [&](int j, int buf) {
-    dma_rows<D>(K + head, j * BCQ, N, smem + buf * 2 * S::TILEB, wave, lane, S::KDMA, S::KRUNS);
-    dma_rows<D>(V + head, j * BCQ, N, smem + buf * 2 * S::TILEB + S::TILEB, wave, lane, S::KDMA, S::KRUNS);
+    dma_rows<D>(K + hq, sq.n, j * BCQ, N, smem + buf * 2 * S::TILEB, wave, lane, S::KDMA, S::KRUNS);
+    dma_rows<D>(V + hq, sq.n, j * BCQ, N, smem + buf * 2 * S::TILEB + S::TILEB, wave, lane, S::KDMA, S::KRUNS);
   };
 
   if (ntiles > 0) {
@@ -505,7 +508,7 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   for (int qb = 0; qb < QB; ++qb) {
     const int q = qw0 + qb * 32 + l32;
     if (q < N) {
-      uint16_t* row = dQ + head + (size_t)q * D;
+      uint16_t* row = dQ + head_off(sg, bh, H) + q * sg.n;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -681,26 +684,26 @@ template <class E, int D>
 static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                      const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq,
                                      uint16_t* dk, uint16_t* dv, int B, int H, int N, float scale, int causal,
-                                     const int* kv_len, void* workspace, hipStream_t stream) {
+                                     const int* kv_len, const Strides* st, void* workspace, hipStream_t stream) {
   const long rows = (long)B * H * N;
   float* lse2 = reinterpret_cast<float*>(workspace);
   float* ndelta = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(workspace) + align256(rows * 4));
   const float c = scale * kLog2e;
   if (stage == 0) {
     hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, stream, o, dO,
-                       lse, lse2, ndelta, rows);
+                       lse, lse2, ndelta, rows, N, H, st[1], st[2]);
   } else if (stage == 1) {
     const int n_kblk = (N + BCK - 1) / BCK;
     const int total = n_kblk * B * H;
     hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, BWD_MB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, ndelta,
-                       dk, dv, N, n_kblk, total, c, scale, kv_len, H, causal);
+                       dk, dv, N, n_kblk, total, c, scale, kv_len, H, causal, st[0], st[2], st[3]);
   } else {
     constexpr int QB = D <= 64 ? 2 : 1;
     constexpr int BR = DqShape<D, QB>::BR;
     const int n_qblk = (N + BR - 1) / BR;
     const int total = n_qblk * B * H;
     hipLaunchKernelGGL((bwd_dq_kernel<E, D, QB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, ndelta, dq,
-                       N, n_qblk, total, c, scale, kv_len, H, causal);
+                       N, n_qblk, total, c, scale, kv_len, H, causal, st[0], st[2], st[3]);
   }
   return hipGetLastError();
 }
@@ -708,9 +711,11 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
 hipError_t launch_bwd_16_stage(bool f16, int stage, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq, uint16_t* dk,
                                  uint16_t* dv, int B, int H, int N, int d, float scale, int causal,
-                                 const int* kv_len, void* workspace, hipStream_t stream) {
+                                 const int* kv_len, const Strides* st, void* workspace,
+                               hipStream_t stream) {
 #define ATTN_BWD_STAGE(E, D) \
-  launch_bwd_stage_t<E, D>(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, causal, kv_len, workspace, stream)
+  launch_bwd_stage_t<E, D>(stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, scale, causal, kv_len, st, workspace, \
+                           stream)
   if (f16) {
     switch (d) {
       case 32: return ATTN_BWD_STAGE(F16, 32);

@@ -208,6 +208,22 @@ __device__ __forceinline__ int xcd_remap(int id, int total) {
   return x * per + (x < rem ? x : rem) + slot;
 }
 
+// Element strides of a group of [B, H, N, d] tensors: batch, head and row
+// (token); the d elements of a row are contiguous. Contiguous [B,H,N,d] is
+// {H N d, N d, d}; token-major [B,N,H,d] is {N H d, d, H d}; Q, K and V
+// packed in one [B,N,3,H,d] buffer use {3 N H d, d, 3 H d} from their own
+// base pointers.
+struct Strides {
+  long long b, h;
+  int n;
+};
+
+// Offset of head (b, h) = (bh / H, bh % H).
+__device__ __forceinline__ size_t head_off(const Strides& s, int bh, int H) {
+  const int b = bh / H;
+  return (size_t)b * (size_t)s.b + (size_t)(bh - b * H) * (size_t)s.h;
+}
+
 // (head, block) of work item `work` (after xcd_remap) for a grid of total =
 // heads * n_blk items. Plain order: head-major, block ascending. With
 // `causal`, blocks carry unequal work (the block with the most is n_blk - 1

@@ -54,6 +54,11 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units a row max may grow before O
 #ifndef FWD_NS64
 #define FWD_NS64 2
 #endif
+// Rows shorter than FWD_LONG_N: K/V tiles in flight (4 = a whole 196-key
+// head issued at once with 64-key tiles).
+#ifndef FWD_NS_SHORT
+#define FWD_NS_SHORT 2
+#endif
 #ifndef FWD_QB128
 #define FWD_QB128 1
 #endif
@@ -89,7 +94,7 @@ template <class E, int D, int QB, int KB, int NS, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(FWD_WAVES_PER_EU, FWD_WAVES_PER_EU)))
 void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                      uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qblk, int total, float c,
-                     uint32_t qsign, const int* __restrict__ kv_len, int H, int causal) {
+                     uint32_t qsign, const int* __restrict__ kv_len, int H, int causal, Strides sq, Strides so) {
   using S = FwdShape<D, QB, KB, NS, WAVES>;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
 
@@ -100,10 +105,10 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
   const int work = xcd_remap(blockIdx.x, total);
   int bh, qblk;  // causal: the last row blocks have the most keys and are handed out first
   work_order(work, total, n_qblk, causal != 0, true, bh, qblk);
-  const size_t head = (size_t)bh * N * D;
-  const uint16_t* Qh = Q + head;
-  const uint16_t* Kh = K + head;
-  const uint16_t* Vh = V + head;
+  const size_t hq = head_off(sq, bh, H);  // Q, K and V share one layout
+  const uint16_t* Qh = Q + hq;
+  const uint16_t* Kh = K + hq;
+  const uint16_t* Vh = V + hq;
   const int qw0 = qblk * S::BR + wave * 32 * QB;
 
   // Visible keys of query q: j < klim(q) with klim(q) = min(kv, q + 1) under
@@ -121,7 +126,7 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
 #pragma unroll
     for (int cc = 0; cc < D / 16; ++cc) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (q < N) v = *reinterpret_cast<const u32x4*>(Qh + (size_t)q * D + cc * 16 + h * 8);
+      if (q < N) v = *reinterpret_cast<const u32x4*>(Qh + q * sq.n + cc * 16 + h * 8);  // q * n < 2^31 (host check)
       v ^= qsign;
       qf[qb][cc] = v;
     }
@@ -156,8 +161,8 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
       const int p = slot0 + lane;
       const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz<S::ROWB>(row);
       const int key = min(j * S::BC + row, N - 1);
-      dma16(Kh + (size_t)key * D + chunk * 8, Ks + slot0 * 16);
-      dma16(Vh + (size_t)key * D + chunk * 8, Vs + slot0 * 16);
+      dma16(Kh + key * sq.n + chunk * 8, Ks + slot0 * 16);
+      dma16(Vh + key * sq.n + chunk * 8, Vs + slot0 * 16);
     }
   };
   // Wait until tile j has landed, given that tiles up to min(j + NS - 2, ntiles - 1)
@@ -314,7 +319,7 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     const int q = qw0 + qb * 32 + l32;
     if (q < N) {
-      uint16_t* orow = O + head + (size_t)q * D;
+      uint16_t* orow = O + head_off(so, bh, H) + q * so.n;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -419,14 +424,14 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 template <class E, int D, int QB, int KB, int NS, int WAVES>
 static hipError_t launch_fwd_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                                     float* lse, int B, int H, int N, float scale, int causal, const int* kv_len,
-                                    hipStream_t stream) {
+                                    Strides sq, Strides so, hipStream_t stream) {
   using S = FwdShape<D, QB, KB, NS, WAVES>;
   const int n_qblk = (N + S::BR - 1) / S::BR;
   const int total = n_qblk * B * H;
   const float c = fabsf(scale) * kLog2e;
   const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
   hipLaunchKernelGGL((fwd_kernel<E, D, QB, KB, NS, WAVES>), dim3(total), dim3(S::THREADS), 0, stream, q, k, v, o,
-                     lse, N, n_qblk, total, c, qsign, kv_len, H, causal);
+                     lse, N, n_qblk, total, c, qsign, kv_len, H, causal, sq, so);
   return hipGetLastError();
 }
 
@@ -439,29 +444,30 @@ static hipError_t launch_fwd_t(const uint16_t* q, const uint16_t* k, const uint1
 template <class E>
 static hipError_t launch_fwd_e(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
                                int B, int H, int N, int d, float scale, int causal, const int* kv_len,
-                               hipStream_t stream) {
+                               Strides sq, Strides so, hipStream_t stream) {
   const bool lng = N >= FWD_LONG_N;
 #define ATTN_FWD(D, QB, KB, NS, W) \
-  launch_fwd_t<E, D, QB, KB, NS, W>(q, k, v, o, lse, B, H, N, scale, causal, kv_len, stream)
+  launch_fwd_t<E, D, QB, KB, NS, W>(q, k, v, o, lse, B, H, N, scale, causal, kv_len, sq, so, stream)
   switch (d) {
     case 32:
-      return lng ? ATTN_FWD(32, 1, 4, 2, FWD_WAVES_LONG) : ATTN_FWD(32, 2, 2, 2, 4);
+      return lng ? ATTN_FWD(32, 1, 4, 2, FWD_WAVES_LONG) : ATTN_FWD(32, 2, 2, FWD_NS_SHORT, 4);
     case 64:
       return lng ? ATTN_FWD(64, FWD_QB64, FWD_KB64, FWD_NS64, FWD_WAVES_LONG)
-                 : ATTN_FWD(64, FWD_QB64, FWD_KB64, FWD_NS64, 4);
+                 : ATTN_FWD(64, FWD_QB64, FWD_KB64, FWD_NS_SHORT, 4);
     case 96:
       return lng ? ATTN_FWD(96, 1, 4, 2, FWD_WAVES_LONG) : ATTN_FWD(96, 1, 4, 2, 4);
     default:
       return lng ? ATTN_FWD(128, FWD_QB128, FWD_KB128, FWD_NS128, FWD_WAVES_LONG)
-                 : ATTN_FWD(128, FWD_QB128, FWD_KB128, FWD_NS128, 4);
+                 : ATTN_FWD(128, FWD_QB128, FWD_KB128, FWD_NS_SHORT, 4);
   }
 #undef ATTN_FWD
 }
 
 hipError_t launch_fwd_16(bool f16, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
-                         int B, int H, int N, int d, float scale, int causal, const int* kv_len, hipStream_t stream) {
-  return f16 ? launch_fwd_e<F16>(q, k, v, o, lse, B, H, N, d, scale, causal, kv_len, stream)
-             : launch_fwd_e<Bf16>(q, k, v, o, lse, B, H, N, d, scale, causal, kv_len, stream);
+                         int B, int H, int N, int d, float scale, int causal, const int* kv_len, Strides sq, Strides so,
+                         hipStream_t stream) {
+  return f16 ? launch_fwd_e<F16>(q, k, v, o, lse, B, H, N, d, scale, causal, kv_len, sq, so, stream)
+             : launch_fwd_e<Bf16>(q, k, v, o, lse, B, H, N, d, scale, causal, kv_len, sq, so, stream);
 }
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,

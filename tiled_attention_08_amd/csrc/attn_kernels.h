@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "attn_device.h"
+
 namespace attn {
 
 // Keys of a head handled by one dK/dV workgroup (32 per wave).
@@ -16,8 +18,10 @@ constexpr int kBwdKeysPerBlock = 128;
 // keys j >= kv_len[b] are hidden from every query of batch entry b (values are
 // clamped to [0, N] on the device).
 // 16-bit storage: bf16, or fp16 when f16 is true.
+// sq: strides of q, k and v; so: of o.
 hipError_t launch_fwd_16(bool f16, const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
-                         int B, int H, int N, int d, float scale, int causal, const int* kv_len, hipStream_t stream);
+                         int B, int H, int N, int d, float scale, int causal, const int* kv_len, Strides sq, Strides so,
+                         hipStream_t stream);
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H, int N,
                           int d, float scale, hipStream_t stream);
@@ -26,11 +30,11 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
 
 // One backward stage: 0 = lse * log2(e) and -delta, 1 = dK and dV, 2 = dQ.
-// Masks as for launch_fwd_bf16.
+// Masks as for launch_fwd_16; st[0..3]: strides of (q, k, v), o, dO and (dq, dk, dv).
 hipError_t launch_bwd_16_stage(bool f16, int stage, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq, uint16_t* dk,
                                  uint16_t* dv, int B, int H, int N, int d, float scale, int causal,
-                                 const int* kv_len, void* workspace, hipStream_t stream);
+                                 const int* kv_len, const Strides* st, void* workspace, hipStream_t stream);
 
 // fp32 backward stage (vector ALU; same stages and workspace as the 16-bit one).
 hipError_t launch_bwd_f32_stage(int stage, const float* q, const float* k, const float* v, const float* o,
