@@ -36,9 +36,15 @@ namespace attn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int BCK = kBwdKeysPerBlock;    // dK/dV kernel: keys per workgroup (32 per wave)
-#ifndef BWD_MB
-#define BWD_MB 2  // dK/dV kernel: 32-query blocks per step
+// dK/dV kernel at d_k = 64: 32-query blocks per step and 32-key blocks per
+// wave (other head dims: 2 and 1; d_k = 128 has no registers for two key
+// blocks, and 32-query tiles of d_k = 32 or 96 would not split evenly over
+// the DMA lanes).
+#ifndef BWD_MB64
+#define BWD_MB64 2
+#endif
+#ifndef BWD_KBW64
+#define BWD_KBW64 1
 #endif
 constexpr int BCQ = 32;                  // dQ kernel: keys per step
 
@@ -119,11 +125,14 @@ struct DkdvShape {
   static constexpr int LDSB = OFF_DL + 2 * LROWS * 4;
 };
 
-// d_k = 96 and 128 need more than 256 registers per lane (the dK and dV
-// accumulators alone take 96 or 128): one wave per SIMD there.
-template <class E, int D, int MB>
+// Each wave owns KBW blocks of 32 keys (one key per lane in each), so every
+// Q, dO, dO^T and Q^T fragment read from LDS feeds KBW matrix products.
+// d_k = 96 and 128, or KBW = 2, need more than 256 registers per lane (the dK
+// and dV accumulators alone take 3 to 8 x 16): one wave per SIMD there.
+template <class E, int D, int MB, int KBW>
 __global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(D <= 64 ? BWD_WAVES_PER_EU : 1, D <= 64 ? BWD_WAVES_PER_EU : 1)))
+__attribute__((amdgpu_waves_per_eu(D <= 64 && KBW == 1 ? BWD_WAVES_PER_EU : 1,
+                                   D <= 64 && KBW == 1 ? BWD_WAVES_PER_EU : 1)))
 void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                      const uint16_t* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ ndelta,
                      uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk, int total, float c,
@@ -131,6 +140,7 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                      Strides sg) {
   using S = DkdvShape<D, MB>;
   constexpr int BRQ = S::BRQ;
+  constexpr int BCK = 4 * 32 * KBW;  // keys per workgroup
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -143,36 +153,41 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   const size_t hq = head_off(sq, bh, H), hd = head_off(sd, bh, H), hg = head_off(sg, bh, H);
   const size_t hrow = (size_t)bh * N;
   const int k0 = kblk * BCK;
-  const int key = k0 + wave * 32 + l32;  // this lane's key
-  const bool key_ok = key < N;
+  int key[KBW];  // this lane's key in each of its blocks
+#pragma unroll
+  for (int kb = 0; kb < KBW; ++kb) key[kb] = k0 + (wave * KBW + kb) * 32 + l32;
   // Query i sees key j iff j < kv and (not causal or j <= i); kv = valid keys
   // of this batch entry.
   const int kv = kv_len ? min(max(kv_len[bh / H], 0), N) : N;
 
   if (k0 >= kv) {  // no query sees any key of this block: zero gradients
-    if (key_ok) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int c8 = 0; c8 < D / 8; ++c8) {
-        *reinterpret_cast<u32x4*>(dK + hg + key * sg.n + c8 * 8) = z;
-        *reinterpret_cast<u32x4*>(dV + hg + key * sg.n + c8 * 8) = z;
+    for (int kb = 0; kb < KBW; ++kb)
+      if (key[kb] < N) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c8 = 0; c8 < D / 8; ++c8) {
+          *reinterpret_cast<u32x4*>(dK + hg + key[kb] * sg.n + c8 * 8) = z;
+          *reinterpret_cast<u32x4*>(dV + hg + key[kb] * sg.n + c8 * 8) = z;
+        }
       }
-    }
     return;
   }
 
   // K and V fragments of this lane's key: B operands of S = Q K^T and dP = dO V^T.
-  u32x4 kf[D / 16], vf[D / 16];
+  u32x4 kf[KBW][D / 16], vf[KBW][D / 16];
 #pragma unroll
-  for (int cc = 0; cc < D / 16; ++cc) {
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (key_ok) {
-      a = *reinterpret_cast<const u32x4*>(K + hq + key * sq.n + cc * 16 + h * 8);
-      b = *reinterpret_cast<const u32x4*>(V + hq + key * sq.n + cc * 16 + h * 8);
+  for (int kb = 0; kb < KBW; ++kb)
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      if (key[kb] < N) {
+        a = *reinterpret_cast<const u32x4*>(K + hq + key[kb] * sq.n + cc * 16 + h * 8);
+        b = *reinterpret_cast<const u32x4*>(V + hq + key[kb] * sq.n + cc * 16 + h * 8);
+      }
+      kf[kb][cc] = a;
+      vf[kb][cc] = b;
     }
-    kf[cc] = a;
-    vf[cc] = b;
-  }
 
   auto dma_step = [&](int i, int buf) {
     const int q0 = i * BRQ;
@@ -183,16 +198,18 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     if (wave == 1) dma4(ndelta + r, smem + S::OFF_DL + buf * S::LROWS * 4);
   };
 
-  f32x16 dvacc[D / 32], dkacc[D / 32];
+  f32x16 dvacc[KBW][D / 32], dkacc[KBW][D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    dvacc[db] = f32x16{};
-    dkacc[db] = f32x16{};
-  }
+  for (int kb = 0; kb < KBW; ++kb)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      dvacc[kb][db] = f32x16{};
+      dkacc[kb][db] = f32x16{};
+    }
 
   // Steps [i_beg, nq) hold a query that sees a key of this block (under the
   // causal mask queries before k0 see none). Steps [u_beg, u_end) need no
-  // mask: all their queries exist and see all 128 keys.
+  // mask: all their queries exist and see all BCK keys.
   const int nq = (N + BRQ - 1) / BRQ;
   const int i_beg = causal ? k0 / BRQ : 0;
   const int u_beg = causal ? (k0 + BCK - 1 + BRQ - 1) / BRQ : 0;
@@ -220,29 +237,38 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     // lane's key. The dP accumulator starts from -delta of its rows (rows
     // 8j + 4h + i, read as four float4 in accumulator order), so no separate
     // subtraction is needed.
-    f32x16 sacc[MB], pacc[MB];
+    f32x16 sacc[KBW][MB], pacc[KBW][MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      sacc[mb] = f32x16{};
+      f32x16 dinit;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const float4 d4 = *reinterpret_cast<const float4*>(DL + mb * 32 + 8 * jj + 4 * h);
-        pacc[mb][4 * jj] = d4.x;
-        pacc[mb][4 * jj + 1] = d4.y;
-        pacc[mb][4 * jj + 2] = d4.z;
-        pacc[mb][4 * jj + 3] = d4.w;
+        dinit[4 * jj] = d4.x;
+        dinit[4 * jj + 1] = d4.y;
+        dinit[4 * jj + 2] = d4.z;
+        dinit[4 * jj + 3] = d4.w;
+      }
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) {
+        sacc[kb][mb] = f32x16{};
+        pacc[kb][mb] = dinit;
       }
 #pragma unroll
       for (int cc = 0; cc < D / 16; ++cc) {
         const int off = tile_off<S::ROWB>(mb * 32 + l32, cc * 16 + h * 8);
-        sacc[mb] = E::mfma(lds_read_b128(Qs, off), kf[cc], sacc[mb]);
-        pacc[mb] = E::mfma(lds_read_b128(dOs, off), vf[cc], pacc[mb]);
+        const u32x4 aq = lds_read_b128(Qs, off), ado = lds_read_b128(dOs, off);
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) {
+          sacc[kb][mb] = E::mfma(aq, kf[kb][cc], sacc[kb][mb]);
+          pacc[kb][mb] = E::mfma(ado, vf[kb][cc], pacc[kb][mb]);
+        }
       }
     }
 
     // ---- P = exp2(S * scale * log2 e - lse * log2 e), dS = P * (dP - delta).
     // pp[mb][c2] / dsb[mb][c2]: B operands (bf16 P and dS) for queries mb*32 + 16*c2 + (0..15).
-    u32x4 pp[MB][2], dsb[MB][2];
+    u32x4 pp[KBW][MB][2], dsb[KBW][MB][2];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -250,21 +276,24 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
         const int r0 = mb * 32 + 8 * jj + 4 * h;
         const float4 l4 = *reinterpret_cast<const float4*>(L + r0);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        float p[4], ds[4];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          p[ii] = __builtin_amdgcn_exp2f(fmaf(sacc[mb][4 * jj + ii], c, -lv[ii]));
-          if (MASKED) {
-            const int qi = q0 + r0 + ii;
-            if (key >= kv || qi >= N || (causal && key > qi)) p[ii] = 0.f;
+        for (int kb = 0; kb < KBW; ++kb) {
+          float p[4], ds[4];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            p[ii] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][mb][4 * jj + ii], c, -lv[ii]));
+            if (MASKED) {
+              const int qi = q0 + r0 + ii;
+              if (key[kb] >= kv || qi >= N || (causal && key[kb] > qi)) p[ii] = 0.f;
+            }
+            ds[ii] = p[ii] * pacc[kb][mb][4 * jj + ii];
           }
-          ds[ii] = p[ii] * pacc[mb][4 * jj + ii];
+          const int c2 = jj >> 1, w0 = 2 * (jj & 1);
+          pp[kb][mb][c2][w0] = E::pack(p[0], p[1]);
+          pp[kb][mb][c2][w0 + 1] = E::pack(p[2], p[3]);
+          dsb[kb][mb][c2][w0] = E::pack(ds[0], ds[1]);
+          dsb[kb][mb][c2][w0 + 1] = E::pack(ds[2], ds[3]);
         }
-        const int c2 = jj >> 1, w0 = 2 * (jj & 1);
-        pp[mb][c2][w0] = E::pack(p[0], p[1]);
-        pp[mb][c2][w0 + 1] = E::pack(p[2], p[3]);
-        dsb[mb][c2][w0] = E::pack(ds[0], ds[1]);
-        dsb[mb][c2][w0 + 1] = E::pack(ds[2], ds[3]);
       }
 
     // ---- dV^T += dO^T P and dK^T += Q^T dS (m = dim, n = key, k = query).
@@ -279,8 +308,11 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
           const int o0 = tile_off<S::ROWB>(row0, col), o1 = tile_off<S::ROWB>(row0 + 8, col);
           const u32x4 adot = cat(lds_read_tr16_b64(dOs, o0), lds_read_tr16_b64(dOs, o1));
           const u32x4 aqt = cat(lds_read_tr16_b64(Qs, o0), lds_read_tr16_b64(Qs, o1));
-          dvacc[db] = E::mfma(adot, pp[mb][c2], dvacc[db]);
-          dkacc[db] = E::mfma(aqt, dsb[mb][c2], dkacc[db]);
+#pragma unroll
+          for (int kb = 0; kb < KBW; ++kb) {
+            dvacc[kb][db] = E::mfma(adot, pp[kb][mb][c2], dvacc[kb][db]);
+            dkacc[kb][db] = E::mfma(aqt, dsb[kb][mb][c2], dkacc[kb][db]);
+          }
         }
       }
 
@@ -324,16 +356,18 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
     }
   }
 
-  // ---- epilogue: dV = (dV^T)^T, dK = scale (dK^T)^T, bf16 RNE. Lane: key, dims db*32 + 8jj + 4h + 0..3.
-  if (key_ok) {
-    uint16_t* dvrow = dV + hg + key * sg.n;
-    uint16_t* dkrow = dK + hg + key * sg.n;
+  // ---- epilogue: dV = (dV^T)^T, dK = scale (dK^T)^T, 16-bit RNE. Lane: key, dims db*32 + 8jj + 4h + 0..3.
+#pragma unroll
+  for (int kb = 0; kb < KBW; ++kb) {
+    if (key[kb] >= N) continue;
+    uint16_t* dvrow = dV + hg + key[kb] * sg.n;
+    uint16_t* dkrow = dK + hg + key[kb] * sg.n;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const f32x16& a = dvacc[db];
-        const f32x16& b = dkacc[db];
+        const f32x16& a = dvacc[kb][db];
+        const f32x16& b = dkacc[kb][db];
         const u32x2 wv = {E::pack(a[4 * jj], a[4 * jj + 1]), E::pack(a[4 * jj + 2], a[4 * jj + 3])};
         const u32x2 wk = {E::pack(b[4 * jj] * scale, b[4 * jj + 1] * scale),
                           E::pack(b[4 * jj + 2] * scale, b[4 * jj + 3] * scale)};
@@ -693,9 +727,11 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
     hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, stream, o, dO,
                        lse, lse2, ndelta, rows, N, H, st[1], st[2]);
   } else if (stage == 1) {
+    constexpr int MB = D == 64 ? BWD_MB64 : 2, KBW = D == 64 ? BWD_KBW64 : 1;
+    constexpr int BCK = 4 * 32 * KBW;
     const int n_kblk = (N + BCK - 1) / BCK;
     const int total = n_kblk * B * H;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, BWD_MB>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, ndelta,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, MB, KBW>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, ndelta,
                        dk, dv, N, n_kblk, total, c, scale, kv_len, H, causal, st[0], st[2], st[3]);
   } else {
     constexpr int QB = D <= 64 ? 2 : 1;

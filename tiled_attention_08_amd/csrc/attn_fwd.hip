@@ -56,6 +56,9 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units a row max may grow before O
 #endif
 // Rows shorter than FWD_LONG_N: K/V tiles in flight (4 = a whole 196-key
 // head issued at once with 64-key tiles).
+#ifndef FWD_QB64_SHORT
+#define FWD_QB64_SHORT 2
+#endif
 #ifndef FWD_NS_SHORT
 #define FWD_NS_SHORT 2
 #endif
@@ -453,7 +456,7 @@ static hipError_t launch_fwd_e(const uint16_t* q, const uint16_t* k, const uint1
       return lng ? ATTN_FWD(32, 1, 4, 2, FWD_WAVES_LONG) : ATTN_FWD(32, 2, 2, FWD_NS_SHORT, 4);
     case 64:
       return lng ? ATTN_FWD(64, FWD_QB64, FWD_KB64, FWD_NS64, FWD_WAVES_LONG)
-                 : ATTN_FWD(64, FWD_QB64, FWD_KB64, FWD_NS_SHORT, 4);
+                 : ATTN_FWD(64, FWD_QB64_SHORT, FWD_KB64, FWD_NS_SHORT, 4);
     case 96:
       return lng ? ATTN_FWD(96, 1, 4, 2, FWD_WAVES_LONG) : ATTN_FWD(96, 1, 4, 2, 4);
     default:

@@ -11,8 +11,6 @@
 
 namespace attn {
 
-// Keys of a head handled by one dK/dV workgroup (32 per wave).
-constexpr int kBwdKeysPerBlock = 128;
 
 // causal != 0: query i sees keys j <= i. kv_len (device, B ints, or null):
 // keys j >= kv_len[b] are hidden from every query of batch entry b (values are
