@@ -198,6 +198,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cold", action="store_true",
                     help="rotate through copies of the inputs (about 1 GiB in all) so that every launch reads its "
                          "inputs from HBM, not from L2 or the MALL")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step (forward + backward launches) in a HIP graph and time graph replays")
     ap.add_argument("--causal", action="store_true",
                     help="time the causal-mask path (attn_fwd_ex / attn_bwd_ex); FLOPs count the N(N+1)/2 visible "
                          "query-key pairs of each head")
@@ -276,16 +278,17 @@ def main(argv=None) -> int:
 
     def step():
         t = next_set()
+        cs = torch.cuda.current_stream()  # the capture stream while a graph is recorded
         if args.causal or args.dtype != "bf16":
-            attn.attn_fwd_ex(t["q"], t["k"], t["v"], t["o"], t["lse"], scale, causal=cz, stream=stream)
+            attn.attn_fwd_ex(t["q"], t["k"], t["v"], t["o"], t["lse"], scale, causal=cz, stream=cs)
             if with_bwd:
                 attn.attn_bwd_ex(t["q"], t["k"], t["v"], t["o"], t["lse"], t["do"], t["dq"], t["dk"], t["dv"], scale,
-                                 t["ws"], causal=cz, stream=stream)
+                                 t["ws"], causal=cz, stream=cs)
             return
-        attn.attn_fwd(t["q"], t["k"], t["v"], t["o"], t["lse"], scale, stream)
+        attn.attn_fwd(t["q"], t["k"], t["v"], t["o"], t["lse"], scale, cs)
         if with_bwd:
             attn.attn_bwd(t["q"], t["k"], t["v"], t["o"], t["lse"], t["do"], t["dq"], t["dk"], t["dv"], scale,
-                          t["ws"], stream)
+                          t["ws"], cs)
 
     # One checked step first, so that the host-side check does not leave the
     # GPU idle (and its clock low) between the warm-up and the timed steps.
@@ -300,6 +303,24 @@ def main(argv=None) -> int:
     for _ in range(args.warmup):
         step()
     log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+    if args.graph:
+        # One graph per input set (each holds its own tensors); a step replays the next one.
+        torch.cuda.synchronize()
+        graphs = []
+        for _ in range(len(sets)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step()
+            graphs.append(g)
+        gturn = [0]
+
+        def step():  # noqa: F811  (the timed step becomes a graph replay)
+            graphs[gturn[0] % len(graphs)].replay()
+            gturn[0] += 1
+
+        for _ in range(args.warmup):
+            step()
+        stream = torch.cuda.current_stream()
 
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
@@ -369,7 +390,7 @@ def main(argv=None) -> int:
         "metric": METRIC if not cz else METRIC + ", causal mask (N(N+1)/2 pairs per head)", "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": args.dtype, "data": "synthetic",
-        "config": {"workload": wkey + ("_cold" if args.cold else ""), "B": B, "H": H, "N": N, "d_k": d, "passes": "+".join(w.passes),
+        "config": {"workload": wkey + ("_cold" if args.cold else "") + ("_graph" if args.graph else ""), "B": B, "H": H, "N": N, "d_k": d, "passes": "+".join(w.passes),
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "frac_of_bf16_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "kernel_ms": {kname: round(t, 5) for kname, t in kernels.items()},
