@@ -2,7 +2,8 @@
 // (gfx950 / CDNA4, wave64).
 //
 // Matrix-core conventions used throughout (v_mfma_f32_32x32x16_bf16, checked
-// on the hardware with an in-bounds lane-layout probe):
+// on the hardware with an in-bounds lane-layout probe; the _f16 form has the
+// same layout, which the fp16 parity tests confirm):
 //   A (32 x 16, M x K): lane l supplies A[l % 32][8 * (l / 32) + s], s = 0..7
 //   B (16 x 32, K x N): lane l supplies B[8 * (l / 32) + s][l % 32]
 //   D (32 x 32):        lane l holds D[8 * j + 4 * (l / 32) + i][l % 32] in acc[4 * j + i]
@@ -45,16 +46,7 @@ struct IntC {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
-
-__device__ __forceinline__ bf16x8 as_bf16x8(const u32x2& lo, const u32x2& hi) {
-  u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
-  return __builtin_bit_cast(bf16x8, v);
-}
 
 // Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
@@ -71,8 +63,6 @@ __device__ __forceinline__ float sum_bf16_pair(uint32_t pk, float acc) {
   const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), one, acc, false);
 }
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // Eight 16-bit elements from two 4-element halves.
 __device__ __forceinline__ u32x4 cat(const u32x2& lo, const u32x2& hi) { return u32x4{lo[0], lo[1], hi[0], hi[1]}; }
@@ -123,13 +113,6 @@ __device__ __forceinline__ float fmax3(float a, float b, float c) {
   return __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
 }
 
-// Value held by the lane 32 positions away (the other half of the wave).
-__device__ __forceinline__ float other_half(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const int lane = __lane_id();
-  return __uint_as_float(lane < 32 ? r[1] : r[0]);
-}
-
 // max / sum of x over lanes l and l ^ 32.
 __device__ __forceinline__ float halves_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -170,10 +153,6 @@ __device__ __forceinline__ int tile_off(int row, int col) {
 
 __device__ __forceinline__ u32x4 lds_read_b128(const unsigned char* base, int off) {
   return *reinterpret_cast<const u32x4*>(base + off);
-}
-
-__device__ __forceinline__ void lds_write_b128(unsigned char* base, int off, const u32x4& v) {
-  *reinterpret_cast<u32x4*>(base + off) = v;
 }
 
 __device__ __forceinline__ u32x2 lds_read_tr16_b64(const unsigned char* base, int off) {
