@@ -84,3 +84,34 @@ def test_layout_against_oracle(gpu_lib, layout):
     assert max_abs(to_f64(o), ro) <= TOL_BF16_O
     for got, r in zip((dq, dk, dv), masked_attention_bwd(Q, K, V, DO, x.scale, causal=True, kv_len=[150, 77])):
         assert rel_l2(to_f64(got), r) <= TOL_GRAD_RELL2
+
+
+def test_stages_equal_whole_backward(gpu_lib):
+    """attn_bwd_stage 0, 1, 2 in order equals attn_bwd_ex bit for bit (fp16, causal, key padding, packed layout)."""
+    import torch
+    x = make_case(2, 3, 300, 64, "f16", seed=9200)
+    q, k, v, do = (to_device(x, n) for n in ("q", "k", "v", "do"))
+    B, H, N, d = q.shape
+    tok = lambda t: t.transpose(1, 2).contiguous()
+    packed = torch.stack([tok(t) for t in (q, k, v)], dim=2).contiguous()
+    ins = tuple(packed[:, :, i] for i in range(3))
+    dob = tok(do)
+    kvt = torch.tensor([300, 123], dtype=torch.int32, device="cuda")
+    o = torch.empty((B, N, H, d), dtype=q.dtype, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    gpu_lib.attn_fwd_ex(*ins, o, lse, x.scale, causal=True, kv_len=kvt, layout="qkv_packed")
+    outs = []
+    for staged in (False, True):
+        g = torch.full_like(packed, float("nan"))
+        grads = tuple(g[:, :, i] for i in range(3))
+        ws = gpu_lib.workspace_for(q)
+        if staged:
+            for st in (0, 1, 2):
+                gpu_lib.attn_bwd_stage(st, *ins, o, lse, dob, *grads, x.scale, ws, causal=True, kv_len=kvt,
+                                       layout="qkv_packed")
+        else:
+            gpu_lib.attn_bwd_ex(*ins, o, lse, dob, *grads, x.scale, ws, causal=True, kv_len=kvt, layout="qkv_packed")
+        torch.cuda.synchronize()
+        outs.append(g)
+    assert torch.equal(outs[0], outs[1])
+    assert torch.isfinite(outs[0].float()).all()
