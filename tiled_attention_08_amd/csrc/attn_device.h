@@ -207,10 +207,18 @@ __device__ __forceinline__ size_t head_off(const Strides& s, int bh, int H) {
 // heads * n_blk items. Plain order: head-major, block ascending. With
 // `causal`, blocks carry unequal work (the block with the most is n_blk - 1
 // when heavy_last, else 0) and are handed out heaviest first: when each XCD's
-// range holds whole heads, the range is ordered by block (heaviest first),
-// then head, so every XCD keeps its own heads (and their K/V in its L2) while
-// the long blocks of all of them start before any short one; otherwise blocks
-// are reversed within each head.
+// range holds whole heads, every group of ATTN_CAUSAL_GROUP heads in it is
+// ordered by block (heaviest first), then head, so every XCD keeps its own
+// heads (and their K/V in its L2) while the long blocks of a group start
+// before any short one; otherwise blocks are reversed within each head.
+// Heads per heaviest-first group: the XCD's range is worked through group by
+// group, heaviest blocks first inside each group, so that the K/V (or Q/dO) of
+// only a few heads compete for its L2 at a time. Measured on the causal
+// B=8, H=16, N=4096 step: 8 heads 1347 us, all 16 at once 1379 us, 4 heads
+// 1365 us, 2 heads 1451 us.
+#ifndef ATTN_CAUSAL_GROUP
+#define ATTN_CAUSAL_GROUP 8
+#endif
 __device__ __forceinline__ void work_order(int work, int total, int n_blk, bool causal, bool heavy_last, int& bh,
                                            int& blk) {
   bh = work / n_blk;
@@ -218,8 +226,10 @@ __device__ __forceinline__ void work_order(int work, int total, int n_blk, bool 
   if (!causal) return;
   const int per = total >> 3;
   if ((total & 7) == 0 && per % n_blk == 0) {
-    const int hpx = per / n_blk, x = work / per, r = work - x * per, rank = r / hpx;
-    bh = x * hpx + (r - rank * hpx);
+    const int hpx = per / n_blk, x = work / per, r = work - x * per;
+    const int G = (ATTN_CAUSAL_GROUP > 0 && hpx % ATTN_CAUSAL_GROUP == 0) ? ATTN_CAUSAL_GROUP : hpx;
+    const int grp = r / (G * n_blk), rg = r - grp * G * n_blk, rank = rg / G;
+    bh = x * hpx + grp * G + (rg - rank * G);
     blk = rank;
   }
   if (heavy_last) blk = n_blk - 1 - blk;
