@@ -184,3 +184,19 @@ def test_binding_has_no_cpu_path():
     src = open(os.path.join(ROOT, "tiled_attention_08_amd", "_lib.py")).read()
     for banned in ("oracle", "softmax", "matmul", "einsum", " @ ", "torch.exp"):
         assert banned not in src, banned
+
+
+def test_c99_caller(tmp_path, L):
+    """The header is plain C99 (gcc -std=c99 -Wall -Werror) and a C program linked against libattn.so gets every
+    rejection from the validation layer (tests/c/abi_check.c)."""
+    import shutil
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    exe = tmp_path / "abi_check"
+    libdir = os.path.dirname(L.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c", "abi_check.c"), "-L", libdir, "-lattn",
+                    f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True, capture_output=True, text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    assert "all checks passed" in r.stdout
