@@ -6,7 +6,8 @@ forward (attn_fwd) followed by the recompute-based backward (attn_bwd: delta, dK
 and dQ launches), on the long-sequence workload B=8, H=16, N=4096, d_k=64, bf16
 (inputs seeded, already resident in device memory when timing starts).
 
-    python bench.py [--steps K] [--warmup W] [--workload 2|3|4|5] [--causal] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload 1|2|3|4|5] [--causal] [--dtype bf16|f16]
+                    [--cold] [--graph] [--no-cpu-baseline]
 
 Prints ONE JSON line on stdout; progress goes to stderr. FLOPs are
 algorithmic: forward 4*B*H*N^2*d (Q K^T and P V), backward 10*B*H*N^2*d
@@ -320,7 +321,6 @@ def main(argv=None) -> int:
 
         for _ in range(args.warmup):
             step()
-        stream = torch.cuda.current_stream()
 
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
