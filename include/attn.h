@@ -175,9 +175,10 @@ int attn_bwd_ex(int dtype, int layout, const void* q, const void* k, const void*
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * One stage of attn_bwd_ex, same arguments plus `stage`; attn_bwd_ex is
- * exactly stages 0, 1, 2 in order on `stream`. For callers that schedule or
- * time the stages separately:
+ * One stage of attn_bwd_ex, same arguments plus `stage`; stages 0, 1, 2 in
+ * order on `stream` compute exactly what attn_bwd_ex computes, bit for bit
+ * (for d_k <= 64 attn_bwd_ex runs stages 1 and 2 as one launch). For callers
+ * that schedule or time the stages separately:
  *   stage 0  prep:  workspace <- lse * log2(e) and -delta_i = -<dO_i, O_i>
  *                   (float32); reads o, dO, lse.
  *   stage 1  dK/dV: rebuilds P from q, k, lse and writes dk, dv; needs the

@@ -220,9 +220,11 @@ int attn_bwd_ex(int dtype, int layout, const void* q, const void* k, const void*
   const int st = bwd_checks(dtype, layout, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len,
                             workspace, workspace_bytes, &L);
   if (st != ATTN_OK) return st;
-  for (int stage = 0; stage < 3; ++stage) {
-    const int r = bwd_launch(dtype, stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, L,
-                             workspace, stream);
+  const int stages_fused[2] = {0, 3}, stages[3] = {0, 1, 2};
+  const bool fuse = attn::bwd_can_fuse(B, H, N, d_k);
+  for (int i = 0; i < (fuse ? 2 : 3); ++i) {
+    const int r = bwd_launch(dtype, fuse ? stages_fused[i] : stages[i], q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k,
+                             scale, causal, kv_len, L, workspace, stream);
     if (r != ATTN_OK) return r;
   }
   return ATTN_OK;

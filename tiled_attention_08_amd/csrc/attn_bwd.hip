@@ -40,6 +40,9 @@ constexpr int kThreads = 256;
 // wave (other head dims: 2 and 1; d_k = 128 has no registers for two key
 // blocks, and 32-query tiles of d_k = 32 or 96 would not split evenly over
 // the DMA lanes).
+#ifndef BWD_FUSE
+#define BWD_FUSE 1
+#endif
 #ifndef BWD_MB64
 #define BWD_MB64 2
 #endif
@@ -130,24 +133,21 @@ struct DkdvShape {
 // d_k = 96 and 128, or KBW = 2, need more than 256 registers per lane (the dK
 // and dV accumulators alone take 3 to 8 x 16): one wave per SIMD there.
 template <class E, int D, int MB, int KBW>
-__global__ __launch_bounds__(kThreads)
-__attribute__((amdgpu_waves_per_eu(D <= 64 && KBW == 1 ? BWD_WAVES_PER_EU : 1,
-                                   D <= 64 && KBW == 1 ? BWD_WAVES_PER_EU : 1)))
-void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                     const uint16_t* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ ndelta,
-                     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk, int total, float c,
-                     float scale, const int* __restrict__ kv_len, int H, int causal, Strides sq, Strides sd,
-                     Strides sg) {
+__device__ __forceinline__ void dkdv_body(unsigned char* smem, int work, const uint16_t* __restrict__ Q,
+                                          const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                          const uint16_t* __restrict__ dO, const float* __restrict__ lse2,
+                                          const float* __restrict__ ndelta, uint16_t* __restrict__ dK,
+                                          uint16_t* __restrict__ dV, int N, int n_kblk, int total, float c,
+                                          float scale, const int* __restrict__ kv_len, int H, int causal, Strides sq,
+                                          Strides sd, Strides sg) {
   using S = DkdvShape<D, MB>;
   constexpr int BRQ = S::BRQ;
   constexpr int BCK = 4 * 32 * KBW;  // keys per workgroup
-  __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, gi = lane & 15;
   const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
-  const int work = xcd_remap(blockIdx.x, total);
   int bh, kblk;  // causal: the first key blocks have the most queries and are handed out first
   work_order(work, total, n_kblk, causal != 0, false, bh, kblk);
   const size_t hq = head_off(sq, bh, H), hd = head_off(sd, bh, H), hg = head_off(sg, bh, H);
@@ -377,6 +377,20 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
   }
 }
 
+template <class E, int D, int MB, int KBW>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(D <= 64 && KBW == 1 ? BWD_WAVES_PER_EU : 1,
+                                   D <= 64 && KBW == 1 ? BWD_WAVES_PER_EU : 1)))
+void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                     const uint16_t* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ ndelta,
+                     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk, int total, float c,
+                     float scale, const int* __restrict__ kv_len, int H, int causal, Strides sq, Strides sd,
+                     Strides sg) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[DkdvShape<D, MB>::LDSB];
+  dkdv_body<E, D, MB, KBW>(smem, xcd_remap(blockIdx.x, total), Q, K, V, dO, lse2, ndelta, dK, dV, N, n_kblk, total, c,
+                           scale, kv_len, H, causal, sq, sd, sg);
+}
+
 // ---------------------------------------------------------------- stage 2: dQ
 template <int D, int QB>
 struct DqShape {
@@ -389,20 +403,19 @@ struct DqShape {
 };
 
 template <class E, int D, int QB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BWD_WAVES_PER_EU, BWD_WAVES_PER_EU)))
-void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                   const uint16_t* __restrict__ dO, const float* __restrict__ lse2_in, const float* __restrict__ ndelta,
-                   uint16_t* __restrict__ dQ, int N, int n_qblk, int total, float c, float scale,
-                   const int* __restrict__ kv_len, int H, int causal, Strides sq, Strides sd, Strides sg) {
+__device__ __forceinline__ void dq_body(unsigned char* smem, int work, const uint16_t* __restrict__ Q,
+                                        const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                        const uint16_t* __restrict__ dO, const float* __restrict__ lse2_in,
+                                        const float* __restrict__ ndelta, uint16_t* __restrict__ dQ, int N,
+                                        int n_qblk, int total, float c, float scale, const int* __restrict__ kv_len,
+                                        int H, int causal, Strides sq, Strides sd, Strides sg) {
   using S = DqShape<D, QB>;
   static_assert((BCQ * D / 8) % 64 == 0, "K/V step tiles are whole 64-slot runs");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, gi = lane & 15;
   const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
-  const int work = xcd_remap(blockIdx.x, total);
   int bh, qblk;  // causal: the last row blocks have the most keys and are handed out first
   work_order(work, total, n_qblk, causal != 0, true, bh, qblk);
   const size_t hq = head_off(sq, bh, H), hd = head_off(sd, bh, H);
@@ -554,6 +567,40 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         }
     }
   }
+}
+
+template <class E, int D, int QB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BWD_WAVES_PER_EU, BWD_WAVES_PER_EU)))
+void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                   const uint16_t* __restrict__ dO, const float* __restrict__ lse2_in, const float* __restrict__ ndelta,
+                   uint16_t* __restrict__ dQ, int N, int n_qblk, int total, float c, float scale,
+                   const int* __restrict__ kv_len, int H, int causal, Strides sq, Strides sd, Strides sg) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[DqShape<D, QB>::LDSB];
+  dq_body<E, D, QB>(smem, xcd_remap(blockIdx.x, total), Q, K, V, dO, lse2_in, ndelta, dQ, N, n_qblk, total, c, scale,
+                    kv_len, H, causal, sq, sd, sg);
+}
+
+// dK/dV and dQ work in one launch (d_k <= 64, where both run two waves per
+// SIMD): blocks [0, total1) are dK/dV workgroups, the rest dQ workgroups, so
+// dQ work fills the CUs that the last dK/dV workgroups leave idle instead of
+// waiting for a second launch. total1 is a multiple of 8, so both halves keep
+// their XCD assignment.
+template <class E, int D, int MB, int QB>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BWD_WAVES_PER_EU, BWD_WAVES_PER_EU)))
+void bwd_dkdv_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                        const uint16_t* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ ndelta,
+                        uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
+                        int n_kblk, int total1, int n_qblk, int total2, float c, float scale,
+                        const int* __restrict__ kv_len, int H, int causal, Strides sq, Strides sd, Strides sg) {
+  constexpr int L1 = DkdvShape<D, MB>::LDSB, L2 = DqShape<D, QB>::LDSB;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L1 > L2 ? L1 : L2];
+  const int id = blockIdx.x;
+  if (id < total1)
+    dkdv_body<E, D, MB, 1>(smem, xcd_remap(id, total1), Q, K, V, dO, lse2, ndelta, dK, dV, N, n_kblk, total1, c, scale,
+                           kv_len, H, causal, sq, sd, sg);
+  else
+    dq_body<E, D, QB>(smem, xcd_remap(id - total1, total2), Q, K, V, dO, lse2, ndelta, dQ, N, n_qblk, total2, c, scale,
+                      kv_len, H, causal, sq, sd, sg);
 }
 
 // ---------------------------------------------------------------- fp32 backward
@@ -708,6 +755,20 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
+// Stages 1 and 2 can run as one launch when both kernels run two waves per
+// SIMD with the same launch shape (d_k <= 64, one key block per wave) and the
+// dK/dV grid is a multiple of the 8 XCDs.
+bool bwd_can_fuse(int B, int H, int N, int d) {
+#if BWD_FUSE
+  if (d > 64 || BWD_KBW64 != 1 || BWD_MB64 != 2) return false;
+  const long total1 = (long)((N + 127) / 128) * B * H;
+  return total1 % 8 == 0;
+#else
+  (void)B, (void)H, (void)N, (void)d;
+  return false;
+#endif
+}
+
 // Workspace: lse * log2(e), then -delta; fp32 [B*H*N] each, 256-byte aligned.
 size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   (void)d;
@@ -726,6 +787,15 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
   if (stage == 0) {
     hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, stream, o, dO,
                        lse, lse2, ndelta, rows, N, H, st[1], st[2]);
+  } else if (stage == 3) {  // stages 1 and 2 in one launch (callers check bwd_can_fuse)
+    constexpr int QB = D <= 64 ? 2 : 1;
+    constexpr int BCK = 4 * 32;
+    const int n_kblk = (N + BCK - 1) / BCK, total1 = n_kblk * B * H;
+    constexpr int BR = DqShape<D, QB>::BR;
+    const int n_qblk = (N + BR - 1) / BR, total2 = n_qblk * B * H;
+    hipLaunchKernelGGL((bwd_dkdv_dq_kernel<E, D, 2, QB>), dim3(total1 + total2), dim3(kThreads), 0, stream, q, k, v,
+                       dO, lse2, ndelta, dq, dk, dv, N, n_kblk, total1, n_qblk, total2, c, scale, kv_len, H, causal,
+                       st[0], st[2], st[3]);
   } else if (stage == 1) {
     constexpr int MB = D == 64 ? BWD_MB64 : 2, KBW = D == 64 ? BWD_KBW64 : 1;
     constexpr int BCK = 4 * 32 * KBW;

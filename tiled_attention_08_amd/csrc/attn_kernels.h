@@ -27,12 +27,16 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 // Workspace layout: lse * log2(e) [B*H*N] fp32, then (256-byte aligned) -delta [B*H*N] fp32.
 size_t bwd_workspace_bytes(int B, int H, int N, int d);
 
-// One backward stage: 0 = lse * log2(e) and -delta, 1 = dK and dV, 2 = dQ.
+// One backward stage: 0 = lse * log2(e) and -delta, 1 = dK and dV, 2 = dQ,
+// 3 = stages 1 and 2 in one launch (only where bwd_can_fuse).
 // Masks as for launch_fwd_16; st[0..3]: strides of (q, k, v), o, dO and (dq, dk, dv).
 hipError_t launch_bwd_16_stage(bool f16, int stage, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                  const uint16_t* o, const float* lse, const uint16_t* dO, uint16_t* dq, uint16_t* dk,
                                  uint16_t* dv, int B, int H, int N, int d, float scale, int causal,
                                  const int* kv_len, const Strides* st, void* workspace, hipStream_t stream);
+
+// Whether stages 1 and 2 may run as the single launch "stage 3" (same results, bit for bit).
+bool bwd_can_fuse(int B, int H, int N, int d);
 
 // fp32 backward stage (vector ALU; same stages and workspace as the 16-bit one).
 hipError_t launch_bwd_f32_stage(int stage, const float* q, const float* k, const float* v, const float* o,
