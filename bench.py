@@ -348,24 +348,33 @@ def main(argv=None) -> int:
         t = next_set()
         attn.attn_fwd_ex(t["q"], t["k"], t["v"], t["o"], t["lse"], scale, causal=cz, stream=stream)
 
+    # The kernels the step launches: forward, delta, and either one combined dK/dV + dQ launch (stage 3, where
+    # attn_bwd_fused says so) or the dK/dV and dQ kernels; the separate two are timed in both cases.
+    fused = with_bwd and attn.attn_bwd_fused(B, H, N, d)
     kernels = {"fwd": time_launches(fwd_only, reps)}
+    separate = {}
     if with_bwd:
-        kernels.update({"bwd_prep": time_launches(stage(0), reps), "bwd_dkdv": time_launches(stage(1), reps),
-                        "bwd_dq": time_launches(stage(2), reps)})
-    log("[bench] kernel ms: " + ", ".join(f"{kname} {t:.4f}" for kname, t in kernels.items()))
+        kernels["bwd_prep"] = time_launches(stage(0), reps)
+        separate = {"bwd_dkdv": time_launches(stage(1), reps), "bwd_dq": time_launches(stage(2), reps)}
+        if fused:
+            kernels["bwd_dkdv_dq"] = time_launches(stage(3), reps)
+        else:
+            kernels.update(separate)
+    log("[bench] kernel ms: " + ", ".join(f"{kname} {t:.4f}" for kname, t in {**kernels, **separate}.items()))
     # Algorithmic FLOPs per launch. The dK/dV kernel performs the S recompute,
     # dP, dV and dK products (8 B H N^2 d). The dQ kernel repeats S and dP to
     # avoid a cross-workgroup reduction; only its dQ product (2 B H N^2 d) is
-    # algorithmic work, so its roofline fraction counts that alone.
+    # algorithmic work, so its roofline fraction counts that alone. The combined
+    # launch counts the whole backward (10 B H N^2 d).
     kflops = {"fwd": fwd_flops(B, H, N, d, cz), "bwd_dkdv": 0.8 * bwd_flops(B, H, N, d, cz),
-              "bwd_dq": 0.2 * bwd_flops(B, H, N, d, cz), "bwd_prep": 0.0}
+              "bwd_dq": 0.2 * bwd_flops(B, H, N, d, cz), "bwd_prep": 0.0, "bwd_dkdv_dq": bwd_flops(B, H, N, d, cz)}
     # Algorithmic HBM bytes per launch: every tensor read or written once (E elements of s bytes per [B,H,N,d]
     # tensor, R fp32 rows per statistic).
     E, R, sz = B * H * N * d, B * H * N, 2
     kbytes = {"fwd": 4 * E * sz + 4 * R, "bwd_prep": 2 * E * sz + 12 * R, "bwd_dkdv": 6 * E * sz + 8 * R,
-              "bwd_dq": 5 * E * sz + 8 * R}
+              "bwd_dq": 5 * E * sz + 8 * R, "bwd_dkdv_dq": 7 * E * sz + 8 * R}
     kname_full = {"fwd": "fwd_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel",
-                  "bwd_prep": "bwd_prep_kernel"}
+                  "bwd_prep": "bwd_prep_kernel", "bwd_dkdv_dq": "bwd_dkdv_dq_kernel"}
     dominant = max(kernels, key=kernels.get)
     wkey = w.name + ("_causal" if cz else "") + ("_f16" if args.dtype == "f16" else "")
     # The kernel's bound: matrix cores when its algorithmic FLOP per HBM byte reaches the machine balance
@@ -394,6 +403,8 @@ def main(argv=None) -> int:
                    "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
         "frac_of_bf16_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "kernel_ms": {kname: round(t, 5) for kname, t in kernels.items()},
+        "bwd_fused": bool(fused),
+        "kernel_ms_separate": {kname: round(t, 5) for kname, t in separate.items()} if fused else None,
         "fwd_tflops": round(fwd_flops(B, H, N, d, cz) / (kernels["fwd"] * 1e-3) / 1e12, 2),
         "roofline": roofline,
         "cpu_baseline": None,

@@ -177,22 +177,34 @@ int attn_bwd_ex(int dtype, int layout, const void* q, const void* k, const void*
 /*
  * One stage of attn_bwd_ex, same arguments plus `stage`; stages 0, 1, 2 in
  * order on `stream` compute exactly what attn_bwd_ex computes, bit for bit
- * (for d_k <= 64 attn_bwd_ex runs stages 1 and 2 as one launch). For callers
- * that schedule or time the stages separately:
+ * (attn_bwd_ex itself runs stages 0 and 3). For callers that schedule or time
+ * the stages separately:
  *   stage 0  prep:  workspace <- lse * log2(e) and -delta_i = -<dO_i, O_i>
  *                   (float32); reads o, dO, lse.
  *   stage 1  dK/dV: rebuilds P from q, k, lse and writes dk, dv; needs the
  *                   workspace of stage 0.
  *   stage 2  dQ:    rebuilds P from q, k, lse and writes dq; needs the
  *                   workspace of stage 0 (stages 1 and 2 are independent).
+ *   stage 3  stages 1 and 2 as attn_bwd_ex runs them: one launch of both
+ *            kernels' work where attn_bwd_fused() says so, otherwise stage 1
+ *            then stage 2.
  * All stages are deterministic: no atomics, bitwise-repeatable results.
  * Every check of attn_bwd_ex applies to every stage (all pointers are
- * required). Returns ATTN_ERR_INVALID_ARG for a stage outside 0..2.
+ * required). Returns ATTN_ERR_INVALID_ARG for a stage outside 0..3.
  */
 int attn_bwd_stage(int stage, int dtype, int layout, const void* q, const void* k, const void* v, const void* o,
                    const float* lse, const void* dO, void* dq, void* dk, void* dv,
                    int B, int H, int N, int d_k, float scale, int causal, const int* kv_len,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * 1 when attn_bwd / attn_bwd_ex run the dK/dV and dQ work of this shape as
+ * one launch (stage 3), 0 when they launch it as stages 1 and 2 (or the shape
+ * is rejected). Depends on the shape only: d_k <= 64 and a small dK/dV grid
+ * (at most 2048 workgroups of 128 keys), where the tail of a separate dK/dV
+ * launch would leave CUs idle. Results are the same either way, bit for bit.
+ */
+int attn_bwd_fused(int B, int H, int N, int d_k);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_status_string(int status);

@@ -48,9 +48,9 @@ int main(void) {
   expect(attn_bwd(addr(0), addr(1), addr(2), addr(3), (const float*)addr(4), addr(5), addr(6), addr(7), addr(8), B, H,
                   N, d, 0.125f, NULL, ws, NULL),
          ATTN_ERR_WORKSPACE, "bwd no workspace");
-  expect(attn_bwd_stage(3, ATTN_DTYPE_BF16, ATTN_LAYOUT_BHND, addr(0), addr(1), addr(2), addr(3), (const float*)addr(4),
+  expect(attn_bwd_stage(4, ATTN_DTYPE_BF16, ATTN_LAYOUT_BHND, addr(0), addr(1), addr(2), addr(3), (const float*)addr(4),
                         addr(5), addr(6), addr(7), addr(8), B, H, N, d, 0.125f, 0, NULL, addr(9), ws, NULL),
-         ATTN_ERR_INVALID_ARG, "bwd stage 3");
+         ATTN_ERR_INVALID_ARG, "bwd stage 4");
   expect(attn_bwd_f32((const float*)addr(0), (const float*)addr(1), (const float*)addr(2), (const float*)addr(3),
                       (const float*)addr(4), (const float*)addr(5), (float*)addr(6), (float*)addr(6), (float*)addr(8),
                       B, H, N, d, 0.125f, addr(9), ws, NULL),

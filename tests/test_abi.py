@@ -29,8 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_bwd", "attn_bwd_f32",
-                                           "attn_bwd_ex", "attn_bwd_stage", "attn_bwd_workspace_bytes",
-                                           "attn_status_string"])
+                                           "attn_bwd_ex", "attn_bwd_stage", "attn_bwd_fused",
+                                           "attn_bwd_workspace_bytes", "attn_status_string"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -134,7 +134,7 @@ def test_layout_rejections(L):
 
 def test_backward_rejections(L):
     INV, UNS, WS = L.ATTN_ERR_INVALID_ARG, L.ATTN_ERR_UNSUPPORTED, L.ATTN_ERR_WORKSPACE
-    for stage in (None, 0, 1, 2):
+    for stage in (None, 0, 1, 2, 3):
         assert bwd(L, stage, dq=None) == INV
         assert bwd(L, stage, do=A[5] + 4) == INV
         assert bwd(L, stage, d=80) == UNS and bwd(L, stage, d=160) == UNS
@@ -145,8 +145,8 @@ def test_backward_rejections(L):
         assert bwd(L, stage, dv=A[0]) == INV              # output aliases q
         assert bwd(L, stage, ws=A[8]) == INV              # workspace overlaps dv
         assert bwd(L, stage, scale=float("-inf")) == INV
-    assert bwd(L, 3) == INV and bwd(L, -1) == INV
-    for stage in (None, 0, 1, 2):
+    assert bwd(L, 4) == INV and bwd(L, -1) == INV
+    for stage in (None, 0, 1, 2, 3):
         assert bwd(L, stage, ex=True, dtype=3) == UNS
         assert bwd(L, stage, ex=True, causal=5) == INV
         assert bwd(L, stage, ex=True, kv_len=A[10] + 1) == INV
@@ -168,6 +168,14 @@ def test_f32_backward_rejections(L):
     assert b32(q=None) == INV and b32(d=80) == UNS and b32(ws=None) == WS
     assert b32(dq=A[0] + 8 * 64 * 2) == INV      # inside q's float32 extent (8 x 64 x 4 bytes), past a 2-byte one
     assert b32(dk=A[6]) == INV
+
+
+def test_fusion_rule(L):
+    """dK/dV and dQ share a launch only for d_k <= 64 and small grids; rejected shapes answer 0."""
+    assert L.attn_bwd_fused(32, 12, 196, 64) and L.attn_bwd_fused(4, 12, 2048, 64)
+    assert not L.attn_bwd_fused(8, 16, 4096, 64)      # 4096 dK/dV workgroups
+    assert not L.attn_bwd_fused(32, 12, 196, 128) and not L.attn_bwd_fused(1, 1, 100, 64)  # d_k 128; grid of 1
+    assert not L.attn_bwd_fused(0, 12, 196, 64) and not L.attn_bwd_fused(32, 12, 196, 80)
 
 
 def test_workspace_size(L):

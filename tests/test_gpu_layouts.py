@@ -86,17 +86,20 @@ def test_layout_against_oracle(gpu_lib, layout):
         assert rel_l2(to_f64(got), r) <= TOL_GRAD_RELL2
 
 
-def test_stages_equal_whole_backward(gpu_lib):
-    """attn_bwd_stage 0, 1, 2 in order equals attn_bwd_ex bit for bit (fp16, causal, key padding, packed layout)."""
+@pytest.mark.parametrize("B,H,N,fused", [(2, 3, 300, False), (2, 4, 196, True)])
+def test_stages_equal_whole_backward(gpu_lib, B, H, N, fused):
+    """attn_bwd_stage 0, 1, 2 in order equals attn_bwd_ex bit for bit (fp16, causal, key padding, packed layout),
+    whether attn_bwd_ex launches the dK/dV and dQ work separately or as one kernel."""
     import torch
-    x = make_case(2, 3, 300, 64, "f16", seed=9200)
+    assert gpu_lib.attn_bwd_fused(B, H, N, 64) == fused
+    x = make_case(B, H, N, 64, "f16", seed=9200)
     q, k, v, do = (to_device(x, n) for n in ("q", "k", "v", "do"))
     B, H, N, d = q.shape
     tok = lambda t: t.transpose(1, 2).contiguous()
     packed = torch.stack([tok(t) for t in (q, k, v)], dim=2).contiguous()
     ins = tuple(packed[:, :, i] for i in range(3))
     dob = tok(do)
-    kvt = torch.tensor([300, 123], dtype=torch.int32, device="cuda")
+    kvt = torch.tensor([N, 123], dtype=torch.int32, device="cuda")
     o = torch.empty((B, N, H, d), dtype=q.dtype, device="cuda")
     lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
     gpu_lib.attn_fwd_ex(*ins, o, lse, x.scale, causal=True, kv_len=kvt, layout="qkv_packed")

@@ -25,7 +25,7 @@ LAYOUTS = {"bhnd": 0, "bnhd": 1, "qkv_packed": 2}
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_bwd", "attn_bwd_f32", "attn_bwd_ex", "attn_bwd_stage",
-           "attn_bwd_workspace_bytes", "attn_status_string")
+           "attn_bwd_fused", "attn_bwd_workspace_bytes", "attn_status_string")
 
 
 def _load() -> ctypes.CDLL:
@@ -49,6 +49,8 @@ def _load() -> ctypes.CDLL:
     lib.attn_bwd_ex.restype = i
     lib.attn_bwd_stage.argtypes = [i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
     lib.attn_bwd_stage.restype = i
+    lib.attn_bwd_fused.argtypes = [i, i, i, i]
+    lib.attn_bwd_fused.restype = i
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     return lib
@@ -188,6 +190,11 @@ def attn_fwd_f32(q, k, v, o, lse, scale: float, stream=None) -> None:
                             _stream(stream)))
 
 
+def attn_bwd_fused(B: int, H: int, N: int, d_k: int) -> bool:
+    """Whether the backward of this shape runs its dK/dV and dQ work as one launch (stage 3)."""
+    return bool(lib.attn_bwd_fused(B, H, N, d_k))
+
+
 def attn_bwd_workspace_bytes(B: int, H: int, N: int, d_k: int) -> int:
     return int(lib.attn_bwd_workspace_bytes(B, H, N, d_k))
 
@@ -231,7 +238,7 @@ def attn_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, causal
 
 def attn_bwd_stage(stage: int, q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, causal: bool = False,
                    kv_len=None, stream=None, layout: str = "bhnd") -> None:
-    """One stage (0 prep, 1 dK/dV, 2 dQ) of attn_bwd_ex; same arguments."""
+    """One stage (0 prep, 1 dK/dV, 2 dQ, 3 = 1 and 2 as attn_bwd_ex runs them) of attn_bwd_ex; same arguments."""
     B, H, N, d = _dims(layout, (q, k, v), (o, do))
     _dims(layout, (dq, dk, dv))
     _check_lse(lse, B, H, N)

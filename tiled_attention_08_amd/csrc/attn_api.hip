@@ -241,13 +241,25 @@ int attn_bwd_stage(int stage, int dtype, int layout, const void* q, const void* 
                    const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k,
                    float scale, int causal, const int* kv_len, void* workspace, size_t workspace_bytes,
                    void* stream) {
-  if (stage < 0 || stage > 2) return ATTN_ERR_INVALID_ARG;
+  if (stage < 0 || stage > 3) return ATTN_ERR_INVALID_ARG;
   Layout L;
   const int st = bwd_checks(dtype, layout, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len,
                             workspace, workspace_bytes, &L);
   if (st != ATTN_OK) return st;
+  if (stage == 3 && !attn::bwd_can_fuse(B, H, N, d_k)) {  // stages 1 and 2 as separate launches
+    const int r = bwd_launch(dtype, 1, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, L,
+                             workspace, stream);
+    if (r != ATTN_OK) return r;
+    stage = 2;
+  }
   return bwd_launch(dtype, stage, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, L, workspace,
                     stream);
+}
+
+int attn_bwd_fused(int B, int H, int N, int d_k) {
+  size_t E = 0, R = 0;
+  if (check_shape(B, H, N, d_k, 1.0f, &E, &R) != ATTN_OK) return 0;
+  return attn::bwd_can_fuse(B, H, N, d_k) ? 1 : 0;
 }
 
 }  // extern "C"

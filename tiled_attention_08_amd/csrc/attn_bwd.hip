@@ -755,14 +755,17 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
-// Stages 1 and 2 can run as one launch when both kernels run two waves per
-// SIMD with the same launch shape (d_k <= 64, one key block per wave) and the
-// dK/dV grid is a multiple of the 8 XCDs.
+// Stages 1 and 2 run as one launch when both kernels run two waves per SIMD
+// with the same launch shape (d_k <= 64, one key block per wave), the dK/dV
+// grid is a multiple of the 8 XCDs, and it is small enough (at most 8
+// workgroups per CU) for the tail of the dK/dV launch to matter: measured per
+// step, 70 -> 64 us at B=32, H=12, N=196 and 277 -> 268 us at B=4, H=12,
+// N=2048, but no change at B=8, H=16, N=4096 (4096 dK/dV workgroups).
 bool bwd_can_fuse(int B, int H, int N, int d) {
 #if BWD_FUSE
   if (d > 64 || BWD_KBW64 != 1 || BWD_MB64 != 2) return false;
   const long total1 = (long)((N + 127) / 128) * B * H;
-  return total1 % 8 == 0;
+  return total1 % 8 == 0 && total1 <= 8 * 256;
 #else
   (void)B, (void)H, (void)N, (void)d;
   return false;
