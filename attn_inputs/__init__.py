@@ -38,6 +38,8 @@ __all__ = [
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
     "bf16_bits_to_f64",
+    "ProjInputs",
+    "make_proj_case",
 ]
 
 
@@ -182,3 +184,52 @@ def make_inputs(wid: int, seed: int = 0, with_grad: Optional[bool] = None) -> In
         with_grad = "bwd" in w.passes
     return make_case(w.B, w.H, w.N, w.d, w.dtype, seed=seed, wid=w.wid, qk_sigma=w.qk_sigma,
                      v_dist=w.v_dist, planted_frac=w.planted_frac, with_grad=with_grad)
+
+
+@dataclasses.dataclass
+class ProjInputs:
+    """One seeded instance of the query/key/value projection that feeds attention.
+
+    ``raw`` holds what is uploaded (uint16 bit patterns for "bf16" and "f16"):
+      "x"    [B, N, D]          token matrix (§1: the N patch vectors of width D);
+      "w"    [D, 3, H, d]       W_Q, W_K, W_V of every head side by side;
+      "dqkv" [B, N, 3, H, d]    gradient with respect to the packed output.
+    """
+    B: int
+    N: int
+    D: int
+    H: int
+    d: int
+    dtype: str
+    raw: Dict[str, np.ndarray]
+
+    def f64(self, name: str) -> np.ndarray:
+        a = self.raw[name]
+        if self.dtype == "bf16":
+            return bf16_bits_to_f64(a)
+        return np.ascontiguousarray(a, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def make_proj_case(B: int, N: int, D: int, H: int, d: int, dtype: str = "bf16", seed: int = 0,
+                   wid: int = 0) -> ProjInputs:
+    """Draw x ~ N(0, 1), w ~ N(0, 1/D) and dqkv ~ N(0, 1), in that order, rounded to ``dtype``.
+
+    The weight spread 1/sqrt(D) keeps the projected values near unit size,
+    the scale of the attention inputs the other workloads draw. The stream is
+    PCG64(SeedSequence([seed, wid, 1])), separate from the attention inputs'.
+    """
+    if dtype not in ("bf16", "f16"):
+        raise ValueError("dtype must be 'bf16' or 'f16'")
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(wid), 1])))
+    arrs = {
+        "x": _draw(rng, (B, N, D), "normal", 1.0),
+        "w": _draw(rng, (D, 3, H, d), "normal", float(1.0 / math.sqrt(D))),
+        "dqkv": _draw(rng, (B, N, 3, H, d), "normal", 1.0),
+    }
+    raw = {}
+    for name, arr in arrs.items():
+        if dtype == "bf16":
+            raw[name] = f32_to_bf16_bits(arr).reshape(arr.shape)
+        else:
+            raw[name] = arr.astype(np.float16).view(np.uint16)
+    return ProjInputs(B, N, D, H, d, dtype, raw)

@@ -4,8 +4,9 @@ Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import or call this package. The GPU library never does, and nothing here is
 shared with it.
 
-See ``oracle.attention`` (the definition) and ``oracle.masked`` (key-padding and
-causal masks) for the definitions and their citations.
+See ``oracle.attention`` (the definition), ``oracle.masked`` (key-padding and
+causal masks) and ``oracle.projection`` (the query/key/value projection that
+feeds attention) for the definitions and their citations.
 """
 from .attention import (  # noqa: F401
     attention_probs,
@@ -15,3 +16,4 @@ from .attention import (  # noqa: F401
     brute_attention_grads_fd,
 )
 from .masked import masked_attention_bwd, masked_attention_fwd, visible_keys  # noqa: F401
+from .projection import brute_qkv_projection, qkv_projection, qkv_projection_bwd, split_qkv  # noqa: F401
