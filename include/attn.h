@@ -206,6 +206,49 @@ int attn_bwd_stage(int stage, int dtype, int layout, const void* q, const void* 
  */
 int attn_bwd_fused(int B, int H, int N, int d_k);
 
+/*
+ * Query/key/value projection (article §1, first bullet: Q = X W_Q,
+ * K = X W_K, V = X W_V, with D x d_k weight matrices, one set per head):
+ *   qkv[b, n, t, h, :] = sum_c x[b, n, c] * w[c, t, h, :],  t = 0 (Q), 1 (K), 2 (V).
+ *   x    [B, N, D]        token matrix, row-major;
+ *   w    [D, 3, H, d_k]   the W_Q, W_K, W_V of every head side by side
+ *                         (row c holds the weights of input feature c);
+ *   qkv  [B, N, 3, H, d_k] output: the packed layout that attn_fwd_ex /
+ *                         attn_bwd_ex read with ATTN_LAYOUT_QKV_PACKED
+ *                         (q = qkv, k = qkv + H d_k, v = qkv + 2 H d_k).
+ * Storage type `dtype` (ATTN_DTYPE_BF16 or ATTN_DTYPE_F16) for all three;
+ * products accumulate in float32 and are rounded once (to nearest even).
+ * No bias (the formula has none). Shapes: B, N, D, H, d_k >= 1; D and H d_k
+ * multiples of 8 (16-byte rows); B N below 2^30; otherwise
+ * ATTN_ERR_UNSUPPORTED (ATTN_ERR_INVALID_ARG for non-positive sizes). qkv
+ * must not overlap x or w. The library allocates nothing.
+ */
+int attn_qkv_proj(int dtype, const void* x, const void* w, void* qkv, int B, int N, int D, int H, int d_k,
+                  void* stream);
+
+/*
+ * Backward of attn_qkv_proj for a loss whose gradient with respect to qkv is
+ * dqkv [B, N, 3, H, d_k] (the packed gradient attn_bwd_ex writes for
+ * ATTN_LAYOUT_QKV_PACKED):
+ *   dx[b, n, c]     = sum_{t,h,j} dqkv[b, n, t, h, j] * w[c, t, h, j]   (dqkv W^T),
+ *   dw[c, t, h, j]  = sum_{b,n}   x[b, n, c] * dqkv[b, n, t, h, j]     (X^T dqkv,
+ *                     summed over every token of the batch).
+ * Same storage type, shapes and rules as attn_qkv_proj; dx and dw are written
+ * in full (not accumulated into) and must overlap neither each other nor an
+ * input. `workspace` (device, 256-byte aligned, caller-owned, contents need
+ * not be initialised) must hold attn_qkv_proj_bwd_workspace_bytes(B, N, D, H,
+ * d_k) bytes, else ATTN_ERR_WORKSPACE; it may be NULL when that size is 0.
+ * It holds float32 partial sums of products whose contraction is split over
+ * several workgroups; a second kernel adds them in a fixed order, so results
+ * are deterministic (bitwise repeatable). It must not overlap any other
+ * argument.
+ */
+int attn_qkv_proj_bwd(int dtype, const void* x, const void* w, const void* dqkv, void* dx, void* dw,
+                      int B, int N, int D, int H, int d_k, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes attn_qkv_proj_bwd needs for this shape (0 for shapes it rejects or that need none). */
+size_t attn_qkv_proj_bwd_workspace_bytes(int B, int N, int D, int H, int d_k);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* attn_status_string(int status);
 

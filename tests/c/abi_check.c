@@ -55,6 +55,16 @@ int main(void) {
                       (const float*)addr(4), (const float*)addr(5), (float*)addr(6), (float*)addr(6), (float*)addr(8),
                       B, H, N, d, 0.125f, addr(9), ws, NULL),
          ATTN_ERR_INVALID_ARG, "bwd_f32 dq == dk");
+  expect(attn_qkv_proj(ATTN_DTYPE_BF16, addr(0), addr(1), addr(0), 2, 5, 64, 2, 32, NULL), ATTN_ERR_INVALID_ARG,
+         "qkv_proj output on x");
+  expect(attn_qkv_proj(ATTN_DTYPE_BF16, addr(0), addr(1), addr(2), 2, 5, 60, 2, 32, NULL), ATTN_ERR_UNSUPPORTED,
+         "qkv_proj D = 60");
+  expect(attn_qkv_proj_bwd(ATTN_DTYPE_F16, addr(0), addr(1), addr(2), addr(3), addr(3), 2, 5, 64, 2, 32, NULL, 0,
+                           NULL),
+         ATTN_ERR_INVALID_ARG, "qkv_proj_bwd dx == dw");
+  expect(attn_qkv_proj_bwd(ATTN_DTYPE_BF16, addr(0), addr(1), addr(2), addr(3), addr(4), 32, 196, 768, 12, 64, NULL, 0,
+                           NULL),
+         ATTN_ERR_WORKSPACE, "qkv_proj_bwd without its workspace");
   if (failures == 0) printf("abi_check: all checks passed\n");
   return failures == 0 ? 0 : 1;
 }

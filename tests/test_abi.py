@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_bwd", "attn_bwd_f32",
                                            "attn_bwd_ex", "attn_bwd_stage", "attn_bwd_fused",
-                                           "attn_bwd_workspace_bytes", "attn_status_string"])
+                                           "attn_bwd_workspace_bytes", "attn_qkv_proj", "attn_qkv_proj_bwd",
+                                           "attn_qkv_proj_bwd_workspace_bytes", "attn_status_string"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -168,6 +169,38 @@ def test_f32_backward_rejections(L):
     assert b32(q=None) == INV and b32(d=80) == UNS and b32(ws=None) == WS
     assert b32(dq=A[0] + 8 * 64 * 2) == INV      # inside q's float32 extent (8 x 64 x 4 bytes), past a 2-byte one
     assert b32(dk=A[6]) == INV
+
+
+def test_projection_rejections(L):
+    """Every call here fails validation before a launch: bad dtype, sizes, alignment, widths, overlaps."""
+    INV, UNS = L.ATTN_ERR_INVALID_ARG, L.ATTN_ERR_UNSUPPORTED
+
+    def pf(dtype=0, x=A[0], w=A[1], y=A[2], B=2, N=5, D=64, H=2, d=32):
+        return L.lib.attn_qkv_proj(dtype, x, w, y, B, N, D, H, d, None)
+
+    def pb(dtype=0, x=A[0], w=A[1], g=A[2], dx=A[3], dw=A[4], B=2, N=5, D=64, H=2, d=32, ws=None, ws_bytes=0):
+        return L.lib.attn_qkv_proj_bwd(dtype, x, w, g, dx, dw, B, N, D, H, d, ws, ws_bytes, None)
+
+    for f in (pf, pb):
+        assert f(dtype=2) == UNS and f(dtype=-1) == UNS
+        assert f(B=0) == INV and f(N=-1) == INV and f(D=0) == INV and f(H=0) == INV and f(d=0) == INV
+        assert f(D=60) == UNS                               # rows of x not a multiple of 16 bytes
+        assert f(H=1, d=4) == UNS                           # H d_k not a multiple of 8
+        assert f(B=1 << 15, N=1 << 15) == UNS               # 2^30 tokens
+        assert f(x=None) == INV and f(w=A[1] + 8) == INV
+    assert pf(y=A[0]) == INV and pf(y=A[1] + 16) == INV     # qkv on x / inside w
+    assert pb(dx=A[4]) == INV                               # dx == dw
+    assert pb(dw=A[2] + 32) == INV and pb(dx=A[0]) == INV   # outputs on inputs
+    assert pb(dx=None) == INV and pb(dw=A[4] + 4) == INV
+    # A shape whose products split their contraction (ViT-B/16 block) needs a workspace.
+    big = dict(B=32, N=196, D=768, H=12, d=64)
+    need = L.attn_qkv_proj_bwd_workspace_bytes(32, 196, 768, 12, 64)
+    assert need > 0 and L.attn_qkv_proj_bwd_workspace_bytes(2, 5, 64, 2, 32) == 0
+    assert L.attn_qkv_proj_bwd_workspace_bytes(2, 5, 60, 2, 32) == 0     # rejected shape
+    assert pb(**big) == L.ATTN_ERR_WORKSPACE
+    assert pb(ws=A[5], ws_bytes=need - 1, **big) == L.ATTN_ERR_WORKSPACE
+    assert pb(ws=A[5] + 16, ws_bytes=need, **big) == INV                # not 256-byte aligned
+    assert pb(ws=A[3], ws_bytes=need, **big) == INV                     # workspace on dx
 
 
 def test_fusion_rule(L):

@@ -25,7 +25,8 @@ LAYOUTS = {"bhnd": 0, "bnhd": 1, "qkv_packed": 2}
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_bwd", "attn_bwd_f32", "attn_bwd_ex", "attn_bwd_stage",
-           "attn_bwd_fused", "attn_bwd_workspace_bytes", "attn_status_string")
+           "attn_bwd_fused", "attn_bwd_workspace_bytes", "attn_qkv_proj", "attn_qkv_proj_bwd",
+           "attn_qkv_proj_bwd_workspace_bytes", "attn_status_string")
 
 
 def _load() -> ctypes.CDLL:
@@ -51,6 +52,12 @@ def _load() -> ctypes.CDLL:
     lib.attn_bwd_stage.restype = i
     lib.attn_bwd_fused.argtypes = [i, i, i, i]
     lib.attn_bwd_fused.restype = i
+    lib.attn_qkv_proj.argtypes = [i, vp, vp, vp, i, i, i, i, i, vp]
+    lib.attn_qkv_proj.restype = i
+    lib.attn_qkv_proj_bwd.argtypes = [i, vp, vp, vp, vp, vp, i, i, i, i, i, vp, sz, vp]
+    lib.attn_qkv_proj_bwd.restype = i
+    lib.attn_qkv_proj_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_qkv_proj_bwd_workspace_bytes.restype = sz
     lib.attn_status_string.argtypes = [i]
     lib.attn_status_string.restype = ctypes.c_char_p
     return lib
@@ -249,6 +256,47 @@ def attn_bwd_stage(stage: int, q, k, v, o, lse, do, dq, dk, dv, scale: float, wo
                               int(bool(causal)), _ptr(kv_len), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
+def _proj_dims(x, w):
+    """(B, N, D, H, d) of a projection: x [B, N, D], w [D, 3, H, d], both contiguous, one 16-bit dtype."""
+    if x.dim() != 3 or w.dim() != 4 or int(w.shape[0]) != int(x.shape[2]) or int(w.shape[1]) != 3:
+        raise ValueError("x must be [B, N, D] and w [D, 3, H, d_k]")
+    if not x.is_contiguous() or not w.is_contiguous() or x.dtype != w.dtype:
+        raise ValueError("x and w must be contiguous and share one dtype")
+    B, N, D = (int(a) for a in x.shape)
+    return B, N, D, int(w.shape[2]), int(w.shape[3])
+
+
+def _check_packed(t, B, N, H, d, dtype, what):
+    if tuple(t.shape) != (B, N, 3, H, d) or not t.is_contiguous() or t.dtype != dtype:
+        raise ValueError(f"{what} must be a contiguous [B, N, 3, H, d_k] tensor of the inputs' dtype")
+
+
+def attn_qkv_proj(x, w, qkv, stream=None) -> None:
+    """qkv[b, n, t, h, :] = sum over c of x[b, n, c] w[c, t, h, :] (t = 0, 1, 2: Q, K, V)."""
+    B, N, D, H, d = _proj_dims(x, w)
+    _check_packed(qkv, B, N, H, d, x.dtype, "qkv")
+    _check(lib.attn_qkv_proj(_dtype_code(x), _ptr(x), _ptr(w), _ptr(qkv), B, N, D, H, d, _stream(stream)))
+
+
+def attn_qkv_proj_bwd_workspace_bytes(B: int, N: int, D: int, H: int, d_k: int) -> int:
+    return int(lib.attn_qkv_proj_bwd_workspace_bytes(B, N, D, H, d_k))
+
+
+def attn_qkv_proj_bwd(x, w, dqkv, dx, dw, workspace, stream=None) -> None:
+    """dx = dqkv W^T per token; dw = X^T dqkv over all tokens. ``workspace``: a device buffer of at least
+    attn_qkv_proj_bwd_workspace_bytes(...) bytes (None when that is 0)."""
+    B, N, D, H, d = _proj_dims(x, w)
+    _check_packed(dqkv, B, N, H, d, x.dtype, "dqkv")
+    if tuple(dx.shape) != tuple(x.shape) or tuple(dw.shape) != tuple(w.shape):
+        raise ValueError("dx / dw must have the shapes of x / w")
+    for t in (dx, dw):
+        if not t.is_contiguous() or t.dtype != x.dtype:
+            raise ValueError("dx / dw must be contiguous tensors of the inputs' dtype")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.attn_qkv_proj_bwd(_dtype_code(x), _ptr(x), _ptr(w), _ptr(dqkv), _ptr(dx), _ptr(dw), B, N, D, H, d,
+                                 _ptr(workspace), nbytes, _stream(stream)))
+
+
 # ---------------------------------------------------------------- allocating conveniences
 
 def forward(q, k, v, scale: float, stream=None, causal: bool = False, kv_len=None):
@@ -289,3 +337,31 @@ def backward(q, k, v, o, lse, do, scale: float, workspace=None, stream=None, cau
     else:
         attn_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale, workspace, causal=causal, kv_len=kv_len, stream=stream)
     return dq, dk, dv
+
+
+def qkv_proj(x, w, stream=None):
+    """Allocate the packed [B, N, 3, H, d_k] output and project; returns (qkv, q, k, v), where q, k, v are the
+    [B, N, H, d_k] slices that attn_fwd_ex / attn_bwd_ex take with layout="qkv_packed"."""
+    import torch
+    B, N, D, H, d = _proj_dims(x, w)
+    qkv = torch.empty((B, N, 3, H, d), dtype=x.dtype, device=x.device)
+    attn_qkv_proj(x, w, qkv, stream)
+    return qkv, qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+
+
+def proj_workspace_for(x, w):
+    """A workspace for attn_qkv_proj_bwd with these inputs (None when the shape needs none)."""
+    import torch
+    B, N, D, H, d = _proj_dims(x, w)
+    n = attn_qkv_proj_bwd_workspace_bytes(B, N, D, H, d)
+    return torch.empty(n, dtype=torch.uint8, device=x.device) if n else None
+
+
+def qkv_proj_bwd(x, w, dqkv, workspace=None, stream=None):
+    """Allocate dx and dw (and the workspace unless given), then run the projection's backward; returns (dx, dw)."""
+    import torch
+    dx, dw = torch.empty_like(x), torch.empty_like(w)
+    if workspace is None:
+        workspace = proj_workspace_for(x, w)
+    attn_qkv_proj_bwd(x, w, dqkv, dx, dw, workspace, stream)
+    return dx, dw

@@ -256,6 +256,67 @@ int attn_bwd_stage(int stage, int dtype, int layout, const void* q, const void* 
                     stream);
 }
 
+// Shape checks of the projection: returns ATTN_OK and the token count and
+// output width 3 H d_k, or an error code.
+static int proj_shape(int dtype, int B, int N, int D, int H, int d_k, long* tokens, int* hd3) {
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_UNSUPPORTED;
+  if (B < 1 || N < 1 || D < 1 || H < 1 || d_k < 1) return ATTN_ERR_INVALID_ARG;
+  const int64_t t = (int64_t)B * N, hd = (int64_t)H * d_k;
+  if (D % 8 != 0 || hd % 8 != 0) return ATTN_ERR_UNSUPPORTED;
+  if (t >= (int64_t)1 << 30 || 3 * hd > INT32_MAX / 2 || D > INT32_MAX / 2) return ATTN_ERR_UNSUPPORTED;
+  *tokens = (long)t;
+  *hd3 = (int)(3 * hd);
+  return ATTN_OK;
+}
+
+int attn_qkv_proj(int dtype, const void* x, const void* w, void* qkv, int B, int N, int D, int H, int d_k,
+                  void* stream) {
+  long T = 0;
+  int HD3 = 0;
+  int st = proj_shape(dtype, B, N, D, H, d_k, &T, &HD3);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(qkv)) return ATTN_ERR_INVALID_ARG;
+  const Range rx = span(x, (size_t)T * D * 2), rw = span(w, (size_t)D * HD3 * 2), ry = span(qkv, (size_t)T * HD3 * 2);
+  if (overlap(ry, rx) || overlap(ry, rw)) return ATTN_ERR_INVALID_ARG;
+  return from_hip(attn::launch_proj_fwd(dtype == ATTN_DTYPE_F16, static_cast<const uint16_t*>(x),
+                                        static_cast<const uint16_t*>(w), static_cast<uint16_t*>(qkv), T, D, HD3,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t attn_qkv_proj_bwd_workspace_bytes(int B, int N, int D, int H, int d_k) {
+  long T = 0;
+  int HD3 = 0;
+  if (proj_shape(ATTN_DTYPE_BF16, B, N, D, H, d_k, &T, &HD3) != ATTN_OK) return 0;
+  return attn::proj_bwd_workspace_bytes(T, D, HD3);
+}
+
+int attn_qkv_proj_bwd(int dtype, const void* x, const void* w, const void* dqkv, void* dx, void* dw, int B, int N,
+                      int D, int H, int d_k, void* workspace, size_t workspace_bytes, void* stream) {
+  long T = 0;
+  int HD3 = 0;
+  int st = proj_shape(dtype, B, N, D, H, d_k, &T, &HD3);
+  if (st != ATTN_OK) return st;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(dqkv) || !aligned16(dx) || !aligned16(dw))
+    return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn::proj_bwd_workspace_bytes(T, D, HD3);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return ATTN_ERR_INVALID_ARG;
+  const Range rx = span(x, (size_t)T * D * 2), rw = span(w, (size_t)D * HD3 * 2);
+  const Range rg = span(dqkv, (size_t)T * HD3 * 2), rdx = span(dx, (size_t)T * D * 2), rdw = span(dw, (size_t)D * HD3 * 2);
+  if (overlap(rdx, rdw)) return ATTN_ERR_INVALID_ARG;
+  for (const Range& o : {rdx, rdw})
+    if (overlap(o, rx) || overlap(o, rw) || overlap(o, rg)) return ATTN_ERR_INVALID_ARG;
+  if (need > 0) {
+    const Range rws = span(workspace, need);
+    for (const Range& o : {rx, rw, rg, rdx, rdw})
+      if (overlap(rws, o)) return ATTN_ERR_INVALID_ARG;
+  }
+  return from_hip(attn::launch_proj_bwd(dtype == ATTN_DTYPE_F16, static_cast<const uint16_t*>(x),
+                                        static_cast<const uint16_t*>(w), static_cast<const uint16_t*>(dqkv),
+                                        static_cast<uint16_t*>(dx), static_cast<uint16_t*>(dw), T, D, HD3,
+                                        need > 0 ? workspace : nullptr, static_cast<hipStream_t>(stream)));
+}
+
 int attn_bwd_fused(int B, int H, int N, int d_k) {
   size_t E = 0, R = 0;
   if (check_shape(B, H, N, d_k, 1.0f, &E, &R) != ATTN_OK) return 0;

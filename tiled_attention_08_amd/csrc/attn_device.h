@@ -124,24 +124,38 @@ __device__ __forceinline__ float halves_sum(float x) {
 }
 
 // LDS tile swizzle. Tiles are row-major 16-bit elements in 16-byte chunks (8
-// elements); chunk c of row r is stored at chunk position c ^ swz(r). gfx950
-// serves a 16-lane quarter of a ds_read_b128 from one 256-byte window of its
-// banks, so the 16 lanes of an operand read (16 consecutive rows, same
-// logical chunk) must land on 16 distinct 16-byte slots of that window:
-//   128-byte rows (two rows per window): swz(r) = (r >> 1) & 7 makes the
-//     8 rows of each parity take 8 different slots;
-//   256-byte rows (one row per window):  swz(r) = r & 15;
+// elements); chunk c of row r is stored at chunk position c ^ swz(r). Two read
+// patterns must be free of bank conflicts (64 banks of 4 bytes, so a 256-byte
+// window of LDS covers every bank once):
+//   plain 16-byte reads: gfx950 serves a ds_read_b128 in 16-lane quarters,
+//     and the 16 lanes of an operand read (16 consecutive rows, the same
+//     logical chunk) must hit 16 distinct 16-byte bank groups;
+//   transposing 8-byte reads: a 32-lane half of a ds_read_b64_tr_b16 reads 4
+//     consecutive rows (the first a multiple of 4) x 4 consecutive chunks
+//     (the first a multiple of 4), 8 bytes per lane, and its 16 (row, chunk)
+//     pairs must hit 16 distinct bank groups.
+// Row sizes and swizzles:
+//   128-byte rows (two rows per window, an odd row in the other half):
+//     swz(r) = bit-reverse of the 3 bits (r >> 1) & 7. The 8 rows of each
+//     parity among 16 consecutive rows take 8 different positions, and rows
+//     r and r + 2 (r a multiple of 4, same half window) differ in bit 2, so
+//     their 4-chunk groups land in opposite halves of the row.
+//   256-byte rows (one row per window): swz(r) = bit-reverse of the 4 bits
+//     r & 15: a bijection over 16 consecutive rows, and rows r .. r + 3 (r a
+//     multiple of 4) differ in bits 2 and 3, so their 4-chunk groups take
+//     all 16 positions.
 //   64-byte rows (four rows per window) and 192-byte rows (rows start at
 //     window offsets 0, 192, 128, 64 in turn): swz(r) = (r >> 2) & 3, which
 //     spreads each group of four rows with the same window offset over four
 //     slots (and keeps the chunk index below 12 for 192-byte rows).
-// Transposing 8-byte reads (4 rows x 2 chunks per 16 lanes) stay
-// conflict-free under these patterns (measured for 128 and 256 bytes,
-// counted bank by bank for 64 and 192).
+// (The plain XOR swizzles (r >> 1) & 7 and r & 15 are conflict-free for the
+// plain reads but put two or four lanes on one bank in the transposing reads.)
 template <int ROWB>
 __device__ __forceinline__ int swz(int row) {
   static_assert(ROWB == 64 || ROWB == 128 || ROWB == 192 || ROWB == 256, "tiles have 64 to 256-byte rows");
-  return ROWB == 128 ? ((row >> 1) & 7) : ROWB == 256 ? (row & 15) : ((row >> 2) & 3);
+  if constexpr (ROWB == 128) return (int)(__builtin_bitreverse32((uint32_t)row >> 1) >> 29);
+  if constexpr (ROWB == 256) return (int)(__builtin_bitreverse32((uint32_t)row) >> 28);
+  return (row >> 2) & 3;
 }
 
 // Byte offset of element (row, col) in a swizzled tile with ROWB bytes per row.

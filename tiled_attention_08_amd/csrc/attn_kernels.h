@@ -43,4 +43,14 @@ hipError_t launch_bwd_f32_stage(int stage, const float* q, const float* k, const
                                 const float* lse, const float* dO, float* dq, float* dk, float* dv, int B, int H, int N,
                                 int d, float scale, void* workspace, hipStream_t stream);
 
+// Query/key/value projection: qkv[tokens, HD3] = x[tokens, D] w[D, HD3] (HD3 = 3 H d);
+// backward dx = dqkv w^T and dw = x^T dqkv. The backward's workspace (its
+// size from proj_bwd_workspace_bytes, 0 when no product splits its
+// contraction) holds the float32 partial sums of split products.
+hipError_t launch_proj_fwd(bool f16, const uint16_t* x, const uint16_t* w, uint16_t* qkv, long tokens, int D, int HD3,
+                           hipStream_t stream);
+size_t proj_bwd_workspace_bytes(long tokens, int D, int HD3);
+hipError_t launch_proj_bwd(bool f16, const uint16_t* x, const uint16_t* w, const uint16_t* dqkv, uint16_t* dx,
+                           uint16_t* dw, long tokens, int D, int HD3, void* ws, hipStream_t stream);
+
 }  // namespace attn
