@@ -8,6 +8,7 @@ and dQ launches), on the long-sequence workload B=8, H=16, N=4096, d_k=64, bf16
 
     python bench.py [--steps K] [--warmup W] [--workload 1|2|3|4|5] [--causal] [--dtype bf16|f16]
                     [--cold] [--graph] [--no-cpu-baseline]
+    python bench.py --workload 2 --proj      (the ViT block with its query/key/value projection)
 
 Prints ONE JSON line on stdout; progress goes to stderr. FLOPs are
 algorithmic: forward 4*B*H*N^2*d (Q K^T and P V), backward 10*B*H*N^2*d
@@ -182,6 +183,178 @@ def bench_f32(args, w) -> int:
     return 0
 
 
+def proj_flops(B, N, D, H, d):
+    """One product of the query/key/value projection: 2 * tokens * D * 3 H d (the forward has one, the backward two)."""
+    return 2.0 * B * N * D * 3 * H * d
+
+
+def cpu_baseline_block(B, N, D, H, d, seed: int, budget_s: float) -> dict:
+    """The fp64 oracle on whole images of the ViT block (projection, attention, their backward), ~budget_s seconds."""
+    from attn_inputs import make_case, make_proj_case
+    from oracle import attention_bwd, attention_fwd, qkv_projection, qkv_projection_bwd, split_qkv
+    import numpy as np
+    c = make_proj_case(B, N, D, H, d, "bf16", seed=seed, wid=2)
+    g = make_case(B, H, N, d, "bf16", seed=seed, wid=2)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    X, W, DO = c.f64("x"), c.f64("w"), g.f64("do")
+    scale = g.scale
+    imgs, elapsed = 0, 0.0
+    while imgs < B and (imgs == 0 or elapsed * (imgs + 1) / imgs <= budget_s):
+        t0 = time.perf_counter()
+        x1 = X[imgs:imgs + 1]
+        q, k, v = split_qkv(qkv_projection(x1, W))
+        dqkv = np.empty((1, N, 3, H, d))
+        for h in range(H):
+            attention_fwd(q[0, h], k[0, h], v[0, h], scale)
+            gq, gk, gv = attention_bwd(q[0, h], k[0, h], v[0, h], DO[imgs, h], scale)
+            dqkv[0, :, 0, h], dqkv[0, :, 1, h], dqkv[0, :, 2, h] = gq, gk, gv
+        qkv_projection_bwd(x1, W, dqkv)
+        elapsed += time.perf_counter() - t0
+        imgs += 1
+    flops = imgs * (3 * proj_flops(1, N, D, H, d) + fwd_flops(1, H, N, d) + bwd_flops(1, H, N, d))
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{imgs} of {B} images of the same block (projection, attention and their backward, fp64), "
+                      f"{elapsed:.1f} s", "seconds": round(elapsed, 3)}
+
+
+def bench_proj(args, w) -> int:
+    """ViT attention block: query/key/value projection, attention in the packed layout, and both backward passes."""
+    import numpy as np
+    import torch
+    from attn_inputs import make_case, make_proj_case
+    from tiled_attention_08_amd import _lib as attn
+    B, H, N, d = w.B, w.H, w.N, w.d
+    D = H * d
+    log(f"[bench] ViT block with projection: B={B} N={N} D={D} H={H} d={d} bf16, seed {args.seed}")
+    c = make_proj_case(B, N, D, H, d, "bf16", seed=args.seed, wid=w.wid)
+    g = make_case(B, H, N, d, "bf16", seed=args.seed, wid=w.wid)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    x, wt = up(c.raw["x"]), up(c.raw["w"])
+    do = up(g.raw["do"]).transpose(1, 2).contiguous()                       # [B, N, H, d]
+    qkv = torch.empty((B, N, 3, H, d), dtype=torch.bfloat16, device="cuda")
+    q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    o = torch.empty((B, N, H, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dqkv = torch.empty_like(qkv)
+    dq, dk, dv = dqkv[:, :, 0], dqkv[:, :, 1], dqkv[:, :, 2]
+    dx, dw = torch.empty_like(x), torch.empty_like(wt)
+    ws = torch.empty(attn.attn_bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    pws = attn.proj_workspace_for(x, wt)
+    scale = g.scale
+    stream = torch.cuda.current_stream()
+
+    def proj_fwd():
+        attn.attn_qkv_proj(x, wt, qkv, stream)
+
+    def att_fwd():
+        attn.attn_fwd_ex(q, k, v, o, lse, scale, stream=stream, layout="qkv_packed")
+
+    def att_bwd_stage(i):
+        return lambda: attn.attn_bwd_stage(i, q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream=stream,
+                                           layout="qkv_packed")
+
+    def att_bwd():
+        attn.attn_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale, ws, stream=stream, layout="qkv_packed")
+
+    def proj_bwd():
+        attn.attn_qkv_proj_bwd(x, wt, dqkv, dx, dw, pws, stream)
+
+    def step():
+        proj_fwd()
+        att_fwd()
+        att_bwd()
+        proj_bwd()
+
+    step()
+    torch.cuda.synchronize()
+    for t in (qkv, o, lse, dqkv, dx, dw):
+        if not torch.isfinite(t.float()).all():
+            log("[bench] non-finite output")
+            return 1
+    for _ in range(args.warmup):
+        step()
+    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    pf = proj_flops(B, N, D, H, d)
+    flops = 3 * pf + fwd_flops(B, H, N, d) + bwd_flops(B, H, N, d)
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] {ms:.4f} ms/step, {value:.1f} TFLOP/s")
+
+    reps = args.kernel_reps
+    fused = attn.attn_bwd_fused(B, H, N, d)
+    kernels = {"proj_fwd": time_launches(proj_fwd, reps), "fwd": time_launches(att_fwd, reps),
+               "bwd_prep": time_launches(att_bwd_stage(0), reps)}
+    if fused:
+        kernels["bwd_dkdv_dq"] = time_launches(att_bwd_stage(3), reps)
+    else:
+        kernels["bwd_dkdv"] = time_launches(att_bwd_stage(1), reps)
+        kernels["bwd_dq"] = time_launches(att_bwd_stage(2), reps)
+    kernels["proj_bwd"] = time_launches(proj_bwd, reps)
+    log("[bench] kernel ms: " + ", ".join(f"{kname} {t:.4f}" for kname, t in kernels.items()))
+    T, E, R, sz = B * N, B * H * N * d, B * H * N, 2
+    kflops = {"proj_fwd": pf, "proj_bwd": 2 * pf, "fwd": fwd_flops(B, H, N, d), "bwd_prep": 0.0,
+              "bwd_dkdv": 0.8 * bwd_flops(B, H, N, d), "bwd_dq": 0.2 * bwd_flops(B, H, N, d),
+              "bwd_dkdv_dq": bwd_flops(B, H, N, d)}
+    kbytes = {"proj_fwd": (T * D + D * 3 * H * d + T * 3 * H * d) * sz,
+              "proj_bwd": (2 * T * D + 2 * D * 3 * H * d + T * 3 * H * d) * sz,
+              "fwd": 4 * E * sz + 4 * R, "bwd_prep": 2 * E * sz + 12 * R, "bwd_dkdv": 6 * E * sz + 8 * R,
+              "bwd_dq": 5 * E * sz + 8 * R, "bwd_dkdv_dq": 7 * E * sz + 8 * R}
+    kname_full = {"proj_fwd": "gemm256_kernel", "proj_bwd": "attn_qkv_proj_bwd (dx and dw products, split sums)",
+                  "fwd": "fwd_kernel", "bwd_prep": "bwd_prep_kernel", "bwd_dkdv": "bwd_dkdv_kernel",
+                  "bwd_dq": "bwd_dq_kernel", "bwd_dkdv_dq": "bwd_dkdv_dq_kernel"}
+    # The roofline describes the longest single kernel (the projection backward is a group of launches).
+    single = {kn: t for kn, t in kernels.items() if kn != "proj_bwd"}
+    dominant = max(single, key=single.get)
+    intensity = kflops[dominant] / kbytes[dominant]
+    t_s = kernels[dominant] * 1e-3
+    if intensity >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = kflops[dominant] / t_s / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = kbytes[dominant] / t_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    wkey = "vit_b16_block_with_qkv_projection"
+    roofline.update({"traffic": measured_traffic(wkey, kname_full[dominant]), "kernel": kname_full[dominant],
+                     "avg_ms": round(kernels[dominant], 5), "algorithmic_bytes": kbytes[dominant],
+                     "flop_per_byte": round(intensity, 1)})
+    record = {
+        "metric": "ViT attention block TFLOP/s fwd+bwd: query/key/value projection (3 products of 2*B*N*D*3*H*d) "
+                  "plus attention (14*B*H*N^2*d), and % of MI355X bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wkey, "B": B, "N": N, "D": D, "H": H, "d_k": d, "passes": "fwd+bwd",
+                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
+        "frac_of_bf16_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "kernel_ms": {kn: round(t, 5) for kn, t in kernels.items()},
+        "proj_tflops": {"fwd": round(pf / (kernels["proj_fwd"] * 1e-3) / 1e12, 2),
+                        "bwd": round(2 * pf / (kernels["proj_bwd"] * 1e-3) / 1e12, 2)},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        record["cpu_baseline"] = cpu_baseline_block(B, N, D, H, d, args.seed, args.cpu_seconds)
+    print(json.dumps(record), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +377,9 @@ def main(argv=None) -> int:
     ap.add_argument("--causal", action="store_true",
                     help="time the causal-mask path (attn_fwd_ex / attn_bwd_ex); FLOPs count the N(N+1)/2 visible "
                          "query-key pairs of each head")
+    ap.add_argument("--proj", action="store_true",
+                    help="with --workload 2: time the ViT attention block including the query/key/value projection "
+                         "(D = H d_k) and its backward, attention in the packed layout")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (three times) and exit: the "
                          "known-size reference for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -236,6 +412,11 @@ def main(argv=None) -> int:
     cz = args.causal
     if w.dtype == "f32":
         return bench_f32(args, w)
+    if args.proj:
+        if args.workload != 2 or args.causal or args.dtype != "bf16" or args.cold or args.graph:
+            log("[bench] --proj times the ViT-B/16 block: use it with --workload 2 only (bf16, no other mode)")
+            return 2
+        return bench_proj(args, w)
     log(f"[bench] workload {w.wid} {w.name}: B={B} H={H} N={N} d={d} {args.dtype}{' causal' if cz else ''}, seed {args.seed}")
     if args.dtype == "bf16":
         x = make_inputs(args.workload, seed=args.seed)
