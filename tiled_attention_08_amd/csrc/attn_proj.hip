@@ -12,21 +12,26 @@
 //   dx       dx[BN, D]    = dqkv[BN, 3Hd] w^T;
 //   dw       dw[D, 3Hd]   = x^T dqkv, summed over all B N tokens.
 //
-// One kernel template computes C = A B (A: M x K, B: K x N, fp32
-// accumulation, C rounded to the 16-bit storage type). An operand is
-// "k-contiguous" when its contraction index runs along memory rows (A
-// row-major, or B stored as B^T row-major). Such an operand is staged as
-// [rows][64 k] tiles and read with plain 16-byte LDS reads. Otherwise it is
-// staged as [64 k][cols] tiles and read with the transposing LDS read.
+// Every product is C = A B (A: M x K, B: K x N, fp32 accumulation, C rounded
+// once to the 16-bit storage type). An operand is "k-contiguous" when its
+// contraction index runs along memory rows (A row-major, or B stored as B^T
+// row-major). Such an operand is staged as [rows][64 k] tiles and read with
+// plain 16-byte LDS reads. Otherwise it is staged as [64 k][cols] tiles and
+// read with the transposing LDS read, so no operand is ever transposed in
+// memory:
 //   forward: A = x (k-contiguous), B = w (not);
 //   dx:      A = dqkv (k-contiguous), B = w^T, i.e. the rows of w (k-contiguous);
 //   dw:      A = x^T (not), B = dqkv (not).
-// Each wave computes one 64 x 64 block of C^T = B^T A^T with 32x32x16 MFMAs:
-// the output tile then holds one row of C per lane column, so a lane stores
-// four consecutive columns of C at a time. A workgroup's 4 waves cover WM x WN
-// such blocks and split the contraction WK ways (WM WN WK = 4). With WK > 1,
-// the waves add their partial sums through LDS at the end, so that skinny
-// products (few output tiles, long contraction) still fill the chip.
+// Waves compute blocks of C^T = B^T A^T with 32x32x16 MFMAs: a lane then holds
+// one row of C and stores four consecutive columns of it at a time.
+// Two kernels:
+//   gemm256_kernel - 256 x 256 tiles, 8 waves, for products with at least 256
+//     rows and columns; a product with few tiles splits its contraction over
+//     several workgroups, which write float32 partial slices to the caller's
+//     workspace for reduce_splits_kernel to add in a fixed order;
+//   gemm_kernel - 128 x 128 or 64 x 64 tiles, 4 waves, for smaller products;
+//     the 64 x 64 form splits the contraction over its 4 waves and adds their
+//     partial sums through LDS.
 #include "attn_device.h"
 #include "attn_kernels.h"
 
@@ -45,16 +50,9 @@ struct GemmShape {
   static constexpr int LDSB = 2 * STEPB > RED ? 2 * STEPB : RED;
 };
 
-// Element (row, col) of an operand sub-tile, as a swizzled LDS byte offset.
-// ROWB: bytes per tile row (128 for [rows][64 k] tiles; 2 * cols otherwise).
-template <int ROWB>
-__device__ __forceinline__ int toff(int row, int col) {
-  return tile_off<ROWB>(row, col);
-}
-
 // DMA one operand sub-tile into LDS. The tile has `rows` rows of ROWB bytes;
 // the 256 threads fill its 16-byte slots in order, and the lane writing slot
-// (row, s) fetches logical chunk s ^ swz(row) (the layout toff() addresses).
+// (row, s) fetches logical chunk s ^ swz(row) (the layout tile_off() addresses).
 // Row r of the tile is global row min(r0 + r, rmax) of `src` (leading
 // dimension ld elements); chunk c starts at global column min(c0 + 8 c, cmax).
 // Clamped rows and columns re-read valid data; the products mask every use.
@@ -142,11 +140,11 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
   auto frag = [&](const unsigned char* T, auto kcontig, auto rowb, int rc0, int kk) -> u32x4 {
     constexpr int RB = decltype(rowb)::value;
     if constexpr (decltype(kcontig)::value) {
-      return lds_read_b128(T, toff<RB>(rc0 + l32, kk * 16 + 8 * h));
+      return lds_read_b128(T, tile_off<RB>(rc0 + l32, kk * 16 + 8 * h));
     } else {
       const int col = rc0 + grp * 16 + 4 * (i16 & 3);
       const int row = kk * 16 + 8 * h + (i16 >> 2);
-      return cat(lds_read_tr16_b64(T, toff<RB>(row, col)), lds_read_tr16_b64(T, toff<RB>(row + 4, col)));
+      return cat(lds_read_tr16_b64(T, tile_off<RB>(row, col)), lds_read_tr16_b64(T, tile_off<RB>(row + 4, col)));
     }
   };
 
