@@ -96,6 +96,24 @@ def measured_traffic(workload: str, kernel: str):
     return None if k is None else int(k["traffic_bytes"])
 
 
+def roofline_of(kernel: str, avg_ms: float, flops: float, nbytes: float, workload: str) -> dict:
+    """The roofline object for one kernel: its bound follows from its algorithmic FLOP per algorithmic HBM byte
+    (matrix cores at or above the machine balance 2516.6 TFLOP/s / 8 TB/s = 315, HBM below it)."""
+    intensity = flops / nbytes
+    t_s = avg_ms * 1e-3
+    if intensity >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
+        achieved = flops / t_s / 1e12
+        r = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    else:
+        achieved = nbytes / t_s / 1e9
+        r = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    r.update({"traffic": measured_traffic(workload, kernel), "kernel": kernel, "avg_ms": round(avg_ms, 5),
+              "algorithmic_bytes": nbytes, "flop_per_byte": round(intensity, 1)})
+    return r
+
+
 def cpu_baseline(wid: int, seed: int, budget_s: float, causal: bool = False) -> dict:
     """The fp64 oracle (forward + backward) on whole heads of the workload, for about ``budget_s`` seconds."""
     import numpy as np
@@ -319,20 +337,8 @@ def bench_proj(args, w) -> int:
     # The roofline describes the longest single kernel (the projection backward is a group of launches).
     single = {kn: t for kn, t in kernels.items() if kn != "proj_bwd"}
     dominant = max(single, key=single.get)
-    intensity = kflops[dominant] / kbytes[dominant]
-    t_s = kernels[dominant] * 1e-3
-    if intensity >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-        achieved = kflops[dominant] / t_s / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    else:
-        achieved = kbytes[dominant] / t_s / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(achieved / PEAK_HBM_GBS, 4)}
     wkey = "vit_b16_block_with_qkv_projection"
-    roofline.update({"traffic": measured_traffic(wkey, kname_full[dominant]), "kernel": kname_full[dominant],
-                     "avg_ms": round(kernels[dominant], 5), "algorithmic_bytes": kbytes[dominant],
-                     "flop_per_byte": round(intensity, 1)})
+    roofline = roofline_of(kname_full[dominant], kernels[dominant], kflops[dominant], kbytes[dominant], wkey)
     record = {
         "metric": "ViT attention block TFLOP/s fwd+bwd: query/key/value projection (3 products of 2*B*N*D*3*H*d) "
                   "plus attention (14*B*H*N^2*d), and % of MI355X bf16 MFMA peak",
@@ -558,21 +564,7 @@ def main(argv=None) -> int:
                   "bwd_prep": "bwd_prep_kernel", "bwd_dkdv_dq": "bwd_dkdv_dq_kernel"}
     dominant = max(kernels, key=kernels.get)
     wkey = w.name + ("_causal" if cz else "") + ("_f16" if args.dtype == "f16" else "")
-    # The kernel's bound: matrix cores when its algorithmic FLOP per HBM byte reaches the machine balance
-    # (2516.6 TFLOP/s / 8 TB/s = 315), HBM below it.
-    intensity = kflops[dominant] / kbytes[dominant]
-    t_s = kernels[dominant] * 1e-3
-    if intensity >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9):
-        achieved = kflops[dominant] / t_s / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    else:
-        achieved = kbytes[dominant] / t_s / 1e9
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                    "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roofline.update({"traffic": measured_traffic(wkey, kname_full[dominant]), "kernel": kname_full[dominant],
-                     "avg_ms": round(kernels[dominant], 5), "algorithmic_bytes": kbytes[dominant],
-                     "flop_per_byte": round(intensity, 1)})
+    roofline = roofline_of(kname_full[dominant], kernels[dominant], kflops[dominant], kbytes[dominant], wkey)
     if args.cold:
         roofline["inputs"] = f"rotating {len(sets)} input sets ({set_bytes * len(sets) / 2**30:.2f} GiB, beyond L2 and MALL)"
 
