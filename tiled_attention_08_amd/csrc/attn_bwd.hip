@@ -791,14 +791,18 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
     hipLaunchKernelGGL((bwd_prep_kernel<E, D>), dim3((unsigned)((rows * 8 + 255) / 256)), dim3(256), 0, stream, o, dO,
                        lse, lse2, ndelta, rows, N, H, st[1], st[2]);
   } else if (stage == 3) {  // stages 1 and 2 in one launch (callers check bwd_can_fuse)
-    constexpr int QB = D <= 64 ? 2 : 1;
-    constexpr int BCK = 4 * 32;
-    const int n_kblk = (N + BCK - 1) / BCK, total1 = n_kblk * B * H;
-    constexpr int BR = DqShape<D, QB>::BR;
-    const int n_qblk = (N + BR - 1) / BR, total2 = n_qblk * B * H;
-    hipLaunchKernelGGL((bwd_dkdv_dq_kernel<E, D, 2, QB>), dim3(total1 + total2), dim3(kThreads), 0, stream, q, k, v,
-                       dO, lse2, ndelta, dq, dk, dv, N, n_kblk, total1, n_qblk, total2, c, scale, kv_len, H, causal,
-                       st[0], st[2], st[3]);
+    if constexpr (D <= 64) {  // only instantiated where bwd_can_fuse can say yes
+      constexpr int QB = 2;
+      constexpr int BCK = 4 * 32;
+      const int n_kblk = (N + BCK - 1) / BCK, total1 = n_kblk * B * H;
+      constexpr int BR = DqShape<D, QB>::BR;
+      const int n_qblk = (N + BR - 1) / BR, total2 = n_qblk * B * H;
+      hipLaunchKernelGGL((bwd_dkdv_dq_kernel<E, D, 2, QB>), dim3(total1 + total2), dim3(kThreads), 0, stream, q, k,
+                         v, dO, lse2, ndelta, dq, dk, dv, N, n_kblk, total1, n_qblk, total2, c, scale, kv_len, H,
+                         causal, st[0], st[2], st[3]);
+    } else {
+      return hipErrorInvalidValue;
+    }
   } else if (stage == 1) {
     constexpr int MB = D == 64 ? BWD_MB64 : 2, KBW = D == 64 ? BWD_KBW64 : 1;
     constexpr int BCK = 4 * 32 * KBW;

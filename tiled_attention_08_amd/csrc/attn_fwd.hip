@@ -195,6 +195,13 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
     int kvalid[QB];  // visible keys of this tile, per row block (MASKED only)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) kvalid[qb] = klim(qw0 + qb * 32 + l32) - j * S::BC;
+    // 32-key blocks of this tile any query of the wave sees (wave-uniform: the
+    // wave's last query sees the most keys). In a masked tile the blocks past
+    // it are skipped whole: no products, no exponentials, no row-sum terms.
+    // (Only masked tiles carry the test: a branch in the unmasked loop costs
+    // more than it saves.)
+    int kbv = KB;
+    if (MASKED) kbv = min(KB, max(1, (klim(qw0 + 32 * QB - 1) - j * S::BC + 31) >> 5));
 
     // ---- S^T tile: BC keys x (32*QB) queries, fp32 accumulate.
     f32x16 sacc[QB][KB];
@@ -202,6 +209,7 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = f32x16{};
+      if (MASKED && kb >= kbv) continue;
 #pragma unroll
       for (int cc = 0; cc < D / 16; ++cc) {
         const u32x4 a = lds_read_b128(Ks, tile_off<S::ROWB>(kb * 32 + l32, cc * 16 + h * 8));
@@ -215,6 +223,7 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
+          if (kb >= kbv) continue;
           const int key = kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
@@ -235,10 +244,12 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
       // MFMA results is needed, unlike fmaxf.
       float mx = sacc[qb][0][0];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb) {
+        if (MASKED && kb >= kbv) continue;
 #pragma unroll
         for (int e = (kb == 0 ? 1 : 0); e < 16; e += 2)
           mx = (e + 1 < 16) ? fmax3(mx, sacc[qb][kb][e], sacc[qb][kb][e + 1]) : fmax2(mx, sacc[qb][kb][e]);
+      }
       mx = halves_max(mx) * c;
       mnew[qb] = fmaxf(m_run[qb], mx);
       need |= mnew[qb] > m_run[qb] + kRescaleSlack;
@@ -265,6 +276,7 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
+          if (MASKED && kb >= kbv) continue;
           float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][e], c, nm));
           float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][e + 1], c, nm));
           if (MASKED) {
@@ -285,6 +297,7 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
+          if (MASKED && kb >= kbv) continue;
           const int row0 = kb * 32 + c2 * 16 + 4 * h + er;
           const int col = db * 32 + dsub * 16 + 4 * qq;
           const u32x2 lo = lds_read_tr16_b64(Vs, tile_off<S::ROWB>(row0, col));
