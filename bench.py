@@ -192,7 +192,7 @@ def bench_f32(args, w) -> int:
         "roofline": {"bound": "alu", "achieved": round(value, 4), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(value / PEAK_F32_TFLOPS, 5), "traffic": None, "kernel": "fwd_f32_kernel",
                      "avg_ms": round(ms, 5),
-                     "note": "one head of 196 rows: 7 workgroups on 256 CUs, so launch latency dominates"},
+                     "note": "one head of 196 rows: 25 workgroups of 8 rows on 256 CUs, so latency dominates"},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -167,6 +167,8 @@ def test_f32_backward_rejections(L):
         return L.lib.attn_bwd_f32(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"], a["dv"],
                                   a["B"], a["H"], a["N"], a["d"], a["scale"], a["ws"], n, None)
     assert b32(q=None) == INV and b32(d=80) == UNS and b32(ws=None) == WS
+    # the fp32 forward's grid (one workgroup per 8 rows) must stay below 2^30 workgroups
+    assert fwd32(L, B=1 << 14, H=1 << 10, N=1 << 10, d=32) == UNS
     assert b32(dq=A[0] + 8 * 64 * 2) == INV      # inside q's float32 extent (8 x 64 x 4 bytes), past a 2-byte one
     assert b32(dk=A[6]) == INV
 

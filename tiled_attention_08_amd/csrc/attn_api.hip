@@ -134,6 +134,8 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
   size_t E = 0, R = 0;
   const int st = check_shape(B, H, N, d_k, scale, &E, &R);
   if (st != ATTN_OK) return st;
+  // The fp32 forward launches one workgroup per 8 rows of a head.
+  if ((int64_t)B * H * ((N + 7) / 8) > INT32_MAX / 2) return ATTN_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse)) return ATTN_ERR_INVALID_ARG;
   const Range rq = span(q, E * 4), rk = span(k, E * 4), rv = span(v, E * 4), ro = span(o, E * 4), rl = span(lse, R * 4);
   if (overlap(ro, rq) || overlap(ro, rk) || overlap(ro, rv) || overlap(ro, rl)) return ATTN_ERR_INVALID_ARG;

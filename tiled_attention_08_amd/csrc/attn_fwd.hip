@@ -351,31 +351,39 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
 
 // ------------------------------------------------------------------------
 // fp32 forward: same method in fp32 storage and fp32 arithmetic (vector
-// ALU). One workgroup = 256 threads for 32 query rows; thread (r, t) with
-// r = tid / 8, t = tid % 8 scores keys t, t+8, ... of each 64-key tile for
-// query row r and owns output columns [t*D/8, (t+1)*D/8).
+// ALU). One workgroup = 256 threads for 8 query rows; thread (r, t) with
+// r = tid / 32, t = tid % 32 scores keys t and t + 32 of each 64-key tile for
+// query row r and owns output columns [t*D/32, (t+1)*D/32). Few rows per
+// workgroup spread a short sequence over many CUs: one head of 196 rows runs
+// as 25 workgroups, each with a quarter of the serial work per thread that 32
+// rows per workgroup gave.
 // ------------------------------------------------------------------------
-constexpr int kF32BR = 32;
+constexpr int kF32BR = 8;
 constexpr int kBC = 64;  // keys per K/V tile of the fp32 kernel
 
 template <int D>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                       const float* __restrict__ V, float* __restrict__ O,
                                                       float* __restrict__ LSE, int N, int n_qblk, float scale) {
-  __shared__ float Ks[kBC][D + 1];
-  __shared__ float Vs[kBC][D];
-  __shared__ float Ps[kF32BR][kBC + 1];
+  // K rows padded to D + 4 floats and P rows to kBC + 4: 16-byte aligned rows
+  // for 16-byte LDS reads. The 32 threads of a row read 32 consecutive keys'
+  // rows (row offsets 4 banks apart: conflict-free in 16-lane quarters) and
+  // consecutive output columns of V; rows of a wave share addresses.
+  constexpr int KS = D + 4, PS = kBC + 4, DC = D / 32;
+  __shared__ __attribute__((aligned(16))) float Ks[kBC * KS];
+  __shared__ __attribute__((aligned(16))) float Vs[kBC * D];
+  __shared__ __attribute__((aligned(16))) float Ps[kF32BR * PS];
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x / n_qblk, qblk = blockIdx.x - bh * n_qblk;
   const size_t head = (size_t)bh * N * D;
-  const int r = tid >> 3, t = tid & 7;
+  const int r = tid >> 5, t = tid & 31;
   const int q = qblk * kF32BR + r;
-  constexpr int DC = D / 8;
 
-  float qv[D];
+  float4 qv[D / 4];
 #pragma unroll
-  for (int i = 0; i < D; ++i) qv[i] = (q < N) ? Q[head + (size_t)q * D + i] : 0.f;
+  for (int i = 0; i < D / 4; ++i)
+    qv[i] = (q < N) ? *reinterpret_cast<const float4*>(Q + head + (size_t)q * D + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
 
   float acc[DC];
 #pragma unroll
@@ -384,47 +392,62 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 
   for (int j0 = 0; j0 < N; j0 += kBC) {
     __syncthreads();
-    for (int idx = tid; idx < kBC * D; idx += 256) {
-      const int kr = idx / D, cc = idx - kr * D;
-      const bool ok = j0 + kr < N;
-      Ks[kr][cc] = ok ? K[head + (size_t)(j0 + kr) * D + cc] : 0.f;
-      Vs[kr][cc] = ok ? V[head + (size_t)(j0 + kr) * D + cc] : 0.f;
+    for (int idx = tid; idx < kBC * D / 4; idx += 256) {
+      const int kr = idx / (D / 4), c4 = idx - kr * (D / 4);
+      float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
+      if (j0 + kr < N) {
+        kk = *reinterpret_cast<const float4*>(K + head + (size_t)(j0 + kr) * D + 4 * c4);
+        vv = *reinterpret_cast<const float4*>(V + head + (size_t)(j0 + kr) * D + 4 * c4);
+      }
+      *reinterpret_cast<float4*>(Ks + kr * KS + 4 * c4) = kk;
+      *reinterpret_cast<float4*>(Vs + kr * D + 4 * c4) = vv;
     }
     __syncthreads();
 
-    float s[kBC / 8];
+    // Scores of keys t and t + 32: two independent dot products, 4 dims per read.
+    float s[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float4 kv = *reinterpret_cast<const float4*>(Ks + (t + 32 * u) * KS + 4 * i);
+        s[u] = fmaf(qv[i].x, kv.x, s[u]);
+        s[u] = fmaf(qv[i].y, kv.y, s[u]);
+        s[u] = fmaf(qv[i].z, kv.z, s[u]);
+        s[u] = fmaf(qv[i].w, kv.w, s[u]);
+      }
     float mx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kBC / 8; ++u) {
-      const int kr = t + 8 * u;
-      float dot = 0.f;
-#pragma unroll
-      for (int i = 0; i < D; ++i) dot = fmaf(qv[i], Ks[kr][i], dot);
-      s[u] = (j0 + kr < N) ? dot * scale : -INFINITY;
+    for (int u = 0; u < 2; ++u) {
+      s[u] = (j0 + t + 32 * u < N) ? s[u] * scale : -INFINITY;
       mx = fmaxf(mx, s[u]);
     }
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
     const float mnew = fmaxf(m, mx);
     const float alpha = expf(m - mnew);
     float rs = 0.f;
 #pragma unroll
-    for (int u = 0; u < kBC / 8; ++u) {
-      const float p = (j0 + t + 8 * u < N) ? expf(s[u] - mnew) : 0.f;
+    for (int u = 0; u < 2; ++u) {
+      const float p = (j0 + t + 32 * u < N) ? expf(s[u] - mnew) : 0.f;
       rs += p;
-      Ps[r][t + 8 * u] = p;
+      Ps[r * PS + t + 32 * u] = p;
     }
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) rs += __shfl_xor(rs, o);
+    for (int o = 1; o < 32; o <<= 1) rs += __shfl_xor(rs, o);
     l = l * alpha + rs;
     m = mnew;
 #pragma unroll
     for (int i = 0; i < DC; ++i) acc[i] *= alpha;
     __syncthreads();
-    for (int kr = 0; kr < kBC; ++kr) {
-      const float p = Ps[r][kr];
+    // O row r, columns t * DC ..: four keys' probabilities per read.
+    for (int k4 = 0; k4 < kBC; k4 += 4) {
+      const float4 p4 = *reinterpret_cast<const float4*>(Ps + r * PS + k4);
+      const float pk[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
-      for (int i = 0; i < DC; ++i) acc[i] = fmaf(p, Vs[kr][t * DC + i], acc[i]);
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < DC; ++i) acc[i] = fmaf(pk[e], Vs[(k4 + e) * D + t * DC + i], acc[i]);
     }
   }
   if (q < N) {
