@@ -149,6 +149,7 @@ def test_backward_rejections(L):
     assert bwd(L, 4) == INV and bwd(L, -1) == INV
     for stage in (None, 0, 1, 2, 3):
         assert bwd(L, stage, ex=True, dtype=3) == UNS
+        assert bwd(L, stage, ex=True, dtype=-1) == UNS      # only attn_bwd_f32 takes float32
         assert bwd(L, stage, ex=True, causal=5) == INV
         assert bwd(L, stage, ex=True, kv_len=A[10] + 1) == INV
         assert bwd(L, stage, ex=True, kv_len=A[7]) == INV     # kv_len inside dk

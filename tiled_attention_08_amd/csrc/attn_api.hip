@@ -218,6 +218,8 @@ int attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
 int attn_bwd_ex(int dtype, int layout, const void* q, const void* k, const void* v, const void* o, const float* lse,
                 const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k, float scale, int causal,
                 const int* kv_len, void* workspace, size_t workspace_bytes, void* stream) {
+  // The 16-bit types only (bwd_checks also serves attn_bwd_f32, with dtype -1).
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_UNSUPPORTED;
   Layout L;
   const int st = bwd_checks(dtype, layout, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len,
                             workspace, workspace_bytes, &L);
@@ -244,6 +246,7 @@ int attn_bwd_stage(int stage, int dtype, int layout, const void* q, const void* 
                    float scale, int causal, const int* kv_len, void* workspace, size_t workspace_bytes,
                    void* stream) {
   if (stage < 0 || stage > 3) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_UNSUPPORTED;
   Layout L;
   const int st = bwd_checks(dtype, layout, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len,
                             workspace, workspace_bytes, &L);
