@@ -9,6 +9,7 @@ and dQ launches), on the long-sequence workload B=8, H=16, N=4096, d_k=64, bf16
     python bench.py [--steps K] [--warmup W] [--workload 1|2|3|4|5] [--causal] [--dtype bf16|f16]
                     [--cold] [--graph] [--no-cpu-baseline]
     python bench.py --workload 2 --proj      (the ViT block with its query/key/value projection)
+    python bench.py --workload 2 --dtype f32 (fp32 storage and arithmetic, forward and backward)
 
 Prints ONE JSON line on stdout; progress goes to stderr. FLOPs are
 algorithmic: forward 4*B*H*N^2*d (Q K^T and P V), backward 10*B*H*N^2*d
@@ -201,6 +202,82 @@ def bench_f32(args, w) -> int:
     return 0
 
 
+def bench_f32_train(args, w) -> int:
+    """fp32 storage and arithmetic (attn_fwd_f32 + attn_bwd_f32) on a workload with a backward: TFLOP/s of the
+    step against the fp32 vector-ALU peak (the fp32 kernels run on the vector ALU, not the matrix cores)."""
+    import numpy as np
+    import torch
+    from attn_inputs import make_case
+    from tiled_attention_08_amd import _lib as attn
+    B, H, N, d = w.B, w.H, w.N, w.d
+    log(f"[bench] workload {w.wid} {w.name} in fp32: B={B} H={H} N={N} d={d}, seed {args.seed}")
+    x = make_case(B, H, N, d, "f32", seed=args.seed, wid=w.wid, qk_sigma=w.qk_sigma, v_dist=w.v_dist,
+                  planted_frac=w.planted_frac)
+    q, k, v, do = (torch.from_numpy(np.ascontiguousarray(x.raw[n])).cuda() for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = attn.workspace_for(q)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        attn.attn_fwd_f32(q, k, v, o, lse, x.scale, stream)
+
+    def bwd():
+        attn.attn_bwd_f32(q, k, v, o, lse, do, dq, dk, dv, x.scale, ws, stream)
+
+    def step():
+        fwd()
+        bwd()
+
+    step()
+    torch.cuda.synchronize()
+    for t in (o, lse, dq, dk, dv):
+        if not torch.isfinite(t).all():
+            log("[bench] non-finite output")
+            return 1
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    flops = fwd_flops(B, H, N, d) + bwd_flops(B, H, N, d)
+    value = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] fp32 {ms:.4f} ms/step, {value:.2f} TFLOP/s")
+    reps = args.kernel_reps
+    # The forward is one kernel; the fp32 backward (delta, dK/dV, dQ) is timed as its three launches together.
+    kernels = {"fwd_f32": time_launches(fwd, reps), "bwd_f32": time_launches(bwd, reps)}
+    log("[bench] kernel ms: " + ", ".join(f"{kn} {t:.4f}" for kn, t in kernels.items()))
+    kflops = {"fwd_f32": fwd_flops(B, H, N, d), "bwd_f32": bwd_flops(B, H, N, d)}
+    names = {"fwd_f32": "fwd_f32_kernel",
+             "bwd_f32": "attn_bwd_f32 (bwd_prep_f32_kernel, bwd_dkdv_f32_kernel, bwd_dq_f32_kernel)"}
+    dominant = max(kernels, key=kernels.get)
+    achieved = kflops[dominant] / (kernels[dominant] * 1e-3) / 1e12
+    record = {
+        "metric": "attention TFLOP/s fwd+bwd in fp32 (vector ALU) and % of MI355X fp32 vector peak",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name + "_f32", "B": B, "H": H, "N": N, "d_k": d, "passes": "fwd+bwd",
+                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
+        "frac_of_f32_vector_peak": round(value / PEAK_F32_TFLOPS, 4),
+        "kernel_ms": {kn: round(t, 5) for kn, t in kernels.items()},
+        "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_F32_TFLOPS, 4), "traffic": None, "kernel": names[dominant],
+                     "avg_ms": round(kernels[dominant], 5)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        record["cpu_baseline"] = cpu_baseline(w.wid, args.seed, args.cpu_seconds)
+    print(json.dumps(record), flush=True)
+    return 0
+
+
 def proj_flops(B, N, D, H, d):
     """One product of the query/key/value projection: 2 * tokens * D * 3 H d (the forward has one, the backward two)."""
     return 2.0 * B * N * D * 3 * H * d
@@ -373,8 +450,9 @@ def main(argv=None) -> int:
     ap.add_argument("--kernel-reps", type=int, default=20, help="launches per kernel for the roofline timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--dtype", default="bf16", choices=("bf16", "f16"),
-                    help="storage type of Q, K, V, O and the gradients (f16 runs attn_fwd_ex / attn_bwd_ex)")
+    ap.add_argument("--dtype", default="bf16", choices=("bf16", "f16", "f32"),
+                    help="storage type of Q, K, V, O and the gradients (f16 runs attn_fwd_ex / attn_bwd_ex; f32 runs "
+                         "the fp32 forward and backward, vector ALU)")
     ap.add_argument("--cold", action="store_true",
                     help="rotate through copies of the inputs (about 1 GiB in all) so that every launch reads its "
                          "inputs from HBM, not from L2 or the MALL")
@@ -418,6 +496,11 @@ def main(argv=None) -> int:
     cz = args.causal
     if w.dtype == "f32":
         return bench_f32(args, w)
+    if args.dtype == "f32":
+        if "bwd" not in w.passes or args.causal or args.cold or args.graph or args.proj:
+            log("[bench] --dtype f32 times the fp32 forward and backward of a workload with a backward, no other mode")
+            return 2
+        return bench_f32_train(args, w)
     if args.proj:
         if args.workload != 2 or args.causal or args.dtype != "bf16" or args.cold or args.graph:
             log("[bench] --proj times the ViT-B/16 block: use it with --workload 2 only (bf16, no other mode)")
