@@ -476,7 +476,9 @@ GemmPlan plan_gemm(int M, int N, int K, bool split_ok) {
   p.big = PROJ_BIG && M >= G2_TILE && N >= G2_TILE;
   if (!p.big) return p;
   p.tiles_n = (N + G2_TILE - 1) / G2_TILE;
-  p.tiles = ((M + G2_TILE - 1) / G2_TILE) * p.tiles_n;
+  const long tiles = (long)((M + G2_TILE - 1) / G2_TILE) * p.tiles_n;
+  p.tiles = tiles > INT32_MAX / 16 ? 0 : (int)tiles;  // 0: too many tiles to launch (gemm_auto refuses)
+  if (p.tiles == 0) return p;
   p.S = 1;
   if (split_ok && p.tiles < 192) p.S = max(1, min(min(256 / p.tiles, K / 512), PROJ_MAX_SPLIT));
   p.kchunk = ((K + p.S - 1) / p.S + 63) / 64 * 64;
@@ -490,6 +492,7 @@ hipError_t gemm_auto(const uint16_t* A, const uint16_t* Bm, uint16_t* C, int M, 
                      int ldc, void* ws, hipStream_t stream) {
   const GemmPlan p = plan_gemm(M, N, K, ws != nullptr);
   if (p.big) {
+    if (p.tiles == 0) return hipErrorInvalidValue;
     float* part = p.S > 1 ? static_cast<float*>(ws) : nullptr;
     hipLaunchKernelGGL((gemm256_kernel<E, AK, BK>), dim3((unsigned)(p.tiles * p.S)), dim3(G2_THREADS), 0, stream, A,
                        Bm, C, M, N, K, lda, ldb, ldc, p.tiles_n, p.tiles, p.S, p.kchunk, part);
