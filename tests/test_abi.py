@@ -206,6 +206,23 @@ def test_projection_rejections(L):
     assert pb(ws=A[3], ws_bytes=need, **big) == INV                     # workspace on dx
 
 
+def test_projection_workspace_follows_the_split_rule(L):
+    """Split products write float32 partial slices: the workspace is the larger of the two products' S * M * N * 4.
+    A product with at least 256 rows and columns but fewer than 192 tiles of 256 x 256 splits its contraction
+    min(256 // tiles, K // 512) ways (rounded to whole 64-steps); everything else needs none."""
+    def ws(B, N, D, H, d):
+        return L.attn_qkv_proj_bwd_workspace_bytes(B, N, D, H, d)
+    # ViT-B/16 block: dx (6272 x 768, K 2304) has 25 x 3 = 75 tiles -> 3 splits; dw (768 x 2304, K 6272) has
+    # 3 x 9 = 27 tiles -> 9 splits (kchunk 704). The larger slice set is dw's.
+    assert ws(32, 196, 768, 12, 64) == max(3 * 6272 * 768, 9 * 768 * 2304) * 4
+    # 8 x 300 tokens, D 512, F 768: dx 10 x 2 = 20 tiles, K 768 -> 1 split; dw 2 x 3 = 6 tiles, K 2400 -> 4 splits.
+    assert ws(8, 300, 512, 4, 64) == 4 * 512 * 768 * 4
+    # 300 tokens, D 1024, F 1536: dx 2 x 4 = 8 tiles, K 1536 -> 3 splits; dw's K of 300 tokens is too short to split.
+    assert ws(1, 300, 1024, 4, 128) == 3 * 300 * 1024 * 4
+    # Under 256 rows or columns: the small-tile kernels, no workspace.
+    assert ws(2, 37, 64, 1, 32) == 0 and ws(5, 7, 136, 3, 64) == 0
+
+
 def test_fusion_rule(L):
     """dK/dV and dQ share a launch only for d_k <= 64 and small grids; rejected shapes answer 0."""
     assert L.attn_bwd_fused(32, 12, 196, 64) and L.attn_bwd_fused(4, 12, 2048, 64)
