@@ -42,9 +42,10 @@ def test_fwd_f32_parity(gpu_lib, N, d):
 
 
 @pytest.mark.parametrize("B,H,N,d", [(1, 1, 1, 64), (2, 2, 196, 64), (1, 2, 333, 32), (1, 1, 150, 96),
-                                     (1, 2, 129, 128), (1, 1, 1000, 64)])
+                                     (1, 2, 129, 128), (1, 1, 1000, 64), (8, 16, 520, 64), (8, 32, 300, 128)])
 def test_f32_fwd_bwd_parity(gpu_lib, B, H, N, d):
-    """fp32 forward and backward (attn_fwd_f32, attn_bwd_f32) against the oracle."""
+    """fp32 forward and backward (attn_fwd_f32, attn_bwd_f32) against the oracle. The small grids run the
+    backward with 16 lanes per row (d >= 64), the last two shapes (over 1024 workgroups of 64 rows) with 4."""
     import torch
     x = make_case(B, H, N, d, "f32", seed=7000 + N + d)
     _say(f"fwd/bwd f32 B={B} H={H} N={N} d={d}")

@@ -605,10 +605,12 @@ void bwd_dkdv_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 
 // ---------------------------------------------------------------- fp32 backward
 // fp32 storage and fp32 arithmetic throughout (vector ALU), the same three
-// deterministic stages. Four lanes share a row (a key in stage 1, a query in
-// stage 2): lane part p owns columns [p * D/4, (p+1) * D/4) of that row, dot
-// products are split over the four lanes and summed with two xor shuffles.
-constexpr int kF32Rows = 64;   // rows (keys or queries) per workgroup: 256 threads / 4
+// deterministic stages. LP lanes share a row (a key in stage 1, a query in
+// stage 2): lane part p owns columns [p * D/LP, (p+1) * D/LP) of that row, dot
+// products are split over the LP lanes and summed with xor shuffles. LP = 4
+// (64 rows per workgroup) where the grid is large; LP = 16 (16 rows per
+// workgroup, four times the workgroups) for few heads and short sequences at
+// D >= 64, where 64-row workgroups would leave most CUs idle.
 constexpr int kF32Step = 32;   // rows of the other side staged in LDS per step
 
 __global__ __launch_bounds__(256) void bwd_prep_f32_kernel(const float* __restrict__ O, const float* __restrict__ dO,
@@ -629,24 +631,26 @@ __global__ __launch_bounds__(256) void bwd_prep_f32_kernel(const float* __restri
   }
 }
 
-__device__ __forceinline__ float sum4(float x) {
-  x += __shfl_xor(x, 1);
-  return x + __shfl_xor(x, 2);
+template <int LP>
+__device__ __forceinline__ float sum_lanes(float x) {
+#pragma unroll
+  for (int o = 1; o < LP; o <<= 1) x += __shfl_xor(x, o);
+  return x;
 }
 
-// Stage 1: dV_j = sum_i P_ij dO_i, dK_j = scale * sum_i dS_ij Q_i for 64 keys j.
-template <int D>
+// Stage 1: dV_j = sum_i P_ij dO_i, dK_j = scale * sum_i dS_ij Q_i for 256 / LP keys j.
+template <int D, int LP>
 __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                            const float* __restrict__ V, const float* __restrict__ dO,
                                                            const float* __restrict__ LSE, const float* __restrict__ ndelta,
                                                            float* __restrict__ dK, float* __restrict__ dV, int N,
                                                            int n_kblk, float scale) {
-  constexpr int DC = D / 4;
+  constexpr int DC = D / LP;
   __shared__ float Qs[kF32Step][D], dOs[kF32Step][D], Ls[kF32Step], Ds[kF32Step];
-  const int tid = threadIdx.x, part = tid & 3;
+  const int tid = threadIdx.x, part = tid % LP;
   const int bh = blockIdx.x / n_kblk, kblk = blockIdx.x - bh * n_kblk;
   const size_t head = (size_t)bh * N * D;
-  const int key = kblk * kF32Rows + (tid >> 2);
+  const int key = kblk * (256 / LP) + tid / LP;
   const bool ok = key < N;
   float kr[DC], vr[DC], dk[DC], dv[DC];
 #pragma unroll
@@ -678,8 +682,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(const float* __restri
         s = fmaf(Qs[r][part * DC + c], kr[c], s);
         dp = fmaf(dOs[r][part * DC + c], vr[c], dp);
       }
-      s = sum4(s);
-      dp = sum4(dp);
+      s = sum_lanes<LP>(s);
+      dp = sum_lanes<LP>(dp);
       const float p = ok ? expf(s * scale - Ls[r]) : 0.f;
       const float ds = p * (dp + Ds[r]);
 #pragma unroll
@@ -698,18 +702,18 @@ __global__ __launch_bounds__(256) void bwd_dkdv_f32_kernel(const float* __restri
   }
 }
 
-// Stage 2: dQ_i = scale * sum_j dS_ij K_j for 64 queries i.
-template <int D>
+// Stage 2: dQ_i = scale * sum_j dS_ij K_j for 256 / LP queries i.
+template <int D, int LP>
 __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                          const float* __restrict__ V, const float* __restrict__ dO,
                                                          const float* __restrict__ LSE, const float* __restrict__ ndelta,
                                                          float* __restrict__ dQ, int N, int n_qblk, float scale) {
-  constexpr int DC = D / 4;
+  constexpr int DC = D / LP;
   __shared__ float Ks[kF32Step][D], Vs[kF32Step][D];
-  const int tid = threadIdx.x, part = tid & 3;
+  const int tid = threadIdx.x, part = tid % LP;
   const int bh = blockIdx.x / n_qblk, qblk = blockIdx.x - bh * n_qblk;
   const size_t head = (size_t)bh * N * D;
-  const int q = qblk * kF32Rows + (tid >> 2);
+  const int q = qblk * (256 / LP) + tid / LP;
   const bool ok = q < N;
   float qr[DC], dor[DC], dq[DC];
 #pragma unroll
@@ -737,8 +741,8 @@ __global__ __launch_bounds__(256) void bwd_dq_f32_kernel(const float* __restrict
         s = fmaf(qr[c], Ks[r][part * DC + c], s);
         dp = fmaf(dor[c], Vs[r][part * DC + c], dp);
       }
-      s = sum4(s);
-      dp = sum4(dp);
+      s = sum_lanes<LP>(s);
+      dp = sum_lanes<LP>(dp);
       const float p = ok ? expf(s * scale - l) : 0.f;
       const float ds = p * (dp + nd);
 #pragma unroll
@@ -846,16 +850,32 @@ hipError_t launch_bwd_16_stage(bool f16, int stage, const uint16_t* q, const uin
 #undef ATTN_BWD_STAGE
 }
 
-template <int D>
-static void launch_f32_stage_t(int stage, dim3 grid, const float* q, const float* k, const float* v,
-                               const float* dO, const float* lse_ws, const float* ndelta, float* dq, float* dk,
-                               float* dv, int N, int nblk, float scale, hipStream_t stream) {
+template <int D, int LP>
+static void launch_f32_stage_lp(int stage, int BH, const float* q, const float* k, const float* v, const float* dO,
+                                const float* lse_ws, const float* ndelta, float* dq, float* dk, float* dv, int N,
+                                float scale, hipStream_t stream) {
+  const int nblk = (N + 256 / LP - 1) / (256 / LP);
+  const dim3 grid((unsigned)(nblk * BH));
   if (stage == 1)
-    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D>), grid, dim3(256), 0, stream, q, k, v, dO, lse_ws, ndelta, dk, dv, N,
-                       nblk, scale);
+    hipLaunchKernelGGL((bwd_dkdv_f32_kernel<D, LP>), grid, dim3(256), 0, stream, q, k, v, dO, lse_ws, ndelta, dk, dv,
+                       N, nblk, scale);
   else
-    hipLaunchKernelGGL((bwd_dq_f32_kernel<D>), grid, dim3(256), 0, stream, q, k, v, dO, lse_ws, ndelta, dq, N, nblk,
-                       scale);
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D, LP>), grid, dim3(256), 0, stream, q, k, v, dO, lse_ws, ndelta, dq, N,
+                       nblk, scale);
+}
+
+// 16 lanes per row while the 64-row grid would be under 1024 workgroups (four
+// per CU), for D >= 64. At D = 32 a lane would keep 2 columns and the 16-lane
+// sums cost more than the extra workgroups gain (measured 8-18 % slower).
+template <int D>
+static void launch_f32_stage_t(int stage, int B, int H, const float* q, const float* k, const float* v,
+                               const float* dO, const float* lse_ws, const float* ndelta, float* dq, float* dk,
+                               float* dv, int N, float scale, hipStream_t stream) {
+  if (D >= 64 && (long)B * H * ((N + 63) / 64) < 1024)
+    launch_f32_stage_lp<D, (D >= 64 ? 16 : 4)>(stage, B * H, q, k, v, dO, lse_ws, ndelta, dq, dk, dv, N, scale,
+                                               stream);
+  else
+    launch_f32_stage_lp<D, 4>(stage, B * H, q, k, v, dO, lse_ws, ndelta, dq, dk, dv, N, scale, stream);
 }
 
 hipError_t launch_bwd_f32_stage(int stage, const float* q, const float* k, const float* v, const float* o,
@@ -869,13 +889,11 @@ hipError_t launch_bwd_f32_stage(int stage, const float* q, const float* k, const
                        lse, lse_ws, ndelta, rows, d);
     return hipGetLastError();
   }
-  const int nblk = (N + kF32Rows - 1) / kF32Rows;
-  const dim3 grid((unsigned)(nblk * B * H));
   switch (d) {
-    case 32: launch_f32_stage_t<32>(stage, grid, q, k, v, dO, lse_ws, ndelta, dq, dk, dv, N, nblk, scale, stream); break;
-    case 64: launch_f32_stage_t<64>(stage, grid, q, k, v, dO, lse_ws, ndelta, dq, dk, dv, N, nblk, scale, stream); break;
-    case 96: launch_f32_stage_t<96>(stage, grid, q, k, v, dO, lse_ws, ndelta, dq, dk, dv, N, nblk, scale, stream); break;
-    default: launch_f32_stage_t<128>(stage, grid, q, k, v, dO, lse_ws, ndelta, dq, dk, dv, N, nblk, scale, stream);
+    case 32: launch_f32_stage_t<32>(stage, B, H, q, k, v, dO, lse_ws, ndelta, dq, dk, dv, N, scale, stream); break;
+    case 64: launch_f32_stage_t<64>(stage, B, H, q, k, v, dO, lse_ws, ndelta, dq, dk, dv, N, scale, stream); break;
+    case 96: launch_f32_stage_t<96>(stage, B, H, q, k, v, dO, lse_ws, ndelta, dq, dk, dv, N, scale, stream); break;
+    default: launch_f32_stage_t<128>(stage, B, H, q, k, v, dO, lse_ws, ndelta, dq, dk, dv, N, scale, stream);
   }
   return hipGetLastError();
 }
