@@ -62,6 +62,8 @@ def _run(gpu_lib, layout, q, k, v, do, scale, causal, kv):
     ("f16", 2, 2, 257, 32, True, None),
     ("bf16", 1, 4, 1100, 64, True, None),
     ("bf16", 2, 2, 1030, 96, False, [1030, 700]),
+    ("bf16", 1, 3, 1030, 128, False, None),
+    ("f16", 2, 2, 1100, 64, False, None),
 ])
 def test_layout_matches_contiguous_bitwise(gpu_lib, layout, dtype, B, H, N, d, causal, kv):
     import torch

@@ -80,7 +80,9 @@ def test_fwd_f32_workload1(gpu_lib):
 
 SMALL = [(1, 1, 1, 64), (1, 2, 7, 64), (2, 3, 65, 64), (2, 2, 196, 64), (2, 3, 333, 64), (1, 1, 1000, 64),
          (1, 1, 1, 128), (1, 2, 129, 128), (2, 2, 196, 128), (1, 2, 517, 128),
-         (1, 1, 1, 32), (2, 2, 100, 32), (1, 2, 1111, 32), (1, 1, 1, 96), (2, 2, 140, 96), (1, 2, 1070, 96)]
+         (1, 1, 1, 32), (2, 2, 100, 32), (1, 2, 1111, 32), (1, 1, 1, 96), (2, 2, 140, 96), (1, 2, 1070, 96),
+         # ping-pong forward (unmasked rows of 1024 keys or more, d = 64 and 128): whole and ragged last tiles
+         (1, 1, 1024, 64), (1, 2, 1100, 64), (2, 1, 2047, 64), (1, 2, 1030, 128), (1, 1, 1987, 128)]
 
 
 @pytest.mark.parametrize("B,H,N,d", SMALL)

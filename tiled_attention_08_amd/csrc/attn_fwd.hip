@@ -62,6 +62,25 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units a row max may grow before O
 #ifndef FWD_NS_SHORT
 #define FWD_NS_SHORT 2
 #endif
+// Unmasked long rows (d = 64, 128) use the ping-pong kernel.
+#ifndef FWD_PINGPONG
+#define FWD_PINGPONG 1
+#endif
+#ifndef FWD_PP_D64
+#define FWD_PP_D64 1
+#endif
+#ifndef FWD_PP_QB64
+#define FWD_PP_QB64 2
+#endif
+#ifndef FWD_PP_KB64
+#define FWD_PP_KB64 2
+#endif
+#ifndef FWD_PP_QB128
+#define FWD_PP_QB128 1
+#endif
+#ifndef FWD_PP_KB128
+#define FWD_PP_KB128 2
+#endif
 #ifndef FWD_QB128
 #define FWD_QB128 1
 #endif
@@ -350,6 +369,333 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
 }
 
 // ------------------------------------------------------------------------
+// Ping-pong forward (long rows, no mask). The same tiles and the same
+// arithmetic per element as fwd_kernel, in a different order: each wave's
+// work on K/V tile j is split into a matrix-core phase (O^T += V_{j-1}^T
+// P_{j-1}^T, then S_j^T = K_j Q^T) and a vector phase (the online softmax of
+// S_j, giving P_j). Waves 0-3 and 4-7 run half a tile apart, separated by a
+// workgroup barrier per phase, so that in every phase one wave of each SIMD
+// feeds the matrix core while the other computes exponentials. The matrix
+// phase runs at raised wave priority, so the arbiter issues the next matrix
+// instruction as soon as it can and fills the gaps with the other wave's
+// vector work.
+//
+// Phase schedule (slot s, barrier after every slot but the last): group g
+// (= wave / 4) runs the matrix phase of tile j in slot 2j + g and the vector
+// phase of tile j in slot 2j + 1 + g, for j = 0 .. ntiles (the last matrix
+// phase only adds P V of the last tile). The K/V ring holds four tiles: each
+// wave fetches its share of tile j + 2 during its matrix phase j, right after
+// its transposing reads of V_{j-1}, and waits for it at the start of its
+// matrix phase j + 1, so tile u is complete before the barrier that ends slot
+// 2u - 1. K of tile u is read in slots 2u and 2u + 1, V in slots 2u + 2 and
+// 2u + 3, and its ring slot is refilled (tile u + 4) from slot 2u + 4 on.
+// Only raw s_barrier is used between phases: a fence would wait for the
+// tiles in flight.
+// ------------------------------------------------------------------------
+// Calls f(IntC<I>{}) for I = B .. E-1 in order (compile-time indices).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IntC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+constexpr int kPPWaves = 8;
+constexpr int kPPRing = 4;
+
+template <class E, int D, int QB, int KB>
+__global__ __launch_bounds__(kPPWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                   uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qblk, int total, float c,
+                   uint32_t qsign, int H, Strides sq, Strides so) {
+  using S = FwdShape<D, QB, KB, kPPRing, kPPWaves>;
+  constexpr int NS = kPPRing;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave >> 2;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 4, gi = lane & 15;
+  const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
+  const int work = xcd_remap(blockIdx.x, total);
+  const int bh = work / n_qblk, qblk = work - bh * n_qblk;
+  const size_t hq = head_off(sq, bh, H);
+  const uint16_t* Qh = Q + hq;
+  const uint16_t* Kh = K + hq;
+  const uint16_t* Vh = V + hq;
+  const int qw0 = qblk * S::BR + wave * 32 * QB;
+
+  u32x4 qf[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int q = qw0 + qb * 32 + l32;
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (q < N) v = *reinterpret_cast<const u32x4*>(Qh + q * sq.n + cc * 16 + h * 8);
+      v ^= qsign;
+      qf[qb][cc] = v;
+    }
+  }
+
+  f32x16 oacc[QB][D / 32];
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
+  }
+
+  const int ntiles = (N + S::BC - 1) / S::BC;
+  const int tail = N - (ntiles - 1) * S::BC;  // valid keys of the last tile (1 .. BC)
+
+  // Tile j into ring slot R (= j % NS).
+  auto dma_tile = [&](int j, auto r_) __attribute__((always_inline)) {
+    constexpr int R = decltype(r_)::value;
+    unsigned char* Ks = smem + R * 2 * S::TILEB;
+    unsigned char* Vs = Ks + S::TILEB;
+#pragma unroll
+    for (int r = 0; r < S::DMA_PER_WAVE; ++r) {
+      const int slot0 = (wave * S::DMA_PER_WAVE + r) * 64;
+      const int p = slot0 + lane;
+      const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz<S::ROWB>(row);
+      const int key = min(j * S::BC + row, N - 1);
+      dma16(Kh + key * sq.n + chunk * 8, Ks + slot0 * 16);
+      dma16(Vh + key * sq.n + chunk * 8, Vs + slot0 * 16);
+    }
+  };
+  // Phase boundary: this wave's LDS reads have returned, then all 8 waves meet.
+  auto phase_end = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  f32x16 sacc[QB][KB];
+  u32x4 pb[QB][KB][2];
+
+  // Matrix-core phase of tile j in chunks of 8 products with D/16 operand
+  // fragments each: chunks 0 .. KB-1 are O^T += V_{j-1}^T P_{j-1}^T for key
+  // block kb (HAS_PV, j >= 1), chunks KB .. 2KB-1 are S_j^T for key block kb
+  // (HAS_S, j < ntiles). The operands of chunk c + 1 are read from LDS while
+  // chunk c runs; scheduling barriers keep the compiler from hoisting every
+  // read of the phase to its top (which would need registers for all of them).
+  constexpr int NOP = D / 16;
+  // Per-lane byte offsets of the operand reads within a tile, for key block
+  // 0: K rows l32 (chunk 2cc + h), and the transposing V reads of rows
+  // 4h + er (+ 8). The swizzle depends only on a row's low 4 bits, so rows
+  // 16m further on are these offsets plus 16m rows: key blocks, 16-row halves
+  // and ring slots are immediate offsets of the LDS reads.
+  int koff[NOP], voff[2][D / 32];
+#pragma unroll
+  for (int cc = 0; cc < NOP; ++cc) koff[cc] = tile_off<S::ROWB>(l32, cc * 16 + h * 8);
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) voff[hi][db] = tile_off<S::ROWB>(4 * h + er + 8 * hi, db * 32 + dsub * 16 + 4 * qq);
+
+  // Operands of chunk C of the matrix phase whose K tile sits in ring slot RK
+  // (and V tile of the previous tile in slot (RK + NS - 1) % NS).
+  auto load_chunk = [&](auto cc_, auto rk_, u32x4 (&a)[NOP]) __attribute__((always_inline)) {
+    constexpr int C = decltype(cc_)::value, RK = decltype(rk_)::value;
+    if constexpr (C < KB) {
+      constexpr int VB = ((RK + NS - 1) % NS) * 2 * S::TILEB + S::TILEB;
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int rowb = VB + (C * 32 + c2 * 16) * S::ROWB;
+          const u32x2 lo = lds_read_tr16_b64(smem, rowb + voff[0][db]);
+          const u32x2 hi = lds_read_tr16_b64(smem, rowb + voff[1][db]);
+          a[c2 * (D / 32) + db] = cat(lo, hi);
+        }
+    } else {
+      constexpr int KBASE = RK * 2 * S::TILEB + (C - KB) * 32 * S::ROWB;
+#pragma unroll
+      for (int cc = 0; cc < NOP; ++cc) a[cc] = lds_read_b128(smem, KBASE + koff[cc]);
+    }
+  };
+  auto run_chunk = [&](auto cc_, const u32x4 (&a)[NOP]) __attribute__((always_inline)) {
+    constexpr int C = decltype(cc_)::value;
+    if constexpr (C < KB) {
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mfma(a[c2 * (D / 32) + db], pb[qb][C][c2], oacc[qb][db]);
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[qb][C - KB] = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < NOP; ++cc)
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[qb][C - KB] = E::mfma(a[cc], qf[qb][cc], sacc[qb][C - KB]);
+    }
+  };
+  // `fetch` runs once every transposing read of V in the phase has been
+  // issued (the compiler makes a transposing LDS read wait for all of the
+  // wave's outstanding LDS DMA, so a fetch issued before them would be waited
+  // for at once).
+  auto mfma_phase = [&](auto has_pv, auto has_s, auto rk_, auto&& fetch) __attribute__((always_inline)) {
+    constexpr int C0 = decltype(has_pv)::value ? 0 : KB;
+    constexpr int C1 = decltype(has_s)::value ? 2 * KB : KB;
+    u32x4 buf[2][NOP];
+    if constexpr (C0 == KB) fetch();
+    load_chunk(IntC<C0>{}, rk_, buf[0]);
+    static_for<C0, C1>([&](auto cc_) __attribute__((always_inline)) {
+      constexpr int C = decltype(cc_)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (C + 1 == KB) fetch();
+      if constexpr (C + 1 < C1) load_chunk(IntC<C + 1>{}, rk_, buf[(C + 1 - C0) & 1]);
+      run_chunk(cc_, buf[(C - C0) & 1]);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Vector phase of tile j: online softmax of S_j (keys >= kvalid masked when MASKED).
+  auto valu_phase = [&](auto masked, int kvalid) __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked)::value;
+    if (MASKED) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            if (key >= kvalid) sacc[qb][kb][e] = -INFINITY;
+        }
+    }
+    float mnew[QB];
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = sacc[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int e = (kb == 0 ? 1 : 0); e < 16; e += 2)
+          mx = (e + 1 < 16) ? fmax3(mx, sacc[qb][kb][e], sacc[qb][kb][e + 1]) : fmax2(mx, sacc[qb][kb][e]);
+      mx = halves_max(mx) * c;
+      mnew[qb] = fmaxf(m_run[qb], mx);
+      need |= mnew[qb] > m_run[qb] + kRescaleSlack;
+    }
+    if (__builtin_amdgcn_ballot_w64(need)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float alpha = mnew[qb] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - mnew[qb]);
+        m_run[qb] = mnew[qb];
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[qb][db] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float nm = -m_run[qb];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][e], c, nm));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][e + 1], c, nm));
+          if (MASKED) {
+            const int key = kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+            if (key >= kvalid) p0 = 0.f;
+            if (key + 1 >= kvalid) p1 = 0.f;
+          }
+          const uint32_t w = E::pack(p0, p1);
+          pb[qb][kb][e >> 3][(e >> 1) & 3] = w;
+          l_run[qb] = E::sum_pair(w, l_run[qb]);
+        }
+    }
+  };
+
+  // Matrix phase of tile j (ring slot R = j % NS) at raised priority. It
+  // first waits for this wave's share of tile j + 1 (fetched in its previous
+  // matrix phase) and fetches its share of tile j + 2 once its reads of V_{j-1}
+  // are issued.
+  auto matrix_slot = [&](auto has_pv, auto has_s, auto r_, int j) __attribute__((always_inline)) {
+    constexpr int R = decltype(r_)::value;
+    wait_vmem_below<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    mfma_phase(has_pv, has_s, r_, [&]() __attribute__((always_inline)) {
+      if (j + 2 < ntiles) dma_tile(j + 2, IntC<(R + 2) % NS>{});
+    });
+    __builtin_amdgcn_s_setprio(0);
+  };
+  auto vector_slot = [&](int j, auto may_mask) __attribute__((always_inline)) {
+    if (decltype(may_mask)::value && j == ntiles - 1 && tail < S::BC)
+      valu_phase(BoolC<true>{}, tail);
+    else
+      valu_phase(BoolC<false>{}, S::BC);
+    phase_end();
+  };
+  // One whole tile j >= 1 in ring slot R.
+  auto full_tile = [&](auto r_, int j, auto may_mask) __attribute__((always_inline)) {
+    matrix_slot(BoolC<true>{}, BoolC<true>{}, r_, j);
+    phase_end();
+    vector_slot(j, may_mask);
+  };
+
+  // Prologue: tiles 0 and 1 resident before slot 0; group 1 sits out slot 0.
+  dma_tile(0, IntC<0>{});
+  if (ntiles > 1) dma_tile(1, IntC<1>{});
+  wait_vmem_below<0>();
+  __syncthreads();
+  if (grp == 1) phase_end();
+  matrix_slot(BoolC<false>{}, BoolC<true>{}, IntC<0>{}, 0);
+  phase_end();
+  vector_slot(0, BoolC<true>{});
+  // Tiles 1 .. ntiles - 1, four per iteration (ring slots 1, 2, 3, 0) while
+  // none of them is the last; then the remaining one to four.
+  int j = 1;
+  for (; j + 4 < ntiles; j += 4) {
+    full_tile(IntC<1>{}, j, BoolC<false>{});
+    full_tile(IntC<2>{}, j + 1, BoolC<false>{});
+    full_tile(IntC<3>{}, j + 2, BoolC<false>{});
+    full_tile(IntC<0>{}, j + 3, BoolC<false>{});
+  }
+  if (j < ntiles) full_tile(IntC<1>{}, j, BoolC<true>{});
+  if (j + 1 < ntiles) full_tile(IntC<2>{}, j + 1, BoolC<true>{});
+  if (j + 2 < ntiles) full_tile(IntC<3>{}, j + 2, BoolC<true>{});
+  if (j + 3 < ntiles) full_tile(IntC<0>{}, j + 3, BoolC<true>{});
+  // Last matrix phase: P V of tile ntiles - 1 (its V in ring slot (ntiles - 1) % NS).
+  switch ((ntiles - 1) % NS) {
+    case 0: matrix_slot(BoolC<true>{}, BoolC<false>{}, IntC<1>{}, ntiles); break;
+    case 1: matrix_slot(BoolC<true>{}, BoolC<false>{}, IntC<2>{}, ntiles); break;
+    case 2: matrix_slot(BoolC<true>{}, BoolC<false>{}, IntC<3>{}, ntiles); break;
+    default: matrix_slot(BoolC<true>{}, BoolC<false>{}, IntC<0>{}, ntiles); break;
+  }
+  if (grp == 0) phase_end();
+
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = halves_sum(l_run[qb]);
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int q = qw0 + qb * 32 + l32;
+    if (q < N) {
+      uint16_t* orow = O + head_off(so, bh, H) + q * so.n;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x16& a = oacc[qb][db];
+          u32x2 w = {E::pack(a[4 * jj] * inv, a[4 * jj + 1] * inv), E::pack(a[4 * jj + 2] * inv, a[4 * jj + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * jj + 4 * h) = w;
+        }
+      if (h == 0) LSE[(size_t)bh * N + q] = lt > 0.f ? (m_run[qb] + log2f(lt)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
 // fp32 forward: same method in fp32 storage and fp32 arithmetic (vector
 // ALU). One workgroup = 256 threads for 8 query rows; thread (r, t) with
 // r = tid / 32, t = tid % 32 scores keys t and t + 32 of each 64-key tile for
@@ -460,6 +806,19 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
 
 }  // namespace
 
+template <class E, int D, int QB, int KB>
+static hipError_t launch_fwd_pp(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                                int B, int H, int N, float scale, Strides sq, Strides so, hipStream_t stream) {
+  using S = FwdShape<D, QB, KB, kPPRing, kPPWaves>;
+  const int n_qblk = (N + S::BR - 1) / S::BR;
+  const int total = n_qblk * B * H;
+  const float c = fabsf(scale) * kLog2e;
+  const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
+  hipLaunchKernelGGL((fwd_pp_kernel<E, D, QB, KB>), dim3(total), dim3(S::THREADS), 0, stream, q, k, v, o, lse, N,
+                     n_qblk, total, c, qsign, H, sq, so);
+  return hipGetLastError();
+}
+
 template <class E, int D, int QB, int KB, int NS, int WAVES>
 static hipError_t launch_fwd_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                                     float* lse, int B, int H, int N, float scale, int causal, const int* kv_len,
@@ -485,6 +844,12 @@ static hipError_t launch_fwd_e(const uint16_t* q, const uint16_t* k, const uint1
                                int B, int H, int N, int d, float scale, int causal, const int* kv_len,
                                Strides sq, Strides so, hipStream_t stream) {
   const bool lng = N >= FWD_LONG_N;
+  if (FWD_PINGPONG && lng && !causal && !kv_len) {
+    if (FWD_PP_D64 && d == 64)
+      return launch_fwd_pp<E, 64, FWD_PP_QB64, FWD_PP_KB64>(q, k, v, o, lse, B, H, N, scale, sq, so, stream);
+    if (d == 128)
+      return launch_fwd_pp<E, 128, FWD_PP_QB128, FWD_PP_KB128>(q, k, v, o, lse, B, H, N, scale, sq, so, stream);
+  }
 #define ATTN_FWD(D, QB, KB, NS, W) \
   launch_fwd_t<E, D, QB, KB, NS, W>(q, k, v, o, lse, B, H, N, scale, causal, kv_len, sq, so, stream)
   switch (d) {
