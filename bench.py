@@ -97,6 +97,12 @@ def measured_traffic(workload: str, kernel: str):
     return None if k is None else int(k["traffic_bytes"])
 
 
+def fwd_kernel_name(N: int, d: int, causal: bool) -> str:
+    """The forward kernel the library launches for a bf16/fp16 shape without key padding: the ping-pong kernel
+    for unmasked rows of 1024 keys or more at d_k 128, the single-phase kernel otherwise."""
+    return "fwd_pp_kernel" if N >= 1024 and not causal and d == 128 else "fwd_kernel"
+
+
 def roofline_of(kernel: str, avg_ms: float, flops: float, nbytes: float, workload: str) -> dict:
     """The roofline object for one kernel: its bound follows from its algorithmic FLOP per algorithmic HBM byte
     (matrix cores at or above the machine balance 2516.6 TFLOP/s / 8 TB/s = 315, HBM below it)."""
@@ -409,7 +415,7 @@ def bench_proj(args, w) -> int:
               "fwd": 4 * E * sz + 4 * R, "bwd_prep": 2 * E * sz + 12 * R, "bwd_dkdv": 6 * E * sz + 8 * R,
               "bwd_dq": 5 * E * sz + 8 * R, "bwd_dkdv_dq": 7 * E * sz + 8 * R}
     kname_full = {"proj_fwd": "gemm256_kernel", "proj_bwd": "attn_qkv_proj_bwd (dx and dw products, split sums)",
-                  "fwd": "fwd_kernel", "bwd_prep": "bwd_prep_kernel", "bwd_dkdv": "bwd_dkdv_kernel",
+                  "fwd": fwd_kernel_name(N, d, False), "bwd_prep": "bwd_prep_kernel", "bwd_dkdv": "bwd_dkdv_kernel",
                   "bwd_dq": "bwd_dq_kernel", "bwd_dkdv_dq": "bwd_dkdv_dq_kernel"}
     # The roofline describes the longest single kernel (the projection backward is a group of launches).
     single = {kn: t for kn, t in kernels.items() if kn != "proj_bwd"}
@@ -643,7 +649,7 @@ def main(argv=None) -> int:
     E, R, sz = B * H * N * d, B * H * N, 2
     kbytes = {"fwd": 4 * E * sz + 4 * R, "bwd_prep": 2 * E * sz + 12 * R, "bwd_dkdv": 6 * E * sz + 8 * R,
               "bwd_dq": 5 * E * sz + 8 * R, "bwd_dkdv_dq": 7 * E * sz + 8 * R}
-    kname_full = {"fwd": "fwd_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel",
+    kname_full = {"fwd": fwd_kernel_name(N, d, cz), "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel",
                   "bwd_prep": "bwd_prep_kernel", "bwd_dkdv_dq": "bwd_dkdv_dq_kernel"}
     dominant = max(kernels, key=kernels.get)
     wkey = w.name + ("_causal" if cz else "") + ("_f16" if args.dtype == "f16" else "")

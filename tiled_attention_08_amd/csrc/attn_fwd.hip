@@ -62,12 +62,15 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units a row max may grow before O
 #ifndef FWD_NS_SHORT
 #define FWD_NS_SHORT 2
 #endif
-// Unmasked long rows (d = 64, 128) use the ping-pong kernel.
+// Unmasked long rows use the ping-pong kernel at d = 128. At d = 64 (FWD_PP_D64)
+// it measured 1.5 % faster than fwd_kernel but needs more than 256 registers
+// per lane outside its main loop, and those spills double its HBM traffic,
+// so d = 64 stays on fwd_kernel.
 #ifndef FWD_PINGPONG
 #define FWD_PINGPONG 1
 #endif
 #ifndef FWD_PP_D64
-#define FWD_PP_D64 1
+#define FWD_PP_D64 0
 #endif
 #ifndef FWD_PP_QB64
 #define FWD_PP_QB64 2
