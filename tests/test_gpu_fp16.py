@@ -34,6 +34,7 @@ def _kv(kv):
     (2, 2, 333, 64, True, [333, 120]), (1, 2, 1100, 64, False, None), (2, 1, 1100, 64, True, None),
     (1, 2, 129, 128, False, None), (2, 1, 517, 128, True, [517, 0]), (1, 1, 1030, 128, False, [700]),
     (2, 2, 200, 32, True, None), (1, 1, 1050, 96, False, None),
+    (1, 2, 1100, 128, False, None),  # the ping-pong forward (unmasked, N >= 1024, d = 128), ragged last tile
 ])
 def test_f16_fwd_bwd_parity(gpu_lib, B, H, N, d, causal, kv):
     import torch
