@@ -473,13 +473,25 @@ __device__ __forceinline__ void dq_body(unsigned char* smem, int work, const uin
   }
   __syncthreads();
 
+  // Per-lane byte offsets of the operand reads within a step tile: K and V
+  // rows l32 (chunk 2cc + h), and the transposing K reads of rows 4h + er
+  // (+ 8). The swizzle depends only on a row's low 4 bits, so the 16-row
+  // halves and the buffer are immediate offsets of the reads.
+  int koff[D / 16], toff[2][D / 32];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) koff[cc] = tile_off<S::ROWB>(l32, cc * 16 + h * 8);
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) toff[hi][db] = tile_off<S::ROWB>(4 * h + er + 8 * hi, db * 32 + dsub * 16 + 4 * qq);
+
   // One 32-key step. MASKED steps give probability 0 to each lane's keys at
   // or beyond klim(query) (keys past N or kv, keys after the query under the
   // causal mask). COMPUTE false: this wave sees no key of the step and only
-  // takes part in the DMA.
-  auto step = [&](int j, auto masked, bool compute) {
+  // takes part in the DMA. BUF (= j & 1) is a compile-time constant.
+  auto step = [&](int j, auto masked, bool compute, auto bufc) {
     constexpr bool MASKED = decltype(masked)::value;
-    const int buf = j & 1;
+    constexpr int buf = decltype(bufc)::value;
     if (j + 1 < ntiles) dma_step(j + 1, buf ^ 1);
     if (!compute) return;
     const unsigned char* Ks = smem + buf * 2 * S::TILEB;
@@ -494,9 +506,8 @@ __device__ __forceinline__ void dq_body(unsigned char* smem, int work, const uin
     }
 #pragma unroll
     for (int cc = 0; cc < D / 16; ++cc) {
-      const int off = tile_off<S::ROWB>(l32, cc * 16 + h * 8);
-      const u32x4 ak = lds_read_b128(Ks, off);
-      const u32x4 av = lds_read_b128(Vs, off);
+      const u32x4 ak = lds_read_b128(Ks, koff[cc]);
+      const u32x4 av = lds_read_b128(Vs, koff[cc]);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         sacc[qb] = E::mfma(ak, qf[qb][cc], sacc[qb]);
@@ -524,26 +535,37 @@ __device__ __forceinline__ void dq_body(unsigned char* smem, int work, const uin
     // ---- dQ^T += K^T dS^T (m = dim, n = query, k = key); K^T by transposing reads.
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
-      const int row0 = c2 * 16 + 4 * h + er;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const int col = db * 32 + dsub * 16 + 4 * qq;
-        const u32x4 a = cat(lds_read_tr16_b64(Ks, tile_off<S::ROWB>(row0, col)),
-                            lds_read_tr16_b64(Ks, tile_off<S::ROWB>(row0 + 8, col)));
+        const u32x4 a = cat(lds_read_tr16_b64(Ks, c2 * 16 * S::ROWB + toff[0][db]),
+                            lds_read_tr16_b64(Ks, c2 * 16 * S::ROWB + toff[1][db]));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) dqacc[qb][db] = E::mfma(a, dsb[qb][c2], dqacc[qb][db]);
       }
     }
   };
 
+  // Steps all queries see in full, two per iteration (buffers 0 and 1), then the rest.
   int j = 0;
-  for (; j < nfull; ++j) {
-    step(j, BoolC<false>{}, true);
+  for (; j + 1 < nfull; j += 2) {
+    step(j, BoolC<false>{}, true, IntC<0>{});
+    wait_vmem();
+    __syncthreads();
+    step(j + 1, BoolC<false>{}, true, IntC<1>{});
     wait_vmem();
     __syncthreads();
   }
+  if (j < nfull) {  // j even
+    step(j, BoolC<false>{}, true, IntC<0>{});
+    wait_vmem();
+    __syncthreads();
+    ++j;
+  }
   for (; j < ntiles; ++j) {
-    step(j, BoolC<true>{}, j < nvis_w);
+    if (j & 1)
+      step(j, BoolC<true>{}, j < nvis_w, IntC<1>{});
+    else
+      step(j, BoolC<true>{}, j < nvis_w, IntC<0>{});
     if (j + 1 < ntiles) {
       wait_vmem();
       __syncthreads();

@@ -122,6 +122,15 @@ __device__ __forceinline__ void wait_vmem_below() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Calls f(IntC<I>{}) for I = B .. E-1 in order (compile-time indices).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IntC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 template <class E, int D, int QB, int KB, int NS, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(FWD_WAVES_PER_EU, FWD_WAVES_PER_EU)))
 void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -217,9 +226,22 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
   // One K/V tile. MASKED tiles (the partial last tile, key padding, the
   // causal diagonal) drop each lane's invisible keys from the row max and give
   // them probability 0; fully visible tiles carry no masking code at all.
-  auto tile = [&](int j, auto masked) {
+  // Per-lane byte offsets of the operand reads within a tile for key block 0:
+  // K rows l32 (chunk 2cc + h) and the transposing V reads of rows 4h + er
+  // (+ 8). The swizzle depends only on a row's low 4 bits, so key blocks,
+  // 16-row halves and the ring slot (SLOT = j % NS, a compile-time constant)
+  // are immediate offsets of the reads.
+  int koff[D / 16], voff[2][D / 32];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) koff[cc] = tile_off<S::ROWB>(l32, cc * 16 + h * 8);
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) voff[hi][db] = tile_off<S::ROWB>(4 * h + er + 8 * hi, db * 32 + dsub * 16 + 4 * qq);
+  auto tile = [&](int j, auto masked, auto slot_c) {
     constexpr bool MASKED = decltype(masked)::value;
-    const unsigned char* Ks = smem + (j % NS) * 2 * S::TILEB;
+    constexpr int SLOT = decltype(slot_c)::value;
+    const unsigned char* Ks = smem + SLOT * 2 * S::TILEB;
     const unsigned char* Vs = Ks + S::TILEB;
     int kvalid[QB];  // visible keys of this tile, per row block (MASKED only)
 #pragma unroll
@@ -241,7 +263,7 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
       if (MASKED && kb >= kbv) continue;
 #pragma unroll
       for (int cc = 0; cc < D / 16; ++cc) {
-        const u32x4 a = lds_read_b128(Ks, tile_off<S::ROWB>(kb * 32 + l32, cc * 16 + h * 8));
+        const u32x4 a = lds_read_b128(Ks, kb * 32 * S::ROWB + koff[cc]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = E::mfma(a, qf[qb][cc], sacc[qb][kb]);
       }
@@ -327,10 +349,9 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
           if (MASKED && kb >= kbv) continue;
-          const int row0 = kb * 32 + c2 * 16 + 4 * h + er;
-          const int col = db * 32 + dsub * 16 + 4 * qq;
-          const u32x2 lo = lds_read_tr16_b64(Vs, tile_off<S::ROWB>(row0, col));
-          const u32x2 hi = lds_read_tr16_b64(Vs, tile_off<S::ROWB>(row0 + 8, col));
+          const int rows = (kb * 32 + c2 * 16) * S::ROWB;
+          const u32x2 lo = lds_read_tr16_b64(Vs, rows + voff[0][db]);
+          const u32x2 hi = lds_read_tr16_b64(Vs, rows + voff[1][db]);
           const u32x4 a = cat(lo, hi);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mfma(a, pb[qb][kb][c2], oacc[qb][db]);
@@ -340,16 +361,27 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
   // Tiles every query of the workgroup sees in full run one single-path
   // loop. In the rest each wave runs the masked tile or, past its last
   // visible key, nothing; all waves still take part in every DMA and barrier.
-  int j = 0;
-  for (; j < nfull_wg; ++j) {
+  // The single-path loop is unrolled by NS (tile j in ring slot j % NS).
+  auto full_tile = [&](int j, auto slot_c) __attribute__((always_inline)) {
     if (j + NS - 1 < ntiles) dma_tile(j + NS - 1);
-    tile(j, BoolC<false>{});
+    tile(j, BoolC<false>{}, slot_c);
     if (j + 1 < ntiles) wait_tile(j + 1);
     __syncthreads();
-  }
+  };
+  // Tile j with its ring slot as a compile-time constant.
+  auto with_slot = [&](int j, auto&& f) __attribute__((always_inline)) {
+    static_for<0, NS>([&](auto s_) __attribute__((always_inline)) {
+      if (j % NS == decltype(s_)::value) f(s_);
+    });
+  };
+  int j = 0;
+  for (; j + NS <= nfull_wg; j += NS)
+    static_for<0, NS>([&](auto s_) __attribute__((always_inline)) { full_tile(j + decltype(s_)::value, s_); });
+  for (; j < nfull_wg; ++j) with_slot(j, [&](auto s_) __attribute__((always_inline)) { full_tile(j, s_); });
   for (; j < ntiles; ++j) {
     if (j + NS - 1 < ntiles) dma_tile(j + NS - 1);
-    if (j < nvis_w) tile(j, BoolC<true>{});  // masks are no-ops on the tiles this wave sees in full
+    if (j < nvis_w)  // masks are no-ops on the tiles this wave sees in full
+      with_slot(j, [&](auto s_) __attribute__((always_inline)) { tile(j, BoolC<true>{}, s_); });
     if (j + 1 < ntiles) {
       wait_tile(j + 1);
       __syncthreads();
@@ -402,15 +434,6 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
 // Only raw s_barrier is used between phases: a fence would wait for the
 // tiles in flight.
 // ------------------------------------------------------------------------
-// Calls f(IntC<I>{}) for I = B .. E-1 in order (compile-time indices).
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(IntC<B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
 constexpr int kPPWaves = 8;
 constexpr int kPPRing = 4;
 
