@@ -113,6 +113,29 @@ __device__ __forceinline__ float fmax3(float a, float b, float c) {
   return __builtin_elementwise_maximum(a, __builtin_elementwise_maximum(b, c));
 }
 
+// Maximum of N values as a tree of three-operand maxima over distinct operands
+// (about (N - 1) / 2 instructions). Written as a running chain
+// max(m, max(a, b)), the compiler re-associates it into three instructions
+// per four values.
+template <int N>
+__device__ __forceinline__ float max_tree(const float* x) {
+  if constexpr (N == 1) {
+    return x[0];
+  } else if constexpr (N == 2) {
+    return fmax2(x[0], x[1]);
+  } else if constexpr (N == 3) {
+    return fmax3(x[0], x[1], x[2]);
+  } else {
+    constexpr int G = (N + 2) / 3;
+    float y[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      y[g] = 3 * g + 2 < N ? fmax3(x[3 * g], x[3 * g + 1], x[3 * g + 2])
+                           : (3 * g + 1 < N ? fmax2(x[3 * g], x[3 * g + 1]) : x[3 * g]);
+    return max_tree<G>(y);
+  }
+}
+
 // max / sum of x over lanes l and l ^ 32.
 __device__ __forceinline__ float halves_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -292,14 +292,25 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       // NaN-propagating maximum (v_maximum3_f32): no canonicalisation of the
-      // MFMA results is needed, unlike fmaxf.
-      float mx = sacc[qb][0][0];
+      // MFMA results is needed, unlike fmaxf. Masked tiles skip the key blocks
+      // they did not compute (their accumulators hold zeros).
+      float mx;
+      if (!MASKED) {
+        float xs[KB * 16];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        if (MASKED && kb >= kbv) continue;
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int e = (kb == 0 ? 1 : 0); e < 16; e += 2)
-          mx = (e + 1 < 16) ? fmax3(mx, sacc[qb][kb][e], sacc[qb][kb][e + 1]) : fmax2(mx, sacc[qb][kb][e]);
+          for (int e = 0; e < 16; ++e) xs[kb * 16 + e] = sacc[qb][kb][e];
+        mx = max_tree<KB * 16>(xs);
+      } else {
+        mx = sacc[qb][0][0];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          if (kb >= kbv) continue;
+#pragma unroll
+          for (int e = (kb == 0 ? 1 : 0); e < 16; e += 2)
+            mx = (e + 1 < 16) ? fmax3(mx, sacc[qb][kb][e], sacc[qb][kb][e + 1]) : fmax2(mx, sacc[qb][kb][e]);
+        }
       }
       mx = halves_max(mx) * c;
       mnew[qb] = fmaxf(m_run[qb], mx);
@@ -608,6 +619,8 @@ void fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     bool need = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
+      // (A running chain here: the three-operand tree of fwd_kernel measured
+      // 2 % slower in this kernel at d = 128.)
       float mx = sacc[qb][0][0];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -878,8 +891,10 @@ static hipError_t launch_fwd_e(const uint16_t* q, const uint16_t* k, const uint1
                                Strides sq, Strides so, hipStream_t stream) {
   const bool lng = N >= FWD_LONG_N;
   if (FWD_PINGPONG && lng && !causal && !kv_len) {
-    if (FWD_PP_D64 && d == 64)
+#if FWD_PP_D64
+    if (d == 64)
       return launch_fwd_pp<E, 64, FWD_PP_QB64, FWD_PP_KB64>(q, k, v, o, lse, B, H, N, scale, sq, so, stream);
+#endif
     if (d == 128)
       return launch_fwd_pp<E, 128, FWD_PP_QB128, FWD_PP_KB128>(q, k, v, o, lse, B, H, N, scale, sq, so, stream);
   }
