@@ -49,6 +49,10 @@ constexpr int kThreads = 256;
 #ifndef BWD_KBW64
 #define BWD_KBW64 1
 #endif
+// dQ kernel at d_k <= 64: 32-query blocks per wave (256 or 128 queries per workgroup).
+#ifndef BWD_DQ_QB64
+#define BWD_DQ_QB64 2
+#endif
 constexpr int BCQ = 32;                  // dQ kernel: keys per step
 
 #ifndef BWD_WAVES_PER_EU
@@ -837,7 +841,7 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
     hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, MB, KBW>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, ndelta,
                        dk, dv, N, n_kblk, total, c, scale, kv_len, H, causal, st[0], st[2], st[3]);
   } else {
-    constexpr int QB = D <= 64 ? 2 : 1;
+    constexpr int QB = D <= 64 ? BWD_DQ_QB64 : 1;
     constexpr int BR = DqShape<D, QB>::BR;
     const int n_qblk = (N + BR - 1) / BR;
     const int total = n_qblk * B * H;
