@@ -12,8 +12,10 @@ from .attention import (  # noqa: F401
     attention_probs,
     attention_fwd,
     attention_bwd,
+    attention_ds,
     brute_attention_fwd,
     brute_attention_grads_fd,
 )
-from .masked import masked_attention_bwd, masked_attention_fwd, visible_keys  # noqa: F401
+from .masked import (masked_attention_bwd, masked_attention_dq_rows, masked_attention_ds,  # noqa: F401
+                     masked_attention_fwd, visible_keys)
 from .projection import brute_qkv_projection, qkv_projection, qkv_projection_bwd, split_qkv  # noqa: F401

@@ -50,6 +50,7 @@ __all__ = [
     "attention_probs",
     "attention_fwd",
     "attention_bwd",
+    "attention_ds",
     "brute_attention_fwd",
     "brute_attention_grads_fd",
 ]
@@ -132,14 +133,31 @@ def attention_bwd(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
     dk = np.empty_like(kh)
     dv = np.empty_like(vh)
     for h in range(qh.shape[0]):
-        p, _ = _head_probs(qh[h], kh[h], scale)
+        p, ds = _head_ds(qh[h], kh[h], vh[h], doh[h], scale)
         dv[h] = p.T @ doh[h]                                   # dL/dV
-        dp = doh[h] @ vh[h].T                                  # dL/dP
-        rowdot = (p * dp).sum(axis=1, keepdims=True)           # sum_k P_ik dP_ik
-        ds = p * (dp - rowdot)                                 # through the row softmax
         dq[h] = scale * (ds @ kh[h])                           # through the scores
         dk[h] = scale * (ds.T @ qh[h])
     return dq.reshape(q.shape), dk.reshape(k.shape), dv.reshape(v.shape)
+
+
+def _head_ds(q, k, v, do, scale):
+    """One head: P and dS = dL/dS, the gradient with respect to the scaled scores (before the scale's chain
+    rule): dP = dO V^T, dS = P * (dP - rowsum(P * dP)), the Jacobian-vector product of the row softmax."""
+    p, _ = _head_probs(q, k, scale)
+    dp = do @ v.T                                              # dL/dP
+    rowdot = (p * dp).sum(axis=1, keepdims=True)               # sum_k P_ik dP_ik
+    return p, p * (dp - rowdot)                                # through the row softmax
+
+
+def attention_ds(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, scale: float) -> np.ndarray:
+    """dS [..., M, N] of attention_bwd (dQ = scale dS K, dK = scale dS^T Q), per head."""
+    q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
+    _check(q, k, v)
+    qh, kh, vh, doh = _heads(q), _heads(k), _heads(v), _heads(do)
+    out = np.empty((qh.shape[0], qh.shape[1], kh.shape[1]), dtype=np.float64)
+    for h in range(qh.shape[0]):
+        out[h] = _head_ds(qh[h], kh[h], vh[h], doh[h], scale)[1]
+    return out.reshape(q.shape[:-1] + (k.shape[-2],))
 
 
 # ----------------------------------------------------------------------------

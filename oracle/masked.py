@@ -25,7 +25,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["visible_keys", "masked_attention_fwd", "masked_attention_bwd"]
+__all__ = ["visible_keys", "masked_attention_fwd", "masked_attention_bwd", "masked_attention_dq_rows",
+           "masked_attention_ds"]
 
 
 def visible_keys(N: int, q_index, causal: bool, kv_len_b: int) -> np.ndarray:
@@ -101,3 +102,45 @@ def masked_attention_bwd(q, k, v, do, scale: float, causal: bool = False, kv_len
             dq[b, h] = scale * (ds @ k[b, h])
             dk[b, h] = scale * (ds.T @ q[b, h])
     return dq, dk, dv
+
+
+def masked_attention_dq_rows(q, k, v, do, scale: float, causal: bool = False, kv_len=None, q_index=None):
+    """dQ of the M query rows given (at sequence positions q_index), for the loss sum(O * dO) over those rows.
+
+    Row i of dQ depends on row i alone: dS_i = P_i * (dP_i - sum_j P_ij dP_ij) with dP_i = dO_i V^T, and
+    dQ_i = scale dS_i K (the same calculus as masked_attention_bwd, restricted to the given rows), so a few
+    rows of a long sequence can be checked without the full N x N matrices. q, do: [B, H, M, d]; k, v:
+    [B, H, N, d]."""
+    q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
+    B, H, M, _ = q.shape
+    N = k.shape[2]
+    qi = np.arange(M) if q_index is None else np.asarray(q_index)
+    kv = _lengths(B, N, kv_len)
+    dq = np.empty_like(q)
+    for b in range(B):
+        vis = visible_keys(N, qi, causal, kv[b])
+        for h in range(H):
+            p, _ = _masked_probs(q[b, h], k[b, h], scale, vis)
+            dp = do[b, h] @ v[b, h].T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            dq[b, h] = scale * (ds @ k[b, h])
+    return dq
+
+
+def masked_attention_ds(q, k, v, do, scale: float, causal: bool = False, kv_len=None):
+    """dS [B, H, N, N] of masked_attention_bwd (dQ = scale dS K, dK = scale dS^T Q): the gradient with respect to
+    the scaled scores, 0 on masked pairs."""
+    q, k, v, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, do))
+    B, H, M, _ = q.shape
+    N = k.shape[2]
+    if M != N:
+        raise ValueError("dS takes every query row of the sequence")
+    kv = _lengths(B, N, kv_len)
+    out = np.empty((B, H, M, N))
+    for b in range(B):
+        vis = visible_keys(N, np.arange(M), causal, kv[b])
+        for h in range(H):
+            p, _ = _masked_probs(q[b, h], k[b, h], scale, vis)
+            dp = do[b, h] @ v[b, h].T
+            out[b, h] = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+    return out

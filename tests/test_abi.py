@@ -261,3 +261,38 @@ def test_c99_caller(tmp_path, L):
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     assert "all checks passed" in r.stdout
+
+
+def test_binding_refuses_host_tensors(L, monkeypatch):
+    """Every wrapper checks that its tensor arguments are GPU tensors before it reaches the C ABI: a host pointer
+    handed to a kernel would fault the GPU. Host tensors here raise ValueError, and the library is never called."""
+    import torch
+
+    class NoLib:
+        def __getattr__(self, name):
+            raise AssertionError(f"libattn.{name} reached with a host tensor")
+
+    monkeypatch.setattr(L, "lib", NoLib())
+    B, H, N, d = 1, 2, 8, 64
+    t = torch.zeros((B, H, N, d), dtype=torch.bfloat16)
+    lse = torch.zeros((B, H, N), dtype=torch.float32)
+    ws = torch.zeros(4096, dtype=torch.uint8)
+    f32 = torch.zeros((B, H, N, d), dtype=torch.float32)
+    x = torch.zeros((B, N, 128), dtype=torch.bfloat16)
+    w = torch.zeros((128, 3, H, d), dtype=torch.bfloat16)
+    qkv = torch.zeros((B, N, 3, H, d), dtype=torch.bfloat16)
+    calls = [
+        lambda: L.attn_fwd(t, t, t, t, lse, 0.125),
+        lambda: L.attn_fwd_ex(t, t, t, t, lse, 0.125, causal=True),
+        lambda: L.attn_fwd_f32(f32, f32, f32, f32, lse, 0.125),
+        lambda: L.attn_bwd(t, t, t, t, lse, t, t, t, t, 0.125, ws),
+        lambda: L.attn_bwd_f32(f32, f32, f32, f32, lse, f32, f32, f32, f32, 0.125, ws),
+        lambda: L.attn_bwd_ex(t, t, t, t, lse, t, t, t, t, 0.125, ws),
+        lambda: L.attn_bwd_stage(1, t, t, t, t, lse, t, t, t, t, 0.125, ws),
+        lambda: L.attn_qkv_proj(x, w, qkv),
+        lambda: L.attn_qkv_proj_bwd(x, w, qkv, x, w, None),
+        lambda: L.forward(t, t, t, 0.125),
+    ]
+    for call in calls:
+        with pytest.raises(ValueError, match="GPU tensors"):
+            call()

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 from attn_inputs import make_case
-from gpu_helpers import TOL_BF16_O, TOL_F16_LSE_REL, TOL_GRAD_RELL2, lse_err, max_abs, rel_l2, to_device, to_f64
+from gpu_helpers import TOL_BF16_O, TOL_GRAD_RELL2, check_lse, max_abs, rel_l2, to_device, to_f64
 from oracle import attention_bwd, attention_fwd, masked_attention_bwd, masked_attention_fwd
 
 pytestmark = pytest.mark.gpu
@@ -53,7 +53,7 @@ def test_f16_fwd_bwd_parity(gpu_lib, B, H, N, d, causal, kv):
     e_o = max_abs(go, ro)
     _say(f"  O max-abs {e_o:.3e}")
     assert e_o <= TOL_BF16_O
-    assert lse_err(gl[~empty], rl[~empty]) <= TOL_F16_LSE_REL
+    _say(f"  lse error / bound {check_lse(gl, rl, Q, K, x.scale, 'f16'):.3f}")
     ref = masked_attention_bwd(Q, K, V, DO, x.scale, causal=causal, kv_len=kv)
     for name, got, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         e = rel_l2(to_f64(got), r)
@@ -93,6 +93,6 @@ def test_f16_long_sequence_sampled_heads(gpu_lib):
         Q, K, V, DO = (x.f64(n, (b, h)) for n in ("q", "k", "v", "do"))
         ro, rl = attention_fwd(Q, K, V, x.scale)
         assert max_abs(to_f64(o[b, h]), ro) <= TOL_BF16_O
-        assert lse_err(to_f64(lse[b, h]), rl) <= TOL_F16_LSE_REL
+        check_lse(to_f64(lse[b, h]), rl, Q, K, x.scale, "f16")
         for got, r in zip((dq, dk, dv), attention_bwd(Q, K, V, DO, x.scale)):
             assert rel_l2(to_f64(got[b, h]), r) <= TOL_GRAD_RELL2

@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 from attn_inputs import make_case
-from gpu_helpers import TOL_BF16_LSE_REL, TOL_BF16_O, TOL_GRAD_RELL2, lse_err, max_abs, rel_l2, to_device, to_f64
+from gpu_helpers import TOL_BF16_O, TOL_GRAD_RELL2, check_lse, max_abs, rel_l2, to_device, to_f64
 from oracle import masked_attention_bwd, masked_attention_fwd
 
 pytestmark = pytest.mark.gpu
@@ -48,12 +48,12 @@ def _run(gpu_lib, x, causal, kv, bwd=True):
     return {n: to_f64(t) for n, t in out.items()}
 
 
-def _check_fwd(got_o, got_lse, ro, rl):
+def _check_fwd(got_o, got_lse, ro, rl, Q, K, scale):
     empty = np.isneginf(rl)
     assert np.array_equal(np.isneginf(got_lse), empty), "rows with no visible key must give lse = -inf"
     assert np.all(got_o[empty] == 0)
     assert max_abs(got_o, ro) <= TOL_BF16_O
-    assert lse_err(got_lse[~empty], rl[~empty]) <= TOL_BF16_LSE_REL
+    check_lse(got_lse, rl, Q, K, scale, "bf16")
 
 
 def _check_grads(got, ref, kv):
@@ -100,7 +100,7 @@ def test_masked_fwd_bwd_parity(gpu_lib, B, H, N, d, causal, kv):
     got = _run(gpu_lib, x, causal, kv)
     Q, K, V, DO = x.f64("q"), x.f64("k"), x.f64("v"), x.f64("do")
     ro, rl = masked_attention_fwd(Q, K, V, x.scale, causal=causal, kv_len=kv)
-    _check_fwd(got["o"], got["lse"], ro, rl)
+    _check_fwd(got["o"], got["lse"], ro, rl, Q, K, x.scale)
     _check_grads(got, masked_attention_bwd(Q, K, V, DO, x.scale, causal=causal, kv_len=kv), kv)
 
 
@@ -128,7 +128,7 @@ def test_out_of_range_kv_len_is_clamped(gpu_lib):
     x = make_case(2, 1, 150, 64, "bf16", seed=32, with_grad=False)
     got = _run(gpu_lib, x, False, [-5, 10 ** 6], bwd=False)
     ro, rl = masked_attention_fwd(x.f64("q"), x.f64("k"), x.f64("v"), x.scale, kv_len=[0, 150])
-    _check_fwd(got["o"], got["lse"], ro, rl)
+    _check_fwd(got["o"], got["lse"], ro, rl, x.f64("q"), x.f64("k"), x.scale)
     del torch
 
 
@@ -155,7 +155,7 @@ def test_long_sequence_masked_sampled_heads(gpu_lib, causal, kv):
         Q, K, V, DO = (_head(x, n, b, h) for n in ("q", "k", "v", "do"))
         kvb = None if kv is None else [kv[b]]
         ro, rl = masked_attention_fwd(Q, K, V, x.scale, causal=causal, kv_len=kvb)
-        _check_fwd(got["o"][b:b + 1, h:h + 1], got["lse"][b:b + 1, h:h + 1], ro, rl)
+        _check_fwd(got["o"][b:b + 1, h:h + 1], got["lse"][b:b + 1, h:h + 1], ro, rl, Q, K, x.scale)
         ref = masked_attention_bwd(Q, K, V, DO, x.scale, causal=causal, kv_len=kvb)
         _check_grads({n: got[n][b:b + 1, h:h + 1] for n in ("dq", "dk", "dv")}, ref, kvb)
     if kv is not None and 0 in kv:
@@ -174,4 +174,4 @@ def test_very_long_causal_forward_sampled_rows(gpu_lib):
         Q = x.f64("q", (b, h))[rows][None, None]
         K, V = _head(x, "k", b, h), _head(x, "v", b, h)
         ro, rl = masked_attention_fwd(Q, K, V, x.scale, causal=True, q_index=rows)
-        _check_fwd(got["o"][b, h][rows][None, None], got["lse"][b, h][rows][None, None], ro, rl)
+        _check_fwd(got["o"][b, h][rows][None, None], got["lse"][b, h][rows][None, None], ro, rl, Q, K, x.scale)

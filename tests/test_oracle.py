@@ -15,7 +15,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import (attention_bwd, attention_fwd, attention_probs, brute_attention_fwd,
+from oracle import (attention_bwd, attention_ds, attention_fwd, attention_probs, brute_attention_fwd,
                     brute_attention_grads_fd)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_2x2.json")
@@ -64,6 +64,20 @@ def test_gradients_match_finite_differences(M, N, d):
     fq, fk, fv = brute_attention_grads_fd(q, k, v, do, scale)
     for a, f in ((dq, fq), (dk, fk), (dv, fv)):
         np.testing.assert_allclose(a, f, rtol=1e-6, atol=1e-8)
+
+
+@pytest.mark.parametrize("N", [2, 3])
+def test_score_gradient_from_finite_differences(N):
+    """dS (the gradient with respect to the scaled scores) against finite differences: with N = d keys and an
+    invertible K, dQ = scale dS K fixes dS = dQ_fd K^-1 / scale from the brute-force differences alone. Its rows
+    sum to 0 (the softmax ignores a common shift of a row)."""
+    rng = np.random.default_rng(70 + N)
+    M, d, scale = 3, N, 0.7
+    q, k, v, do = _rand(rng, M, d), _rand(rng, N, d), _rand(rng, N, 2), _rand(rng, M, 2)
+    fq, _, _ = brute_attention_grads_fd(q, k, v, do, scale)
+    ds = attention_ds(q, k, v, do, scale)
+    np.testing.assert_allclose(ds, fq @ np.linalg.inv(k) / scale, rtol=1e-5, atol=1e-8)
+    np.testing.assert_allclose(ds.sum(axis=1), 0.0, atol=1e-14)
 
 
 def test_torch_cpu_fp64_cross_check():

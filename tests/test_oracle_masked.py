@@ -14,7 +14,8 @@ import numpy as np
 import pytest
 
 from oracle import (attention_bwd, attention_fwd, brute_attention_fwd, brute_attention_grads_fd,
-                    masked_attention_bwd, masked_attention_fwd, visible_keys)
+                    masked_attention_bwd, masked_attention_dq_rows, masked_attention_ds, masked_attention_fwd,
+                    visible_keys)
 
 
 def _r(rng, *shape, s=1.0):
@@ -135,6 +136,50 @@ def test_sampled_rows_match_full_rows():
     o2, lse2 = masked_attention_fwd(q[:, :, rows], k, v, 0.5, causal=True, kv_len=[30, 40], q_index=rows)
     np.testing.assert_array_equal(o2, o[:, :, rows])
     np.testing.assert_array_equal(lse2, lse[:, :, rows])
+
+
+@pytest.mark.parametrize("causal,kv", [(True, None), (False, [25, 40]), (True, [30, 7])])
+def test_dq_rows_match_full_backward(causal, kv):
+    """dQ of sampled rows at their sequence positions equals those rows of the full masked backward (itself pinned
+    by finite differences), including rows with no visible key (dQ = 0)."""
+    rng = np.random.default_rng(48)
+    q, k, v, do = (_r(rng, 2, 2, 40, 4) for _ in range(4))
+    dq = masked_attention_bwd(q, k, v, do, 0.45, causal=causal, kv_len=kv)[0]
+    rows = np.array([0, 1, 6, 7, 24, 25, 39])
+    got = masked_attention_dq_rows(q[:, :, rows], k, v, do[:, :, rows], 0.45, causal=causal, kv_len=kv,
+                                   q_index=rows)
+    np.testing.assert_allclose(got, dq[:, :, rows], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("causal,kv", [(True, None), (False, [2]), (True, [3])])
+def test_masked_score_gradient_from_finite_differences(causal, kv):
+    """dS against finite differences: with N = d keys and an invertible K, dQ = scale dS K fixes
+    dS = dQ_fd K^-1 / scale from brute-force differences alone; 0 on masked pairs."""
+    rng = np.random.default_rng(50)
+    N = d = 3
+    q, k, v, do = (_r(rng, 1, 1, N, d) for _ in range(4))
+    vis = visible_keys(N, np.arange(N), causal, N if kv is None else kv[0])
+    fq, _, _ = brute_attention_grads_fd(q[0, 0], k[0, 0], v[0, 0], do[0, 0], 0.6, allowed=vis.tolist())
+    ds = masked_attention_ds(q, k, v, do, 0.6, causal=causal, kv_len=kv)[0, 0]
+    np.testing.assert_allclose(ds, fq @ np.linalg.inv(k[0, 0]) / 0.6, rtol=1e-5, atol=1e-8)
+    assert np.all(ds[~vis] == 0)
+
+
+def test_dq_rows_match_finite_differences():
+    """The per-row dQ against central differences of sum(O * dO) over the given rows (causal, tiny case)."""
+    rng = np.random.default_rng(49)
+    N, d, rows = 6, 3, np.array([1, 4])
+    q, k, v, do = (_r(rng, 1, 1, N, d) for _ in range(4))
+    got = masked_attention_dq_rows(q[:, :, rows], k, v, do[:, :, rows], 0.8, causal=True, q_index=rows)
+    h = 1e-6
+    for r, i in enumerate(rows):
+        for c in range(d):
+            qp, qm = q.copy(), q.copy()
+            qp[0, 0, i, c] += h
+            qm[0, 0, i, c] -= h
+            fp = (masked_attention_fwd(qp, k, v, 0.8, causal=True)[0][0, 0, rows] * do[0, 0, rows]).sum()
+            fm = (masked_attention_fwd(qm, k, v, 0.8, causal=True)[0][0, 0, rows] * do[0, 0, rows]).sum()
+            assert abs(got[0, 0, r, c] - (fp - fm) / (2 * h)) <= 1e-7
 
 
 def test_torch_cpu_fp64_masked_cross_check():

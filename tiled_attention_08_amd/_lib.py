@@ -94,6 +94,21 @@ def _stream(stream) -> Optional[int]:
     return int(stream)
 
 
+def _on_gpu(*ts) -> None:
+    """Every tensor argument must be in GPU memory, all on one device (a host pointer reaching a kernel would fault
+    the GPU). Checked before anything is launched; None (an absent optional buffer) is skipped."""
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"tensor arguments must be GPU tensors (got one on {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensor arguments must share one device ({t.device} vs {dev})")
+
+
 def _shape(q, *others):
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d_k]")
@@ -168,6 +183,7 @@ def _check_kv_len(kv_len, B):
 def attn_fwd(q, k, v, o, lse, scale: float, stream=None) -> None:
     """bf16 forward into caller-provided ``o`` (bf16 [B,H,N,d]) and ``lse`` (float32 [B,H,N])."""
     import torch
+    _on_gpu(q, k, v, o, lse)
     B, H, N, d = _shape(q, k, v, o)
     if q.dtype != torch.bfloat16:
         raise ValueError("attn_fwd takes bfloat16 tensors")
@@ -179,6 +195,7 @@ def attn_fwd_ex(q, k, v, o, lse, scale: float, causal: bool = False, kv_len=None
                 layout: str = "bhnd") -> None:
     """Forward with masks and layouts: ``causal`` (query i sees keys j <= i), ``kv_len`` (int32 [B] device tensor
     of valid keys), ``layout`` "bhnd", "bnhd" or "qkv_packed" (see ``_dims``)."""
+    _on_gpu(q, k, v, o, lse, kv_len)
     B, H, N, d = _dims(layout, (q, k, v), (o,))
     _check_lse(lse, B, H, N)
     _check_kv_len(kv_len, B)
@@ -189,6 +206,7 @@ def attn_fwd_ex(q, k, v, o, lse, scale: float, causal: bool = False, kv_len=None
 def attn_fwd_f32(q, k, v, o, lse, scale: float, stream=None) -> None:
     """float32 forward into caller-provided ``o`` (float32 [B,H,N,d]) and ``lse``."""
     import torch
+    _on_gpu(q, k, v, o, lse)
     B, H, N, d = _shape(q, k, v, o)
     if q.dtype != torch.float32:
         raise ValueError("attn_fwd_f32 takes float32 tensors")
@@ -209,6 +227,7 @@ def attn_bwd_workspace_bytes(B: int, H: int, N: int, d_k: int) -> int:
 def attn_bwd(q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, stream=None) -> None:
     """bf16 backward into caller-provided ``dq``, ``dk``, ``dv``; ``workspace`` is a uint8 device tensor."""
     import torch
+    _on_gpu(q, k, v, o, lse, do, dq, dk, dv, workspace)
     B, H, N, d = _shape(q, k, v, o, do, dq, dk, dv)
     if q.dtype != torch.bfloat16:
         raise ValueError("attn_bwd takes bfloat16 tensors")
@@ -221,6 +240,7 @@ def attn_bwd(q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, stream=No
 def attn_bwd_f32(q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, stream=None) -> None:
     """float32 backward into caller-provided ``dq``, ``dk``, ``dv`` (float32 [B,H,N,d])."""
     import torch
+    _on_gpu(q, k, v, o, lse, do, dq, dk, dv, workspace)
     B, H, N, d = _shape(q, k, v, o, do, dq, dk, dv)
     if q.dtype != torch.float32:
         raise ValueError("attn_bwd_f32 takes float32 tensors")
@@ -233,6 +253,7 @@ def attn_bwd_f32(q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, strea
 def attn_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, causal: bool = False, kv_len=None,
                 stream=None, layout: str = "bhnd") -> None:
     """Backward with the masks and layout of attn_fwd_ex (which must match the forward's)."""
+    _on_gpu(q, k, v, o, lse, do, dq, dk, dv, kv_len, workspace)
     B, H, N, d = _dims(layout, (q, k, v), (o, do))
     _dims(layout, (dq, dk, dv))
     _check_lse(lse, B, H, N)
@@ -246,6 +267,7 @@ def attn_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, causal
 def attn_bwd_stage(stage: int, q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, causal: bool = False,
                    kv_len=None, stream=None, layout: str = "bhnd") -> None:
     """One stage (0 prep, 1 dK/dV, 2 dQ, 3 = 1 and 2 as attn_bwd_ex runs them) of attn_bwd_ex; same arguments."""
+    _on_gpu(q, k, v, o, lse, do, dq, dk, dv, kv_len, workspace)
     B, H, N, d = _dims(layout, (q, k, v), (o, do))
     _dims(layout, (dq, dk, dv))
     _check_lse(lse, B, H, N)
@@ -273,6 +295,7 @@ def _check_packed(t, B, N, H, d, dtype, what):
 
 def attn_qkv_proj(x, w, qkv, stream=None) -> None:
     """qkv[b, n, t, h, :] = sum over c of x[b, n, c] w[c, t, h, :] (t = 0, 1, 2: Q, K, V)."""
+    _on_gpu(x, w, qkv)
     B, N, D, H, d = _proj_dims(x, w)
     _check_packed(qkv, B, N, H, d, x.dtype, "qkv")
     _check(lib.attn_qkv_proj(_dtype_code(x), _ptr(x), _ptr(w), _ptr(qkv), B, N, D, H, d, _stream(stream)))
@@ -285,6 +308,7 @@ def attn_qkv_proj_bwd_workspace_bytes(B: int, N: int, D: int, H: int, d_k: int) 
 def attn_qkv_proj_bwd(x, w, dqkv, dx, dw, workspace, stream=None) -> None:
     """dx = dqkv W^T per token; dw = X^T dqkv over all tokens. ``workspace``: a device buffer of at least
     attn_qkv_proj_bwd_workspace_bytes(...) bytes (None when that is 0)."""
+    _on_gpu(x, w, dqkv, dx, dw, workspace)
     B, N, D, H, d = _proj_dims(x, w)
     _check_packed(dqkv, B, N, H, d, x.dtype, "dqkv")
     if tuple(dx.shape) != tuple(x.shape) or tuple(dw.shape) != tuple(w.shape):

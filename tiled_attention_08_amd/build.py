@@ -45,19 +45,25 @@ def build(verbose: bool = False, asm: bool = False) -> str:
     cc = hipcc()
     objdir = os.path.join(ROOT, "_build", "obj")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
+    jobs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".hip", ".o"))
-        cmd = [cc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
-        objs.append(obj)
+        jobs.append(([cc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj], obj))
         if asm:
             asmdir = os.path.join(ROOT, "_build", "asm")
             os.makedirs(asmdir, exist_ok=True)
-            subprocess.run([cc, *flags(), "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o",
-                            os.path.join(asmdir, src.replace(".hip", f"-{ARCH}.s"))], check=True)
+            jobs.append(([cc, *flags(), "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o",
+                          os.path.join(asmdir, src.replace(".hip", f"-{ARCH}.s"))], None))
+    # The translation units are independent: compile them side by side.
+    procs = []
+    for cmd, _ in jobs:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd))
+    failed = [" ".join(cmd) for (cmd, _), p in zip(jobs, procs) if p.wait() != 0]
+    if failed:
+        raise RuntimeError("compilation failed: " + "; ".join(failed))
+    objs = [obj for _, obj in jobs if obj is not None]
     tmp = LIB + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
