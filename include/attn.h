@@ -198,6 +198,24 @@ int attn_bwd_stage(int stage, int dtype, int layout, const void* q, const void* 
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * attn_bwd_ex without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). The workspace is a 16 MiB array inside the library
+ * (one per GPU, reserved when the library's code is loaded on that GPU and
+ * held until the process ends); the call itself allocates nothing. Same
+ * arguments, checks, kernels and results (bit for bit) as attn_bwd_ex.
+ * Limit: attn_bwd_workspace_bytes(B, H, N, d_k) <= 16 MiB (8 bytes per row
+ * of B H N, so about 2 million rows), else ATTN_ERR_WORKSPACE. Every call on
+ * one GPU shares that GPU's array: calls that may overlap in time on one GPU
+ * (concurrent streams, several host threads) race and must be serialised by
+ * the caller. Returns ATTN_ERR_HIP if the array's device address cannot be
+ * obtained.
+ */
+int attn_bwd_ex_noalloc(int dtype, int layout, const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                        int B, int H, int N, int d_k, float scale, int causal, const int* kv_len, void* stream);
+
+/*
  * 1 when attn_bwd / attn_bwd_ex run the dK/dV and dQ work of this shape as
  * one launch (stage 3), 0 when they launch it as stages 1 and 2 (or the shape
  * is rejected). Depends on the shape only: d_k <= 64 and a small dK/dV grid

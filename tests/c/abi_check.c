@@ -51,6 +51,10 @@ int main(void) {
   expect(attn_bwd_stage(4, ATTN_DTYPE_BF16, ATTN_LAYOUT_BHND, addr(0), addr(1), addr(2), addr(3), (const float*)addr(4),
                         addr(5), addr(6), addr(7), addr(8), B, H, N, d, 0.125f, 0, NULL, addr(9), ws, NULL),
          ATTN_ERR_INVALID_ARG, "bwd stage 4");
+  expect(attn_bwd_ex_noalloc(ATTN_DTYPE_BF16, ATTN_LAYOUT_BHND, addr(0), addr(1), addr(2), addr(3),
+                             (const float*)addr(4), addr(5), addr(6), addr(7), addr(8), 8, 16, 16448, d, 0.125f, 0,
+                             NULL, NULL),
+         ATTN_ERR_WORKSPACE, "bwd_ex_noalloc beyond its 16 MiB workspace");
   expect(attn_bwd_f32((const float*)addr(0), (const float*)addr(1), (const float*)addr(2), (const float*)addr(3),
                       (const float*)addr(4), (const float*)addr(5), (float*)addr(6), (float*)addr(6), (float*)addr(8),
                       B, H, N, d, 0.125f, addr(9), ws, NULL),

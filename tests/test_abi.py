@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_bwd", "attn_bwd_f32",
-                                           "attn_bwd_ex", "attn_bwd_stage", "attn_bwd_fused",
+                                           "attn_bwd_ex", "attn_bwd_stage", "attn_bwd_ex_noalloc", "attn_bwd_fused",
                                            "attn_bwd_workspace_bytes", "attn_qkv_proj", "attn_qkv_proj_bwd",
                                            "attn_qkv_proj_bwd_workspace_bytes", "attn_status_string"])
 
@@ -154,6 +154,26 @@ def test_backward_rejections(L):
         assert bwd(L, stage, ex=True, kv_len=A[10] + 1) == INV
         assert bwd(L, stage, ex=True, kv_len=A[7]) == INV     # kv_len inside dk
         assert bwd(L, stage, ex=True, kv_len=A[9] + 8) == INV  # kv_len inside the workspace
+
+
+def test_noalloc_backward_rejections(L):
+    """attn_bwd_ex_noalloc runs attn_bwd_ex's checks (no workspace argument) and refuses shapes whose workspace
+    exceeds its 16 MiB array, before any HIP call."""
+    INV, UNS, WS = L.ATTN_ERR_INVALID_ARG, L.ATTN_ERR_UNSUPPORTED, L.ATTN_ERR_WORKSPACE
+
+    def na(dtype=0, layout=0, causal=0, kv_len=None, **kw):
+        a = dict(q=A[0], k=A[1], v=A[2], o=A[3], lse=A[4], do=A[5], dq=A[6], dk=A[7], dv=A[8], B=1, H=1, N=8, d=64,
+                 scale=0.125)
+        a.update(kw)
+        return L.lib.attn_bwd_ex_noalloc(dtype, layout, a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"],
+                                         a["dk"], a["dv"], a["B"], a["H"], a["N"], a["d"], a["scale"], causal, kv_len,
+                                         None)
+    assert na(dq=None) == INV and na(do=A[5] + 4) == INV and na(dk=A[6]) == INV and na(dv=A[0]) == INV
+    assert na(d=80) == UNS and na(dtype=2) == UNS and na(dtype=-1) == UNS and na(layout=5) == UNS
+    assert na(causal=3) == INV and na(kv_len=A[7]) == INV and na(scale=float("nan")) == INV
+    # 8 bytes of workspace per row: 2^21 rows fill the 16 MiB array exactly, one more 64-row block does not.
+    assert L.attn_bwd_workspace_bytes(8, 16, 16384, 64) == 16 << 20
+    assert na(B=8, H=16, N=16384 + 64, d=64) == WS and na(B=1, H=1, N=3_000_000, d=32) == WS
 
 
 def test_f32_backward_rejections(L):
@@ -289,6 +309,7 @@ def test_binding_refuses_host_tensors(L, monkeypatch):
         lambda: L.attn_bwd_f32(f32, f32, f32, f32, lse, f32, f32, f32, f32, 0.125, ws),
         lambda: L.attn_bwd_ex(t, t, t, t, lse, t, t, t, t, 0.125, ws),
         lambda: L.attn_bwd_stage(1, t, t, t, t, lse, t, t, t, t, 0.125, ws),
+        lambda: L.attn_bwd_ex_noalloc(t, t, t, t, lse, t, t, t, t, 0.125),
         lambda: L.attn_qkv_proj(x, w, qkv),
         lambda: L.attn_qkv_proj_bwd(x, w, qkv, x, w, None),
         lambda: L.forward(t, t, t, 0.125),

@@ -25,7 +25,7 @@ LAYOUTS = {"bhnd": 0, "bnhd": 1, "qkv_packed": 2}
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_fwd", "attn_fwd_f32", "attn_fwd_ex", "attn_bwd", "attn_bwd_f32", "attn_bwd_ex", "attn_bwd_stage",
-           "attn_bwd_fused", "attn_bwd_workspace_bytes", "attn_qkv_proj", "attn_qkv_proj_bwd",
+           "attn_bwd_ex_noalloc", "attn_bwd_fused", "attn_bwd_workspace_bytes", "attn_qkv_proj", "attn_qkv_proj_bwd",
            "attn_qkv_proj_bwd_workspace_bytes", "attn_status_string")
 
 
@@ -50,6 +50,8 @@ def _load() -> ctypes.CDLL:
     lib.attn_bwd_ex.restype = i
     lib.attn_bwd_stage.argtypes = [i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp, sz, vp]
     lib.attn_bwd_stage.restype = i
+    lib.attn_bwd_ex_noalloc.argtypes = [i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, vp, vp]
+    lib.attn_bwd_ex_noalloc.restype = i
     lib.attn_bwd_fused.argtypes = [i, i, i, i]
     lib.attn_bwd_fused.restype = i
     lib.attn_qkv_proj.argtypes = [i, vp, vp, vp, i, i, i, i, i, vp]
@@ -262,6 +264,20 @@ def attn_bwd_ex(q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, causal
     _check(lib.attn_bwd_ex(_dtype_code(q), LAYOUTS[layout], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do),
                            _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale), int(bool(causal)), _ptr(kv_len),
                            _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def attn_bwd_ex_noalloc(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool = False, kv_len=None,
+                        stream=None, layout: str = "bhnd") -> None:
+    """attn_bwd_ex with the library's own device workspace (16 MiB per GPU): for callers that cannot allocate.
+    Calls that overlap in time on one GPU race on that workspace."""
+    _on_gpu(q, k, v, o, lse, do, dq, dk, dv, kv_len)
+    B, H, N, d = _dims(layout, (q, k, v), (o, do))
+    _dims(layout, (dq, dk, dv))
+    _check_lse(lse, B, H, N)
+    _check_kv_len(kv_len, B)
+    _check(lib.attn_bwd_ex_noalloc(_dtype_code(q), LAYOUTS[layout], _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                   _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, float(scale),
+                                   int(bool(causal)), _ptr(kv_len), _stream(stream)))
 
 
 def attn_bwd_stage(stage: int, q, k, v, o, lse, do, dq, dk, dv, scale: float, workspace, causal: bool = False,

@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/attn.h"
 #include "attn_kernels.h"
 
@@ -152,9 +154,11 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N, int d_k) {
 namespace {
 
 // dtype -1 stands for float32 storage (attn_bwd_f32, contiguous layout only).
+// with_ws false: the workspace is the library's own scratch array (checked by
+// the caller), so only the other arguments are validated here.
 int bwd_checks(int dtype, int layout, const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k, float scale, int causal,
-               const int* kv_len, void* workspace, size_t workspace_bytes, Layout* L) {
+               const int* kv_len, void* workspace, size_t workspace_bytes, Layout* L, bool with_ws = true) {
   size_t E = 0, R = 0;
   int st = check_shape(B, H, N, d_k, scale, &E, &R);
   if (st != ATTN_OK) return st;
@@ -169,18 +173,21 @@ int bwd_checks(int dtype, int layout, const void* q, const void* k, const void* 
   const size_t hd_bytes = (size_t)H * d_k * esz;
   if (L->packed && (!packed_trio(q, k, v, hd_bytes) || !packed_trio(dq, dk, dv, hd_bytes))) return ATTN_ERR_INVALID_ARG;
   const size_t need = attn::bwd_workspace_bytes(B, H, N, d_k);
-  if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
+  if (with_ws) {
+    if (workspace == nullptr || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
+  }
   // Extents: packed q, k, v (and dq, dk, dv) are one 3 E element buffer each.
   const size_t tb = E * esz, pb = L->packed ? 3 * tb : tb;
   const Range ins[6] = {span(q, pb), L->packed ? span(q, pb) : span(k, tb), L->packed ? span(q, pb) : span(v, tb),
                         span(o, tb), span(dO, tb), span(lse, R * 4)};
   const Range outs[4] = {span(dq, pb), L->packed ? span(dq, pb) : span(dk, tb), L->packed ? span(dq, pb) : span(dv, tb),
                          span(workspace, need)};
-  for (int a = 0; a < 4; ++a) {
+  const int n_out = with_ws ? 4 : 3;
+  for (int a = 0; a < n_out; ++a) {
     for (int b = 0; b < 6; ++b)
       if (overlap(outs[a], ins[b])) return ATTN_ERR_INVALID_ARG;
-    for (int b = a + 1; b < 4; ++b)  // packed dq, dk, dv interleave by construction
+    for (int b = a + 1; b < n_out; ++b)  // packed dq, dk, dv interleave by construction
       if (!(L->packed && b < 3) && overlap(outs[a], outs[b])) return ATTN_ERR_INVALID_ARG;
     if (kv_len != nullptr && overlap(outs[a], span(kv_len, (size_t)B * 4))) return ATTN_ERR_INVALID_ARG;
   }
@@ -196,6 +203,38 @@ int bwd_launch(int dtype, int stage, const void* q, const void* k, const void* v
       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(o), lse, static_cast<const uint16_t*>(dO),
       static_cast<uint16_t*>(dq), static_cast<uint16_t*>(dk), static_cast<uint16_t*>(dv), B, H, N, d_k, scale, causal,
       kv_len, st, workspace, static_cast<hipStream_t>(stream)));
+}
+
+// The backward's workspace for callers that cannot allocate (attn_bwd_ex_noalloc):
+// a file-scope device array, one copy per GPU, held until the process ends.
+// In host code `scratch` names a host-side stand-in, never the device memory:
+// kernels get the per-device address from hipGetSymbolAddress below.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device `stream` belongs to, looked up once
+// per device with that device current.
+int scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess) return ATTN_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return ATTN_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return ATTN_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return ATTN_ERR_HIP;
+    if (e != hipSuccess || p == nullptr) return ATTN_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return ATTN_OK;
 }
 
 }  // namespace
@@ -239,6 +278,28 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              void* stream) {
   return attn_bwd_ex(ATTN_DTYPE_BF16, ATTN_LAYOUT_BHND, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, 0,
                      nullptr, workspace, workspace_bytes, stream);
+}
+
+int attn_bwd_ex_noalloc(int dtype, int layout, const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dO, void* dq, void* dk, void* dv, int B, int H, int N, int d_k,
+                        float scale, int causal, const int* kv_len, void* stream) {
+  if (dtype != ATTN_DTYPE_BF16 && dtype != ATTN_DTYPE_F16) return ATTN_ERR_UNSUPPORTED;
+  Layout L;
+  int st = bwd_checks(dtype, layout, q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k, scale, causal, kv_len, nullptr, 0,
+                      &L, false);
+  if (st != ATTN_OK) return st;
+  if (attn::bwd_workspace_bytes(B, H, N, d_k) > kScratchBytes) return ATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_for_stream(static_cast<hipStream_t>(stream), &ws)) != ATTN_OK) return st;
+  // The same launches as attn_bwd_ex; stage 0 writes every workspace element the later stages read.
+  const int stages_fused[2] = {0, 3}, stages[3] = {0, 1, 2};
+  const bool fuse = attn::bwd_can_fuse(B, H, N, d_k);
+  for (int i = 0; i < (fuse ? 2 : 3); ++i) {
+    const int r = bwd_launch(dtype, fuse ? stages_fused[i] : stages[i], q, k, v, o, lse, dO, dq, dk, dv, B, H, N, d_k,
+                             scale, causal, kv_len, L, ws, stream);
+    if (r != ATTN_OK) return r;
+  }
+  return ATTN_OK;
 }
 
 int attn_bwd_stage(int stage, int dtype, int layout, const void* q, const void* k, const void* v, const void* o,
