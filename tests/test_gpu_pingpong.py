@@ -1,12 +1,14 @@
-"""The two 16-bit forward kernels agree bit for bit.
+"""The 16-bit forward kernels agree bit for bit.
 
 Unmasked rows of 1024 keys or more at d_k = 128 run the ping-pong forward,
-which computes the same tiles with the same arithmetic per element as the
-single-phase forward in a different order of phases. A key-padding length
-equal to N hides no key but routes the same inputs to the single-phase
-kernel, so the two results must be identical (O and lse), whole and ragged
-last tiles, bf16 and fp16, contiguous and packed layouts. Both are also
-checked against the fp64 oracle by the parity tests.
+and unmasked rows of whole 64-key tiles (256 keys or more) at d_k = 64 the
+software-pipelined forward; both compute the same tiles with the same
+arithmetic per element as the single-phase forward, in another order. A
+key-padding length equal to N hides no key but routes the same inputs to the
+single-phase kernel, so the results must be identical (O and lse): bf16 and
+fp16, contiguous and packed layouts, and (pipelined forward) inputs whose
+scores are large enough that many tiles take its full rescale path. All are
+also checked against the fp64 oracle by the parity tests.
 """
 from __future__ import annotations
 
@@ -47,3 +49,29 @@ def test_pingpong_equals_single_phase(gpu_lib, dtype, B, H, N, layout):
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]), "O"
     assert torch.equal(outs[0][1], outs[1][1]), "lse"
+
+
+@pytest.mark.parametrize("dtype,B,H,N,sigma,layout", [
+    ("bf16", 1, 2, 256, 1.0, "bhnd"), ("bf16", 2, 3, 320, 1.0, "bhnd"), ("f16", 1, 2, 1024, 1.0, "bhnd"),
+    ("bf16", 1, 4, 4096, 1.0, "bhnd"), ("bf16", 2, 3, 2048, 8.0, "bhnd"), ("f16", 1, 2, 576, 8.0, "bhnd"),
+    ("bf16", 2, 2, 512, 1.0, "qkv_packed"),
+])
+def test_pipelined_equals_single_phase(gpu_lib, dtype, B, H, N, sigma, layout):
+    import torch
+    d = 64
+    x = make_case(B, H, N, d, dtype, seed=7100 + N, qk_sigma=sigma, with_grad=False)
+    print(f"pipelined {dtype} B={B} H={H} N={N} d={d} sigma={sigma} layout={layout}", flush=True)
+    sys.stdout.flush()
+    q, k, v = (to_device(x, n) for n in ("q", "k", "v"))
+    if layout == "qkv_packed":
+        qkv = torch.stack([q.permute(0, 2, 1, 3), k.permute(0, 2, 1, 3), v.permute(0, 2, 1, 3)], dim=2).contiguous()
+        q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    full = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    outs = []
+    for kv in (None, full):
+        o = torch.empty((B, N, H, d) if layout == "qkv_packed" else (B, H, N, d), dtype=q.dtype, device="cuda")
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        gpu_lib.attn_fwd_ex(q, k, v, o, lse, x.scale, kv_len=kv, layout=layout)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])

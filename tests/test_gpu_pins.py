@@ -171,7 +171,7 @@ TILE_MAX = [0.0, 7.9, 7.9, 8.1, 38.1, 33.1, 46.0, 46.2, 6.2, 106.2, 114.3, 122.2
             146.3, 154.4, 54.4, 162.5, 170.6]
 
 
-def _slack_inputs(dtype: str, d: int, B: int = 1, H: int = 2, seed: int = 0):
+def _slack_inputs(dtype: str, d: int, B: int = 1, H: int = 2, seed: int = 0, last: int = 20):
     """Q, K, V, dO (exact 16-bit values, float64) and the designed row mask.
 
     Designed rows (3 of every 4) carry q = (16, 1, noise); the others (0, 1, noise): their scores are small and
@@ -180,7 +180,7 @@ def _slack_inputs(dtype: str, d: int, B: int = 1, H: int = 2, seed: int = 0):
     TILE_MAX[t] / (scale log2 e), the others 1 to 12 log2 units less. Noise components ~ N(0, 1/1024) (about
     0.002 log2 units of score spread, so every tile maximum lands within 0.05 of its design)."""
     n_tiles = len(TILE_MAX)
-    N = TILE * (n_tiles - 1) + 20
+    N = TILE * (n_tiles - 1) + last
     scale = float(np.float32(1.0 / math.sqrt(d)))
     c = scale * math.log2(math.e)
     rng = np.random.default_rng(seed + d)
@@ -202,11 +202,14 @@ def _slack_inputs(dtype: str, d: int, B: int = 1, H: int = 2, seed: int = 0):
     return Q, K, V, DO, designed, scale
 
 
-@pytest.mark.parametrize("dtype,d,causal", [("bf16", 64, False), ("f16", 64, False), ("bf16", 128, False),
-                                            ("f16", 128, False), ("bf16", 64, True)])
-def test_rescale_slack(gpu_lib, dtype, d, causal):
+# The last tile holds 20 keys (ragged: the single-phase forward at d = 64) or 64 (whole tiles: the pipelined
+# forward at d = 64, which takes the reference move only on its full path).
+@pytest.mark.parametrize("dtype,d,causal,last", [("bf16", 64, False, 20), ("f16", 64, False, 20), ("bf16", 128, False, 20),
+                                                 ("f16", 128, False, 20), ("bf16", 64, True, 20), ("bf16", 64, False, 64),
+                                                 ("f16", 64, False, 64)])
+def test_rescale_slack(gpu_lib, dtype, d, causal, last):
     import torch
-    Q, K, V, DO, designed, scale = _slack_inputs(dtype, d, seed=9300)
+    Q, K, V, DO, designed, scale = _slack_inputs(dtype, d, seed=9300, last=last)
     B, H, N, _ = Q.shape
     _say(f"rescale slack {dtype} B={B} H={H} N={N} d={d} causal={causal}")
     # The realised tile maxima of every designed row, from the oracle's exact probabilities, are the designed

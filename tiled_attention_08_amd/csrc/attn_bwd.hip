@@ -103,8 +103,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 // `runs` (total 64-slot runs of the tile) may be below 4 * per_lane: the last
 // waves then issue fewer DMAs (callers wait for all of a wave's loads).
 template <int D>
-__device__ __forceinline__ void dma_rows(const uint16_t* head_src, int row_stride, int row0, int N,
-                                         unsigned char* dst, int wave, int lane, int per_lane, int runs) {
+__device__ __forceinline__ void dma_rows(Rsrc head_src, int row_stride, int row0, int N, unsigned char* dst, int wave,
+                                         int lane, int per_lane, int runs) {
   constexpr int ROWB = D * 2;
   for (int r = 0; r < per_lane; ++r) {
     if (wave * per_lane + r >= runs) break;
@@ -112,7 +112,7 @@ __device__ __forceinline__ void dma_rows(const uint16_t* head_src, int row_strid
     const int p = slot0 + lane;
     const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz<ROWB>(row);
     const int gr = min(row0 + row, N - 1);
-    dma16(head_src + gr * row_stride + chunk * 8, dst + slot0 * 16);
+    dma16(head_src, (uint32_t)(gr * row_stride + chunk * 8) * 2u, dst + slot0 * 16);
   }
 }
 
@@ -193,13 +193,15 @@ __device__ __forceinline__ void dkdv_body(unsigned char* smem, int work, const u
       vf[kb][cc] = b;
     }
 
+  const Rsrc rQ = make_rsrc(Q + hq), rdO = make_rsrc(dO + hd);
+  const Rsrc rL = make_rsrc(lse2 + hrow), rDL = make_rsrc(ndelta + hrow);
   auto dma_step = [&](int i, int buf) {
     const int q0 = i * BRQ;
-    dma_rows<D>(Q + hq, sq.n, q0, N, smem + S::OFF_Q + buf * S::QTILEB, wave, lane, S::QDMA, 4 * S::QDMA);
-    dma_rows<D>(dO + hd, sd.n, q0, N, smem + S::OFF_DO + buf * S::QTILEB, wave, lane, S::QDMA, 4 * S::QDMA);
-    const size_t r = hrow + min(q0 + lane, N - 1);
-    if (wave == 0) dma4(lse2 + r, smem + S::OFF_L + buf * S::LROWS * 4);
-    if (wave == 1) dma4(ndelta + r, smem + S::OFF_DL + buf * S::LROWS * 4);
+    dma_rows<D>(rQ, sq.n, q0, N, smem + S::OFF_Q + buf * S::QTILEB, wave, lane, S::QDMA, 4 * S::QDMA);
+    dma_rows<D>(rdO, sd.n, q0, N, smem + S::OFF_DO + buf * S::QTILEB, wave, lane, S::QDMA, 4 * S::QDMA);
+    const uint32_t r = (uint32_t)min(q0 + lane, N - 1) * 4u;
+    if (wave == 0) dma4(rL, r, smem + S::OFF_L + buf * S::LROWS * 4);
+    if (wave == 1) dma4(rDL, r, smem + S::OFF_DL + buf * S::LROWS * 4);
   };
 
   f32x16 dvacc[KBW][D / 32], dkacc[KBW][D / 32];
@@ -403,11 +405,14 @@ struct DqShape {
   static constexpr int TILEB = BCQ * ROWB;              // one K or V step tile
   static constexpr int KRUNS = BCQ * D / 8 / 64;        // 64-slot DMA runs per K or V tile (2 to 8)
   static constexpr int KDMA = (KRUNS + 3) / 4;          // runs per wave (the last waves may do fewer)
-  static constexpr int LDSB = 4 * TILEB;                // K and V, two buffers each
+  static constexpr int BUFB = 2 * TILEB;                // one buffer: K and V of a step
 };
 
+// buf0, buf1: the two step buffers (K tile, then V tile), separate LDS arrays
+// so that the compiler can tell the DMA into one from the transposing reads
+// of the other (otherwise those reads wait for the step in flight).
 template <class E, int D, int QB>
-__device__ __forceinline__ void dq_body(unsigned char* smem, int work, const uint16_t* __restrict__ Q,
+__device__ __forceinline__ void dq_body(unsigned char* buf0, unsigned char* buf1, int work, const uint16_t* __restrict__ Q,
                                         const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                         const uint16_t* __restrict__ dO, const float* __restrict__ lse2_in,
                                         const float* __restrict__ ndelta, uint16_t* __restrict__ dQ, int N,
@@ -466,13 +471,15 @@ __device__ __forceinline__ void dq_body(unsigned char* smem, int work, const uin
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) dqacc[qb][db] = f32x16{};
 
-  auto dma_step = [&](int j, int buf) {
-    dma_rows<D>(K + hq, sq.n, j * BCQ, N, smem + buf * 2 * S::TILEB, wave, lane, S::KDMA, S::KRUNS);
-    dma_rows<D>(V + hq, sq.n, j * BCQ, N, smem + buf * 2 * S::TILEB + S::TILEB, wave, lane, S::KDMA, S::KRUNS);
+  const Rsrc rK = make_rsrc(K + hq), rV = make_rsrc(V + hq);
+  auto dma_step = [&](int j, auto buf_c) {
+    unsigned char* dst = decltype(buf_c)::value ? buf1 : buf0;
+    dma_rows<D>(rK, sq.n, j * BCQ, N, dst, wave, lane, S::KDMA, S::KRUNS);
+    dma_rows<D>(rV, sq.n, j * BCQ, N, dst + S::TILEB, wave, lane, S::KDMA, S::KRUNS);
   };
 
   if (ntiles > 0) {
-    dma_step(0, 0);
+    dma_step(0, IntC<0>{});
     wait_vmem();
   }
   __syncthreads();
@@ -496,9 +503,9 @@ __device__ __forceinline__ void dq_body(unsigned char* smem, int work, const uin
   auto step = [&](int j, auto masked, bool compute, auto bufc) {
     constexpr bool MASKED = decltype(masked)::value;
     constexpr int buf = decltype(bufc)::value;
-    if (j + 1 < ntiles) dma_step(j + 1, buf ^ 1);
+    if (j + 1 < ntiles) dma_step(j + 1, IntC<buf ^ 1>{});
     if (!compute) return;
-    const unsigned char* Ks = smem + buf * 2 * S::TILEB;
+    const unsigned char* Ks = buf ? buf1 : buf0;
     const unsigned char* Vs = Ks + S::TILEB;
 
     // ---- S^T = K Q^T and dP^T = V dO^T: 32 keys x (32*QB) queries.
@@ -601,8 +608,9 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                    const uint16_t* __restrict__ dO, const float* __restrict__ lse2_in, const float* __restrict__ ndelta,
                    uint16_t* __restrict__ dQ, int N, int n_qblk, int total, float c, float scale,
                    const int* __restrict__ kv_len, int H, int causal, Strides sq, Strides sd, Strides sg) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[DqShape<D, QB>::LDSB];
-  dq_body<E, D, QB>(smem, xcd_remap(blockIdx.x, total), Q, K, V, dO, lse2_in, ndelta, dQ, N, n_qblk, total, c, scale,
+  __shared__ __attribute__((aligned(16))) unsigned char buf0[DqShape<D, QB>::BUFB];
+  __shared__ __attribute__((aligned(16))) unsigned char buf1[DqShape<D, QB>::BUFB];
+  dq_body<E, D, QB>(buf0, buf1, xcd_remap(blockIdx.x, total), Q, K, V, dO, lse2_in, ndelta, dQ, N, n_qblk, total, c, scale,
                     kv_len, H, causal, sq, sd, sg);
 }
 
@@ -618,14 +626,15 @@ void bwd_dkdv_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
                         uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
                         int n_kblk, int total1, int n_qblk, int total2, float c, float scale,
                         const int* __restrict__ kv_len, int H, int causal, Strides sq, Strides sd, Strides sg) {
-  constexpr int L1 = DkdvShape<D, MB>::LDSB, L2 = DqShape<D, QB>::LDSB;
+  constexpr int L1 = DkdvShape<D, MB>::LDSB, L2 = DqShape<D, QB>::BUFB;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L1 > L2 ? L1 : L2];
+  __shared__ __attribute__((aligned(16))) unsigned char smem1[L2];
   const int id = blockIdx.x;
   if (id < total1)
     dkdv_body<E, D, MB, 1>(smem, xcd_remap(id, total1), Q, K, V, dO, lse2, ndelta, dK, dV, N, n_kblk, total1, c, scale,
                            kv_len, H, causal, sq, sd, sg);
   else
-    dq_body<E, D, QB>(smem, xcd_remap(id - total1, total2), Q, K, V, dO, lse2, ndelta, dQ, N, n_qblk, total2, c, scale,
+    dq_body<E, D, QB>(smem, smem1, xcd_remap(id - total1, total2), Q, K, V, dO, lse2, ndelta, dQ, N, n_qblk, total2, c, scale,
                       kv_len, H, causal, sq, sd, sg);
 }
 

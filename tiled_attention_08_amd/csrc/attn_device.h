@@ -212,6 +212,27 @@ __device__ __forceinline__ void dma4(const void* src, unsigned char* lds_base) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_base, 4, 0, 0);
 }
 
+// The same copies through a buffer resource (buffer_load_dword{,x4} ... lds):
+// lane l writes lds_base + size * l with the bytes at byte offset `off` of the
+// resource. The attention kernels use these: the compiler counts a
+// global_load_lds as both a vector-memory and an LDS access and, while one is
+// in flight, makes every LDS read wait for all LDS reads issued (lgkmcnt(0)),
+// which defeats reading operands ahead; buffer copies count as vector memory
+// only. A resource covers one head of one tensor (offsets below 2^31, which
+// the host-side index checks guarantee); word 3 is the gfx9 raw-buffer format.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ Rsrc make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ void dma16(Rsrc r, uint32_t off, unsigned char* lds_base) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(Rsrc r, uint32_t off, unsigned char* lds_base) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 4, off, 0, 0, 0);
+}
+
 // Wait until every outstanding global load of this wave (including LDS DMA) has landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

@@ -80,6 +80,25 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units a row max may grow before O
 #ifndef FWD_PINGPONG
 #define FWD_PINGPONG 1
 #endif
+// Software-pipelined forward for d = 64 rows without masks (N a multiple of 64, at least FWD_SP_MIN_N keys).
+#ifndef FWD_SP
+#define FWD_SP 1
+#endif
+#ifndef FWD_SP_MIN_N
+#define FWD_SP_MIN_N 256
+#endif
+// Schedule of the pipelined forward: operands read FWD_SP_AHEAD products ahead;
+// FWD_SP_SKEW packs and sums each pair of weights one chunk after its
+// exponentials; FWD_SP_BARRIER keeps the compiler from moving work across chunks.
+#ifndef FWD_SP_AHEAD
+#define FWD_SP_AHEAD 2
+#endif
+#ifndef FWD_SP_SKEW
+#define FWD_SP_SKEW 0
+#endif
+#ifndef FWD_SP_BARRIER
+#define FWD_SP_BARRIER 1
+#endif
 #ifndef FWD_PP_D64
 #define FWD_PP_D64 0
 #endif
@@ -141,7 +160,22 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
                      uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qblk, int total, float c,
                      uint32_t qsign, const int* __restrict__ kv_len, int H, int causal, Strides sq, Strides so) {
   using S = FwdShape<D, QB, KB, NS, WAVES>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDSB];
+  static_assert(NS >= 2 && NS <= 4, "K/V ring of 2 to 4 tiles");
+  // One LDS array per ring slot (K tile then V tile), addressed with a
+  // compile-time slot index: the compiler can then tell a DMA into one slot
+  // from the transposing reads of another, and does not make those reads wait
+  // for the tile in flight (with one array it waits for every outstanding DMA).
+  __shared__ __attribute__((aligned(16))) unsigned char ring0[2 * S::TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring1[2 * S::TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring2[NS > 2 ? 2 * S::TILEB : 16];
+  __shared__ __attribute__((aligned(16))) unsigned char ring3[NS > 3 ? 2 * S::TILEB : 16];
+  auto slot_base = [&](auto r_) __attribute__((always_inline)) -> unsigned char* {
+    constexpr int R = decltype(r_)::value;
+    if constexpr (R == 0) return ring0;
+    else if constexpr (R == 1) return ring1;
+    else if constexpr (R == 2) return ring2;
+    else return ring3;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -154,6 +188,7 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
   const uint16_t* Qh = Q + hq;
   const uint16_t* Kh = K + hq;
   const uint16_t* Vh = V + hq;
+  const Rsrc rK = make_rsrc(Kh), rV = make_rsrc(Vh);
   const int qw0 = qblk * S::BR + wave * 32 * QB;
 
   // Visible keys of query q: j < klim(q) with klim(q) = min(kv, q + 1) under
@@ -193,12 +228,12 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
   const int nfull_wg = klim(qblk * S::BR) / S::BC;
   const int nvis_w = (klim(qw0 + 32 * QB - 1) + S::BC - 1) / S::BC;
 
-  // K/V tile j -> ring slot j % NS by DMA. Wave w fills a contiguous run of
-  // 16-byte LDS slots; the lane writing slot (row, s) fetches global chunk
+  // K/V tile j -> ring slot R = j % NS by DMA. Wave w fills a contiguous run
+  // of 16-byte LDS slots; the lane writing slot (row, s) fetches global chunk
   // s ^ swz(row), which yields the swizzled layout tile_off() addresses.
   // Rows past N re-read row N-1 (finite data; their scores are masked below).
-  auto dma_tile = [&](int j) {
-    unsigned char* Ks = smem + (j % NS) * 2 * S::TILEB;
+  auto dma_tile = [&](int j, auto r_) __attribute__((always_inline)) {
+    unsigned char* Ks = slot_base(r_);
     unsigned char* Vs = Ks + S::TILEB;
 #pragma unroll
     for (int r = 0; r < S::DMA_PER_WAVE; ++r) {
@@ -206,8 +241,9 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
       const int p = slot0 + lane;
       const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz<S::ROWB>(row);
       const int key = min(j * S::BC + row, N - 1);
-      dma16(Kh + key * sq.n + chunk * 8, Ks + slot0 * 16);
-      dma16(Vh + key * sq.n + chunk * 8, Vs + slot0 * 16);
+      const uint32_t off = (uint32_t)(key * sq.n + chunk * 8) * 2u;
+      dma16(rK, off, Ks + slot0 * 16);
+      dma16(rV, off, Vs + slot0 * 16);
     }
   };
   // Wait until tile j has landed, given that tiles up to min(j + NS - 2, ntiles - 1)
@@ -223,7 +259,15 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
       wait_vmem_below<0>();
   };
 
-  for (int j = 0; j < NS - 1 && j < ntiles; ++j) dma_tile(j);
+  // Tile j with its ring slot as a compile-time constant.
+  auto with_slot = [&](int j, auto&& f) __attribute__((always_inline)) {
+    static_for<0, NS>([&](auto s_) __attribute__((always_inline)) {
+      if (j % NS == decltype(s_)::value) f(s_);
+    });
+  };
+  static_for<0, NS - 1>([&](auto s_) __attribute__((always_inline)) {
+    if (decltype(s_)::value < ntiles) dma_tile(decltype(s_)::value, s_);
+  });
   if (ntiles > 0) wait_tile(0);
   __syncthreads();
 
@@ -245,7 +289,7 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
   auto tile = [&](int j, auto masked, auto slot_c) {
     constexpr bool MASKED = decltype(masked)::value;
     constexpr int SLOT = decltype(slot_c)::value;
-    const unsigned char* Ks = smem + SLOT * 2 * S::TILEB;
+    const unsigned char* Ks = slot_base(slot_c);
     const unsigned char* Vs = Ks + S::TILEB;
     int kvalid[QB];  // visible keys of this tile, per row block (MASKED only)
 #pragma unroll
@@ -290,9 +334,11 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
     // The reference point m_run only moves when the tile max exceeds it by
     // more than kRescaleSlack; any reference point gives the same softmax
     // (it cancels between O and l), so skipping small moves only bounds the
-    // probabilities by 2^kRescaleSlack and saves the O rescale.
+    // probabilities by 2^kRescaleSlack and saves the O rescale. The decision
+    // is taken per 32-query block: when any lane of the wave needs a move,
+    // every lane of that block moves its reference to its own maximum.
     float mnew[QB];
-    bool need = false;
+    bool need[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       // NaN-propagating maximum (v_maximum3_f32): no canonicalisation of the
@@ -318,11 +364,11 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
       }
       mx = halves_max(mx) * c;
       mnew[qb] = fmaxf(m_run[qb], mx);
-      need |= mnew[qb] > m_run[qb] + kRescaleSlack;
+      need[qb] = mnew[qb] > m_run[qb] + kRescaleSlack;
     }
-    if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
+      if (__builtin_amdgcn_ballot_w64(need[qb])) {
         // A lane that has seen no visible key yet keeps max -inf (alpha = 1).
         const float alpha = mnew[qb] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - mnew[qb]);
         m_run[qb] = mnew[qb];
@@ -378,23 +424,18 @@ void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, 
   // visible key, nothing; all waves still take part in every DMA and barrier.
   // The single-path loop is unrolled by NS (tile j in ring slot j % NS).
   auto full_tile = [&](int j, auto slot_c) __attribute__((always_inline)) {
-    if (j + NS - 1 < ntiles) dma_tile(j + NS - 1);
+    if (j + NS - 1 < ntiles) dma_tile(j + NS - 1, IntC<(decltype(slot_c)::value + NS - 1) % NS>{});
     tile(j, BoolC<false>{}, slot_c);
     if (j + 1 < ntiles) wait_tile(j + 1);
     __syncthreads();
-  };
-  // Tile j with its ring slot as a compile-time constant.
-  auto with_slot = [&](int j, auto&& f) __attribute__((always_inline)) {
-    static_for<0, NS>([&](auto s_) __attribute__((always_inline)) {
-      if (j % NS == decltype(s_)::value) f(s_);
-    });
   };
   int j = 0;
   for (; j + NS <= nfull_wg; j += NS)
     static_for<0, NS>([&](auto s_) __attribute__((always_inline)) { full_tile(j + decltype(s_)::value, s_); });
   for (; j < nfull_wg; ++j) with_slot(j, [&](auto s_) __attribute__((always_inline)) { full_tile(j, s_); });
   for (; j < ntiles; ++j) {
-    if (j + NS - 1 < ntiles) dma_tile(j + NS - 1);
+    if (j + NS - 1 < ntiles)
+      with_slot(j + NS - 1, [&](auto s_) __attribute__((always_inline)) { dma_tile(j + NS - 1, s_); });
     if (j < nvis_w)  // masks are no-ops on the tiles this wave sees in full
       with_slot(j, [&](auto s_) __attribute__((always_inline)) { tile(j, BoolC<true>{}, s_); });
     if (j + 1 < ntiles) {
@@ -472,6 +513,7 @@ void fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const uint16_t* Qh = Q + hq;
   const uint16_t* Kh = K + hq;
   const uint16_t* Vh = V + hq;
+  const Rsrc rK = make_rsrc(Kh), rV = make_rsrc(Vh);
   const int qw0 = qblk * S::BR + wave * 32 * QB;
 
   u32x4 qf[QB][D / 16];
@@ -511,8 +553,9 @@ void fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       const int p = slot0 + lane;
       const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz<S::ROWB>(row);
       const int key = min(j * S::BC + row, N - 1);
-      dma16(Kh + key * sq.n + chunk * 8, Ks + slot0 * 16);
-      dma16(Vh + key * sq.n + chunk * 8, Vs + slot0 * 16);
+      const uint32_t off = (uint32_t)(key * sq.n + chunk * 8) * 2u;
+      dma16(rK, off, Ks + slot0 * 16);
+      dma16(rV, off, Vs + slot0 * 16);
     }
   };
   // Phase boundary: this wave's LDS reads have returned, then all 8 waves meet.
@@ -620,7 +663,7 @@ void fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         }
     }
     float mnew[QB];
-    bool need = false;
+    bool need[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       // (A running chain here: the three-operand tree of fwd_kernel measured
@@ -633,11 +676,11 @@ void fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
           mx = (e + 1 < 16) ? fmax3(mx, sacc[qb][kb][e], sacc[qb][kb][e + 1]) : fmax2(mx, sacc[qb][kb][e]);
       mx = halves_max(mx) * c;
       mnew[qb] = fmaxf(m_run[qb], mx);
-      need |= mnew[qb] > m_run[qb] + kRescaleSlack;
+      need[qb] = mnew[qb] > m_run[qb] + kRescaleSlack;
     }
-    if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
+      if (__builtin_amdgcn_ballot_w64(need[qb])) {
         const float alpha = mnew[qb] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - mnew[qb]);
         m_run[qb] = mnew[qb];
         l_run[qb] *= alpha;
@@ -724,6 +767,331 @@ void fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     default: matrix_slot(BoolC<true>{}, BoolC<false>{}, IntC<0>{}, ntiles); break;
   }
   if (grp == 0) phase_end();
+
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float lt = halves_sum(l_run[qb]);
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int q = qw0 + qb * 32 + l32;
+    if (q < N) {
+      uint16_t* orow = O + head_off(so, bh, H) + q * so.n;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const f32x16& a = oacc[qb][db];
+          u32x2 w = {E::pack(a[4 * jj] * inv, a[4 * jj + 1] * inv), E::pack(a[4 * jj + 2] * inv, a[4 * jj + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + db * 32 + 8 * jj + 4 * h) = w;
+        }
+      if (h == 0) LSE[(size_t)bh * N + q] = lt > 0.f ? (m_run[qb] + log2f(lt)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// Software-pipelined forward (rows without masks, N a multiple of 64, d = 64).
+// The same tiles and the same arithmetic per element as fwd_kernel, issued so
+// that every wave keeps the matrix cores and the vector ALU busy at once.
+//
+// A unit is one 32-query block of the wave against one 64-key tile; tile j
+// holds units (j, 0) and (j, 1). While the vector ALU computes the softmax
+// of unit u, the matrix cores compute S of unit u + 1 and O^T += V^T P^T of
+// unit u - 1 (independent instructions in one stream, interleaved by the
+// hardware). So S of tile j + 1 is read from LDS while V of tile j - 1 is
+// still in use: the K/V ring holds four tiles, one LDS array per slot.
+//
+// The softmax is speculative: the weights are computed against the current
+// reference maximum without first taking the tile's maximum. The reference
+// only has to move when a weight exceeds 2^kRescaleSlack, and then the
+// tile's share of the row sum exceeds it too; only then (ballot over the
+// wave) the tile takes the full path of fwd_kernel: maximum, move, rescale
+// and exponentials again. A tile that passes computed exactly the
+// exponentials fwd_kernel computes, so the outputs are equal bit for bit.
+// ------------------------------------------------------------------------
+constexpr int kSPRing = 4;
+// Row-sum share of one tile above which the full path runs: below 2^kRescaleSlack
+// by more than the rounding of the fp32 sum, so that no weight above that bound
+// can pass unchecked.
+constexpr float kSpecLimit = 128.0f;
+
+template <class E, int D, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                   uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qblk, int total, float c,
+                   uint32_t qsign, int H, Strides sq, Strides so) {
+  constexpr int QB = 2, KB = 2, NS = kSPRing;
+  using S = FwdShape<D, QB, KB, NS, WAVES>;
+  constexpr int PER = 2 * S::DMA_PER_WAVE;  // DMA instructions per wave per tile
+  __shared__ __attribute__((aligned(16))) unsigned char ring0[2 * S::TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring1[2 * S::TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring2[2 * S::TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring3[2 * S::TILEB];
+  auto slot_base = [&](auto r_) __attribute__((always_inline)) -> unsigned char* {
+    constexpr int R = decltype(r_)::value % NS;
+    if constexpr (R == 0) return ring0;
+    else if constexpr (R == 1) return ring1;
+    else if constexpr (R == 2) return ring2;
+    else return ring3;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 4, gi = lane & 15;
+  const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
+  const int work = xcd_remap(blockIdx.x, total);
+  const int bh = work / n_qblk, qblk = work - bh * n_qblk;
+  const size_t hq = head_off(sq, bh, H);
+  const uint16_t* Qh = Q + hq;
+  const uint16_t* Kh = K + hq;
+  const uint16_t* Vh = V + hq;
+  const Rsrc rK = make_rsrc(Kh), rV = make_rsrc(Vh);
+  const int qw0 = qblk * S::BR + wave * 32 * QB;
+
+  u32x4 qf[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int q = qw0 + qb * 32 + l32;
+#pragma unroll
+    for (int cc = 0; cc < D / 16; ++cc) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (q < N) v = *reinterpret_cast<const u32x4*>(Qh + q * sq.n + cc * 16 + h * 8);
+      v ^= qsign;
+      qf[qb][cc] = v;
+    }
+  }
+
+  f32x16 oacc[QB][D / 32];
+  float m_run[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_run[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
+  }
+
+  const int nt = N / S::BC;  // tiles (N is a multiple of the tile; the launcher checks nt >= 4)
+
+  auto dma_tile = [&](int j, auto r_) __attribute__((always_inline)) {
+    unsigned char* Ks = slot_base(r_);
+    unsigned char* Vs = Ks + S::TILEB;
+#pragma unroll
+    for (int r = 0; r < S::DMA_PER_WAVE; ++r) {
+      const int slot0 = (wave * S::DMA_PER_WAVE + r) * 64;
+      const int p = slot0 + lane;
+      const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz<S::ROWB>(row);
+      const int key = j * S::BC + row;
+      const uint32_t off = (uint32_t)(key * sq.n + chunk * 8) * 2u;
+      dma16(rK, off, Ks + slot0 * 16);
+      dma16(rV, off, Vs + slot0 * 16);
+    }
+  };
+
+  int koff[D / 16], voff[2][D / 32];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) koff[cc] = tile_off<S::ROWB>(l32, cc * 16 + h * 8);
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) voff[hi][db] = tile_off<S::ROWB>(4 * h + er + 8 * hi, db * 32 + dsub * 16 + 4 * qq);
+
+  // One unit's work is issued as 16 chunks, each one matrix product, the
+  // exponentials of one pair of S^T entries and the LDS read of the operand
+  // two products ahead, with scheduling barriers between chunks: the compiler
+  // keeps them in order (left alone, it hoists every operand read of the
+  // iteration and spills). Products: first P V of the previous unit (PV, 8:
+  // key block, 16-key half, 32-dim block; the two 32-dim accumulators
+  // alternate), then S^T of the next one (S, 8: the two key blocks' chains
+  // alternate, 16-dim chunks in order). The kinds are not interleaved: the
+  // compiler assumes transposing and plain LDS reads may complete out of
+  // order, and waits for every read in flight when the two are mixed.
+  // Operand of product m of a unit: V^T fragment (PV) or K fragment (S).
+  auto pv_operand = [&](auto r_, int p) __attribute__((always_inline)) -> u32x4 {
+    const unsigned char* Vs = slot_base(r_) + S::TILEB;
+    const int kb = p >> 2, c2 = (p >> 1) & 1, db = p & 1;
+    const int rows = (kb * 32 + c2 * 16) * S::ROWB;
+    return cat(lds_read_tr16_b64(Vs, rows + voff[0][db]), lds_read_tr16_b64(Vs, rows + voff[1][db]));
+  };
+  auto s_operand = [&](auto r_, int sidx) __attribute__((always_inline)) -> u32x4 {
+    const unsigned char* Ks = slot_base(r_);
+    return lds_read_b128(Ks, (sidx >> 2) * 32 * S::ROWB + koff[sidx & 3]);
+  };
+  // Weights of entries 2i, 2i + 1 of query block QB_'s S^T tile (i = 0 .. 15).
+  auto weight_pair = [&](auto qb_, int i, const f32x16 (&sv)[KB], u32x4 (&p)[KB][2], float& l)
+                         __attribute__((always_inline)) {
+    constexpr int QB_ = decltype(qb_)::value;
+    const int kb = i >> 3, e = 2 * (i & 7);
+    const float nm = -m_run[QB_];
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[kb][e], c, nm));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[kb][e + 1], c, nm));
+    const uint32_t w = E::pack(p0, p1);
+    p[kb][e >> 3][(e >> 1) & 3] = w;
+    l = E::sum_pair(w, l);
+  };
+  // The full path of fwd_kernel for one unit whose speculative weights failed
+  // the check (rare): maximum, reference move and rescale, weights again.
+  auto softmax_slow = [&](auto qb_, const f32x16 (&sv)[KB], u32x4 (&p)[KB][2], float l_old, float& l)
+                          __attribute__((always_inline)) {
+    constexpr int QB_ = decltype(qb_)::value;
+    float xs[KB * 16];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xs[kb * 16 + e] = sv[kb][e];
+    const float mx = halves_max(max_tree<KB * 16>(xs)) * c;
+    const float mnew = fmaxf(m_run[QB_], mx);
+    if (__builtin_amdgcn_ballot_w64(mnew > m_run[QB_] + kRescaleSlack)) {
+      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[QB_] - mnew);
+      m_run[QB_] = mnew;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[QB_][db] *= alpha;
+      l = l_old * alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) weight_pair(qb_, i, sv, p, l);
+    }
+  };
+
+  // One unit: softmax of query block QS (S^T in sv -> P^T in pw), with S^T of
+  // query block QN against the K tile in slot RS into sn (HAS_S) and P V of
+  // query block QP (P^T in pr) against the V tile in slot RV (HAS_PV).
+  auto unit = [&](auto has_s, auto rs_, auto qn_, f32x16 (&sn)[KB], auto has_pv, auto rv_, auto qp_,
+                  const u32x4 (&pr)[KB][2], auto qs_, const f32x16 (&sv)[KB], u32x4 (&pw)[KB][2])
+                  __attribute__((always_inline)) {
+    constexpr bool HS = decltype(has_s)::value, HP = decltype(has_pv)::value;
+    constexpr int QN = decltype(qn_)::value, QP = decltype(qp_)::value, QS = decltype(qs_)::value;
+    constexpr int NM = (HS ? 8 : 0) + (HP ? 8 : 0);
+    // Product m: PV index m (m < 8, HAS_PV), then S index m - 8 (or m without
+    // PV products), S index t meaning key block t & 1 and 16-dim chunk t >> 1.
+    auto is_pv = [&](int m) { return HP && m < 8; };
+    auto s_index = [&](int m) { return HP ? m - 8 : m; };
+    auto operand = [&](int m) __attribute__((always_inline)) -> u32x4 {
+      if (is_pv(m)) return pv_operand(rv_, m);
+      const int t = s_index(m);
+      return s_operand(rs_, (t & 1) * 4 + (t >> 1));
+    };
+    if constexpr (HS) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) sn[kb] = f32x16{};
+    }
+    const float l_old = l_run[QS];
+    float l = l_old;
+    constexpr int AH = FWD_SP_AHEAD, NO = AH + 1;  // operands read AH products ahead
+    u32x4 ops[NO];
+    static_for<0, AH>([&](auto a_) __attribute__((always_inline)) {
+      if constexpr (decltype(a_)::value < NM) ops[decltype(a_)::value] = operand(decltype(a_)::value);
+    });
+    const float nm = -m_run[QS];
+    float e0 = 0.f, e1 = 0.f;  // exponentials of the previous pair (FWD_SP_SKEW)
+    static_for<0, 16>([&](auto i_) __attribute__((always_inline)) {
+      constexpr int I = decltype(i_)::value;
+      if (FWD_SP_BARRIER) __builtin_amdgcn_sched_barrier(0);
+      if constexpr (I < NM) {
+        constexpr bool PVM = HP && I < 8;
+        if constexpr (PVM) {
+          constexpr int kb = I >> 2, c2 = (I >> 1) & 1, db = I & 1;
+          oacc[QP][db] = E::mfma(ops[I % NO], pr[kb][c2], oacc[QP][db]);
+        } else {
+          constexpr int T = HP ? I - 8 : I, kb = T & 1, cc = T >> 1;
+          sn[kb] = E::mfma(ops[I % NO], qf[QN][cc], sn[kb]);
+        }
+      }
+      if constexpr (I + AH < NM) ops[(I + AH) % NO] = operand(I + AH);
+      if constexpr (FWD_SP_SKEW) {
+        constexpr int kb = I >> 3, e = 2 * (I & 7);
+        const float f0 = __builtin_amdgcn_exp2f(fmaf(sv[kb][e], c, nm));
+        const float f1 = __builtin_amdgcn_exp2f(fmaf(sv[kb][e + 1], c, nm));
+        if constexpr (I > 0) {
+          constexpr int pk = (I - 1) >> 3, pe = 2 * ((I - 1) & 7);
+          const uint32_t w = E::pack(e0, e1);
+          pw[pk][pe >> 3][(pe >> 1) & 3] = w;
+          l = E::sum_pair(w, l);
+        }
+        e0 = f0;
+        e1 = f1;
+      } else {
+        weight_pair(qs_, I, sv, pw, l);
+      }
+    });
+    if constexpr (FWD_SP_SKEW) {
+      const uint32_t w = E::pack(e0, e1);
+      pw[1][1][3] = w;
+      l = E::sum_pair(w, l);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (__builtin_amdgcn_ballot_w64(!(l - l_old <= kSpecLimit))) softmax_slow(qs_, sv, pw, l_old, l);
+    l_run[QS] = l;
+  };
+
+  // End of tile j's first unit: tile j + 1 landed and visible to every wave,
+  // every wave done with tile j - 1 (its slot takes tile j + 3).
+  auto boundary = [&](int j, auto r_) __attribute__((always_inline)) {
+    constexpr int R = decltype(r_)::value;
+    if (j + 2 >= 3 && j + 2 < nt)
+      wait_vmem_below<PER>();
+    else
+      wait_vmem_below<0>();
+    __syncthreads();
+    if (j + 3 < nt) dma_tile(j + 3, IntC<(R + 3) % NS>{});
+  };
+
+  f32x16 sa[KB], sb[KB];          // S^T of query blocks 0 and 1 (one tile apart)
+  u32x4 pa[KB][2], pb[KB][2];     // P^T of query blocks 1 and 0
+  // Tile j in ring slot R: units (j, 0) and (j, 1). FIRST: no P V of tile
+  // j - 1; LAST: no S of tile j + 1.
+  auto tile = [&](int j, auto r_, auto first_, auto last_) __attribute__((always_inline)) {
+    constexpr int R = decltype(r_)::value;
+    constexpr bool FIRST = decltype(first_)::value, LAST = decltype(last_)::value;
+    // unit (j, 0): S^T(j, 1) -> sb, P V(j - 1, 1) from pa, softmax(j, 0): sa -> pb
+    unit(BoolC<true>{}, r_, IntC<1>{}, sb, BoolC<!FIRST>{}, IntC<(R + NS - 1) % NS>{}, IntC<1>{}, pa, IntC<0>{}, sa, pb);
+    boundary(j, r_);
+    // unit (j, 1): S^T(j + 1, 0) -> sa, P V(j, 0) from pb, softmax(j, 1): sb -> pa
+    unit(BoolC<!LAST>{}, IntC<(R + 1) % NS>{}, IntC<0>{}, sa, BoolC<true>{}, r_, IntC<0>{}, pb, IntC<1>{}, sb, pa);
+  };
+  // S^T of unit (0, 0) and P V of the last unit, outside any tile.
+  auto s_only = [&](auto r_, auto qb_, f32x16 (&acc)[KB]) __attribute__((always_inline)) {
+    constexpr int QB_ = decltype(qb_)::value;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      acc[kb] = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < D / 16; ++cc) acc[kb] = E::mfma(s_operand(r_, kb * 4 + cc), qf[QB_][cc], acc[kb]);
+    }
+  };
+  auto pv_only = [&](auto r_, auto qb_, const u32x4 (&p)[KB][2]) __attribute__((always_inline)) {
+    constexpr int QB_ = decltype(qb_)::value;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) oacc[QB_][m & 1] = E::mfma(pv_operand(r_, m), p[m >> 2][(m >> 1) & 1], oacc[QB_][m & 1]);
+  };
+
+  // Prologue: tiles 0 .. 2 resident, S of unit (0, 0).
+  dma_tile(0, IntC<0>{});
+  dma_tile(1, IntC<1>{});
+  dma_tile(2, IntC<2>{});
+  wait_vmem_below<0>();
+  __syncthreads();
+  s_only(IntC<0>{}, IntC<0>{}, sa);
+  tile(0, IntC<0>{}, BoolC<true>{}, BoolC<false>{});
+  // Tiles 1 .. nt - 1, four per iteration (ring slots 1, 2, 3, 0), then the
+  // rest. The last tile's second unit also computes S^T of a tile nt that does
+  // not exist, from the slot it would occupy (which holds tile nt - 4: finite
+  // data, nt >= 4); the result is never used. This keeps one tile body.
+  int j = 1;
+  for (; j + 4 <= nt; j += 4) {
+    tile(j, IntC<1>{}, BoolC<false>{}, BoolC<false>{});
+    tile(j + 1, IntC<2>{}, BoolC<false>{}, BoolC<false>{});
+    tile(j + 2, IntC<3>{}, BoolC<false>{}, BoolC<false>{});
+    tile(j + 3, IntC<0>{}, BoolC<false>{}, BoolC<false>{});
+  }
+  if (j < nt) tile(j, IntC<1>{}, BoolC<false>{}, BoolC<false>{});
+  if (j + 1 < nt) tile(j + 1, IntC<2>{}, BoolC<false>{}, BoolC<false>{});
+  if (j + 2 < nt) tile(j + 2, IntC<3>{}, BoolC<false>{}, BoolC<false>{});
+  // P V of the last unit (tile nt - 1, query block 1).
+  switch ((nt - 1) % NS) {
+    case 0: pv_only(IntC<0>{}, IntC<1>{}, pa); break;
+    case 1: pv_only(IntC<1>{}, IntC<1>{}, pa); break;
+    case 2: pv_only(IntC<2>{}, IntC<1>{}, pa); break;
+    default: pv_only(IntC<3>{}, IntC<1>{}, pa); break;
+  }
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -869,6 +1237,19 @@ static hipError_t launch_fwd_pp(const uint16_t* q, const uint16_t* k, const uint
   return hipGetLastError();
 }
 
+template <class E, int D, int WAVES>
+static hipError_t launch_fwd_sp(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
+                                int B, int H, int N, float scale, Strides sq, Strides so, hipStream_t stream) {
+  using S = FwdShape<D, 2, 2, kSPRing, WAVES>;
+  const int n_qblk = (N + S::BR - 1) / S::BR;
+  const int total = n_qblk * B * H;
+  const float c = fabsf(scale) * kLog2e;
+  const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
+  hipLaunchKernelGGL((fwd_sp_kernel<E, D, WAVES>), dim3(total), dim3(S::THREADS), 0, stream, q, k, v, o, lse, N,
+                     n_qblk, total, c, qsign, H, sq, so);
+  return hipGetLastError();
+}
+
 template <class E, int D, int QB, int KB, int NS, int WAVES>
 static hipError_t launch_fwd_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o,
                                     float* lse, int B, int H, int N, float scale, int causal, const int* kv_len,
@@ -901,6 +1282,9 @@ static hipError_t launch_fwd_e(const uint16_t* q, const uint16_t* k, const uint1
   // -18 %; d = 32 -9 %, causal -17 %; at N = 16384, d = 64, 8 waves are 1.5 %
   // faster). d = 96 and 128 measured 18-24 % slower with 4 waves.
   const bool lng_small_d = N >= FWD_LONG_N_SMALL_D;
+  // Rows without masks, whole 64-key tiles, d = 64: the software-pipelined forward.
+  if (FWD_SP && d == 64 && !causal && !kv_len && N % 64 == 0 && N >= FWD_SP_MIN_N)
+    return launch_fwd_sp<E, 64, 4>(q, k, v, o, lse, B, H, N, scale, sq, so, stream);
   if (FWD_PINGPONG && lng && !causal && !kv_len) {
 #if FWD_PP_D64
     if (d == 64)
