@@ -1,4 +1,4 @@
-"""The 16-bit forward kernels agree bit for bit.
+"""The 16-bit forward kernels agree bit for bit, and so do the two dK/dV kernels.
 
 Unmasked rows of 1024 keys or more at d_k = 128 run the ping-pong forward,
 and unmasked rows of whole 64-key tiles (256 keys or more) at d_k = 64 the
@@ -75,3 +75,48 @@ def test_pipelined_equals_single_phase(gpu_lib, dtype, B, H, N, sigma, layout):
         outs.append((o, lse))
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("dtype,B,H,N,sigma,layout", [
+    ("bf16", 1, 2, 256, 1.0, "bhnd"), ("bf16", 2, 3, 320, 1.0, "bhnd"), ("bf16", 1, 2, 576, 1.0, "bhnd"),
+    ("f16", 1, 2, 1088, 1.0, "bhnd"), ("bf16", 1, 4, 4096, 1.0, "bhnd"), ("bf16", 2, 3, 2048, 8.0, "bhnd"),
+    ("bf16", 2, 2, 704, 1.0, "qkv_packed"),
+])
+def test_pipelined_dkdv_equals_single_phase(gpu_lib, dtype, B, H, N, sigma, layout):
+    """Unmasked rows of whole 64-query steps (256 queries or more) at d_k = 64 run the software-pipelined dK/dV
+    kernel; a key-padding length equal to N routes the same inputs to the single-phase kernel, which performs
+    the same operations per element in the same order: dK and dV must be identical. The stage is called on its
+    own, so that the fused dK/dV + dQ launch of small grids does not take over."""
+    import torch
+    d = 64
+    x = make_case(B, H, N, d, dtype, seed=7200 + N, qk_sigma=sigma)
+    print(f"pipelined dK/dV {dtype} B={B} H={H} N={N} d={d} sigma={sigma} layout={layout}", flush=True)
+    sys.stdout.flush()
+    q, k, v, do = (to_device(x, n) for n in ("q", "k", "v", "do"))
+    if layout == "qkv_packed":
+        qkv = torch.stack([q.permute(0, 2, 1, 3), k.permute(0, 2, 1, 3), v.permute(0, 2, 1, 3)], dim=2).contiguous()
+        q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+        do = do.permute(0, 2, 1, 3).contiguous()
+    shape = (B, N, H, d) if layout == "qkv_packed" else (B, H, N, d)
+    o = torch.empty(shape, dtype=q.dtype, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    gpu_lib.attn_fwd_ex(q, k, v, o, lse, x.scale, layout=layout)
+    ws = gpu_lib.workspace_for(q)
+
+    def grads():  # dQ, dK, dV filled with NaN (slices of one packed buffer for the packed layout)
+        if layout == "qkv_packed":
+            g = torch.full((B, N, 3, H, d), float("nan"), dtype=q.dtype, device="cuda")
+            return g[:, :, 0], g[:, :, 1], g[:, :, 2]
+        return tuple(torch.full(shape, float("nan"), dtype=q.dtype, device="cuda") for _ in range(3))
+
+    gpu_lib.attn_bwd_stage(0, q, k, v, o, lse, do, *grads(), x.scale, ws, layout=layout)
+    full = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    outs = []
+    for kv in (None, full):
+        dq, dk, dv = grads()
+        gpu_lib.attn_bwd_stage(1, q, k, v, o, lse, do, dq, dk, dv, x.scale, ws, kv_len=kv, layout=layout)
+        outs.append((dk, dv))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(outs[0][0].float()).all()) and bool(torch.isfinite(outs[0][1].float()).all())
+    assert torch.equal(outs[0][0], outs[1][0]), "dK"
+    assert torch.equal(outs[0][1], outs[1][1]), "dV"

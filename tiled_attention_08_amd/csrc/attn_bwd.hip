@@ -397,6 +397,310 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
                            scale, kv_len, H, causal, sq, sd, sg);
 }
 
+// ---------------------------------------------------------------- stage 1, software-pipelined (d_k = 64)
+// The dK/dV kernel above runs each 64-query step as three dependent phases
+// (S and dP products, then the exponentials, then the dV and dK products), so
+// a wave's matrix products and its vector ALU work never overlap; the other
+// wave on the SIMD is left to fill the gaps, which it does poorly (a wave
+// issuing exponentials slows a neighbour's matrix products far more than the
+// same exponentials interleaved in the product stream of one wave). This
+// variant is for the unmasked case with N a multiple of 64 and d_k = 64 (the
+// long-sequence shapes). It splits a step into two 32-query units
+// and runs one slot per unit: the slot of unit t issues the dV and dK products
+// of unit t - 1 and the S and dP products of unit t + 1 while computing P and
+// dS of unit t from the S and dP accumulators of the previous slot. Each of
+// the 16 chunks of a slot holds one matrix product, one exponential and its
+// fma, multiply and half a pack. Same arithmetic in the same order as the
+// kernel above: bit-identical results. Measured at B=8, H=16, N=4096: 997.6
+// -> 987.3 us with a ring of 3 step tiles (4: 989.3 us; operands read 1, 2
+// or 3 products ahead: 1044.5, 987.3, 987.6 us); matrix-core busy time stays
+// near 60 % of the cycles. The products' power draw with random operands,
+// not the instruction schedule, sets the pace.
+#ifndef BWD_SP
+#define BWD_SP 1
+#endif
+#ifndef BWD_SP_RING
+#define BWD_SP_RING 3
+#endif
+#ifndef BWD_SP_AHEAD
+#define BWD_SP_AHEAD 2
+#endif
+// Chunks of a slot that read the next unit's -delta and lse.
+#ifndef BWD_SP_DLREAD
+#define BWD_SP_DLREAD 4
+#endif
+#ifndef BWD_SP_LREAD
+#define BWD_SP_LREAD 12
+#endif
+
+struct DkdvSpShape {
+  static constexpr int D = 64, BRQ = 64, ROWB = 2 * D;
+  static constexpr int QTILEB = BRQ * ROWB;            // one Q or dO step tile (8 KB)
+  static constexpr int QDMA = BRQ * D / 8 / kThreads;  // 16-byte DMAs per lane per tile (2)
+  static constexpr int OFF_Q = 0;
+  static constexpr int OFF_DO = QTILEB;
+  static constexpr int OFF_L = 2 * QTILEB;             // lse * log2(e) of the step's 64 queries
+  static constexpr int OFF_DL = OFF_L + BRQ * 4;       // -delta
+  static constexpr int SLOTB = OFF_DL + BRQ * 4;       // one ring slot
+};
+
+template <class E, int NS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                        const uint16_t* __restrict__ dO, const float* __restrict__ lse2,
+                        const float* __restrict__ ndelta, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
+                        int n_kblk, int total, float c, float scale, int H, Strides sq, Strides sd, Strides sg) {
+  using S = DkdvSpShape;
+  constexpr int D = S::D;
+  static_assert(NS == 3 || NS == 4, "ring of 3 or 4 step tiles");
+  // One LDS array per ring slot: the compiler then sees that the copy into
+  // one slot cannot alias the reads of another.
+  __shared__ __attribute__((aligned(16))) unsigned char ring0[S::SLOTB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring1[S::SLOTB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring2[S::SLOTB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring3[NS == 4 ? S::SLOTB : 16];
+  auto slot_base = [&](auto r_) __attribute__((always_inline)) -> unsigned char* {
+    constexpr int R = decltype(r_)::value % NS;
+    if constexpr (R == 0) return ring0;
+    else if constexpr (R == 1) return ring1;
+    else if constexpr (R == 2) return ring2;
+    else return ring3;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 4, gi = lane & 15;
+  const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
+  const int work = xcd_remap(blockIdx.x, total);
+  const int bh = work / n_kblk, kblk = work - bh * n_kblk;
+  const size_t hq = head_off(sq, bh, H), hd = head_off(sd, bh, H), hg = head_off(sg, bh, H);
+  const size_t hrow = (size_t)bh * N;
+  const int key = kblk * 128 + wave * 32 + l32;  // this lane's key (keys past N compute unused gradients)
+
+  u32x4 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) {
+    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+    if (key < N) {
+      a = *reinterpret_cast<const u32x4*>(K + hq + key * sq.n + cc * 16 + h * 8);
+      b = *reinterpret_cast<const u32x4*>(V + hq + key * sq.n + cc * 16 + h * 8);
+    }
+    kf[cc] = a;
+    vf[cc] = b;
+  }
+
+  const Rsrc rQ = make_rsrc(Q + hq), rdO = make_rsrc(dO + hd);
+  const Rsrc rL = make_rsrc(lse2 + hrow), rDL = make_rsrc(ndelta + hrow);
+  // DMA counts per tile: 2 * QDMA for every wave, one more for waves 0 and 1.
+  constexpr int PER = 2 * S::QDMA;
+  auto dma_tile = [&](int i, auto r_) __attribute__((always_inline)) {
+    unsigned char* base = slot_base(r_);
+    const int q0 = i * S::BRQ;
+#pragma unroll
+    for (int r = 0; r < S::QDMA; ++r) {
+      const int slot0 = (wave * S::QDMA + r) * 64;
+      const int p = slot0 + lane;
+      const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz<S::ROWB>(row);
+      dma16(rQ, (uint32_t)((q0 + row) * sq.n + chunk * 8) * 2u, base + S::OFF_Q + slot0 * 16);
+      dma16(rdO, (uint32_t)((q0 + row) * sd.n + chunk * 8) * 2u, base + S::OFF_DO + slot0 * 16);
+    }
+    if (wave == 0) dma4(rL, (uint32_t)(q0 + lane) * 4u, base + S::OFF_L);
+    if (wave == 1) dma4(rDL, (uint32_t)(q0 + lane) * 4u, base + S::OFF_DL);
+  };
+
+  // Per-lane LDS offsets (query block 0, 16-query half 0; the other blocks
+  // and halves add whole rows, which leave the swizzle unchanged).
+  int koff[D / 16], toff[2][2];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) koff[cc] = tile_off<S::ROWB>(l32, cc * 16 + h * 8);
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) toff[db][hi] = tile_off<S::ROWB>(4 * h + er + 8 * hi, db * 32 + dsub * 16 + 4 * qq);
+
+  // Product m of a slot: m < 8 the dV / dK products of the previous unit
+  // (kind m & 1: dV^T += dO^T P or dK^T += Q^T dS; 32-dim block (m >> 1) & 1;
+  // 16-query half m >> 2), m >= 8 the S / dP products of the next unit
+  // (b = m - 8: kind b & 1: S = Q K^T or dP = dO V^T; 16-dim chunk b >> 1).
+  // Operand of product m: transposed dO or Q fragment, or a Q or dO fragment.
+  auto operand = [&](int m, auto ra_, auto mba_, auto rb_, auto mbb_) __attribute__((always_inline)) -> u32x4 {
+    if (m < 8) {
+      const unsigned char* T = slot_base(ra_) + ((m & 1) ? S::OFF_Q : S::OFF_DO);
+      const int rows = (decltype(mba_)::value * 32 + (m >> 2) * 16) * S::ROWB, db = (m >> 1) & 1;
+      return cat(lds_read_tr16_b64(T, rows + toff[db][0]), lds_read_tr16_b64(T, rows + toff[db][1]));
+    }
+    const int b = m - 8;
+    const unsigned char* T = slot_base(rb_) + ((b & 1) ? S::OFF_DO : S::OFF_Q);
+    return lds_read_b128(T, decltype(mbb_)::value * 32 * S::ROWB + koff[b >> 1]);
+  };
+
+  f32x16 dvacc[2], dkacc[2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    dvacc[db] = f32x16{};
+    dkacc[db] = f32x16{};
+  }
+
+  // One slot. A (HA): dV / dK products of the unit in query block MBA of the
+  // tile in ring slot RA, from its bf16 P and dS in ya / yd. B (HB): S and
+  // dP - delta of the unit in query block MBB of the tile in slot RB into sn
+  // / pn, and that unit's lse into ln. V (HV): P and dS of the current unit
+  // from sv / pv and lse lv into xp / xd (pair i of entries 2i, 2i + 1 goes
+  // to word i & 3 of operand i >> 2).
+  auto slot = [&](auto hasA, auto ra_, auto mba_, const u32x4 (&ya)[2], const u32x4 (&yd)[2], auto hasB, auto rb_,
+                  auto mbb_, f32x16& sn, f32x16& pn, float (&ln)[16], auto hasV, const f32x16& sv, const f32x16& pv,
+                  const float (&lv)[16], u32x4 (&xp)[2], u32x4 (&xd)[2]) __attribute__((always_inline)) {
+    constexpr bool HA = decltype(hasA)::value, HB = decltype(hasB)::value, HV = decltype(hasV)::value;
+    constexpr int MBB = decltype(mbb_)::value;
+    constexpr int AH = BWD_SP_AHEAD, NO = AH + 1;
+    constexpr int M0 = HA ? 0 : 8, M1 = HB ? 16 : 8;  // products [M0, M1)
+    u32x4 ops[NO];
+    static_for<0, AH>([&](auto a_) __attribute__((always_inline)) {
+      constexpr int m = M0 + decltype(a_)::value;
+      if constexpr (m < M1) ops[m % NO] = operand(m, ra_, mba_, rb_, mbb_);
+    });
+    float pe = 0.f, de = 0.f;  // P and dS of the even entry of the pair
+    static_for<0, 16>([&](auto k_) __attribute__((always_inline)) {
+      constexpr int KK = decltype(k_)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (HB && KK == BWD_SP_DLREAD) {
+        // -delta of the next unit's rows (8j + 4h + i) starts its dP accumulator.
+        const float* DL = reinterpret_cast<const float*>(slot_base(rb_) + S::OFF_DL) + MBB * 32 + 4 * h;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float4 d4 = *reinterpret_cast<const float4*>(DL + 8 * jj);
+          pn[4 * jj] = d4.x;
+          pn[4 * jj + 1] = d4.y;
+          pn[4 * jj + 2] = d4.z;
+          pn[4 * jj + 3] = d4.w;
+        }
+      }
+      if constexpr (HB && KK == BWD_SP_LREAD) {
+        const float* L = reinterpret_cast<const float*>(slot_base(rb_) + S::OFF_L) + MBB * 32 + 4 * h;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float4 l4 = *reinterpret_cast<const float4*>(L + 8 * jj);
+          ln[4 * jj] = l4.x;
+          ln[4 * jj + 1] = l4.y;
+          ln[4 * jj + 2] = l4.z;
+          ln[4 * jj + 3] = l4.w;
+        }
+      }
+      if constexpr (KK >= M0 && KK < M1) {
+        if constexpr (KK < 8) {
+          constexpr int db = (KK >> 1) & 1, c2 = KK >> 2;
+          if constexpr (KK & 1)
+            dkacc[db] = E::mfma(ops[KK % NO], yd[c2], dkacc[db]);
+          else
+            dvacc[db] = E::mfma(ops[KK % NO], ya[c2], dvacc[db]);
+        } else {
+          constexpr int b = KK - 8, cc = b >> 1;
+          if constexpr (b == 0) sn = f32x16{};
+          if constexpr (b & 1)
+            pn = E::mfma(ops[KK % NO], vf[cc], pn);
+          else
+            sn = E::mfma(ops[KK % NO], kf[cc], sn);
+        }
+      }
+      if constexpr (KK >= M0 && KK + AH < M1) ops[(KK + AH) % NO] = operand(KK + AH, ra_, mba_, rb_, mbb_);
+      if constexpr (HV) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sv[KK], c, -lv[KK]));
+        const float ds = p * pv[KK];
+        if constexpr (KK & 1) {
+          constexpr int i = KK >> 1;
+          xp[i >> 2][i & 3] = E::pack(pe, p);
+          xd[i >> 2][i & 3] = E::pack(de, ds);
+        } else {
+          pe = p;
+          de = ds;
+        }
+      }
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  const int nq = N / S::BRQ;  // steps (the launcher checks N % 64 == 0 and nq >= NS)
+  // Before the slot of unit (i, 1): tile i + 1 landed and visible to every
+  // wave, every wave done with tile i - 1, whose ring slot takes tile
+  // i - 1 + NS.
+  auto boundary = [&](int i, auto r_) __attribute__((always_inline)) {
+    constexpr int R = decltype(r_)::value;
+    if (i + 1 >= nq) return;
+    if constexpr (NS == 4) {
+      if (i + 2 < nq)
+        wait_vmem_below<PER>();
+      else
+        wait_vmem_below<0>();
+    } else {
+      wait_vmem_below<0>();
+    }
+    __syncthreads();
+    if (i - 1 + NS < nq) dma_tile(i - 1 + NS, IntC<(R + NS - 1) % NS>{});
+  };
+
+  f32x16 s_0, g_0, s_1, g_1;          // S and dP - delta of the current units of query blocks 0 and 1
+  float l_0[16], l_1[16];             // their lse * log2(e)
+  u32x4 wp_0[2], wd_0[2], wp_1[2], wd_1[2];  // bf16 P and dS of query blocks 0 and 1
+  // Step i in ring slot R: the slots of units (i, 0) and (i, 1).
+  auto step = [&](int i, auto r_, auto first_, auto last_) __attribute__((always_inline)) {
+    constexpr int R = decltype(r_)::value;
+    constexpr bool FIRST = decltype(first_)::value, LAST = decltype(last_)::value;
+    // unit (i, 0): dV / dK of (i - 1, 1), S / dP of (i, 1), P / dS of (i, 0)
+    slot(BoolC<!FIRST>{}, IntC<(R + NS - 1) % NS>{}, IntC<1>{}, wp_1, wd_1, BoolC<true>{}, r_, IntC<1>{}, s_1, g_1, l_1,
+         BoolC<true>{}, s_0, g_0, l_0, wp_0, wd_0);
+    boundary(i, r_);
+    // unit (i, 1): dV / dK of (i, 0), S / dP of (i + 1, 0), P / dS of (i, 1)
+    slot(BoolC<true>{}, r_, IntC<0>{}, wp_0, wd_0, BoolC<!LAST>{}, IntC<(R + 1) % NS>{}, IntC<0>{}, s_0, g_0, l_0,
+         BoolC<true>{}, s_1, g_1, l_1, wp_1, wd_1);
+  };
+
+  // Prologue: tiles 0 .. NS - 2 in flight, tile 0 resident, S / dP of unit (0, 0).
+  static_for<0, NS - 1>([&](auto r_) __attribute__((always_inline)) { dma_tile(decltype(r_)::value, r_); });
+  wait_vmem_below<0>();
+  __syncthreads();
+  slot(BoolC<false>{}, IntC<0>{}, IntC<0>{}, wp_1, wd_1, BoolC<true>{}, IntC<0>{}, IntC<0>{}, s_0, g_0, l_0,
+       BoolC<false>{}, s_1, g_1, l_1, wp_0, wd_0);
+  // Steps 0 .. nq - 2, NS per iteration (compile-time ring slots), then the
+  // rest and the last step, and the dV / dK of the last unit.
+  step(0, IntC<0>{}, BoolC<true>{}, BoolC<false>{});
+  int i = 1;
+  for (; i + NS <= nq - 1; i += NS) {
+    static_for<0, NS>([&](auto u_) __attribute__((always_inline)) {
+      step(i + decltype(u_)::value, IntC<(1 + decltype(u_)::value) % NS>{}, BoolC<false>{}, BoolC<false>{});
+    });
+  }
+  static_for<0, NS - 1>([&](auto u_) __attribute__((always_inline)) {
+    constexpr int U = decltype(u_)::value;
+    if (i + U < nq - 1) step(i + U, IntC<(1 + U) % NS>{}, BoolC<false>{}, BoolC<false>{});
+  });
+  // The last step, nq - 1, in ring slot (nq - 1) % NS.
+  static_for<0, NS>([&](auto r_) __attribute__((always_inline)) {
+    if ((nq - 1) % NS == decltype(r_)::value) {
+      step(nq - 1, r_, BoolC<false>{}, BoolC<true>{});
+      slot(BoolC<true>{}, r_, IntC<1>{}, wp_1, wd_1, BoolC<false>{}, r_, IntC<0>{}, s_0, g_0, l_0, BoolC<false>{}, s_1, g_1,
+           l_1, wp_0, wd_0);
+    }
+  });
+
+  // Epilogue: dV = (dV^T)^T, dK = scale (dK^T)^T, 16-bit RNE. Lane: key, dims db*32 + 8jj + 4h + 0..3.
+  if (key < N) {
+    uint16_t* dvrow = dV + hg + key * sg.n;
+    uint16_t* dkrow = dK + hg + key * sg.n;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x16& a = dvacc[db];
+        const f32x16& b = dkacc[db];
+        const u32x2 wv = {E::pack(a[4 * jj], a[4 * jj + 1]), E::pack(a[4 * jj + 2], a[4 * jj + 3])};
+        const u32x2 wk = {E::pack(b[4 * jj] * scale, b[4 * jj + 1] * scale),
+                          E::pack(b[4 * jj + 2] * scale, b[4 * jj + 3] * scale)};
+        *reinterpret_cast<u32x2*>(dvrow + db * 32 + 8 * jj + 4 * h) = wv;
+        *reinterpret_cast<u32x2*>(dkrow + db * 32 + 8 * jj + 4 * h) = wk;
+      }
+  }
+}
+
 // ---------------------------------------------------------------- stage 2: dQ
 template <int D, int QB>
 struct DqShape {
@@ -843,6 +1147,15 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
       return hipErrorInvalidValue;
     }
   } else if (stage == 1) {
+    if constexpr (D == 64) {
+      constexpr int NS = BWD_SP_RING;
+      if (BWD_SP && !causal && !kv_len && N % 64 == 0 && N / 64 >= NS) {
+        const int n_kblk = (N + 127) / 128, total = n_kblk * B * H;
+        hipLaunchKernelGGL((bwd_dkdv_sp_kernel<E, NS>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2,
+                           ndelta, dk, dv, N, n_kblk, total, c, scale, H, st[0], st[2], st[3]);
+        return hipGetLastError();
+      }
+    }
     constexpr int MB = D == 64 ? BWD_MB64 : 2, KBW = D == 64 ? BWD_KBW64 : 1;
     constexpr int BCK = 4 * 32 * KBW;
     const int n_kblk = (N + BCK - 1) / BCK;

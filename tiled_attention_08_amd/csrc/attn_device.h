@@ -236,6 +236,23 @@ __device__ __forceinline__ void dma4(Rsrc r, uint32_t off, unsigned char* lds_ba
 // Wait until every outstanding global load of this wave (including LDS DMA) has landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt encoding (gfx9): wait until at most N vector-memory operations of
+// this wave are outstanding; LGKM and export counters are left alone.
+template <int N>
+__device__ __forceinline__ void wait_vmem_below() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Calls f(IntC<I>{}) for I = B .. E-1 in order (compile-time indices).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(IntC<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Work-item index for a 1-D grid, grouping consecutive work items on one XCD.
 // Workgroups are handed to the 8 XCDs round-robin by launch index; this
 // bijection gives XCD x a contiguous block of work items (the same heads, so

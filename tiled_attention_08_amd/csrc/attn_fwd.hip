@@ -137,23 +137,6 @@ struct FwdShape {
                 "every lane takes part in each tile DMA, the same number of times");
 };
 
-// s_waitcnt encoding (gfx9): wait until at most N vector-memory operations of
-// this wave are outstanding; LGKM and export counters are left alone.
-template <int N>
-__device__ __forceinline__ void wait_vmem_below() {
-  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
-// Calls f(IntC<I>{}) for I = B .. E-1 in order (compile-time indices).
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(IntC<B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
 template <class E, int D, int QB, int KB, int NS, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(FWD_WAVES_PER_EU, FWD_WAVES_PER_EU)))
 void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
