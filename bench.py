@@ -121,6 +121,19 @@ def roofline_of(kernel: str, avg_ms: float, flops: float, nbytes: float, workloa
     return r
 
 
+def host_threads() -> dict:
+    """Threads the oracle runs on: "cores" = the BLAS pool's thread count (numpy's products are the only
+    multi-threaded part), "affinity_cores" = len(os.sched_getaffinity(0)), the host cores this process may use."""
+    affinity = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [int(p.get("num_threads", 1)) for p in threadpool_info() if p.get("user_api") == "blas"]
+    except Exception:  # threadpoolctl missing: numpy's BLAS uses the affinity set
+        blas = []
+    threads = max(blas) if blas else affinity
+    return {"cores": threads, "blas_threads": threads if blas else None, "affinity_cores": affinity}
+
+
 def cpu_baseline(wid: int, seed: int, budget_s: float, causal: bool = False) -> dict:
     """The fp64 oracle (forward + backward) on whole heads of the workload, for about ``budget_s`` seconds."""
     import numpy as np
@@ -128,11 +141,6 @@ def cpu_baseline(wid: int, seed: int, budget_s: float, causal: bool = False) -> 
     from oracle import attention_bwd, attention_fwd, masked_attention_bwd, masked_attention_fwd
     w = WORKLOADS[wid]
     x = make_inputs(wid, seed=seed)
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing: numpy's BLAS uses the affinity set
-        cores = len(os.sched_getaffinity(0))
     heads, elapsed = 0, 0.0
     order = [(b, h) for b in range(w.B) for h in range(w.H)]
     while heads < len(order) and (heads == 0 or elapsed * (heads + 1) / heads <= budget_s):
@@ -151,7 +159,7 @@ def cpu_baseline(wid: int, seed: int, budget_s: float, causal: bool = False) -> 
         elapsed += time.perf_counter() - t0
         heads += 1
     flops = (fwd_flops(1, heads, w.N, w.d, causal) + (bwd_flops(1, heads, w.N, w.d, causal) if "bwd" in w.passes else 0.0))
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", **host_threads(), "kind": "oracle",
             "sample": f"{heads} of {w.B * w.H} heads of the same workload ({'+'.join(w.passes)}{', causal' if causal else ''}, fp64, full N x N per head), "
                       f"{elapsed:.1f} s", "seconds": round(elapsed, 3)}
 
@@ -296,11 +304,6 @@ def cpu_baseline_block(B, N, D, H, d, seed: int, budget_s: float) -> dict:
     import numpy as np
     c = make_proj_case(B, N, D, H, d, "bf16", seed=seed, wid=2)
     g = make_case(B, H, N, d, "bf16", seed=seed, wid=2)
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([int(p.get("num_threads", 1)) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-    except Exception:
-        cores = len(os.sched_getaffinity(0))
     X, W, DO = c.f64("x"), c.f64("w"), g.f64("do")
     scale = g.scale
     imgs, elapsed = 0, 0.0
@@ -317,7 +320,7 @@ def cpu_baseline_block(B, N, D, H, d, seed: int, budget_s: float) -> dict:
         elapsed += time.perf_counter() - t0
         imgs += 1
     flops = imgs * (3 * proj_flops(1, N, D, H, d) + fwd_flops(1, H, N, d) + bwd_flops(1, H, N, d))
-    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", **host_threads(), "kind": "oracle",
             "sample": f"{imgs} of {B} images of the same block (projection, attention and their backward, fp64), "
                       f"{elapsed:.1f} s", "seconds": round(elapsed, 3)}
 
