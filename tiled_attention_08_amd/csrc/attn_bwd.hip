@@ -923,8 +923,24 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 // dQ work fills the CUs that the last dK/dV workgroups leave idle instead of
 // waiting for a second launch. total1 is a multiple of 8, so both halves keep
 // their XCD assignment.
+// Launch shape of the fused kernel: one 32-query block per dQ wave (128
+// queries per dQ workgroup), and 32-query dK/dV steps for rows shorter than
+// BWD_FUSE_MB1_N (64-query steps otherwise). Measured per launch (identical
+// outputs): B=32, H=12, N=196 45.9 -> 38.5 us; causal B=16, H=12, N=197
+// 22.8 -> 18.6 us; B=4, H=12, N=2048 190.4 -> 182.7 us (32-query dK/dV steps
+// there: 192.4 us). Three waves per SIMD spill (168 registers) and measured
+// 1.3-2x slower.
+#ifndef BWD_FUSE_QB
+#define BWD_FUSE_QB 1
+#endif
+#ifndef BWD_FUSE_MB1_N
+#define BWD_FUSE_MB1_N 1024
+#endif
+#ifndef BWD_FUSE_WPE
+#define BWD_FUSE_WPE BWD_WAVES_PER_EU
+#endif
 template <class E, int D, int MB, int QB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BWD_WAVES_PER_EU, BWD_WAVES_PER_EU)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BWD_FUSE_WPE, BWD_FUSE_WPE)))
 void bwd_dkdv_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                         const uint16_t* __restrict__ dO, const float* __restrict__ lse2, const float* __restrict__ ndelta,
                         uint16_t* __restrict__ dQ, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
@@ -1135,14 +1151,19 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
                        lse, lse2, ndelta, rows, N, H, st[1], st[2]);
   } else if (stage == 3) {  // stages 1 and 2 in one launch (callers check bwd_can_fuse)
     if constexpr (D <= 64) {  // only instantiated where bwd_can_fuse can say yes
-      constexpr int QB = 2;
+      constexpr int QB = BWD_FUSE_QB;
       constexpr int BCK = 4 * 32;
       const int n_kblk = (N + BCK - 1) / BCK, total1 = n_kblk * B * H;
       constexpr int BR = DqShape<D, QB>::BR;
       const int n_qblk = (N + BR - 1) / BR, total2 = n_qblk * B * H;
-      hipLaunchKernelGGL((bwd_dkdv_dq_kernel<E, D, 2, QB>), dim3(total1 + total2), dim3(kThreads), 0, stream, q, k,
-                         v, dO, lse2, ndelta, dq, dk, dv, N, n_kblk, total1, n_qblk, total2, c, scale, kv_len, H,
-                         causal, st[0], st[2], st[3]);
+      if (D == 64 && N < BWD_FUSE_MB1_N)  // 32-query steps split evenly over the DMA lanes at d_k = 64 only
+        hipLaunchKernelGGL((bwd_dkdv_dq_kernel<E, D, (D == 64 ? 1 : 2), QB>), dim3(total1 + total2), dim3(kThreads),
+                           0, stream, q, k, v, dO, lse2, ndelta, dq, dk, dv, N, n_kblk, total1, n_qblk, total2, c,
+                           scale, kv_len, H, causal, st[0], st[2], st[3]);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_dq_kernel<E, D, 2, QB>), dim3(total1 + total2), dim3(kThreads), 0, stream, q, k,
+                           v, dO, lse2, ndelta, dq, dk, dv, N, n_kblk, total1, n_qblk, total2, c, scale, kv_len, H,
+                           causal, st[0], st[2], st[3]);
     } else {
       return hipErrorInvalidValue;
     }

@@ -65,14 +65,31 @@ constexpr float kRescaleSlack = 8.0f;  // log2 units a row max may grow before O
 #ifndef FWD_NS64
 #define FWD_NS64 2
 #endif
-// Rows shorter than FWD_LONG_N: K/V tiles in flight (4 = a whole 196-key
-// head issued at once with 64-key tiles).
+// Rows shorter than FWD_LONG_N at d = 64 (the ViT heads): 4-wave workgroups
+// of one 32-query block per wave (128 queries), a ring of 2 K/V tiles (32 KB
+// of LDS) and three waves per SIMD (at most 168 registers, no spills), so
+// that three workgroups share each CU: B=32, H=12, N=196 is 768 workgroups,
+// one round of exactly three per CU. Measured (bit-identical outputs): 19.2
+// -> 15.0 us per forward, causal B=16, H=12, N=197 15.6 -> 10.2 us. Two
+// 32-query blocks per wave (one 256-query workgroup per head, 1.5 rounds of
+// two per CU) were the previous shape; one block per wave with four waves
+// per SIMD spills, and with a ring of 4 tiles only two workgroups fit per CU
+// (24.7 and 19.3 us).
 #ifndef FWD_QB64_SHORT
-#define FWD_QB64_SHORT 2
+#define FWD_QB64_SHORT 1
 #endif
 #ifndef FWD_NS_SHORT
 #define FWD_NS_SHORT 2
 #endif
+#ifndef FWD_WAVES_SHORT64
+#define FWD_WAVES_SHORT64 4
+#endif
+#ifndef FWD_SHORT_WPE
+#define FWD_SHORT_WPE 3
+#endif
+constexpr int fwd_waves_per_eu(int D, int QB, int WAVES) {
+  return D == 64 && QB == 1 && WAVES == FWD_WAVES_SHORT64 ? FWD_SHORT_WPE : FWD_WAVES_PER_EU;
+}
 // Unmasked long rows use the ping-pong kernel at d = 128. At d = 64 (FWD_PP_D64)
 // it measured 1.5 % faster than fwd_kernel but needs more than 256 registers
 // per lane outside its main loop, and those spills double its HBM traffic,
@@ -138,7 +155,8 @@ struct FwdShape {
 };
 
 template <class E, int D, int QB, int KB, int NS, int WAVES>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(FWD_WAVES_PER_EU, FWD_WAVES_PER_EU)))
+__global__ __launch_bounds__(WAVES * 64)
+__attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu(D, QB, WAVES), fwd_waves_per_eu(D, QB, WAVES))))
 void fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                      uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qblk, int total, float c,
                      uint32_t qsign, const int* __restrict__ kv_len, int H, int causal, Strides sq, Strides so) {
@@ -1284,7 +1302,7 @@ static hipError_t launch_fwd_e(const uint16_t* q, const uint16_t* k, const uint1
                          : (lng ? ATTN_FWD(32, 1, 4, 2, 4) : ATTN_FWD(32, 2, 2, FWD_NS_SHORT, 4));
     case 64:
       return lng_small_d ? ATTN_FWD(64, FWD_QB64, FWD_KB64, FWD_NS64, FWD_WAVES_LONG)
-                         : ATTN_FWD(64, FWD_QB64_SHORT, FWD_KB64, FWD_NS_SHORT, 4);
+                         : ATTN_FWD(64, FWD_QB64_SHORT, FWD_KB64, FWD_NS_SHORT, FWD_WAVES_SHORT64);
     case 96:
       return lng ? ATTN_FWD(96, 1, 4, 2, FWD_WAVES_LONG) : ATTN_FWD(96, 1, 4, 2, 4);
     default:
