@@ -105,13 +105,9 @@ constexpr int fwd_waves_per_eu(int D, int QB, int WAVES) {
 #define FWD_SP_MIN_N 256
 #endif
 // Schedule of the pipelined forward: operands read FWD_SP_AHEAD products ahead;
-// FWD_SP_SKEW packs and sums each pair of weights one chunk after its
-// exponentials; FWD_SP_BARRIER keeps the compiler from moving work across chunks.
+// FWD_SP_BARRIER keeps the compiler from moving work across chunks.
 #ifndef FWD_SP_AHEAD
 #define FWD_SP_AHEAD 2
-#endif
-#ifndef FWD_SP_SKEW
-#define FWD_SP_SKEW 0
 #endif
 #ifndef FWD_SP_BARRIER
 #define FWD_SP_BARRIER 1
@@ -808,6 +804,9 @@ void fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 // wave) the tile takes the full path of fwd_kernel: maximum, move, rescale
 // and exponentials again. A tile that passes computed exactly the
 // exponentials fwd_kernel computes, so the outputs are equal bit for bit.
+// After a unit whose reference moved, the next unit of that query block
+// takes the maximum first, as fwd_kernel does (the same result, without the
+// wasted exponentials when the maximum keeps rising).
 // ------------------------------------------------------------------------
 constexpr int kSPRing = 4;
 // Row-sum share of one tile above which the full path runs: below 2^kRescaleSlack
@@ -929,10 +928,11 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     p[kb][e >> 3][(e >> 1) & 3] = w;
     l = E::sum_pair(w, l);
   };
-  // The full path of fwd_kernel for one unit whose speculative weights failed
-  // the check (rare): maximum, reference move and rescale, weights again.
-  auto softmax_slow = [&](auto qb_, const f32x16 (&sv)[KB], u32x4 (&p)[KB][2], float l_old, float& l)
-                          __attribute__((always_inline)) {
+  // The first step of fwd_kernel's softmax for one unit: the maximum of its
+  // scores and, when the reference has to move (ballot over the wave), the
+  // move and the rescale of O. Returns the factor for l (1 without a move)
+  // and whether the reference moved (wave-uniform).
+  auto move_reference = [&](auto qb_, const f32x16 (&sv)[KB], float& alpha) __attribute__((always_inline)) -> bool {
     constexpr int QB_ = decltype(qb_)::value;
     float xs[KB * 16];
 #pragma unroll
@@ -941,16 +941,36 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       for (int e = 0; e < 16; ++e) xs[kb * 16 + e] = sv[kb][e];
     const float mx = halves_max(max_tree<KB * 16>(xs)) * c;
     const float mnew = fmaxf(m_run[QB_], mx);
+    alpha = 1.f;
     if (__builtin_amdgcn_ballot_w64(mnew > m_run[QB_] + kRescaleSlack)) {
-      const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[QB_] - mnew);
+      alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[QB_] - mnew);
       m_run[QB_] = mnew;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) oacc[QB_][db] *= alpha;
-      l = l_old * alpha;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) weight_pair(qb_, i, sv, p, l);
+      return true;
     }
+    return false;
   };
+  // The full path of fwd_kernel for one unit whose speculative weights failed
+  // the check: maximum, reference move and rescale, weights again. Returns
+  // whether the reference moved.
+  auto softmax_slow = [&](auto qb_, const f32x16 (&sv)[KB], u32x4 (&p)[KB][2], float l_old, float& l)
+                          __attribute__((always_inline)) -> bool {
+    float alpha;
+    if (!move_reference(qb_, sv, alpha)) return false;
+    l = l_old * alpha;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) weight_pair(qb_, i, sv, p, l);
+    return true;
+  };
+  // Per query block: the last unit moved the reference. Then the next unit
+  // takes the maximum first (fwd_kernel's order) instead of speculating: with
+  // peaked scores the row maximum keeps rising for many tiles and most
+  // speculative weights would be computed twice. Every row block starts with
+  // a move (from -infinity).
+  bool moved_last[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) moved_last[qb] = true;
 
   // One unit: softmax of query block QS (S^T in sv -> P^T in pw), with S^T of
   // query block QN against the K tile in slot RS into sn (HAS_S) and P V of
@@ -974,15 +994,20 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) sn[kb] = f32x16{};
     }
-    const float l_old = l_run[QS];
+    const bool max_first = moved_last[QS];
+    bool moved = false;
+    float l_old = l_run[QS];
+    if (max_first) {
+      float alpha;
+      moved = move_reference(qs_, sv, alpha);
+      l_old *= alpha;
+    }
     float l = l_old;
     constexpr int AH = FWD_SP_AHEAD, NO = AH + 1;  // operands read AH products ahead
     u32x4 ops[NO];
     static_for<0, AH>([&](auto a_) __attribute__((always_inline)) {
       if constexpr (decltype(a_)::value < NM) ops[decltype(a_)::value] = operand(decltype(a_)::value);
     });
-    const float nm = -m_run[QS];
-    float e0 = 0.f, e1 = 0.f;  // exponentials of the previous pair (FWD_SP_SKEW)
     static_for<0, 16>([&](auto i_) __attribute__((always_inline)) {
       constexpr int I = decltype(i_)::value;
       if (FWD_SP_BARRIER) __builtin_amdgcn_sched_barrier(0);
@@ -997,29 +1022,14 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         }
       }
       if constexpr (I + AH < NM) ops[(I + AH) % NO] = operand(I + AH);
-      if constexpr (FWD_SP_SKEW) {
-        constexpr int kb = I >> 3, e = 2 * (I & 7);
-        const float f0 = __builtin_amdgcn_exp2f(fmaf(sv[kb][e], c, nm));
-        const float f1 = __builtin_amdgcn_exp2f(fmaf(sv[kb][e + 1], c, nm));
-        if constexpr (I > 0) {
-          constexpr int pk = (I - 1) >> 3, pe = 2 * ((I - 1) & 7);
-          const uint32_t w = E::pack(e0, e1);
-          pw[pk][pe >> 3][(pe >> 1) & 3] = w;
-          l = E::sum_pair(w, l);
-        }
-        e0 = f0;
-        e1 = f1;
-      } else {
-        weight_pair(qs_, I, sv, pw, l);
-      }
+      weight_pair(qs_, I, sv, pw, l);
     });
-    if constexpr (FWD_SP_SKEW) {
-      const uint32_t w = E::pack(e0, e1);
-      pw[1][1][3] = w;
-      l = E::sum_pair(w, l);
-    }
     __builtin_amdgcn_sched_barrier(0);
-    if (__builtin_amdgcn_ballot_w64(!(l - l_old <= kSpecLimit))) softmax_slow(qs_, sv, pw, l_old, l);
+    // After the maximum-first path the weights are those of fwd_kernel (at
+    // most 2^kRescaleSlack each) and need no check.
+    if (!max_first && __builtin_amdgcn_ballot_w64(!(l - l_old <= kSpecLimit)))
+      moved = softmax_slow(qs_, sv, pw, l_old, l);
+    moved_last[QS] = moved;
     l_run[QS] = l;
   };
 
