@@ -98,9 +98,48 @@ def measured_traffic(workload: str, kernel: str):
 
 
 def fwd_kernel_name(N: int, d: int, causal: bool) -> str:
-    """The forward kernel the library launches for a bf16/fp16 shape without key padding: the ping-pong kernel
-    for unmasked rows of 1024 keys or more at d_k 128, the single-phase kernel otherwise."""
+    """The forward kernel the library launches for a bf16/fp16 shape without key padding: the software-pipelined
+    kernel for unmasked rows of whole 64-key tiles (256 keys or more) at d_k 64, the ping-pong kernel for unmasked
+    rows of 1024 keys or more at d_k 128, the single-phase kernel otherwise."""
+    if d == 64 and not causal and N % 64 == 0 and N >= 256:
+        return "fwd_sp_kernel"
     return "fwd_pp_kernel" if N >= 1024 and not causal and d == 128 else "fwd_kernel"
+
+
+def dkdv_kernel_name(N: int, d: int, causal: bool) -> str:
+    """The stand-alone dK/dV kernel for a shape without key padding: the software-pipelined kernel for unmasked
+    rows of at least three whole 64-query steps at d_k 64, the single-phase kernel otherwise."""
+    return "bwd_dkdv_sp_kernel" if d == 64 and not causal and N % 64 == 0 and N >= 192 else "bwd_dkdv_kernel"
+
+
+def mix_of_kernel(kernel: str, d: int):
+    """The instruction mix (libattn_ceiling.so) a 16-bit kernel issues per product, where one was counted:
+    d_k = 64 for the backward kernels and the d_k = 64 forward, d_k = 128 for the forward."""
+    if d == 64:
+        return {"bwd_dkdv_kernel": "dkdv", "bwd_dkdv_sp_kernel": "dkdv", "bwd_dkdv_dq_kernel": "dkdv",
+                "bwd_dq_kernel": "dq", "fwd_kernel": "fwd64", "fwd_sp_kernel": "fwd64"}.get(kernel)
+    if d == 128:
+        return {"fwd_kernel": "fwd128", "fwd_pp_kernel": "fwd128"}.get(kernel)
+    return None
+
+
+# Matrix-core work per unit of algorithmic work: the dQ kernel repeats the S and dP products (3 of its products
+# per algorithmic one), the fused backward launch likewise (14 per 10).
+MFMA_PER_ALGORITHMIC = {"bwd_dq_kernel": 3.0, "bwd_dkdv_dq_kernel": 1.4}
+
+
+def attach_attainable(roofline: dict, d: int, causal: bool) -> None:
+    """Adds the measured matrix-core ceiling of the kernel's instruction mix to an MFMA-bound roofline object:
+    what that mix allows on this chip with random operands (see include/attn_ceiling.h), and the kernel's
+    matrix-core rate as a fraction of it. "peak" and "frac" stay the published figure and the fraction of it.
+    Not for causal launches, whose diagonal tiles do more products than the visible pairs count."""
+    mix = mix_of_kernel(roofline["kernel"], d)
+    if roofline.get("bound") != "mfma" or mix is None or causal:
+        return
+    from tiled_attention_08_amd.ceiling import mix_ceiling
+    c = mix_ceiling(mix)
+    rate = roofline["achieved"] * MFMA_PER_ALGORITHMIC.get(roofline["kernel"], 1.0)
+    roofline["attainable"] = {**c, "kernel_mfma_rate": round(rate, 2), "frac": round(rate / c["value"], 4)}
 
 
 def roofline_of(kernel: str, avg_ms: float, flops: float, nbytes: float, workload: str) -> dict:
@@ -418,7 +457,7 @@ def bench_proj(args, w) -> int:
               "fwd": 4 * E * sz + 4 * R, "bwd_prep": 2 * E * sz + 12 * R, "bwd_dkdv": 6 * E * sz + 8 * R,
               "bwd_dq": 5 * E * sz + 8 * R, "bwd_dkdv_dq": 7 * E * sz + 8 * R}
     kname_full = {"proj_fwd": "gemm256_kernel", "proj_bwd": "attn_qkv_proj_bwd (dx and dw products, split sums)",
-                  "fwd": fwd_kernel_name(N, d, False), "bwd_prep": "bwd_prep_kernel", "bwd_dkdv": "bwd_dkdv_kernel",
+                  "fwd": fwd_kernel_name(N, d, False), "bwd_prep": "bwd_prep_kernel", "bwd_dkdv": dkdv_kernel_name(N, d, False),
                   "bwd_dq": "bwd_dq_kernel", "bwd_dkdv_dq": "bwd_dkdv_dq_kernel"}
     # The roofline describes the longest single kernel (the projection backward is a group of launches).
     single = {kn: t for kn, t in kernels.items() if kn != "proj_bwd"}
@@ -473,10 +512,23 @@ def main(argv=None) -> int:
     ap.add_argument("--proj", action="store_true",
                     help="with --workload 2: time the ViT attention block including the query/key/value projection "
                          "(D = H d_k) and its backward, attention in the packed layout")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the instruction-mix probe that adds the roofline's 'attainable' object")
+    ap.add_argument("--mix-ceiling", action="store_true",
+                    help="only run the instruction-mix probe (libattn_ceiling.so) for every mix and print one JSON "
+                         "line: the sustained matrix-core rate each kernel's mix allows")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (three times) and exit: the "
                          "known-size reference for scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args(argv)
+    if args.mix_ceiling:
+        from tiled_attention_08_amd.ceiling import MIXES, mix_ceiling
+        res = {m: mix_ceiling(m) for m in MIXES}
+        print(json.dumps({"metric": "sustained bf16 matrix-core rate per instruction mix", "unit": "TFLOP/s",
+                          "peak": PEAK_BF16_TFLOPS,
+                          "mixes": {m: {**r, "frac_of_peak": round(r["value"] / PEAK_BF16_TFLOPS, 4)}
+                                    for m, r in res.items()}}), flush=True)
+        return 0
     if args.copy_calibration_mib:
         import torch
         n = args.copy_calibration_mib << 20
@@ -652,11 +704,13 @@ def main(argv=None) -> int:
     E, R, sz = B * H * N * d, B * H * N, 2
     kbytes = {"fwd": 4 * E * sz + 4 * R, "bwd_prep": 2 * E * sz + 12 * R, "bwd_dkdv": 6 * E * sz + 8 * R,
               "bwd_dq": 5 * E * sz + 8 * R, "bwd_dkdv_dq": 7 * E * sz + 8 * R}
-    kname_full = {"fwd": fwd_kernel_name(N, d, cz), "bwd_dkdv": "bwd_dkdv_kernel", "bwd_dq": "bwd_dq_kernel",
+    kname_full = {"fwd": fwd_kernel_name(N, d, cz), "bwd_dkdv": dkdv_kernel_name(N, d, cz), "bwd_dq": "bwd_dq_kernel",
                   "bwd_prep": "bwd_prep_kernel", "bwd_dkdv_dq": "bwd_dkdv_dq_kernel"}
     dominant = max(kernels, key=kernels.get)
     wkey = w.name + ("_causal" if cz else "") + ("_f16" if args.dtype == "f16" else "")
     roofline = roofline_of(kname_full[dominant], kernels[dominant], kflops[dominant], kbytes[dominant], wkey)
+    if not args.no_ceiling:
+        attach_attainable(roofline, d, cz)
     if args.cold:
         roofline["inputs"] = f"rotating {len(sets)} input sets ({set_bytes * len(sets) / 2**30:.2f} GiB, beyond L2 and MALL)"
 

@@ -317,3 +317,28 @@ def test_binding_refuses_host_tensors(L, monkeypatch):
     for call in calls:
         with pytest.raises(ValueError, match="GPU tensors"):
             call()
+
+
+def test_ceiling_library_exports_its_header():
+    """libattn_ceiling.so (the instruction-mix probe) exports what include/attn_ceiling.h declares, the binding
+    lists the same names, and the mixes it names match the header's enum."""
+    from tiled_attention_08_amd import ceiling
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "attn_ceiling.h")).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+    assert declared == sorted(ceiling.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", ceiling.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    assert set(declared) <= set(re.findall(r"\bT (attn_\w+)", out))
+    enum = dict((k.lower(), int(v)) for k, v in re.findall(r"ATTN_MIX_(\w+)\s*=\s*(\d+)", text))
+    assert enum == {k: v[0] for k, v in ceiling.MIXES.items()}
+    L = ceiling.load()
+    assert L.attn_mix_ceiling_workspace_bytes() > 0
+    assert L.attn_mix_ceiling_flop(10) == 256 * 8 * 10 * 8 * 32768.0
+    # Rejected on the host before any HIP call: unknown mix, bad iteration count, null workspace.
+    import ctypes
+    ms = ctypes.c_float()
+    big = L.attn_mix_ceiling_workspace_bytes()
+    assert L.attn_mix_ceiling(9, 10, 0x1000, big, ctypes.byref(ms), None) == -1
+    assert L.attn_mix_ceiling(1, 0, 0x1000, big, ctypes.byref(ms), None) == -1
+    assert L.attn_mix_ceiling(1, 10, None, big, ctypes.byref(ms), None) == -1
+    assert L.attn_mix_ceiling(1, 10, 0x1000, 16, ctypes.byref(ms), None) == -3

@@ -1,9 +1,10 @@
-"""Build libattn.so (the HIP kernels and the C ABI) in-tree for gfx950.
+"""Build libattn.so (the HIP kernels and the C ABI) and libattn_ceiling.so (the instruction-mix probe that
+measured roofline fractions are read against) in-tree for gfx950.
 
     python -m tiled_attention_08_amd.build          # compile
     python -m tiled_attention_08_amd.build --asm    # also keep the gfx950 assembly under _build/asm
 
-Always recompiles; the result lands next to this file as ``libattn.so``.
+Always recompiles; the results land next to this file.
 """
 from __future__ import annotations
 
@@ -17,6 +18,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libattn.so")
+CEILING_LIB = os.path.join(PKG, "libattn_ceiling.so")
+CEILING_SRC = "mix_ceiling.hip"
 SOURCES = ["attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_proj.hip"]
 ARCH = "gfx950"
 
@@ -54,6 +57,8 @@ def build(verbose: bool = False, asm: bool = False) -> str:
             os.makedirs(asmdir, exist_ok=True)
             jobs.append(([cc, *flags(), "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o",
                           os.path.join(asmdir, src.replace(".hip", f"-{ARCH}.s"))], None))
+    ceiling_obj = os.path.join(objdir, CEILING_SRC.replace(".hip", ".o"))
+    jobs.append(([cc, *flags(), "-c", os.path.join(CSRC, CEILING_SRC), "-o", ceiling_obj], None))
     # The translation units are independent: compile them side by side.
     procs = []
     for cmd, _ in jobs:
@@ -70,6 +75,12 @@ def build(verbose: bool = False, asm: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    tmp = CEILING_LIB + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", ceiling_obj, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, CEILING_LIB)
     return LIB
 
 
