@@ -71,12 +71,13 @@ def time_launches(fn, reps: int) -> float:
 
 
 def sources_sha256() -> str:
-    """sha256 over the library's kernel sources (csrc/*.hip and *.h, sorted by path)."""
+    """sha256 over the attention library's kernel sources (csrc/attn_*.hip and *.h, sorted by path; the
+    instruction-mix probe's source is not part of it)."""
     import glob
     import hashlib
     csrc = os.path.join(ROOT, "tiled_attention_08_amd", "csrc")
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+    for p in sorted(glob.glob(os.path.join(csrc, "attn_*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
