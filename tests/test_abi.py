@@ -229,12 +229,13 @@ def test_projection_rejections(L):
 def test_projection_workspace_follows_the_split_rule(L):
     """Split products write float32 partial slices: the workspace is the larger of the two products' S * M * N * 4.
     A product with at least 256 rows and columns but fewer than 192 tiles of 256 x 256 splits its contraction
-    min(256 // tiles, K // 512) ways (rounded to whole 64-steps); everything else needs none."""
+    min(256 // tiles, K // 512) ways (rounded to whole 64-steps), unless it has at least 192 tiles of 128 x 128 and
+    a contraction of at most 4096 (then it runs those tiles unsplit); everything else needs none."""
     def ws(B, N, D, H, d):
         return L.attn_qkv_proj_bwd_workspace_bytes(B, N, D, H, d)
-    # ViT-B/16 block: dx (6272 x 768, K 2304) has 25 x 3 = 75 tiles -> 3 splits; dw (768 x 2304, K 6272) has
-    # 3 x 9 = 27 tiles -> 9 splits (kchunk 704). The larger slice set is dw's.
-    assert ws(32, 196, 768, 12, 64) == max(3 * 6272 * 768, 9 * 768 * 2304) * 4
+    # ViT-B/16 block: dx (6272 x 768, K 2304) has 25 x 3 = 75 big tiles but 49 x 6 = 294 of 128 x 128 -> unsplit;
+    # dw (768 x 2304, K 6272) has 3 x 9 = 27 big tiles (6 x 18 = 108 small ones) -> 9 splits (kchunk 704).
+    assert ws(32, 196, 768, 12, 64) == 9 * 768 * 2304 * 4
     # 8 x 300 tokens, D 512, F 768: dx 10 x 2 = 20 tiles, K 768 -> 1 split; dw 2 x 3 = 6 tiles, K 2400 -> 4 splits.
     assert ws(8, 300, 512, 4, 64) == 4 * 512 * 768 * 4
     # 300 tokens, D 1024, F 1536: dx 2 x 4 = 8 tiles, K 1536 -> 3 splits; dw's K of 300 tokens is too short to split.

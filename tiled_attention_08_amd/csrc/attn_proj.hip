@@ -464,6 +464,19 @@ hipError_t launch_gemm(const uint16_t* A, const uint16_t* Bm, uint16_t* C, int M
 #ifndef PROJ_MAX_SPLIT
 #define PROJ_MAX_SPLIT 16
 #endif
+// A product whose 256 x 256 tiles would need a contraction split runs 128 x
+// 128 tiles instead, unsplit (no float32 partial slices, no reduction pass),
+// when those number at least PROJ_MID_NOSPLIT and the contraction is at most
+// PROJ_MID_NOSPLIT_MAXK long. Measured per backward call: B=32, N=196,
+// D=768, H=12 (dX: 294 such tiles, K = 2304) 95.4 -> 85.5 us; B=4, N=1024
+// 79.1 -> 66.6 us; a long contraction (dW at 32768 tokens, 192 tiles) went
+// 456 -> 792 us unsplit, hence the cap.
+#ifndef PROJ_MID_NOSPLIT
+#define PROJ_MID_NOSPLIT 192
+#endif
+#ifndef PROJ_MID_NOSPLIT_MAXK
+#define PROJ_MID_NOSPLIT_MAXK 4096
+#endif
 
 struct GemmPlan {
   bool big;
@@ -480,6 +493,11 @@ GemmPlan plan_gemm(int M, int N, int K, bool split_ok) {
   p.tiles = tiles > INT32_MAX / 16 ? 0 : (int)tiles;  // 0: too many tiles to launch (gemm_auto refuses)
   if (p.tiles == 0) return p;
   p.S = 1;
+  if (PROJ_MID_NOSPLIT > 0 && p.tiles < 192 && K <= PROJ_MID_NOSPLIT_MAXK &&
+      (long)((M + 127) / 128) * ((N + 127) / 128) >= PROJ_MID_NOSPLIT) {
+    p.big = false;  // the 128 x 128 kernel (gemm_auto picks it: at least PROJ_MID_NOSPLIT <= PROJ_MIN_TILES tiles)
+    return p;
+  }
   if (split_ok && p.tiles < 192) p.S = max(1, min(min(256 / p.tiles, K / 512), PROJ_MAX_SPLIT));
   p.kchunk = ((K + p.S - 1) / p.S + 63) / 64 * 64;
   p.S = (K + p.kchunk - 1) / p.kchunk;
@@ -504,7 +522,8 @@ hipError_t gemm_auto(const uint16_t* A, const uint16_t* Bm, uint16_t* C, int M, 
     return hipGetLastError();
   }
   const long mid = (long)((M + 127) / 128) * ((N + 127) / 128);
-  if (mid >= PROJ_MIN_TILES) return launch_gemm<E, AK, BK, 2, 2, 1>(A, Bm, C, M, N, K, lda, ldb, ldc, stream);
+  if (mid >= PROJ_MIN_TILES || (PROJ_MID_NOSPLIT > 0 && mid >= PROJ_MID_NOSPLIT && K <= PROJ_MID_NOSPLIT_MAXK))
+    return launch_gemm<E, AK, BK, 2, 2, 1>(A, Bm, C, M, N, K, lda, ldb, ldc, stream);
   return launch_gemm<E, AK, BK, 1, 1, 4>(A, Bm, C, M, N, K, lda, ldb, ldc, stream);
 }
 
