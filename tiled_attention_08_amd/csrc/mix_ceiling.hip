@@ -67,10 +67,14 @@ __device__ __forceinline__ u32x2 read_tr8(const u32x4* base, int idx) {
 // through the neg/abs modifiers), PACK bf16 packs (v_cvt_pk_bf16_f32),
 // OTHER further vector instructions (fma, multiply and add in turn), R16
 // 16-byte LDS reads and R8 8-byte transposing LDS reads (ds_read_b64_tr_b16,
-// in pairs). Every result is used, so the compiler keeps each instruction:
+// in pairs). The vector instructions are single-instruction volatile asm
+// statements (arithmetic only; no memory access), so each iteration issues
+// exactly these counts; the values they produce are irrelevant. Every result
+// is used besides:
 // exponential e writes X[e], which the other instructions read; other
-// instruction k updates Y[k] once per iteration (a loop-carried value summed
-// at the end, the exponentials' inputs); pack p writes word p / 4 of operand
+// instruction k updates Y[k] once per iteration from the exponentials just
+// computed (a loop-carried value summed at the end, the exponentials'
+// inputs); pack p writes word p / 4 of operand
 // A[4 + p % 4], which a product consumes; the 16-byte reads refill B[j] and
 // the 8-byte pairs A[j] (j < 4) right after product j consumed it. All LDS
 // addresses are fixed per lane. RANDOM = false: constant operands.
@@ -124,21 +128,21 @@ __global__ __launch_bounds__(kThreads) void mix_kernel(const u32x4* __restrict__
       }
       // This product's share of the exponentials, other instructions and packs.
 #pragma unroll
-      for (int e = r * EXP / 8; e < (r + 1) * EXP / 8; ++e) X[e] = __builtin_amdgcn_exp2f(-__builtin_fabsf(Y[e % 40]));
+      for (int e = r * EXP / 8; e < (r + 1) * EXP / 8; ++e)
+        asm volatile("v_exp_f32 %0, -|%1|" : "=v"(X[e]) : "v"(Y[e % 40]));
 #pragma unroll
       for (int k = r * OTHER / 8; k < (r + 1) * OTHER / 8; ++k) {
-        const float xa = X[(k + 1) % (EXP > 0 ? EXP : 16)], xb = X[(k + 2) % (EXP > 0 ? EXP : 16)];
-        if (k % 3 == 0) Y[k] = fmaf(Y[k], xa, xb);
-        else if (k % 3 == 1) Y[k] = Y[k] * xa;
-        else Y[k] = Y[k] + xb;
+        const int e = EXP > 0 ? k * EXP / OTHER : k;
+        const float xa = X[e % 16], xb = X[(e + 1) % (EXP > 0 ? EXP : 16)];
+        if (k % 3 == 0) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(Y[k]) : "v"(xa), "v"(xb));
+        else if (k % 3 == 1) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(Y[k]) : "v"(xa));
+        else asm volatile("v_add_f32 %0, %0, %1" : "+v"(Y[k]) : "v"(xb));
       }
 #pragma unroll
       for (int q = r * PACK / 8; q < (r + 1) * PACK / 8; ++q) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        bf16x2 pr;
-        pr[0] = (__bf16)Y[q % 40];
-        pr[1] = (__bf16)X[q % (EXP > 0 ? EXP : 16)];
-        A[4 + q % 4][(q / 4) % 4] = __builtin_bit_cast(uint32_t, pr);
+        uint32_t w;
+        asm volatile("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(w) : "v"(Y[q % 40]), "v"(X[q % (EXP > 0 ? EXP : 16)]));
+        A[4 + q % 4][(q / 4) % 4] = w;
       }
     }
   }
@@ -161,17 +165,16 @@ hipError_t launch(const u32x4* w, float* out, int iters, hipStream_t s) {
 
 // Per 8 products: exponentials, packs, other vector instructions, 16-byte and 8-byte LDS reads. The
 // exponential and LDS counts are the kernels' (SQ_INSTS_VALU_TRANS_F32, SQ_INSTS_LDS per product x 8); the
-// other count is set so that the compiled loop's vector instructions (with the register moves and address
-// operations the compiler adds) total the kernel's SQ_INSTS_VALU per product x 8, less the products: 35, 49,
-// 54 and 40 instructions in the gfx950 code of the four mixes.
+// other count is set so that the loop's vector instructions (with the 2 the loop itself needs) total the
+// kernel's SQ_INSTS_VALU per product x 8, less the products: 36, 51, 54 and 39.
 hipError_t launch_mix(int mix, const u32x4* w, float* out, int iters, hipStream_t s) {
   switch (mix) {
     case ATTN_MIX_CONSTANT: return launch<false, 0, 0, 0, 0, 0>(w, out, iters, s);
     case ATTN_MIX_RANDOM: return launch<true, 0, 0, 0, 0, 0>(w, out, iters, s);
-    case ATTN_MIX_DKDV: return launch<true, 8, 8, 15, 8, 8>(w, out, iters, s);
-    case ATTN_MIX_DQ: return launch<true, 11, 5, 25, 2, 4>(w, out, iters, s);
-    case ATTN_MIX_FWD64: return launch<true, 16, 8, 17, 4, 8>(w, out, iters, s);
-    case ATTN_MIX_FWD128: return launch<true, 8, 4, 21, 4, 8>(w, out, iters, s);
+    case ATTN_MIX_DKDV: return launch<true, 8, 8, 18, 8, 8>(w, out, iters, s);
+    case ATTN_MIX_DQ: return launch<true, 11, 5, 33, 2, 4>(w, out, iters, s);
+    case ATTN_MIX_FWD64: return launch<true, 16, 8, 28, 4, 8>(w, out, iters, s);
+    case ATTN_MIX_FWD128: return launch<true, 8, 4, 25, 4, 8>(w, out, iters, s);
     default: return hipErrorInvalidValue;
   }
 }
