@@ -100,9 +100,11 @@ def measured_traffic(workload: str, kernel: str):
 
 def fwd_kernel_name(N: int, d: int, causal: bool) -> str:
     """The forward kernel the library launches for a bf16/fp16 shape without key padding: the software-pipelined
-    kernel for unmasked rows of whole 64-key tiles (256 keys or more) at d_k 64, the ping-pong kernel for unmasked
-    rows of 1024 keys or more at d_k 128, the single-phase kernel otherwise."""
+    kernel for unmasked rows of whole 64-key tiles (256 keys or more at d_k 64, 1024 or more at d_k 128), the
+    ping-pong kernel for other unmasked rows of 1024 keys or more at d_k 128, the single-phase kernel otherwise."""
     if d == 64 and not causal and N % 64 == 0 and N >= 256:
+        return "fwd_sp_kernel"
+    if d == 128 and not causal and N % 64 == 0 and N >= 1024:
         return "fwd_sp_kernel"
     return "fwd_pp_kernel" if N >= 1024 and not causal and d == 128 else "fwd_kernel"
 
@@ -120,7 +122,7 @@ def mix_of_kernel(kernel: str, d: int):
         return {"bwd_dkdv_kernel": "dkdv", "bwd_dkdv_sp_kernel": "dkdv", "bwd_dkdv_dq_kernel": "dkdv",
                 "bwd_dq_kernel": "dq", "fwd_kernel": "fwd64", "fwd_sp_kernel": "fwd64"}.get(kernel)
     if d == 128:
-        return {"fwd_kernel": "fwd128", "fwd_pp_kernel": "fwd128"}.get(kernel)
+        return {"fwd_kernel": "fwd128", "fwd_pp_kernel": "fwd128", "fwd_sp_kernel": "fwd128"}.get(kernel)
     return None
 
 

@@ -120,3 +120,32 @@ def test_pipelined_dkdv_equals_single_phase(gpu_lib, dtype, B, H, N, sigma, layo
     assert bool(torch.isfinite(outs[0][0].float()).all()) and bool(torch.isfinite(outs[0][1].float()).all())
     assert torch.equal(outs[0][0], outs[1][0]), "dK"
     assert torch.equal(outs[0][1], outs[1][1]), "dV"
+
+
+@pytest.mark.parametrize("dtype,B,H,N,sigma,layout", [
+    ("bf16", 1, 2, 1024, 1.0, "bhnd"), ("bf16", 2, 2, 2048, 1.0, "bhnd"), ("f16", 2, 1, 1088, 1.0, "bhnd"),
+    ("bf16", 1, 2, 4096, 8.0, "bhnd"), ("bf16", 2, 2, 1152, 1.0, "qkv_packed"),
+])
+def test_pipelined128_equals_single_phase(gpu_lib, dtype, B, H, N, sigma, layout):
+    """Unmasked rows of whole 64-key tiles (1024 keys or more) at d_k = 128 run the software-pipelined forward with
+    one query block per wave; a key-padding length of N routes the same inputs to the single-phase kernel: O and lse
+    must be identical (including peaked scores, whose units take the maximum-first path)."""
+    import torch
+    d = 128
+    x = make_case(B, H, N, d, dtype, seed=7300 + N, qk_sigma=sigma, with_grad=False)
+    print(f"pipelined d=128 {dtype} B={B} H={H} N={N} sigma={sigma} layout={layout}", flush=True)
+    sys.stdout.flush()
+    q, k, v = (to_device(x, n) for n in ("q", "k", "v"))
+    if layout == "qkv_packed":
+        qkv = torch.stack([q.permute(0, 2, 1, 3), k.permute(0, 2, 1, 3), v.permute(0, 2, 1, 3)], dim=2).contiguous()
+        q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    full = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    outs = []
+    for kv in (None, full):
+        o = torch.empty((B, N, H, d) if layout == "qkv_packed" else (B, H, N, d), dtype=q.dtype, device="cuda")
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        gpu_lib.attn_fwd_ex(q, k, v, o, lse, x.scale, kv_len=kv, layout=layout)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]), "O"
+    assert torch.equal(outs[0][1], outs[1][1]), "lse"

@@ -104,6 +104,13 @@ constexpr int fwd_waves_per_eu(int D, int QB, int WAVES) {
 #ifndef FWD_SP_MIN_N
 #define FWD_SP_MIN_N 256
 #endif
+// The same pipelined forward at d = 128 (one query block per wave).
+#ifndef FWD_SP128
+#define FWD_SP128 1
+#endif
+#ifndef FWD_SP128_MIN_N
+#define FWD_SP128_MIN_N 1024
+#endif
 // Schedule of the pipelined forward: operands read FWD_SP_AHEAD products ahead;
 // FWD_SP_BARRIER keeps the compiler from moving work across chunks.
 #ifndef FWD_SP_AHEAD
@@ -814,13 +821,18 @@ constexpr int kSPRing = 4;
 // can pass unchecked.
 constexpr float kSpecLimit = 128.0f;
 
-template <class E, int D, int WAVES>
+template <class E, int D, int QB, int WAVES>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qblk, int total, float c,
                    uint32_t qsign, int H, Strides sq, Strides so) {
-  constexpr int QB = 2, KB = 2, NS = kSPRing;
+  static_assert((D == 64 && QB == 2) || (D == 128 && QB == 1), "shapes with a register plan");
+  constexpr int KB = 2, NS = kSPRing;
   using S = FwdShape<D, QB, KB, NS, WAVES>;
+  constexpr int NDB = D / 32, NCC = D / 16;
+  constexpr int NPV = KB * 2 * NDB;  // P V products per unit (key block, 16-key half, 32-dim block)
+  constexpr int NSP = KB * NCC;      // S^T products per unit (key block, 16-dim chunk)
+  constexpr int PPC = (NPV + NSP) / 16;  // products per chunk of a unit: 1 at d = 64, 2 at d = 128
   constexpr int PER = 2 * S::DMA_PER_WAVE;  // DMA instructions per wave per tile
   __shared__ __attribute__((aligned(16))) unsigned char ring0[2 * S::TILEB];
   __shared__ __attribute__((aligned(16))) unsigned char ring1[2 * S::TILEB];
@@ -908,13 +920,13 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // Operand of product m of a unit: V^T fragment (PV) or K fragment (S).
   auto pv_operand = [&](auto r_, int p) __attribute__((always_inline)) -> u32x4 {
     const unsigned char* Vs = slot_base(r_) + S::TILEB;
-    const int kb = p >> 2, c2 = (p >> 1) & 1, db = p & 1;
+    const int kb = p / (2 * NDB), c2 = (p / NDB) & 1, db = p % NDB;
     const int rows = (kb * 32 + c2 * 16) * S::ROWB;
     return cat(lds_read_tr16_b64(Vs, rows + voff[0][db]), lds_read_tr16_b64(Vs, rows + voff[1][db]));
   };
   auto s_operand = [&](auto r_, int sidx) __attribute__((always_inline)) -> u32x4 {
     const unsigned char* Ks = slot_base(r_);
-    return lds_read_b128(Ks, (sidx >> 2) * 32 * S::ROWB + koff[sidx & 3]);
+    return lds_read_b128(Ks, (sidx / NCC) * 32 * S::ROWB + koff[sidx % NCC]);
   };
   // Weights of entries 2i, 2i + 1 of query block QB_'s S^T tile (i = 0 .. 15).
   auto weight_pair = [&](auto qb_, int i, const f32x16 (&sv)[KB], u32x4 (&p)[KB][2], float& l)
@@ -930,8 +942,9 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   };
   // The first step of fwd_kernel's softmax for one unit: the maximum of its
   // scores and, when the reference has to move (ballot over the wave), the
-  // move and the rescale of O. Returns the factor for l (1 without a move)
-  // and whether the reference moved (wave-uniform).
+  // move. Returns the rescale factor for O and l (1 without a move) and
+  // whether the reference moved (wave-uniform); the caller rescales O once
+  // every product into it that predates the move has been issued.
   auto move_reference = [&](auto qb_, const f32x16 (&sv)[KB], float& alpha) __attribute__((always_inline)) -> bool {
     constexpr int QB_ = decltype(qb_)::value;
     float xs[KB * 16];
@@ -945,8 +958,6 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     if (__builtin_amdgcn_ballot_w64(mnew > m_run[QB_] + kRescaleSlack)) {
       alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[QB_] - mnew);
       m_run[QB_] = mnew;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[QB_][db] *= alpha;
       return true;
     }
     return false;
@@ -956,8 +967,11 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // whether the reference moved.
   auto softmax_slow = [&](auto qb_, const f32x16 (&sv)[KB], u32x4 (&p)[KB][2], float l_old, float& l)
                           __attribute__((always_inline)) -> bool {
+    constexpr int QB_ = decltype(qb_)::value;
     float alpha;
     if (!move_reference(qb_, sv, alpha)) return false;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[QB_][db] *= alpha;
     l = l_old * alpha;
 #pragma unroll
     for (int i = 0; i < 16; ++i) weight_pair(qb_, i, sv, p, l);
@@ -980,15 +994,16 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                   __attribute__((always_inline)) {
     constexpr bool HS = decltype(has_s)::value, HP = decltype(has_pv)::value;
     constexpr int QN = decltype(qn_)::value, QP = decltype(qp_)::value, QS = decltype(qs_)::value;
-    constexpr int NM = (HS ? 8 : 0) + (HP ? 8 : 0);
-    // Product m: PV index m (m < 8, HAS_PV), then S index m - 8 (or m without
-    // PV products), S index t meaning key block t & 1 and 16-dim chunk t >> 1.
-    auto is_pv = [&](int m) { return HP && m < 8; };
-    auto s_index = [&](int m) { return HP ? m - 8 : m; };
+    constexpr int NM = (HS ? NSP : 0) + (HP ? NPV : 0);
+    // Product m: PV index m (m < NPV, HAS_PV), then S index m - NPV (or m
+    // without PV products), S index t meaning key block t % KB and 16-dim
+    // chunk t / KB (the key blocks' accumulation chains alternate).
+    auto is_pv = [&](int m) { return HP && m < NPV; };
+    auto s_index = [&](int m) { return HP ? m - NPV : m; };
     auto operand = [&](int m) __attribute__((always_inline)) -> u32x4 {
       if (is_pv(m)) return pv_operand(rv_, m);
       const int t = s_index(m);
-      return s_operand(rs_, (t & 1) * 4 + (t >> 1));
+      return s_operand(rs_, (t % KB) * NCC + t / KB);
     };
     if constexpr (HS) {
 #pragma unroll
@@ -996,11 +1011,10 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     }
     const bool max_first = moved_last[QS];
     bool moved = false;
-    float l_old = l_run[QS];
+    float l_old = l_run[QS], alpha_first = 1.f;
     if (max_first) {
-      float alpha;
-      moved = move_reference(qs_, sv, alpha);
-      l_old *= alpha;
+      moved = move_reference(qs_, sv, alpha_first);
+      l_old *= alpha_first;
     }
     float l = l_old;
     constexpr int AH = FWD_SP_AHEAD, NO = AH + 1;  // operands read AH products ahead
@@ -1011,20 +1025,30 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     static_for<0, 16>([&](auto i_) __attribute__((always_inline)) {
       constexpr int I = decltype(i_)::value;
       if (FWD_SP_BARRIER) __builtin_amdgcn_sched_barrier(0);
-      if constexpr (I < NM) {
-        constexpr bool PVM = HP && I < 8;
-        if constexpr (PVM) {
-          constexpr int kb = I >> 2, c2 = (I >> 1) & 1, db = I & 1;
-          oacc[QP][db] = E::mfma(ops[I % NO], pr[kb][c2], oacc[QP][db]);
-        } else {
-          constexpr int T = HP ? I - 8 : I, kb = T & 1, cc = T >> 1;
-          sn[kb] = E::mfma(ops[I % NO], qf[QN][cc], sn[kb]);
+      static_for<0, PPC>([&](auto u_) __attribute__((always_inline)) {
+        constexpr int M = I * PPC + decltype(u_)::value;
+        if constexpr (M < NM) {
+          constexpr bool PVM = HP && M < NPV;
+          if constexpr (PVM) {
+            constexpr int kb = M / (2 * NDB), c2 = (M / NDB) & 1, db = M % NDB;
+            oacc[QP][db] = E::mfma(ops[M % NO], pr[kb][c2], oacc[QP][db]);
+          } else {
+            constexpr int T = HP ? M - NPV : M, kb = T % KB, cc = T / KB;
+            sn[kb] = E::mfma(ops[M % NO], qf[QN][cc], sn[kb]);
+          }
         }
-      }
-      if constexpr (I + AH < NM) ops[(I + AH) % NO] = operand(I + AH);
+        if constexpr (M + AH < NM) ops[(M + AH) % NO] = operand(M + AH);
+      });
       weight_pair(qs_, I, sv, pw, l);
     });
     __builtin_amdgcn_sched_barrier(0);
+    // A maximum-first move rescales O now: with one query block per wave the
+    // P V products of this unit went into the same accumulator, relative to
+    // the old reference.
+    if (max_first && moved) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[QS][db] *= alpha_first;
+    }
     // After the maximum-first path the weights are those of fwd_kernel (at
     // most 2^kRescaleSlack each) and need no check.
     if (!max_first && __builtin_amdgcn_ballot_w64(!(l - l_old <= kSpecLimit)))
@@ -1033,30 +1057,52 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     l_run[QS] = l;
   };
 
-  // End of tile j's first unit: tile j + 1 landed and visible to every wave,
-  // every wave done with tile j - 1 (its slot takes tile j + 3).
+  // Two query blocks per wave: at the end of tile j's first unit, tile j + 1
+  // landed and visible to every wave, every wave done with tile j - 1 (its
+  // slot takes tile j + 3). One block per wave: at the end of tile j's unit,
+  // tile j + 2 landed and visible (the next unit computes its S^T), every
+  // wave done with tile j - 1 (its V fed this unit's P V).
   auto boundary = [&](int j, auto r_) __attribute__((always_inline)) {
     constexpr int R = decltype(r_)::value;
-    if (j + 2 >= 3 && j + 2 < nt)
-      wait_vmem_below<PER>();
-    else
+    if constexpr (QB == 2) {
+      if (j + 2 >= 3 && j + 2 < nt)
+        wait_vmem_below<PER>();
+      else
+        wait_vmem_below<0>();
+    } else {
       wait_vmem_below<0>();
+    }
     __syncthreads();
     if (j + 3 < nt) dma_tile(j + 3, IntC<(R + 3) % NS>{});
   };
 
-  f32x16 sa[KB], sb[KB];          // S^T of query blocks 0 and 1 (one tile apart)
-  u32x4 pa[KB][2], pb[KB][2];     // P^T of query blocks 1 and 0
-  // Tile j in ring slot R: units (j, 0) and (j, 1). FIRST: no P V of tile
-  // j - 1; LAST: no S of tile j + 1.
+  // Two query blocks: S^T of blocks 0 and 1 (one tile apart) in sa / sb, P^T
+  // of blocks 1 and 0 in pa / pb. One block: S^T and P^T of even tiles in sa
+  // / pa, of odd tiles in sb / pb.
+  f32x16 sa[KB], sb[KB];
+  u32x4 pa[KB][2], pb[KB][2];
+  // Tile j in ring slot R. FIRST: no P V of tile j - 1; LAST: no S of tile j + 1.
   auto tile = [&](int j, auto r_, auto first_, auto last_) __attribute__((always_inline)) {
     constexpr int R = decltype(r_)::value;
     constexpr bool FIRST = decltype(first_)::value, LAST = decltype(last_)::value;
-    // unit (j, 0): S^T(j, 1) -> sb, P V(j - 1, 1) from pa, softmax(j, 0): sa -> pb
-    unit(BoolC<true>{}, r_, IntC<1>{}, sb, BoolC<!FIRST>{}, IntC<(R + NS - 1) % NS>{}, IntC<1>{}, pa, IntC<0>{}, sa, pb);
-    boundary(j, r_);
-    // unit (j, 1): S^T(j + 1, 0) -> sa, P V(j, 0) from pb, softmax(j, 1): sb -> pa
-    unit(BoolC<!LAST>{}, IntC<(R + 1) % NS>{}, IntC<0>{}, sa, BoolC<true>{}, r_, IntC<0>{}, pb, IntC<1>{}, sb, pa);
+    if constexpr (QB == 2) {
+      // unit (j, 0): S^T(j, 1) -> sb, P V(j - 1, 1) from pa, softmax(j, 0): sa -> pb
+      unit(BoolC<true>{}, r_, IntC<1>{}, sb, BoolC<!FIRST>{}, IntC<(R + NS - 1) % NS>{}, IntC<1>{}, pa, IntC<0>{}, sa,
+           pb);
+      boundary(j, r_);
+      // unit (j, 1): S^T(j + 1, 0) -> sa, P V(j, 0) from pb, softmax(j, 1): sb -> pa
+      unit(BoolC<!LAST>{}, IntC<(R + 1) % NS>{}, IntC<0>{}, sa, BoolC<true>{}, r_, IntC<0>{}, pb, IntC<1>{}, sb, pa);
+    } else if constexpr (R % 2 == 0) {  // even tile (the ring has an even number of slots)
+      // unit j: S^T(j + 1) -> sb, P V(j - 1) from pb, softmax(j): sa -> pa
+      unit(BoolC<!LAST>{}, IntC<(R + 1) % NS>{}, IntC<0>{}, sb, BoolC<!FIRST>{}, IntC<(R + NS - 1) % NS>{}, IntC<0>{},
+           pb, IntC<0>{}, sa, pa);
+      boundary(j, r_);
+    } else {
+      // unit j: S^T(j + 1) -> sa, P V(j - 1) from pa, softmax(j): sb -> pb
+      unit(BoolC<!LAST>{}, IntC<(R + 1) % NS>{}, IntC<0>{}, sa, BoolC<!FIRST>{}, IntC<(R + NS - 1) % NS>{}, IntC<0>{},
+           pa, IntC<0>{}, sb, pb);
+      boundary(j, r_);
+    }
   };
   // S^T of unit (0, 0) and P V of the last unit, outside any tile.
   auto s_only = [&](auto r_, auto qb_, f32x16 (&acc)[KB]) __attribute__((always_inline)) {
@@ -1065,13 +1111,14 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     for (int kb = 0; kb < KB; ++kb) {
       acc[kb] = f32x16{};
 #pragma unroll
-      for (int cc = 0; cc < D / 16; ++cc) acc[kb] = E::mfma(s_operand(r_, kb * 4 + cc), qf[QB_][cc], acc[kb]);
+      for (int cc = 0; cc < NCC; ++cc) acc[kb] = E::mfma(s_operand(r_, kb * NCC + cc), qf[QB_][cc], acc[kb]);
     }
   };
   auto pv_only = [&](auto r_, auto qb_, const u32x4 (&p)[KB][2]) __attribute__((always_inline)) {
     constexpr int QB_ = decltype(qb_)::value;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) oacc[QB_][m & 1] = E::mfma(pv_operand(r_, m), p[m >> 2][(m >> 1) & 1], oacc[QB_][m & 1]);
+    for (int m = 0; m < NPV; ++m)
+      oacc[QB_][m % NDB] = E::mfma(pv_operand(r_, m), p[m / (2 * NDB)][(m / NDB) & 1], oacc[QB_][m % NDB]);
   };
 
   // Prologue: tiles 0 .. 2 resident, S of unit (0, 0).
@@ -1083,9 +1130,10 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   s_only(IntC<0>{}, IntC<0>{}, sa);
   tile(0, IntC<0>{}, BoolC<true>{}, BoolC<false>{});
   // Tiles 1 .. nt - 1, four per iteration (ring slots 1, 2, 3, 0), then the
-  // rest. The last tile's second unit also computes S^T of a tile nt that does
+  // rest. The last tile's last unit also computes S^T of a tile nt that does
   // not exist, from the slot it would occupy (which holds tile nt - 4: finite
-  // data, nt >= 4); the result is never used. This keeps one tile body.
+  // data, nt >= 4, no copy in flight); the result is never used. This keeps
+  // one tile body.
   int j = 1;
   for (; j + 4 <= nt; j += 4) {
     tile(j, IntC<1>{}, BoolC<false>{}, BoolC<false>{});
@@ -1096,12 +1144,14 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   if (j < nt) tile(j, IntC<1>{}, BoolC<false>{}, BoolC<false>{});
   if (j + 1 < nt) tile(j + 1, IntC<2>{}, BoolC<false>{}, BoolC<false>{});
   if (j + 2 < nt) tile(j + 2, IntC<3>{}, BoolC<false>{}, BoolC<false>{});
-  // P V of the last unit (tile nt - 1, query block 1).
+  // P V of the last unit (tile nt - 1; query block 1 with two blocks, P^T in
+  // pa; with one block, pa or pb by the tile's parity).
+  constexpr int QL = QB - 1;
   switch ((nt - 1) % NS) {
-    case 0: pv_only(IntC<0>{}, IntC<1>{}, pa); break;
-    case 1: pv_only(IntC<1>{}, IntC<1>{}, pa); break;
-    case 2: pv_only(IntC<2>{}, IntC<1>{}, pa); break;
-    default: pv_only(IntC<3>{}, IntC<1>{}, pa); break;
+    case 0: pv_only(IntC<0>{}, IntC<QL>{}, pa); break;
+    case 1: pv_only(IntC<1>{}, IntC<QL>{}, QB == 2 ? pa : pb); break;
+    case 2: pv_only(IntC<2>{}, IntC<QL>{}, pa); break;
+    default: pv_only(IntC<3>{}, IntC<QL>{}, QB == 2 ? pa : pb); break;
   }
 
 #pragma unroll
@@ -1248,15 +1298,15 @@ static hipError_t launch_fwd_pp(const uint16_t* q, const uint16_t* k, const uint
   return hipGetLastError();
 }
 
-template <class E, int D, int WAVES>
+template <class E, int D, int QB, int WAVES>
 static hipError_t launch_fwd_sp(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
                                 int B, int H, int N, float scale, Strides sq, Strides so, hipStream_t stream) {
-  using S = FwdShape<D, 2, 2, kSPRing, WAVES>;
+  using S = FwdShape<D, QB, 2, kSPRing, WAVES>;
   const int n_qblk = (N + S::BR - 1) / S::BR;
   const int total = n_qblk * B * H;
   const float c = fabsf(scale) * kLog2e;
   const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_sp_kernel<E, D, WAVES>), dim3(total), dim3(S::THREADS), 0, stream, q, k, v, o, lse, N,
+  hipLaunchKernelGGL((fwd_sp_kernel<E, D, QB, WAVES>), dim3(total), dim3(S::THREADS), 0, stream, q, k, v, o, lse, N,
                      n_qblk, total, c, qsign, H, sq, so);
   return hipGetLastError();
 }
@@ -1295,7 +1345,10 @@ static hipError_t launch_fwd_e(const uint16_t* q, const uint16_t* k, const uint1
   const bool lng_small_d = N >= FWD_LONG_N_SMALL_D;
   // Rows without masks, whole 64-key tiles, d = 64: the software-pipelined forward.
   if (FWD_SP && d == 64 && !causal && !kv_len && N % 64 == 0 && N >= FWD_SP_MIN_N)
-    return launch_fwd_sp<E, 64, 4>(q, k, v, o, lse, B, H, N, scale, sq, so, stream);
+    return launch_fwd_sp<E, 64, 2, 4>(q, k, v, o, lse, B, H, N, scale, sq, so, stream);
+  // d = 128: one query block per wave, 8 waves sharing the ring (128 KB of LDS, one workgroup per CU).
+  if (FWD_SP128 && d == 128 && !causal && !kv_len && N % 64 == 0 && N >= FWD_SP128_MIN_N)
+    return launch_fwd_sp<E, 128, 1, 8>(q, k, v, o, lse, B, H, N, scale, sq, so, stream);
   if (FWD_PINGPONG && lng && !causal && !kv_len) {
 #if FWD_PP_D64
     if (d == 64)
