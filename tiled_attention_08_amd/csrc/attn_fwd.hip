@@ -793,16 +793,18 @@ void fwd_pp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 }
 
 // ------------------------------------------------------------------------
-// Software-pipelined forward (rows without masks, N a multiple of 64, d = 64).
-// The same tiles and the same arithmetic per element as fwd_kernel, issued so
-// that every wave keeps the matrix cores and the vector ALU busy at once.
+// Software-pipelined forward (rows without masks, N a multiple of 64; d = 64
+// with two 32-query blocks per wave, d = 128 with one). The same tiles and
+// the same arithmetic per element as fwd_kernel, issued so that every wave
+// keeps the matrix cores and the vector ALU busy at once.
 //
-// A unit is one 32-query block of the wave against one 64-key tile; tile j
-// holds units (j, 0) and (j, 1). While the vector ALU computes the softmax
-// of unit u, the matrix cores compute S of unit u + 1 and O^T += V^T P^T of
-// unit u - 1 (independent instructions in one stream, interleaved by the
-// hardware). So S of tile j + 1 is read from LDS while V of tile j - 1 is
-// still in use: the K/V ring holds four tiles, one LDS array per slot.
+// A unit is one 32-query block of the wave against one 64-key tile: with two
+// blocks tile j holds units (j, 0) and (j, 1), with one block tile j is unit
+// j. While the vector ALU computes the softmax of unit u, the matrix cores
+// compute S of unit u + 1 and O^T += V^T P^T of unit u - 1 (independent
+// instructions in one stream, interleaved by the hardware). So S of tile
+// j + 1 is read from LDS while V of tile j - 1 is still in use: the K/V ring
+// holds four tiles, one LDS array per slot.
 //
 // The softmax is speculative: the weights are computed against the current
 // reference maximum without first taking the tile's maximum. The reference
