@@ -248,6 +248,8 @@ def test_fusion_rule(L):
     """dK/dV and dQ share a launch only for d_k <= 64 and small grids; rejected shapes answer 0."""
     assert L.attn_bwd_fused(32, 12, 196, 64) and L.attn_bwd_fused(4, 12, 2048, 64)
     assert not L.attn_bwd_fused(8, 16, 4096, 64)      # 4096 dK/dV workgroups
+    assert L.attn_bwd_fused(4, 16, 2048, 64) and not L.attn_bwd_fused(6, 16, 2048, 64)  # 1024 yes, 1536 no
+    assert not L.attn_bwd_fused(2, 16, 8192, 64)      # 2048 dK/dV workgroups
     assert not L.attn_bwd_fused(32, 12, 196, 128) and not L.attn_bwd_fused(1, 1, 100, 64)  # d_k 128; grid of 1
     assert not L.attn_bwd_fused(0, 12, 196, 64) and not L.attn_bwd_fused(32, 12, 196, 80)
 

@@ -422,6 +422,12 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #ifndef BWD_SP_RING
 #define BWD_SP_RING 3
 #endif
+// Waves per workgroup (32 keys each), all sharing each Q / dO step tile. 8
+// waves (one workgroup per CU, half the tile copies per key) measured no
+// faster: B=8, H=16, N=4096 973 -> 983-990 us, B=4, H=12, N=2048 103 -> 119 us.
+#ifndef BWD_SP_WAVES
+#define BWD_SP_WAVES 4
+#endif
 #ifndef BWD_SP_AHEAD
 #define BWD_SP_AHEAD 2
 #endif
@@ -433,10 +439,13 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #define BWD_SP_LREAD 12
 #endif
 
+template <int WAVES>
 struct DkdvSpShape {
-  static constexpr int D = 64, BRQ = 64, ROWB = 2 * D;
+  static constexpr int D = 64, BRQ = 64, ROWB = 2 * D, THREADS = 64 * WAVES;
+  static constexpr int BCK = 32 * WAVES;               // keys per workgroup (32 per wave)
   static constexpr int QTILEB = BRQ * ROWB;            // one Q or dO step tile (8 KB)
-  static constexpr int QDMA = BRQ * D / 8 / kThreads;  // 16-byte DMAs per lane per tile (2)
+  static constexpr int QDMA = BRQ * D / 8 / THREADS;   // 16-byte DMAs per lane per tile (2 with 4 waves, 1 with 8)
+  static_assert(QDMA >= 1 && (BRQ * D / 8) % THREADS == 0, "step tiles split evenly over the lanes");
   static constexpr int OFF_Q = 0;
   static constexpr int OFF_DO = QTILEB;
   static constexpr int OFF_L = 2 * QTILEB;             // lse * log2(e) of the step's 64 queries
@@ -444,13 +453,13 @@ struct DkdvSpShape {
   static constexpr int SLOTB = OFF_DL + BRQ * 4;       // one ring slot
 };
 
-template <class E, int NS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <class E, int NS, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                         const uint16_t* __restrict__ dO, const float* __restrict__ lse2,
                         const float* __restrict__ ndelta, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
                         int n_kblk, int total, float c, float scale, int H, Strides sq, Strides sd, Strides sg) {
-  using S = DkdvSpShape;
+  using S = DkdvSpShape<WAVES>;
   constexpr int D = S::D;
   static_assert(NS == 3 || NS == 4, "ring of 3 or 4 step tiles");
   // One LDS array per ring slot: the compiler then sees that the copy into
@@ -475,7 +484,7 @@ void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   const int bh = work / n_kblk, kblk = work - bh * n_kblk;
   const size_t hq = head_off(sq, bh, H), hd = head_off(sd, bh, H), hg = head_off(sg, bh, H);
   const size_t hrow = (size_t)bh * N;
-  const int key = kblk * 128 + wave * 32 + l32;  // this lane's key (keys past N compute unused gradients)
+  const int key = kblk * S::BCK + wave * 32 + l32;  // this lane's key (keys past N compute unused gradients)
 
   u32x4 kf[D / 16], vf[D / 16];
 #pragma unroll
@@ -1116,15 +1125,17 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Stages 1 and 2 run as one launch when both kernels run two waves per SIMD
 // with the same launch shape (d_k <= 64, one key block per wave), the dK/dV
-// grid is a multiple of the 8 XCDs, and it is small enough (at most 8
+// grid is a multiple of the 8 XCDs, and it is small enough (at most 4
 // workgroups per CU) for the tail of the dK/dV launch to matter: measured per
 // step, 70 -> 64 us at B=32, H=12, N=196 and 277 -> 268 us at B=4, H=12,
-// N=2048, but no change at B=8, H=16, N=4096 (4096 dK/dV workgroups).
+// N=2048. Against the two launches (the dK/dV one pipelined where the rows
+// allow), per backward: 768 dK/dV workgroups 108 -> 99 us, 1024 246 -> 239
+// us, but 1536 336 -> 350 us and 2048 1648 -> 1761 us.
 bool bwd_can_fuse(int B, int H, int N, int d) {
 #if BWD_FUSE
   if (d > 64 || BWD_KBW64 != 1 || BWD_MB64 != 2) return false;
   const long total1 = (long)((N + 127) / 128) * B * H;
-  return total1 % 8 == 0 && total1 <= 8 * 256;
+  return total1 % 8 == 0 && total1 <= 4 * 256;
 #else
   (void)B, (void)H, (void)N, (void)d;
   return false;
@@ -1171,8 +1182,9 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
     if constexpr (D == 64) {
       constexpr int NS = BWD_SP_RING;
       if (BWD_SP && !causal && !kv_len && N % 64 == 0 && N / 64 >= NS) {
-        const int n_kblk = (N + 127) / 128, total = n_kblk * B * H;
-        hipLaunchKernelGGL((bwd_dkdv_sp_kernel<E, NS>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2,
+        constexpr int W = BWD_SP_WAVES, BCK = DkdvSpShape<W>::BCK;
+        const int n_kblk = (N + BCK - 1) / BCK, total = n_kblk * B * H;
+        hipLaunchKernelGGL((bwd_dkdv_sp_kernel<E, NS, W>), dim3(total), dim3(64 * W), 0, stream, q, k, v, dO, lse2,
                            ndelta, dk, dv, N, n_kblk, total, c, scale, H, st[0], st[2], st[3]);
         return hipGetLastError();
       }
