@@ -166,7 +166,7 @@ hipError_t launch(const u32x4* w, float* out, int iters, hipStream_t s) {
 // Per 8 products: exponentials, packs, other vector instructions, 16-byte and 8-byte LDS reads. The
 // exponential and LDS counts are the kernels' (SQ_INSTS_VALU_TRANS_F32, SQ_INSTS_LDS per product x 8); the
 // other count is set so that the loop's vector instructions (with the 2 the loop itself needs) total the
-// kernel's SQ_INSTS_VALU per product x 8, less the products: 36, 51, 54 and 39.
+// kernel's SQ_INSTS_VALU per product x 8, less the products: 36, 51, 54 and 30.
 hipError_t launch_mix(int mix, const u32x4* w, float* out, int iters, hipStream_t s) {
   switch (mix) {
     case ATTN_MIX_CONSTANT: return launch<false, 0, 0, 0, 0, 0>(w, out, iters, s);
@@ -174,7 +174,7 @@ hipError_t launch_mix(int mix, const u32x4* w, float* out, int iters, hipStream_
     case ATTN_MIX_DKDV: return launch<true, 8, 8, 18, 8, 8>(w, out, iters, s);
     case ATTN_MIX_DQ: return launch<true, 11, 5, 33, 2, 4>(w, out, iters, s);
     case ATTN_MIX_FWD64: return launch<true, 16, 8, 28, 4, 8>(w, out, iters, s);
-    case ATTN_MIX_FWD128: return launch<true, 8, 4, 25, 4, 8>(w, out, iters, s);
+    case ATTN_MIX_FWD128: return launch<true, 8, 4, 16, 4, 8>(w, out, iters, s);
     default: return hipErrorInvalidValue;
   }
 }
