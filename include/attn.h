@@ -219,8 +219,9 @@ int attn_bwd_ex_noalloc(int dtype, int layout, const void* q, const void* k, con
  * 1 when attn_bwd / attn_bwd_ex run the dK/dV and dQ work of this shape as
  * one launch (stage 3), 0 when they launch it as stages 1 and 2 (or the shape
  * is rejected). Depends on the shape only: d_k <= 64 and a small dK/dV grid
- * (at most 2048 workgroups of 128 keys), where the tail of a separate dK/dV
- * launch would leave CUs idle. Results are the same either way, bit for bit.
+ * (a multiple of 8 and at most 1024 workgroups of 128 keys), where the tail
+ * of a separate dK/dV launch would leave CUs idle. Results are the same
+ * either way, bit for bit.
  */
 int attn_bwd_fused(int B, int H, int N, int d_k);
 
