@@ -111,8 +111,14 @@ def fwd_kernel_name(N: int, d: int, causal: bool) -> str:
 
 def dkdv_kernel_name(N: int, d: int, causal: bool) -> str:
     """The stand-alone dK/dV kernel for a shape without key padding: the software-pipelined kernel for unmasked
-    rows of at least three whole 64-query steps at d_k 64, the single-phase kernel otherwise."""
-    return "bwd_dkdv_sp_kernel" if d == 64 and not causal and N % 64 == 0 and N >= 192 else "bwd_dkdv_kernel"
+    rows of at least three 64-query steps (the last may be partial) at d_k 64, the single-phase kernel otherwise."""
+    return "bwd_dkdv_sp_kernel" if d == 64 and not causal and (N + 63) // 64 >= 3 else "bwd_dkdv_kernel"
+
+
+def fused_kernel_name(N: int, d: int, causal: bool) -> str:
+    """The combined dK/dV + dQ launch for a shape without key padding: with the pipelined dK/dV body where the
+    stand-alone pipelined kernel applies, with the single-phase one otherwise."""
+    return "bwd_dkdv_sp_dq_kernel" if dkdv_kernel_name(N, d, causal) == "bwd_dkdv_sp_kernel" else "bwd_dkdv_dq_kernel"
 
 
 def mix_of_kernel(kernel: str, d: int):
@@ -120,6 +126,7 @@ def mix_of_kernel(kernel: str, d: int):
     d_k = 64 for the backward kernels and the d_k = 64 forward, d_k = 128 for the forward."""
     if d == 64:
         return {"bwd_dkdv_kernel": "dkdv", "bwd_dkdv_sp_kernel": "dkdv", "bwd_dkdv_dq_kernel": "dkdv",
+                "bwd_dkdv_sp_dq_kernel": "dkdv",
                 "bwd_dq_kernel": "dq", "fwd_kernel": "fwd64", "fwd_sp_kernel": "fwd64"}.get(kernel)
     if d == 128:
         return {"fwd_kernel": "fwd128", "fwd_pp_kernel": "fwd128", "fwd_sp_kernel": "fwd128"}.get(kernel)
@@ -128,7 +135,7 @@ def mix_of_kernel(kernel: str, d: int):
 
 # Matrix-core work per unit of algorithmic work: the dQ kernel repeats the S and dP products (3 of its products
 # per algorithmic one), the fused backward launch likewise (14 per 10).
-MFMA_PER_ALGORITHMIC = {"bwd_dq_kernel": 3.0, "bwd_dkdv_dq_kernel": 1.4}
+MFMA_PER_ALGORITHMIC = {"bwd_dq_kernel": 3.0, "bwd_dkdv_dq_kernel": 1.4, "bwd_dkdv_sp_dq_kernel": 1.4}
 
 
 def attach_attainable(roofline: dict, d: int, causal: bool) -> None:
@@ -461,7 +468,7 @@ def bench_proj(args, w) -> int:
               "bwd_dq": 5 * E * sz + 8 * R, "bwd_dkdv_dq": 7 * E * sz + 8 * R}
     kname_full = {"proj_fwd": "gemm256_kernel", "proj_bwd": "attn_qkv_proj_bwd (dx and dw products, split sums)",
                   "fwd": fwd_kernel_name(N, d, False), "bwd_prep": "bwd_prep_kernel", "bwd_dkdv": dkdv_kernel_name(N, d, False),
-                  "bwd_dq": "bwd_dq_kernel", "bwd_dkdv_dq": "bwd_dkdv_dq_kernel"}
+                  "bwd_dq": "bwd_dq_kernel", "bwd_dkdv_dq": fused_kernel_name(N, d, False)}
     # The roofline describes the longest single kernel (the projection backward is a group of launches).
     single = {kn: t for kn, t in kernels.items() if kn != "proj_bwd"}
     dominant = max(single, key=single.get)
@@ -708,7 +715,7 @@ def main(argv=None) -> int:
     kbytes = {"fwd": 4 * E * sz + 4 * R, "bwd_prep": 2 * E * sz + 12 * R, "bwd_dkdv": 6 * E * sz + 8 * R,
               "bwd_dq": 5 * E * sz + 8 * R, "bwd_dkdv_dq": 7 * E * sz + 8 * R}
     kname_full = {"fwd": fwd_kernel_name(N, d, cz), "bwd_dkdv": dkdv_kernel_name(N, d, cz), "bwd_dq": "bwd_dq_kernel",
-                  "bwd_prep": "bwd_prep_kernel", "bwd_dkdv_dq": "bwd_dkdv_dq_kernel"}
+                  "bwd_prep": "bwd_prep_kernel", "bwd_dkdv_dq": fused_kernel_name(N, d, cz)}
     dominant = max(kernels, key=kernels.get)
     wkey = w.name + ("_causal" if cz else "") + ("_f16" if args.dtype == "f16" else "")
     roofline = roofline_of(kname_full[dominant], kernels[dominant], kflops[dominant], kbytes[dominant], wkey)

@@ -21,14 +21,20 @@ def test_forward_kernel_names():
 
 def test_dkdv_kernel_names():
     assert bench.dkdv_kernel_name(4096, 64, False) == "bwd_dkdv_sp_kernel"
-    assert bench.dkdv_kernel_name(196, 64, False) == "bwd_dkdv_kernel"
+    assert bench.dkdv_kernel_name(196, 64, False) == "bwd_dkdv_sp_kernel"    # 4 steps, the last partial
+    assert bench.dkdv_kernel_name(128, 64, False) == "bwd_dkdv_kernel"       # 2 steps: under the ring of 3
+    assert bench.dkdv_kernel_name(129, 64, False) == "bwd_dkdv_sp_kernel"
     assert bench.dkdv_kernel_name(4096, 64, True) == "bwd_dkdv_kernel"
     assert bench.dkdv_kernel_name(4096, 128, False) == "bwd_dkdv_kernel"
+    assert bench.fused_kernel_name(196, 64, False) == "bwd_dkdv_sp_dq_kernel"
+    assert bench.fused_kernel_name(197, 64, True) == "bwd_dkdv_dq_kernel"
+    assert bench.fused_kernel_name(100, 64, False) == "bwd_dkdv_dq_kernel"
 
 
 def test_mix_of_kernel():
     from tiled_attention_08_amd.ceiling import MIXES
     for kernel, d, mix in (("bwd_dkdv_sp_kernel", 64, "dkdv"), ("bwd_dkdv_dq_kernel", 64, "dkdv"),
+                           ("bwd_dkdv_sp_dq_kernel", 64, "dkdv"),
                            ("bwd_dq_kernel", 64, "dq"), ("fwd_sp_kernel", 64, "fwd64"), ("fwd_sp_kernel", 128, "fwd128"),
                            ("fwd_pp_kernel", 128, "fwd128")):
         assert bench.mix_of_kernel(kernel, d) == mix and mix in MIXES

@@ -81,12 +81,15 @@ def test_pipelined_equals_single_phase(gpu_lib, dtype, B, H, N, sigma, layout):
     ("bf16", 1, 2, 256, 1.0, "bhnd"), ("bf16", 2, 3, 320, 1.0, "bhnd"), ("bf16", 1, 2, 576, 1.0, "bhnd"),
     ("f16", 1, 2, 1088, 1.0, "bhnd"), ("bf16", 1, 4, 4096, 1.0, "bhnd"), ("bf16", 2, 3, 2048, 8.0, "bhnd"),
     ("bf16", 2, 2, 704, 1.0, "qkv_packed"),
+    # ragged last steps: rows past N read as row N - 1 and masked
+    ("bf16", 2, 3, 196, 1.0, "bhnd"), ("bf16", 1, 2, 129, 1.0, "bhnd"), ("f16", 2, 2, 1000, 8.0, "bhnd"),
+    ("bf16", 2, 2, 197, 1.0, "qkv_packed"),
 ])
 def test_pipelined_dkdv_equals_single_phase(gpu_lib, dtype, B, H, N, sigma, layout):
-    """Unmasked rows of whole 64-query steps (256 queries or more) at d_k = 64 run the software-pipelined dK/dV
-    kernel; a key-padding length equal to N routes the same inputs to the single-phase kernel, which performs
-    the same operations per element in the same order: dK and dV must be identical. The stage is called on its
-    own, so that the fused dK/dV + dQ launch of small grids does not take over."""
+    """Unmasked rows of at least three 64-query steps (the last may be partial) at d_k = 64 run the
+    software-pipelined dK/dV kernel; a key-padding length equal to N routes the same inputs to the single-phase
+    kernel, which performs the same operations per element in the same order: dK and dV must be identical. The
+    stage is called on its own, so that the fused dK/dV + dQ launch of small grids does not take over."""
     import torch
     d = 64
     x = make_case(B, H, N, d, dtype, seed=7200 + N, qk_sigma=sigma)
@@ -120,6 +123,47 @@ def test_pipelined_dkdv_equals_single_phase(gpu_lib, dtype, B, H, N, sigma, layo
     assert bool(torch.isfinite(outs[0][0].float()).all()) and bool(torch.isfinite(outs[0][1].float()).all())
     assert torch.equal(outs[0][0], outs[1][0]), "dK"
     assert torch.equal(outs[0][1], outs[1][1]), "dV"
+
+
+@pytest.mark.parametrize("dtype,B,H,N,layout", [
+    ("bf16", 2, 4, 196, "bhnd"), ("f16", 4, 2, 256, "bhnd"), ("bf16", 2, 4, 1000, "bhnd"), ("bf16", 2, 4, 197, "qkv_packed"),
+])
+def test_combined_pipelined_launch_equals_stages(gpu_lib, dtype, B, H, N, layout):
+    """Where the combined dK/dV + dQ launch applies and the rows are unmasked, it runs the pipelined dK/dV body
+    (ragged last step masked) beside the dQ body: stage 3 must give dQ, dK, dV identical to stages 1 and 2."""
+    import torch
+    d = 64
+    assert gpu_lib.attn_bwd_fused(B, H, N, d)
+    x = make_case(B, H, N, d, dtype, seed=7300 + N)
+    print(f"combined pipelined launch {dtype} B={B} H={H} N={N} layout={layout}", flush=True)
+    q, k, v, do = (to_device(x, n) for n in ("q", "k", "v", "do"))
+    if layout == "qkv_packed":
+        qkv = torch.stack([q.permute(0, 2, 1, 3), k.permute(0, 2, 1, 3), v.permute(0, 2, 1, 3)], dim=2).contiguous()
+        q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+        do = do.permute(0, 2, 1, 3).contiguous()
+    shape = (B, N, H, d) if layout == "qkv_packed" else (B, H, N, d)
+    o = torch.empty(shape, dtype=q.dtype, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    gpu_lib.attn_fwd_ex(q, k, v, o, lse, x.scale, layout=layout)
+    ws = gpu_lib.workspace_for(q)
+
+    def grads():
+        if layout == "qkv_packed":
+            g = torch.full((B, N, 3, H, d), float("nan"), dtype=q.dtype, device="cuda")
+            return g, (g[:, :, 0], g[:, :, 1], g[:, :, 2])
+        g = torch.full((3,) + shape, float("nan"), dtype=q.dtype, device="cuda")
+        return g, (g[0], g[1], g[2])
+
+    gpu_lib.attn_bwd_stage(0, q, k, v, o, lse, do, *grads()[1], x.scale, ws, layout=layout)
+    outs = []
+    for stages in ((1, 2), (3,)):
+        g, g3 = grads()
+        for st in stages:
+            gpu_lib.attn_bwd_stage(st, q, k, v, o, lse, do, *g3, x.scale, ws, layout=layout)
+        outs.append(g)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(outs[1].float()).all())
+    assert torch.equal(outs[0], outs[1])
 
 
 @pytest.mark.parametrize("dtype,B,H,N,sigma,layout", [

@@ -459,34 +459,34 @@ struct DkdvSpShape {
   static constexpr int SLOTB = OFF_DL + BRQ * 4;       // one ring slot
 };
 
-template <class E, int NS, int WAVES>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                        const uint16_t* __restrict__ dO, const float* __restrict__ lse2,
-                        const float* __restrict__ ndelta, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
-                        int n_kblk, int total, float c, float scale, int H, Strides sq, Strides sd, Strides sg) {
+// The ring slots of the pipelined dK/dV body: one LDS array each, declared by
+// the kernel, so that the compiler sees that the copy into one slot cannot
+// alias the reads of another.
+struct SpRing {
+  unsigned char* s[4];
+};
+
+// RAGGED: N is not a multiple of the 64-query step; rows past N are read as
+// row N - 1 and get probability 0 in the last step.
+template <class E, int NS, int WAVES, bool RAGGED>
+__device__ __forceinline__ void dkdv_sp_body(const SpRing& ring, int work, const uint16_t* __restrict__ Q,
+                                             const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                             const uint16_t* __restrict__ dO, const float* __restrict__ lse2,
+                                             const float* __restrict__ ndelta, uint16_t* __restrict__ dK,
+                                             uint16_t* __restrict__ dV, int N, int n_kblk, float c, float scale,
+                                             int H, Strides sq, Strides sd, Strides sg) {
   using S = DkdvSpShape<WAVES>;
   constexpr int D = S::D;
   static_assert(NS == 3 || NS == 4, "ring of 3 or 4 step tiles");
-  // One LDS array per ring slot: the compiler then sees that the copy into
-  // one slot cannot alias the reads of another.
-  __shared__ __attribute__((aligned(16))) unsigned char ring0[S::SLOTB];
-  __shared__ __attribute__((aligned(16))) unsigned char ring1[S::SLOTB];
-  __shared__ __attribute__((aligned(16))) unsigned char ring2[S::SLOTB];
-  __shared__ __attribute__((aligned(16))) unsigned char ring3[NS == 4 ? S::SLOTB : 16];
   auto slot_base = [&](auto r_) __attribute__((always_inline)) -> unsigned char* {
     constexpr int R = decltype(r_)::value % NS;
-    if constexpr (R == 0) return ring0;
-    else if constexpr (R == 1) return ring1;
-    else if constexpr (R == 2) return ring2;
-    else return ring3;
+    return ring.s[R];
   };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, gi = lane & 15;
   const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
-  const int work = xcd_remap(blockIdx.x, total);
   const int bh = work / n_kblk, kblk = work - bh * n_kblk;
   const size_t hq = head_off(sq, bh, H), hd = head_off(sd, bh, H), hg = head_off(sg, bh, H);
   const size_t hrow = (size_t)bh * N;
@@ -508,6 +508,8 @@ void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   const Rsrc rL = make_rsrc(lse2 + hrow), rDL = make_rsrc(ndelta + hrow);
   // DMA counts per tile: 2 * QDMA for every wave, one more for waves 0 and 1.
   constexpr int PER = 2 * S::QDMA;
+  // RAGGED: rows past N repeat row N - 1 (finite data, whose probabilities
+  // the last step sets to 0).
   auto dma_tile = [&](int i, auto r_) __attribute__((always_inline)) {
     unsigned char* base = slot_base(r_);
     const int q0 = i * S::BRQ;
@@ -516,11 +518,13 @@ void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
       const int slot0 = (wave * S::QDMA + r) * 64;
       const int p = slot0 + lane;
       const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz<S::ROWB>(row);
-      dma16(rQ, (uint32_t)((q0 + row) * sq.n + chunk * 8) * 2u, base + S::OFF_Q + slot0 * 16);
-      dma16(rdO, (uint32_t)((q0 + row) * sd.n + chunk * 8) * 2u, base + S::OFF_DO + slot0 * 16);
+      const int qr = RAGGED ? min(q0 + row, N - 1) : q0 + row;
+      dma16(rQ, (uint32_t)(qr * sq.n + chunk * 8) * 2u, base + S::OFF_Q + slot0 * 16);
+      dma16(rdO, (uint32_t)(qr * sd.n + chunk * 8) * 2u, base + S::OFF_DO + slot0 * 16);
     }
-    if (wave == 0) dma4(rL, (uint32_t)(q0 + lane) * 4u, base + S::OFF_L);
-    if (wave == 1) dma4(rDL, (uint32_t)(q0 + lane) * 4u, base + S::OFF_DL);
+    const uint32_t lr = (uint32_t)(RAGGED ? min(q0 + lane, N - 1) : q0 + lane) * 4u;
+    if (wave == 0) dma4(rL, lr, base + S::OFF_L);
+    if (wave == 1) dma4(rDL, lr, base + S::OFF_DL);
   };
 
   // Per-lane LDS offsets (query block 0, 16-query half 0; the other blocks
@@ -564,8 +568,11 @@ void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   // to word i & 3 of operand i >> 2).
   auto slot = [&](auto hasA, auto ra_, auto mba_, const u32x4 (&ya)[2], const u32x4 (&yd)[2], auto hasB, auto rb_,
                   auto mbb_, f32x16& sn, f32x16& pn, float (&ln)[16], auto hasV, const f32x16& sv, const f32x16& pv,
-                  const float (&lv)[16], u32x4 (&xp)[2], u32x4 (&xd)[2]) __attribute__((always_inline)) {
+                  const float (&lv)[16], u32x4 (&xp)[2], u32x4 (&xd)[2], auto maskV, int qv0)
+                  __attribute__((always_inline)) {
+    // maskV: the current unit (first query qv0) has rows past N, whose P and dS are 0.
     constexpr bool HA = decltype(hasA)::value, HB = decltype(hasB)::value, HV = decltype(hasV)::value;
+    constexpr bool MV = decltype(maskV)::value;
     constexpr int MBB = decltype(mbb_)::value;
     constexpr int AH = BWD_SP_AHEAD, NO = AH + 1;
     constexpr int M0 = HA ? 0 : 8, M1 = HB ? 16 : 8;  // products [M0, M1)
@@ -619,7 +626,10 @@ void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
       }
       if constexpr (KK >= M0 && KK + AH < M1) ops[(KK + AH) % NO] = operand(KK + AH, ra_, mba_, rb_, mbb_);
       if constexpr (HV) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sv[KK], c, -lv[KK]));
+        float p = __builtin_amdgcn_exp2f(fmaf(sv[KK], c, -lv[KK]));
+        if constexpr (MV) {
+          if (qv0 + 8 * (KK >> 2) + 4 * h + (KK & 3) >= N) p = 0.f;
+        }
         const float ds = p * pv[KK];
         if constexpr (KK & 1) {
           constexpr int i = KK >> 1;
@@ -640,7 +650,7 @@ void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  const int nq = N / S::BRQ;  // steps (the launcher checks N % 64 == 0 and nq >= NS)
+  const int nq = (N + S::BRQ - 1) / S::BRQ;  // steps (the launcher checks nq >= NS)
   // Before the slot of unit (i, 1): tile i + 1 landed and visible to every
   // wave, every wave done with tile i - 1, whose ring slot takes tile
   // i - 1 + NS.
@@ -662,17 +672,18 @@ void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   f32x16 s_0, g_0, s_1, g_1;          // S and dP - delta of the current units of query blocks 0 and 1
   float l_0[16], l_1[16];             // their lse * log2(e)
   u32x4 wp_0[2], wd_0[2], wp_1[2], wd_1[2];  // bf16 P and dS of query blocks 0 and 1
-  // Step i in ring slot R: the slots of units (i, 0) and (i, 1).
-  auto step = [&](int i, auto r_, auto first_, auto last_) __attribute__((always_inline)) {
+  // Step i in ring slot R: the slots of units (i, 0) and (i, 1). MASK: the
+  // step holds rows past N (the last step of a ragged sequence).
+  auto step = [&](int i, auto r_, auto first_, auto last_, auto mask_) __attribute__((always_inline)) {
     constexpr int R = decltype(r_)::value;
     constexpr bool FIRST = decltype(first_)::value, LAST = decltype(last_)::value;
     // unit (i, 0): dV / dK of (i - 1, 1), S / dP of (i, 1), P / dS of (i, 0)
     slot(BoolC<!FIRST>{}, IntC<(R + NS - 1) % NS>{}, IntC<1>{}, wp_1, wd_1, BoolC<true>{}, r_, IntC<1>{}, s_1, g_1, l_1,
-         BoolC<true>{}, s_0, g_0, l_0, wp_0, wd_0);
+         BoolC<true>{}, s_0, g_0, l_0, wp_0, wd_0, mask_, i * S::BRQ);
     boundary(i, r_);
     // unit (i, 1): dV / dK of (i, 0), S / dP of (i + 1, 0), P / dS of (i, 1)
     slot(BoolC<true>{}, r_, IntC<0>{}, wp_0, wd_0, BoolC<!LAST>{}, IntC<(R + 1) % NS>{}, IntC<0>{}, s_0, g_0, l_0,
-         BoolC<true>{}, s_1, g_1, l_1, wp_1, wd_1);
+         BoolC<true>{}, s_1, g_1, l_1, wp_1, wd_1, mask_, i * S::BRQ + 32);
   };
 
   // Prologue: tiles 0 .. NS - 2 in flight, tile 0 resident, S / dP of unit (0, 0).
@@ -680,26 +691,29 @@ void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   wait_vmem_below<0>();
   __syncthreads();
   slot(BoolC<false>{}, IntC<0>{}, IntC<0>{}, wp_1, wd_1, BoolC<true>{}, IntC<0>{}, IntC<0>{}, s_0, g_0, l_0,
-       BoolC<false>{}, s_1, g_1, l_1, wp_0, wd_0);
+       BoolC<false>{}, s_1, g_1, l_1, wp_0, wd_0, BoolC<false>{}, 0);
   // Steps 0 .. nq - 2, NS per iteration (compile-time ring slots), then the
   // rest and the last step, and the dV / dK of the last unit.
-  step(0, IntC<0>{}, BoolC<true>{}, BoolC<false>{});
+  step(0, IntC<0>{}, BoolC<true>{}, BoolC<false>{}, BoolC<false>{});
   int i = 1;
   for (; i + NS <= nq - 1; i += NS) {
     static_for<0, NS>([&](auto u_) __attribute__((always_inline)) {
-      step(i + decltype(u_)::value, IntC<(1 + decltype(u_)::value) % NS>{}, BoolC<false>{}, BoolC<false>{});
+      step(i + decltype(u_)::value, IntC<(1 + decltype(u_)::value) % NS>{}, BoolC<false>{}, BoolC<false>{},
+           BoolC<false>{});
     });
   }
   static_for<0, NS - 1>([&](auto u_) __attribute__((always_inline)) {
     constexpr int U = decltype(u_)::value;
-    if (i + U < nq - 1) step(i + U, IntC<(1 + U) % NS>{}, BoolC<false>{}, BoolC<false>{});
+    if (i + U < nq - 1) step(i + U, IntC<(1 + U) % NS>{}, BoolC<false>{}, BoolC<false>{}, BoolC<false>{});
   });
-  // The last step, nq - 1, in ring slot (nq - 1) % NS.
+  // The last step, nq - 1, in ring slot (nq - 1) % NS, with the row mask when
+  // RAGGED (a template parameter: a second, runtime-selected copy of the step
+  // pushes the kernel over 256 registers).
   static_for<0, NS>([&](auto r_) __attribute__((always_inline)) {
     if ((nq - 1) % NS == decltype(r_)::value) {
-      step(nq - 1, r_, BoolC<false>{}, BoolC<true>{});
+      step(nq - 1, r_, BoolC<false>{}, BoolC<true>{}, BoolC<RAGGED>{});
       slot(BoolC<true>{}, r_, IntC<1>{}, wp_1, wd_1, BoolC<false>{}, r_, IntC<0>{}, s_0, g_0, l_0, BoolC<false>{}, s_1, g_1,
-           l_1, wp_0, wd_0);
+           l_1, wp_0, wd_0, BoolC<false>{}, 0);
     }
   });
 
@@ -720,6 +734,21 @@ void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
         *reinterpret_cast<u32x2*>(dkrow + db * 32 + 8 * jj + 4 * h) = wk;
       }
   }
+}
+
+template <class E, int NS, int WAVES, bool RAGGED>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                        const uint16_t* __restrict__ dO, const float* __restrict__ lse2,
+                        const float* __restrict__ ndelta, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N,
+                        int n_kblk, int total, float c, float scale, int H, Strides sq, Strides sd, Strides sg) {
+  using S = DkdvSpShape<WAVES>;
+  __shared__ __attribute__((aligned(16))) unsigned char ring0[S::SLOTB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring1[S::SLOTB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring2[S::SLOTB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring3[NS == 4 ? S::SLOTB : 16];
+  dkdv_sp_body<E, NS, WAVES, RAGGED>(SpRing{{ring0, ring1, ring2, ring3}}, xcd_remap(blockIdx.x, total), Q, K, V,
+                                     dO, lse2, ndelta, dK, dV, N, n_kblk, c, scale, H, sq, sd, sg);
 }
 
 // ---------------------------------------------------------------- stage 2: dQ
@@ -960,6 +989,14 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #ifndef BWD_FUSE_WPE
 #define BWD_FUSE_WPE BWD_WAVES_PER_EU
 #endif
+// The combined launch takes the pipelined dK/dV body where that kernel applies.
+// Measured per launch (bit-identical outputs): B=32, H=12, N=196 38.5 / 36.1
+// -> 35.0 / 34.0 us (two runs), B=8, H=16, N=1000 141 -> 122 us, B=4, H=12,
+// N=2048 178 -> 172 us; the pipelined stand-alone dK/dV kernel on ragged rows
+// 28 -> 23.6 us at N=196 and 95 -> 70 us at N=1000.
+#ifndef BWD_SP_FUSE
+#define BWD_SP_FUSE 1
+#endif
 template <class E, int D, int MB, int QB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BWD_FUSE_WPE, BWD_FUSE_WPE)))
 void bwd_dkdv_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -977,6 +1014,33 @@ void bwd_dkdv_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   else
     dq_body<E, D, QB>(smem, smem1, xcd_remap(id - total1, total2), Q, K, V, dO, lse2, ndelta, dQ, N, n_qblk, total2, c, scale,
                       kv_len, H, causal, sq, sd, sg);
+}
+
+// The combined launch with the pipelined dK/dV body (d_k = 64, no mask, at
+// least BWD_SP_RING 64-query steps; a ragged last step is masked): blocks
+// [0, total1) run dkdv_sp_body on 128 keys each, the rest dq_body on 32 * 4 *
+// QB queries each, whose two step buffers are the first two ring slots.
+template <class E, int NS, int QB, bool RAGGED>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dkdv_sp_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                           const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                           const float* __restrict__ lse2, const float* __restrict__ ndelta, uint16_t* __restrict__ dQ,
+                           uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int n_kblk, int total1,
+                           int n_qblk, int total2, float c, float scale, const int* __restrict__ kv_len, int H,
+                           int causal, Strides sq, Strides sd, Strides sg) {
+  using S = DkdvSpShape<kThreads / 64>;
+  static_assert(DqShape<S::D, QB>::BUFB <= S::SLOTB, "a dQ step buffer fits in a ring slot");
+  __shared__ __attribute__((aligned(16))) unsigned char ring0[S::SLOTB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring1[S::SLOTB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring2[S::SLOTB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring3[NS == 4 ? S::SLOTB : 16];
+  const int id = blockIdx.x;
+  if (id < total1)
+    dkdv_sp_body<E, NS, kThreads / 64, RAGGED>(SpRing{{ring0, ring1, ring2, ring3}}, xcd_remap(id, total1), Q, K, V,
+                                               dO, lse2, ndelta, dK, dV, N, n_kblk, c, scale, H, sq, sd, sg);
+  else
+    dq_body<E, S::D, QB>(ring0, ring1, xcd_remap(id - total1, total2), Q, K, V, dO, lse2, ndelta, dQ, N, n_qblk, total2,
+                         c, scale, kv_len, H, causal, sq, sd, sg);
 }
 
 // ---------------------------------------------------------------- fp32 backward
@@ -1179,7 +1243,16 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
       const int n_kblk = (N + BCK - 1) / BCK, total1 = n_kblk * B * H;
       constexpr int BR = DqShape<D, QB>::BR;
       const int n_qblk = (N + BR - 1) / BR, total2 = n_qblk * B * H;
-      if (D == 64 && N < BWD_FUSE_MB1_N)  // 32-query steps split evenly over the DMA lanes at d_k = 64 only
+      if (D == 64 && BWD_SP_FUSE && BWD_SP && !causal && !kv_len && (N + 63) / 64 >= BWD_SP_RING) {
+        if (N % 64)
+          hipLaunchKernelGGL((bwd_dkdv_sp_dq_kernel<E, BWD_SP_RING, QB, true>), dim3(total1 + total2), dim3(kThreads),
+                             0, stream, q, k, v, dO, lse2, ndelta, dq, dk, dv, N, n_kblk, total1, n_qblk, total2, c,
+                             scale, kv_len, H, causal, st[0], st[2], st[3]);
+        else
+          hipLaunchKernelGGL((bwd_dkdv_sp_dq_kernel<E, BWD_SP_RING, QB, false>), dim3(total1 + total2), dim3(kThreads),
+                             0, stream, q, k, v, dO, lse2, ndelta, dq, dk, dv, N, n_kblk, total1, n_qblk, total2, c,
+                             scale, kv_len, H, causal, st[0], st[2], st[3]);
+      } else if (D == 64 && N < BWD_FUSE_MB1_N)  // 32-query steps split evenly over the DMA lanes at d_k = 64 only
         hipLaunchKernelGGL((bwd_dkdv_dq_kernel<E, D, (D == 64 ? 1 : 2), QB>), dim3(total1 + total2), dim3(kThreads),
                            0, stream, q, k, v, dO, lse2, ndelta, dq, dk, dv, N, n_kblk, total1, n_qblk, total2, c,
                            scale, kv_len, H, causal, st[0], st[2], st[3]);
@@ -1193,11 +1266,15 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
   } else if (stage == 1) {
     if constexpr (D == 64) {
       constexpr int NS = BWD_SP_RING;
-      if (BWD_SP && !causal && !kv_len && N % 64 == 0 && N / 64 >= NS) {
+      if (BWD_SP && !causal && !kv_len && (N + 63) / 64 >= NS) {
         constexpr int W = BWD_SP_WAVES, BCK = DkdvSpShape<W>::BCK;
         const int n_kblk = (N + BCK - 1) / BCK, total = n_kblk * B * H;
-        hipLaunchKernelGGL((bwd_dkdv_sp_kernel<E, NS, W>), dim3(total), dim3(64 * W), 0, stream, q, k, v, dO, lse2,
-                           ndelta, dk, dv, N, n_kblk, total, c, scale, H, st[0], st[2], st[3]);
+        if (N % 64)
+          hipLaunchKernelGGL((bwd_dkdv_sp_kernel<E, NS, W, true>), dim3(total), dim3(64 * W), 0, stream, q, k, v, dO,
+                             lse2, ndelta, dk, dv, N, n_kblk, total, c, scale, H, st[0], st[2], st[3]);
+        else
+          hipLaunchKernelGGL((bwd_dkdv_sp_kernel<E, NS, W, false>), dim3(total), dim3(64 * W), 0, stream, q, k, v, dO,
+                             lse2, ndelta, dk, dv, N, n_kblk, total, c, scale, H, st[0], st[2], st[3]);
         return hipGetLastError();
       }
     }
