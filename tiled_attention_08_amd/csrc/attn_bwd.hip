@@ -54,6 +54,13 @@ constexpr int kThreads = 256;
 #define BWD_DQ_QB64 2
 #endif
 constexpr int BCQ = 32;                  // dQ kernel: keys per step
+// dQ kernel: the dP accumulator starts from -delta (see dq_body). Measured per
+// launch: B=8, H=16, N=4096 783 / 778 -> 762 / 761 us, combined launch B=4,
+// H=12, N=2048 187 -> 183 us; causal unchanged. dQ rounds differently (the
+// sum starts from -delta), within every tolerance of the parity tests.
+#ifndef BWD_DQ_DINIT
+#define BWD_DQ_DINIT 1
+#endif
 
 #ifndef BWD_WAVES_PER_EU
 #define BWD_WAVES_PER_EU 2
@@ -862,12 +869,16 @@ __device__ __forceinline__ void dq_body(unsigned char* buf0, unsigned char* buf1
     const unsigned char* Ks = buf ? buf1 : buf0;
     const unsigned char* Vs = Ks + S::TILEB;
 
-    // ---- S^T = K Q^T and dP^T = V dO^T: 32 keys x (32*QB) queries.
+    // ---- S^T = K Q^T and dP^T - delta = V dO^T - delta: 32 keys x (32*QB)
+    // queries. With BWD_DQ_DINIT the dP accumulator starts from -delta of its
+    // query (every entry of a lane column), as the dK/dV kernel's does, which
+    // saves an add per entry.
     f32x16 sacc[QB], pacc[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       sacc[qb] = f32x16{};
-      pacc[qb] = f32x16{};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) pacc[qb][e] = BWD_DQ_DINIT ? dl[qb] : 0.f;
     }
 #pragma unroll
     for (int cc = 0; cc < D / 16; ++cc) {
@@ -894,7 +905,9 @@ __device__ __forceinline__ void dq_body(unsigned char* buf0, unsigned char* buf1
           if (key >= klq[qb]) p0 = 0.f;
           if (key + 1 >= klq[qb]) p1 = 0.f;
         }
-        dsb[qb][e >> 3][(e >> 1) & 3] = E::pack(p0 * (pacc[qb][e] + dl[qb]), p1 * (pacc[qb][e + 1] + dl[qb]));
+        const float g0 = BWD_DQ_DINIT ? pacc[qb][e] : pacc[qb][e] + dl[qb];
+        const float g1 = BWD_DQ_DINIT ? pacc[qb][e + 1] : pacc[qb][e + 1] + dl[qb];
+        dsb[qb][e >> 3][(e >> 1) & 3] = E::pack(p0 * g0, p1 * g1);
       }
 
     // ---- dQ^T += K^T dS^T (m = dim, n = query, k = key); K^T by transposing reads.
