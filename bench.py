@@ -115,6 +115,15 @@ def dkdv_kernel_name(N: int, d: int, causal: bool) -> str:
     return "bwd_dkdv_sp_kernel" if d == 64 and not causal and (N + 63) // 64 >= 3 else "bwd_dkdv_kernel"
 
 
+def dq_kernel_name(B: int, H: int, N: int, d: int, causal: bool) -> str:
+    """The stand-alone dQ kernel for a shape without key padding: the software-pipelined kernel (one 32-query block
+    per wave) for unmasked rows of at least three 64-key tiles at d_k 64 when the two-block kernel's grid would be
+    under 4 workgroups per CU, the two-block single-phase kernel otherwise."""
+    if d == 64 and not causal and (N + 63) // 64 >= 3 and B * H * ((N + 255) // 256) < 4 * 256:
+        return "bwd_dq_sp_kernel"
+    return "bwd_dq_kernel"
+
+
 def fused_kernel_name(N: int, d: int, causal: bool) -> str:
     """The combined dK/dV + dQ launch for a shape without key padding: with the pipelined dK/dV body where the
     stand-alone pipelined kernel applies, with the single-phase one otherwise."""
@@ -126,7 +135,7 @@ def mix_of_kernel(kernel: str, d: int):
     d_k = 64 for the backward kernels and the d_k = 64 forward, d_k = 128 for the forward."""
     if d == 64:
         return {"bwd_dkdv_kernel": "dkdv", "bwd_dkdv_sp_kernel": "dkdv", "bwd_dkdv_dq_kernel": "dkdv",
-                "bwd_dkdv_sp_dq_kernel": "dkdv",
+                "bwd_dkdv_sp_dq_kernel": "dkdv", "bwd_dq_sp_kernel": "dq",
                 "bwd_dq_kernel": "dq", "fwd_kernel": "fwd64", "fwd_sp_kernel": "fwd64"}.get(kernel)
     if d == 128:
         return {"fwd_kernel": "fwd128", "fwd_pp_kernel": "fwd128", "fwd_sp_kernel": "fwd128"}.get(kernel)
@@ -135,7 +144,8 @@ def mix_of_kernel(kernel: str, d: int):
 
 # Matrix-core work per unit of algorithmic work: the dQ kernel repeats the S and dP products (3 of its products
 # per algorithmic one), the fused backward launch likewise (14 per 10).
-MFMA_PER_ALGORITHMIC = {"bwd_dq_kernel": 3.0, "bwd_dkdv_dq_kernel": 1.4, "bwd_dkdv_sp_dq_kernel": 1.4}
+MFMA_PER_ALGORITHMIC = {"bwd_dq_kernel": 3.0, "bwd_dq_sp_kernel": 3.0, "bwd_dkdv_dq_kernel": 1.4,
+                        "bwd_dkdv_sp_dq_kernel": 1.4}
 
 
 def attach_attainable(roofline: dict, d: int, causal: bool) -> None:
@@ -483,7 +493,7 @@ def bench_proj(args, w) -> int:
               "bwd_dq": 5 * E * sz + 8 * R, "bwd_dkdv_dq": 7 * E * sz + 8 * R}
     kname_full = {"proj_fwd": "gemm256_kernel", "proj_bwd": "attn_qkv_proj_bwd (dx and dw products, split sums)",
                   "fwd": fwd_kernel_name(N, d, False), "bwd_prep": "bwd_prep_kernel", "bwd_dkdv": dkdv_kernel_name(N, d, False),
-                  "bwd_dq": "bwd_dq_kernel", "bwd_dkdv_dq": fused_kernel_name(N, d, False)}
+                  "bwd_dq": dq_kernel_name(B, H, N, d, False), "bwd_dkdv_dq": fused_kernel_name(N, d, False)}
     # The roofline describes the longest single kernel (the projection backward is a group of launches).
     single = {kn: t for kn, t in kernels.items() if kn != "proj_bwd"}
     dominant = max(single, key=single.get)
@@ -729,7 +739,8 @@ def main(argv=None) -> int:
     E, R, sz = B * H * N * d, B * H * N, 2
     kbytes = {"fwd": 4 * E * sz + 4 * R, "bwd_prep": 2 * E * sz + 12 * R, "bwd_dkdv": 6 * E * sz + 8 * R,
               "bwd_dq": 5 * E * sz + 8 * R, "bwd_dkdv_dq": 7 * E * sz + 8 * R}
-    kname_full = {"fwd": fwd_kernel_name(N, d, cz), "bwd_dkdv": dkdv_kernel_name(N, d, cz), "bwd_dq": "bwd_dq_kernel",
+    kname_full = {"fwd": fwd_kernel_name(N, d, cz), "bwd_dkdv": dkdv_kernel_name(N, d, cz),
+                  "bwd_dq": dq_kernel_name(B, H, N, d, cz),
                   "bwd_prep": "bwd_prep_kernel", "bwd_dkdv_dq": fused_kernel_name(N, d, cz)}
     dominant = max(kernels, key=kernels.get)
     wkey = w.name + ("_causal" if cz else "") + ("_f16" if args.dtype == "f16" else "")

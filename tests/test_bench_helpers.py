@@ -29,12 +29,16 @@ def test_dkdv_kernel_names():
     assert bench.fused_kernel_name(196, 64, False) == "bwd_dkdv_sp_dq_kernel"
     assert bench.fused_kernel_name(197, 64, True) == "bwd_dkdv_dq_kernel"
     assert bench.fused_kernel_name(100, 64, False) == "bwd_dkdv_dq_kernel"
+    assert bench.dq_kernel_name(8, 16, 4096, 64, False) == "bwd_dq_kernel"     # 2048 two-block workgroups
+    assert bench.dq_kernel_name(4, 12, 2048, 64, False) == "bwd_dq_sp_kernel"  # 384
+    assert bench.dq_kernel_name(4, 12, 2048, 64, True) == "bwd_dq_kernel"
+    assert bench.dq_kernel_name(4, 12, 128, 64, False) == "bwd_dq_kernel"      # 2 tiles: under the ring of 3
 
 
 def test_mix_of_kernel():
     from tiled_attention_08_amd.ceiling import MIXES
     for kernel, d, mix in (("bwd_dkdv_sp_kernel", 64, "dkdv"), ("bwd_dkdv_dq_kernel", 64, "dkdv"),
-                           ("bwd_dkdv_sp_dq_kernel", 64, "dkdv"),
+                           ("bwd_dkdv_sp_dq_kernel", 64, "dkdv"), ("bwd_dq_sp_kernel", 64, "dq"),
                            ("bwd_dq_kernel", 64, "dq"), ("fwd_sp_kernel", 64, "fwd64"), ("fwd_sp_kernel", 128, "fwd128"),
                            ("fwd_pp_kernel", 128, "fwd128")):
         assert bench.mix_of_kernel(kernel, d) == mix and mix in MIXES

@@ -125,6 +125,48 @@ def test_pipelined_dkdv_equals_single_phase(gpu_lib, dtype, B, H, N, sigma, layo
     assert torch.equal(outs[0][1], outs[1][1]), "dV"
 
 
+@pytest.mark.parametrize("dtype,B,H,N,sigma,layout", [
+    ("bf16", 2, 3, 256, 1.0, "bhnd"), ("bf16", 4, 12, 2048, 8.0, "bhnd"), ("f16", 2, 2, 1088, 1.0, "bhnd"),
+    ("bf16", 2, 3, 196, 1.0, "bhnd"), ("bf16", 1, 2, 129, 1.0, "bhnd"), ("bf16", 2, 2, 1000, 8.0, "qkv_packed"),
+])
+def test_pipelined_dq_equals_single_phase(gpu_lib, dtype, B, H, N, sigma, layout):
+    """Small unmasked grids at d_k = 64 (at least three 64-key tiles, the last may be partial) run the
+    software-pipelined dQ kernel; a key-padding length equal to N routes the same inputs to the single-phase
+    kernel, which sums the same products in the same order: dQ must be identical."""
+    import torch
+    d = 64
+    x = make_case(B, H, N, d, dtype, seed=7400 + N, qk_sigma=sigma)
+    print(f"pipelined dQ {dtype} B={B} H={H} N={N} d={d} sigma={sigma} layout={layout}", flush=True)
+    sys.stdout.flush()
+    q, k, v, do = (to_device(x, n) for n in ("q", "k", "v", "do"))
+    if layout == "qkv_packed":
+        qkv = torch.stack([q.permute(0, 2, 1, 3), k.permute(0, 2, 1, 3), v.permute(0, 2, 1, 3)], dim=2).contiguous()
+        q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+        do = do.permute(0, 2, 1, 3).contiguous()
+    shape = (B, N, H, d) if layout == "qkv_packed" else (B, H, N, d)
+    o = torch.empty(shape, dtype=q.dtype, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    gpu_lib.attn_fwd_ex(q, k, v, o, lse, x.scale, layout=layout)
+    ws = gpu_lib.workspace_for(q)
+
+    def grads():
+        if layout == "qkv_packed":
+            g = torch.full((B, N, 3, H, d), float("nan"), dtype=q.dtype, device="cuda")
+            return g[:, :, 0], g[:, :, 1], g[:, :, 2]
+        return tuple(torch.full(shape, float("nan"), dtype=q.dtype, device="cuda") for _ in range(3))
+
+    gpu_lib.attn_bwd_stage(0, q, k, v, o, lse, do, *grads(), x.scale, ws, layout=layout)
+    full = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    outs = []
+    for kv in (None, full):
+        dq, dk, dv = grads()
+        gpu_lib.attn_bwd_stage(2, q, k, v, o, lse, do, dq, dk, dv, x.scale, ws, kv_len=kv, layout=layout)
+        outs.append(dq)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(outs[0].float()).all())
+    assert torch.equal(outs[0], outs[1]), "dQ"
+
+
 @pytest.mark.parametrize("dtype,B,H,N,layout", [
     ("bf16", 2, 4, 196, "bhnd"), ("f16", 4, 2, 256, "bhnd"), ("bf16", 2, 4, 1000, "bhnd"), ("bf16", 2, 4, 197, "qkv_packed"),
 ])

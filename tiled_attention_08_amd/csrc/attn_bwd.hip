@@ -981,6 +981,283 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                     kv_len, H, causal, sq, sd, sg);
 }
 
+// ---------------------------------------------------------------- stage 2, software-pipelined (d_k = 64)
+// The dQ kernel above runs each 32-key step as three dependent phases (S^T
+// and dP^T products, then the exponentials, then the dQ^T products), so a
+// wave's products and its vector work overlap only with the other wave of
+// its SIMD. This variant (unmasked rows, N a multiple of 64, d_k = 64) gives
+// each wave one 32-query block and runs one slot per 32-key unit: the slot of
+// unit u issues the dQ^T products of unit u - 1 and the S^T and dP^T products
+// of unit u + 1 while it computes dS^T of unit u from the accumulators of the
+// previous slot, one score per chunk (its exponential, fma and multiply, and
+// half a pack). Each accumulator sums the same products in the same order as
+// in bwd_dq_kernel: bit-identical dQ. K/V tiles of 64 keys (two units) in a
+// ring of BWD_DQ_SP_RING slots, one LDS array each.
+#ifndef BWD_DQ_SP
+#define BWD_DQ_SP 1
+#endif
+#ifndef BWD_DQ_SP_RING
+#define BWD_DQ_SP_RING 3
+#endif
+#ifndef BWD_DQ_SP_AHEAD
+#define BWD_DQ_SP_AHEAD 2
+#endif
+
+template <int WAVES>
+struct DqSpShape {
+  static constexpr int D = 64, BCK = 64, ROWB = 2 * D, THREADS = 64 * WAVES;
+  static constexpr int BR = 32 * WAVES;              // queries per workgroup (32 per wave)
+  static constexpr int TILEB = BCK * ROWB;           // one K or V tile (8 KB)
+  static constexpr int KDMA = BCK * D / 8 / THREADS; // 16-byte DMAs per lane per tensor per tile
+  static_assert(KDMA >= 1 && (BCK * D / 8) % THREADS == 0, "tiles split evenly over the lanes");
+  static constexpr int OFF_K = 0, OFF_V = TILEB, SLOTB = 2 * TILEB;
+};
+
+// RAGGED: N is not a multiple of the 64-key tile; key rows past N are read
+// as row N - 1 and get probability 0 in the last tile.
+template <class E, int NS, int WAVES, bool RAGGED>
+__device__ __forceinline__ void dq_sp_body(const SpRing& ring, int work, const uint16_t* __restrict__ Q,
+                                           const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                           const uint16_t* __restrict__ dO, const float* __restrict__ lse2_in,
+                                           const float* __restrict__ ndelta, uint16_t* __restrict__ dQ, int N,
+                                           int n_qblk, float c, float scale, int H, Strides sq, Strides sd,
+                                           Strides sg) {
+  using S = DqSpShape<WAVES>;
+  constexpr int D = S::D;
+  static_assert(NS == 3 || NS == 4, "ring of 3 or 4 tiles");
+  auto slot_base = [&](auto r_) __attribute__((always_inline)) -> unsigned char* {
+    constexpr int R = decltype(r_)::value % NS;
+    return ring.s[R];
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
+  const int g = lane >> 4, gi = lane & 15;
+  const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
+  const int bh = work / n_qblk, qblk = work - bh * n_qblk;
+  const size_t hq = head_off(sq, bh, H), hd = head_off(sd, bh, H);
+  const size_t hrow = (size_t)bh * N;
+  const int q = qblk * S::BR + wave * 32 + l32;  // this lane's query (queries past N compute unused rows)
+  const bool ok = q < N;
+
+  // Q and dO fragments of this lane's query (B operands of S^T = K Q^T and
+  // dP^T = V dO^T), its lse in log2 units and -delta (as in dq_body).
+  u32x4 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) {
+    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+    if (ok) {
+      a = *reinterpret_cast<const u32x4*>(Q + hq + q * sq.n + cc * 16 + h * 8);
+      b = *reinterpret_cast<const u32x4*>(dO + hd + q * sd.n + cc * 16 + h * 8);
+    }
+    qf[cc] = a;
+    df[cc] = b;
+  }
+  const float lse2 = ok ? lse2_in[hrow + q] : 0.f;
+  const float dl = ok ? ndelta[hrow + q] : 0.f;
+
+  const Rsrc rK = make_rsrc(K + hq), rV = make_rsrc(V + hq);
+  auto dma_tile = [&](int j, auto r_) __attribute__((always_inline)) {
+    unsigned char* base = slot_base(r_);
+#pragma unroll
+    for (int r = 0; r < S::KDMA; ++r) {
+      const int slot0 = (wave * S::KDMA + r) * 64;
+      const int p = slot0 + lane;
+      const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz<S::ROWB>(row);
+      const int kr = RAGGED ? min(j * S::BCK + row, N - 1) : j * S::BCK + row;
+      const uint32_t off = (uint32_t)(kr * sq.n + chunk * 8) * 2u;
+      dma16(rK, off, base + S::OFF_K + slot0 * 16);
+      dma16(rV, off, base + S::OFF_V + slot0 * 16);
+    }
+  };
+
+  // Per-lane LDS offsets (key block 0 of a tile; the other block and the
+  // 16-key halves add whole rows, which leave the swizzle unchanged): K and V
+  // rows l32 (chunk 2cc + h), and the transposing K reads of rows 4h + er (+ 8).
+  int koff[D / 16], toff[2][2];
+#pragma unroll
+  for (int cc = 0; cc < D / 16; ++cc) koff[cc] = tile_off<S::ROWB>(l32, cc * 16 + h * 8);
+#pragma unroll
+  for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+    for (int db = 0; db < 2; ++db) toff[hi][db] = tile_off<S::ROWB>(4 * h + er + 8 * hi, db * 32 + dsub * 16 + 4 * qq);
+
+  // Product m of a slot: m < 4 the dQ^T products of the previous unit (16-key
+  // half m >> 1, 32-dim block m & 1: dq_body's order), m >= 4 the S^T and
+  // dP^T products of the next unit (b = m - 4: kind b & 1, 16-dim chunk b >> 1).
+  auto operand = [&](int m, auto ra_, auto kba_, auto rb_, auto kbb_) __attribute__((always_inline)) -> u32x4 {
+    if (m < 4) {
+      const unsigned char* T = slot_base(ra_) + S::OFF_K;
+      const int rows = (decltype(kba_)::value * 32 + (m >> 1) * 16) * S::ROWB, db = m & 1;
+      return cat(lds_read_tr16_b64(T, rows + toff[0][db]), lds_read_tr16_b64(T, rows + toff[1][db]));
+    }
+    const int b = m - 4;
+    const unsigned char* T = slot_base(rb_) + ((b & 1) ? S::OFF_V : S::OFF_K);
+    return lds_read_b128(T, decltype(kbb_)::value * 32 * S::ROWB + koff[b >> 1]);
+  };
+
+  f32x16 dqacc[2];
+#pragma unroll
+  for (int db = 0; db < 2; ++db) dqacc[db] = f32x16{};
+
+  // One slot. A (HA): dQ^T += K^T dS^T of the unit in key block KBA of the
+  // tile in ring slot RA, from its bf16 dS^T in ya. B (HB): S^T and dP^T -
+  // delta of the unit in key block KBB of the tile in slot RB into sn / pn. V
+  // (HV): dS^T of the current unit from sv / pv into xd (the pair of entries
+  // 2i, 2i + 1 goes to word i & 3 of operand i >> 2).
+  // maskV: the current unit (first key kv0) has keys past N, whose P and dS are 0.
+  auto slot = [&](auto hasA, auto ra_, auto kba_, const u32x4 (&ya)[2], auto hasB, auto rb_, auto kbb_, f32x16& sn,
+                  f32x16& pn, auto hasV, const f32x16& sv, const f32x16& pv, u32x4 (&xd)[2], auto maskV, int kv0)
+                  __attribute__((always_inline)) {
+    constexpr bool HA = decltype(hasA)::value, HB = decltype(hasB)::value, HV = decltype(hasV)::value;
+    constexpr bool MV = decltype(maskV)::value;
+    constexpr int AH = BWD_DQ_SP_AHEAD, NO = AH + 1;
+    constexpr int M0 = HA ? 0 : 4, M1 = HB ? 12 : 4;  // products [M0, M1)
+    u32x4 ops[NO];
+    static_for<0, AH>([&](auto a_) __attribute__((always_inline)) {
+      constexpr int m = M0 + decltype(a_)::value;
+      if constexpr (m < M1) ops[m % NO] = operand(m, ra_, kba_, rb_, kbb_);
+    });
+    // 12 chunks, one product each (when the slot has all 12); the 16 scores of
+    // the current unit are spread over them, score e in chunk 3e / 4.
+    float de = 0.f;  // dS of the even entry of the pair
+    auto score = [&](auto e_) __attribute__((always_inline)) {
+      constexpr int EE = decltype(e_)::value;
+      float p = __builtin_amdgcn_exp2f(fmaf(sv[EE], c, -lse2));
+      if constexpr (MV) {
+        if (kv0 + 8 * (EE >> 2) + 4 * h + (EE & 3) >= N) p = 0.f;
+      }
+      const float ds = p * (BWD_DQ_DINIT ? pv[EE] : pv[EE] + dl);
+      if constexpr (EE & 1) {
+        constexpr int i = EE >> 1;
+        xd[i >> 2][i & 3] = E::pack(de, ds);
+        // An empty use keeps this pair's vector work in this chunk (see BWD_SP_PIN).
+        __asm__ volatile("" : : "v"(xd[i >> 2][i & 3]));
+      } else {
+        de = ds;
+      }
+    };
+    static_for<0, 12>([&](auto k_) __attribute__((always_inline)) {
+      constexpr int KK = decltype(k_)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (HB && KK == 0) {
+        sn = f32x16{};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) pn[e] = BWD_DQ_DINIT ? dl : 0.f;
+      }
+      constexpr int M = M0 + KK;  // this chunk's product (the first M1 - M0 chunks carry one)
+      if constexpr (M < M1) {
+        if constexpr (M < 4) {
+          constexpr int c2 = M >> 1, db = M & 1;
+          dqacc[db] = E::mfma(ops[M % NO], ya[c2], dqacc[db]);
+        } else {
+          constexpr int b = M - 4, cc = b >> 1;
+          if constexpr (b & 1)
+            pn = E::mfma(ops[M % NO], df[cc], pn);
+          else
+            sn = E::mfma(ops[M % NO], qf[cc], sn);
+        }
+        if constexpr (M + AH < M1) ops[(M + AH) % NO] = operand(M + AH, ra_, kba_, rb_, kbb_);
+      }
+      if constexpr (HV) {
+        static_for<(4 * KK + 2) / 3, (4 * KK + 6) / 3>([&](auto e_) __attribute__((always_inline)) { score(e_); });
+      }
+    });
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  const int nt = (N + S::BCK - 1) / S::BCK;  // tiles (the launcher checks nt >= NS)
+  // Before the slot of unit (j, 1): tile j + 1 landed and visible to every
+  // wave, every wave done with tile j - 1, whose ring slot takes tile j - 1 + NS.
+  auto boundary = [&](int j, auto r_) __attribute__((always_inline)) {
+    constexpr int R = decltype(r_)::value;
+    if (j + 1 >= nt) return;
+    if constexpr (NS == 4) {
+      if (j + 2 < nt)
+        wait_vmem_below<2 * S::KDMA>();
+      else
+        wait_vmem_below<0>();
+    } else {
+      wait_vmem_below<0>();
+    }
+    __syncthreads();
+    if (j - 1 + NS < nt) dma_tile(j - 1 + NS, IntC<(R + NS - 1) % NS>{});
+  };
+
+  f32x16 s_0, g_0, s_1, g_1;  // S^T and dP^T - delta of the current units of key blocks 0 and 1
+  u32x4 wd_0[2], wd_1[2];     // bf16 dS^T of key blocks 0 and 1
+  // Tile j in ring slot R: the slots of units (j, 0) and (j, 1). MASK: the
+  // tile holds keys past N (the last tile when RAGGED).
+  auto tile = [&](int j, auto r_, auto first_, auto last_, auto mask_) __attribute__((always_inline)) {
+    constexpr int R = decltype(r_)::value;
+    constexpr bool FIRST = decltype(first_)::value, LAST = decltype(last_)::value;
+    // unit (j, 0): dQ of (j - 1, 1), S / dP of (j, 1), dS of (j, 0)
+    slot(BoolC<!FIRST>{}, IntC<(R + NS - 1) % NS>{}, IntC<1>{}, wd_1, BoolC<true>{}, r_, IntC<1>{}, s_1, g_1,
+         BoolC<true>{}, s_0, g_0, wd_0, mask_, j * S::BCK);
+    boundary(j, r_);
+    // unit (j, 1): dQ of (j, 0), S / dP of (j + 1, 0), dS of (j, 1)
+    slot(BoolC<true>{}, r_, IntC<0>{}, wd_0, BoolC<!LAST>{}, IntC<(R + 1) % NS>{}, IntC<0>{}, s_0, g_0, BoolC<true>{},
+         s_1, g_1, wd_1, mask_, j * S::BCK + 32);
+  };
+
+  // Prologue: tiles 0 .. NS - 2 in flight, tile 0 resident, S / dP of unit (0, 0).
+  static_for<0, NS - 1>([&](auto r_) __attribute__((always_inline)) { dma_tile(decltype(r_)::value, r_); });
+  wait_vmem_below<0>();
+  __syncthreads();
+  slot(BoolC<false>{}, IntC<0>{}, IntC<0>{}, wd_1, BoolC<true>{}, IntC<0>{}, IntC<0>{}, s_0, g_0, BoolC<false>{}, s_1,
+       g_1, wd_0, BoolC<false>{}, 0);
+  tile(0, IntC<0>{}, BoolC<true>{}, BoolC<false>{}, BoolC<false>{});
+  int j = 1;
+  for (; j + NS <= nt - 1; j += NS) {
+    static_for<0, NS>([&](auto u_) __attribute__((always_inline)) {
+      tile(j + decltype(u_)::value, IntC<(1 + decltype(u_)::value) % NS>{}, BoolC<false>{}, BoolC<false>{},
+           BoolC<false>{});
+    });
+  }
+  static_for<0, NS - 1>([&](auto u_) __attribute__((always_inline)) {
+    constexpr int U = decltype(u_)::value;
+    if (j + U < nt - 1) tile(j + U, IntC<(1 + U) % NS>{}, BoolC<false>{}, BoolC<false>{}, BoolC<false>{});
+  });
+  // The last tile, nt - 1, in ring slot (nt - 1) % NS (with the key mask when
+  // RAGGED), then dQ of its unit (nt - 1, 1).
+  static_for<0, NS>([&](auto r_) __attribute__((always_inline)) {
+    if ((nt - 1) % NS == decltype(r_)::value) {
+      tile(nt - 1, r_, BoolC<false>{}, BoolC<true>{}, BoolC<RAGGED>{});
+      slot(BoolC<true>{}, r_, IntC<1>{}, wd_1, BoolC<false>{}, r_, IntC<0>{}, s_0, g_0, BoolC<false>{}, s_1, g_1,
+           wd_0, BoolC<false>{}, 0);
+    }
+  });
+
+  // Epilogue: dQ = scale (dQ^T)^T, 16-bit RNE (as dq_body's). Lane: query, dims db*32 + 8jj + 4h + 0..3.
+  if (ok) {
+    uint16_t* row = dQ + head_off(sg, bh, H) + q * sg.n;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x16& a = dqacc[db];
+        const u32x2 w = {E::pack(a[4 * jj] * scale, a[4 * jj + 1] * scale),
+                         E::pack(a[4 * jj + 2] * scale, a[4 * jj + 3] * scale)};
+        *reinterpret_cast<u32x2*>(row + db * 32 + 8 * jj + 4 * h) = w;
+      }
+  }
+}
+
+template <class E, int NS, int WAVES, bool RAGGED>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void bwd_dq_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                      const uint16_t* __restrict__ dO, const float* __restrict__ lse2_in,
+                      const float* __restrict__ ndelta, uint16_t* __restrict__ dQ, int N, int n_qblk, int total,
+                      float c, float scale, int H, Strides sq, Strides sd, Strides sg) {
+  using S = DqSpShape<WAVES>;
+  __shared__ __attribute__((aligned(16))) unsigned char ring0[S::SLOTB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring1[S::SLOTB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring2[S::SLOTB];
+  __shared__ __attribute__((aligned(16))) unsigned char ring3[NS == 4 ? S::SLOTB : 16];
+  dq_sp_body<E, NS, WAVES, RAGGED>(SpRing{{ring0, ring1, ring2, ring3}}, xcd_remap(blockIdx.x, total), Q, K, V, dO,
+                                   lse2_in, ndelta, dQ, N, n_qblk, c, scale, H, sq, sd, sg);
+}
+
 // dK/dV and dQ work in one launch (d_k <= 64, where both run two waves per
 // SIMD): blocks [0, total1) are dK/dV workgroups, the rest dQ workgroups, so
 // dQ work fills the CUs that the last dK/dV workgroups leave idle instead of
@@ -1030,10 +1307,15 @@ void bwd_dkdv_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 }
 
 // The combined launch with the pipelined dK/dV body (d_k = 64, no mask, at
-// least BWD_SP_RING 64-query steps; a ragged last step is masked): blocks
-// [0, total1) run dkdv_sp_body on 128 keys each, the rest dq_body on 32 * 4 *
-// QB queries each, whose two step buffers are the first two ring slots.
-template <class E, int NS, int QB, bool RAGGED>
+// least BWD_SP_RING 64-row steps; a ragged last step is masked): blocks [0,
+// total1) run dkdv_sp_body on 128 keys each, the rest dQ on 128 queries each,
+// with the pipelined dq_sp_body where its 64-key tiles cover no more keys
+// than dq_body's 32-key steps (DQSP: N % 64 is 0 or above 32), dq_body
+// otherwise, on the same ring of LDS arrays. Measured per launch (identical
+// results): B=4, H=12, N=2048 173-176 -> 167 us and B=8, H=16, N=1000 123-128
+// -> 119 us with dq_sp_body; at B=32, H=12, N=196 (256 keys in tiles against
+// 224 in steps) it measured 3 % slower than with dq_body.
+template <class E, int NS, bool RAGGED, bool DQSP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_sp_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                            const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -1042,7 +1324,8 @@ void bwd_dkdv_sp_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
                            int n_qblk, int total2, float c, float scale, const int* __restrict__ kv_len, int H,
                            int causal, Strides sq, Strides sd, Strides sg) {
   using S = DkdvSpShape<kThreads / 64>;
-  static_assert(DqShape<S::D, QB>::BUFB <= S::SLOTB, "a dQ step buffer fits in a ring slot");
+  static_assert(DqSpShape<kThreads / 64>::SLOTB <= S::SLOTB && DqShape<S::D, 1>::BUFB <= S::SLOTB,
+                "a dQ tile or step buffer fits in a ring slot");
   __shared__ __attribute__((aligned(16))) unsigned char ring0[S::SLOTB];
   __shared__ __attribute__((aligned(16))) unsigned char ring1[S::SLOTB];
   __shared__ __attribute__((aligned(16))) unsigned char ring2[S::SLOTB];
@@ -1051,9 +1334,12 @@ void bwd_dkdv_sp_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
   if (id < total1)
     dkdv_sp_body<E, NS, kThreads / 64, RAGGED>(SpRing{{ring0, ring1, ring2, ring3}}, xcd_remap(id, total1), Q, K, V,
                                                dO, lse2, ndelta, dK, dV, N, n_kblk, c, scale, H, sq, sd, sg);
+  else if constexpr (DQSP)
+    dq_sp_body<E, NS, kThreads / 64, RAGGED>(SpRing{{ring0, ring1, ring2, ring3}}, xcd_remap(id - total1, total2), Q,
+                                             K, V, dO, lse2, ndelta, dQ, N, n_qblk, c, scale, H, sq, sd, sg);
   else
-    dq_body<E, S::D, QB>(ring0, ring1, xcd_remap(id - total1, total2), Q, K, V, dO, lse2, ndelta, dQ, N, n_qblk, total2,
-                         c, scale, kv_len, H, causal, sq, sd, sg);
+    dq_body<E, S::D, 1>(ring0, ring1, xcd_remap(id - total1, total2), Q, K, V, dO, lse2, ndelta, dQ, N, n_qblk, total2,
+                        c, scale, kv_len, H, causal, sq, sd, sg);
 }
 
 // ---------------------------------------------------------------- fp32 backward
@@ -1231,6 +1517,20 @@ bool bwd_can_fuse(int B, int H, int N, int d) {
 #endif
 }
 
+// The stand-alone dQ launch takes the pipelined kernel (one 32-query block per
+// wave) where rows are unmasked, at least BWD_DQ_SP_RING 64-key tiles long at
+// d_k = 64, and the grid of the single-phase kernel (two blocks per wave, 256
+// queries per workgroup) would be under 4 workgroups per CU: measured per
+// launch (identical dQ) B=4, H=12, N=2048 87-97 -> 74 us, B=8, H=16, N=1024
+// 56-62 -> 52 us, B=2, H=3, N=192 9.6 -> 6.5 us, but B=8, H=16, N=4096 (2048
+// workgroups) 687 -> 702 us and B=2, H=16, N=8192 697 -> 720 us: with ample
+// workgroups the two-block kernel's operand reuse (each K / V fragment feeds
+// two products) wins.
+static bool bwd_dq_pipelined(int B, int H, int N, int d, int causal, bool kv_len) {
+  if (!BWD_DQ_SP || d != 64 || causal || kv_len || (N + 63) / 64 < BWD_DQ_SP_RING) return false;
+  return (long)B * H * ((N + 255) / 256) < 4 * 256;
+}
+
 // Workspace: lse * log2(e), then -delta; fp32 [B*H*N] each, 256-byte aligned.
 size_t bwd_workspace_bytes(int B, int H, int N, int d) {
   (void)d;
@@ -1257,14 +1557,22 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
       constexpr int BR = DqShape<D, QB>::BR;
       const int n_qblk = (N + BR - 1) / BR, total2 = n_qblk * B * H;
       if (D == 64 && BWD_SP_FUSE && BWD_SP && !causal && !kv_len && (N + 63) / 64 >= BWD_SP_RING) {
-        if (N % 64)
-          hipLaunchKernelGGL((bwd_dkdv_sp_dq_kernel<E, BWD_SP_RING, QB, true>), dim3(total1 + total2), dim3(kThreads),
-                             0, stream, q, k, v, dO, lse2, ndelta, dq, dk, dv, N, n_kblk, total1, n_qblk, total2, c,
-                             scale, kv_len, H, causal, st[0], st[2], st[3]);
-        else
-          hipLaunchKernelGGL((bwd_dkdv_sp_dq_kernel<E, BWD_SP_RING, QB, false>), dim3(total1 + total2), dim3(kThreads),
-                             0, stream, q, k, v, dO, lse2, ndelta, dq, dk, dv, N, n_kblk, total1, n_qblk, total2, c,
-                             scale, kv_len, H, causal, st[0], st[2], st[3]);
+        static_assert(DqSpShape<kThreads / 64>::BR == BR && QB == 1, "the same dQ grid for both dQ bodies");
+        const dim3 grid(total1 + total2);
+#define ATTN_SP_DQ(RAG, DQSP)                                                                                      \
+  hipLaunchKernelGGL((bwd_dkdv_sp_dq_kernel<E, BWD_SP_RING, RAG, DQSP>), grid, dim3(kThreads), 0, stream, q, k, v, dO, \
+                     lse2, ndelta, dq, dk, dv, N, n_kblk, total1, n_qblk, total2, c, scale, kv_len, H, causal, st[0], \
+                     st[2], st[3])
+        const bool dqsp = BWD_DQ_SP && (N % 64 == 0 || N % 64 > 32);
+        if (N % 64) {
+          if (dqsp)
+            ATTN_SP_DQ(true, true);
+          else
+            ATTN_SP_DQ(true, false);
+        } else {
+          ATTN_SP_DQ(false, true);
+        }
+#undef ATTN_SP_DQ
       } else if (D == 64 && N < BWD_FUSE_MB1_N)  // 32-query steps split evenly over the DMA lanes at d_k = 64 only
         hipLaunchKernelGGL((bwd_dkdv_dq_kernel<E, D, (D == 64 ? 1 : 2), QB>), dim3(total1 + total2), dim3(kThreads),
                            0, stream, q, k, v, dO, lse2, ndelta, dq, dk, dv, N, n_kblk, total1, n_qblk, total2, c,
@@ -1298,6 +1606,20 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
     hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, MB, KBW>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, ndelta,
                        dk, dv, N, n_kblk, total, c, scale, kv_len, H, causal, st[0], st[2], st[3]);
   } else {
+    if constexpr (D == 64) {
+      constexpr int NS = BWD_DQ_SP_RING;
+      if (bwd_dq_pipelined(B, H, N, D, causal, kv_len != nullptr)) {
+        constexpr int W = 4, BR = DqSpShape<W>::BR;
+        const int n_qblk = (N + BR - 1) / BR, total = n_qblk * B * H;
+        if (N % 64)
+          hipLaunchKernelGGL((bwd_dq_sp_kernel<E, NS, W, true>), dim3(total), dim3(64 * W), 0, stream, q, k, v, dO,
+                             lse2, ndelta, dq, N, n_qblk, total, c, scale, H, st[0], st[2], st[3]);
+        else
+          hipLaunchKernelGGL((bwd_dq_sp_kernel<E, NS, W, false>), dim3(total), dim3(64 * W), 0, stream, q, k, v, dO,
+                             lse2, ndelta, dq, N, n_qblk, total, c, scale, H, st[0], st[2], st[3]);
+        return hipGetLastError();
+      }
+    }
     constexpr int QB = D <= 64 ? BWD_DQ_QB64 : 1;
     constexpr int BR = DqShape<D, QB>::BR;
     const int n_qblk = (N + BR - 1) / BR;
