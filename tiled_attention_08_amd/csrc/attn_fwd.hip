@@ -108,6 +108,13 @@ constexpr int fwd_waves_per_eu(int D, int QB, int WAVES) {
 #ifndef FWD_SP128
 #define FWD_SP128 1
 #endif
+// K and V tiles of the pipelined forward in separate LDS arrays, K first:
+// at d_k = 128 no LDS read needs an address add (bit-identical; 14-16 vector
+// instructions fewer per 32 products, B=2, H=16, N=16384 3594-3607 ->
+// 3578-3586 us).
+#ifndef FWD_SP_KV_SPLIT
+#define FWD_SP_KV_SPLIT 1
+#endif
 #ifndef FWD_SP128_MIN_N
 #define FWD_SP128_MIN_N 1024
 #endif
@@ -124,6 +131,13 @@ constexpr int fwd_waves_per_eu(int D, int QB, int WAVES) {
 // us, B=8, H=16, N=4096, d_k=64 546 -> 540 us (means of two runs each). Also
 // pinning the row sums (FWD_SP_PIN 2) measured 2.5 % slower at d_k = 128, and
 // reading operands 3 or 4 products ahead (FWD_SP_AHEAD) changed nothing.
+// At d_k = 128 (two products per chunk) each chunk is split in two, one
+// product and one exponential each, so that one wave's vector work fits in
+// the shadow of its own products: bit-identical, B=2, H=16, N=16384
+// 3447-3508 -> 3365-3434 us, B=4, H=16, N=4096 455-478 -> 446-448 us.
+#ifndef FWD_SP_FINE
+#define FWD_SP_FINE 1
+#endif
 #ifndef FWD_SP_PIN
 #define FWD_SP_PIN 1
 #endif
@@ -844,6 +858,40 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   constexpr int NSP = KB * NCC;      // S^T products per unit (key block, 16-dim chunk)
   constexpr int PPC = (NPV + NSP) / 16;  // products per chunk of a unit: 1 at d = 64, 2 at d = 128
   constexpr int PER = 2 * S::DMA_PER_WAVE;  // DMA instructions per wave per tile
+#if FWD_SP_KV_SPLIT
+  // K tiles of the four slots first, then the V tiles (declaration order is
+  // allocation order): at d = 128 the K tiles fill the first 64 KB and every
+  // K read reaches its slot through the 16-bit offset field; the V reads
+  // reach theirs from per-lane offsets biased by 64 KB (below). One array per
+  // tile keeps the copies into different tiles apart for the compiler's
+  // wait placement.
+  __shared__ __attribute__((aligned(16))) unsigned char kring0[S::TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char kring1[S::TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char kring2[S::TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char kring3[S::TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char vring0[S::TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char vring1[S::TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char vring2[S::TILEB];
+  __shared__ __attribute__((aligned(16))) unsigned char vring3[S::TILEB];
+  auto k_base = [&](auto r_) __attribute__((always_inline)) -> unsigned char* {
+    constexpr int R = decltype(r_)::value % NS;
+    if constexpr (R == 0) return kring0;
+    else if constexpr (R == 1) return kring1;
+    else if constexpr (R == 2) return kring2;
+    else return kring3;
+  };
+  auto v_base = [&](auto r_) __attribute__((always_inline)) -> unsigned char* {
+    constexpr int R = decltype(r_)::value % NS;
+    if constexpr (R == 0) return vring0;
+    else if constexpr (R == 1) return vring1;
+    else if constexpr (R == 2) return vring2;
+    else return vring3;
+  };
+  // Bias of the V offsets: the V tiles start after the four K tiles; past
+  // 64 KB the offset field cannot hold the slot, so the per-lane offsets
+  // carry the first 64 KB.
+  constexpr int VBIAS = NS * S::TILEB >= 65536 ? 65536 : 0;
+#else
   __shared__ __attribute__((aligned(16))) unsigned char ring0[2 * S::TILEB];
   __shared__ __attribute__((aligned(16))) unsigned char ring1[2 * S::TILEB];
   __shared__ __attribute__((aligned(16))) unsigned char ring2[2 * S::TILEB];
@@ -855,6 +903,10 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     else if constexpr (R == 2) return ring2;
     else return ring3;
   };
+  auto k_base = [&](auto r_) __attribute__((always_inline)) -> unsigned char* { return slot_base(r_); };
+  auto v_base = [&](auto r_) __attribute__((always_inline)) -> unsigned char* { return slot_base(r_) + S::TILEB; };
+  constexpr int VBIAS = 0;
+#endif
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -895,8 +947,8 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int nt = N / S::BC;  // tiles (N is a multiple of the tile; the launcher checks nt >= 4)
 
   auto dma_tile = [&](int j, auto r_) __attribute__((always_inline)) {
-    unsigned char* Ks = slot_base(r_);
-    unsigned char* Vs = Ks + S::TILEB;
+    unsigned char* Ks = k_base(r_);
+    unsigned char* Vs = v_base(r_);
 #pragma unroll
     for (int r = 0; r < S::DMA_PER_WAVE; ++r) {
       const int slot0 = (wave * S::DMA_PER_WAVE + r) * 64;
@@ -915,7 +967,12 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
   for (int hi = 0; hi < 2; ++hi)
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) voff[hi][db] = tile_off<S::ROWB>(4 * h + er + 8 * hi, db * 32 + dsub * 16 + 4 * qq);
+    for (int db = 0; db < D / 32; ++db) {
+      voff[hi][db] = tile_off<S::ROWB>(4 * h + er + 8 * hi, db * 32 + dsub * 16 + 4 * qq) + VBIAS;
+      // Hidden from the optimiser, so that it cannot take the bias back out
+      // of the register and into a per-read address add.
+      if constexpr (VBIAS != 0) __asm__("" : "+v"(voff[hi][db]));
+    }
 
   // One unit's work is issued as 16 chunks, each one matrix product, the
   // exponentials of one pair of S^T entries and the LDS read of the operand
@@ -929,13 +986,13 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // order, and waits for every read in flight when the two are mixed.
   // Operand of product m of a unit: V^T fragment (PV) or K fragment (S).
   auto pv_operand = [&](auto r_, int p) __attribute__((always_inline)) -> u32x4 {
-    const unsigned char* Vs = slot_base(r_) + S::TILEB;
+    const unsigned char* Vs = v_base(r_);
     const int kb = p / (2 * NDB), c2 = (p / NDB) & 1, db = p % NDB;
-    const int rows = (kb * 32 + c2 * 16) * S::ROWB;
+    const int rows = (kb * 32 + c2 * 16) * S::ROWB - VBIAS;
     return cat(lds_read_tr16_b64(Vs, rows + voff[0][db]), lds_read_tr16_b64(Vs, rows + voff[1][db]));
   };
   auto s_operand = [&](auto r_, int sidx) __attribute__((always_inline)) -> u32x4 {
-    const unsigned char* Ks = slot_base(r_);
+    const unsigned char* Ks = k_base(r_);
     return lds_read_b128(Ks, (sidx / NCC) * 32 * S::ROWB + koff[sidx % NCC]);
   };
   // Weights of entries 2i, 2i + 1 of query block QB_'s S^T tile (i = 0 .. 15).
@@ -958,6 +1015,25 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #if FWD_SP_PIN > 1
     __asm__ volatile("" : : "v"(l));  // the same for the row sum
 #endif
+  };
+  // The same pair in two steps, one exponential each, for chunks of one
+  // product (FWD_SP_FINE).
+  auto weight_first = [&](auto qb_, int i, const f32x16 (&sv)[KB]) __attribute__((always_inline)) -> float {
+    constexpr int QB_ = decltype(qb_)::value;
+    const int kb = i >> 3, e = 2 * (i & 7);
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[kb][e], c, -m_run[QB_]));
+    __asm__ volatile("" : : "v"(p0));
+    return p0;
+  };
+  auto weight_second = [&](auto qb_, int i, const f32x16 (&sv)[KB], float p0, u32x4 (&p)[KB][2], float& l)
+                           __attribute__((always_inline)) {
+    constexpr int QB_ = decltype(qb_)::value;
+    const int kb = i >> 3, e = 2 * (i & 7);
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[kb][e + 1], c, -m_run[QB_]));
+    const uint32_t w = E::pack(p0, p1);
+    __asm__ volatile("" : : "v"(w));
+    p[kb][e >> 3][(e >> 1) & 3] = w;
+    l = E::sum_pair(w, l);
   };
   // The first step of fwd_kernel's softmax for one unit: the maximum of its
   // scores and, when the reference has to move (ballot over the wave), the
@@ -1041,11 +1117,14 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     static_for<0, AH>([&](auto a_) __attribute__((always_inline)) {
       if constexpr (decltype(a_)::value < NM) ops[decltype(a_)::value] = operand(decltype(a_)::value);
     });
-    static_for<0, 16>([&](auto i_) __attribute__((always_inline)) {
-      constexpr int I = decltype(i_)::value;
+    constexpr bool FINE = FWD_SP_FINE && PPC == 2;
+    float p_first = 0.f;
+    static_for<0, FINE ? 32 : 16>([&](auto i_) __attribute__((always_inline)) {
+      constexpr int I = FINE ? decltype(i_)::value / 2 : decltype(i_)::value;
+      constexpr int HALF = FINE ? decltype(i_)::value % 2 : 0;
       if (FWD_SP_BARRIER) __builtin_amdgcn_sched_barrier(0);
-      static_for<0, PPC>([&](auto u_) __attribute__((always_inline)) {
-        constexpr int M = I * PPC + decltype(u_)::value;
+      static_for<0, FINE ? 1 : PPC>([&](auto u_) __attribute__((always_inline)) {
+        constexpr int M = FINE ? decltype(i_)::value : I * PPC + decltype(u_)::value;
         if constexpr (M < NM) {
           constexpr bool PVM = HP && M < NPV;
           if constexpr (PVM) {
@@ -1058,7 +1137,12 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
         }
         if constexpr (M + AH < NM) ops[(M + AH) % NO] = operand(M + AH);
       });
-      weight_pair(qs_, I, sv, pw, l);
+      if constexpr (!FINE)
+        weight_pair(qs_, I, sv, pw, l);
+      else if constexpr (HALF == 0)
+        p_first = weight_first(qs_, I, sv);
+      else
+        weight_second(qs_, I, sv, p_first, pw, l);
     });
     __builtin_amdgcn_sched_barrier(0);
     // A maximum-first move rescales O now: with one query block per wave the
