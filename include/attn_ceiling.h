@@ -38,7 +38,7 @@ enum {
   ATTN_MIX_DKDV = 2,     /* dK/dV kernels, d_k = 64:   36 VALU (8 exp),  8 + 8 LDS   */
   ATTN_MIX_DQ = 3,       /* dQ kernel, d_k = 64:       40 VALU (11 exp), 2 + 4 LDS   */
   ATTN_MIX_FWD64 = 4,    /* forward, d_k = 64:         54 VALU (16 exp), 4 + 8 LDS   */
-  ATTN_MIX_FWD128 = 5    /* forward, d_k = 128:        30 VALU (8 exp),  4 + 8 LDS   */
+  ATTN_MIX_FWD128 = 5    /* forward, d_k = 128:        26 VALU (8 exp),  4 + 8 LDS   */
 };
 
 /* Device workspace the probe needs (random operands, LDS contents, outputs). */

@@ -15,7 +15,7 @@ MIXES = {"constant": (0, "products only, constant operands"),
          "dkdv": (2, "dK/dV kernels, d_k 64: 36 VALU (8 exp), 8 + 8 LDS reads per 8 products"),
          "dq": (3, "dQ kernel, d_k 64: 40 VALU (11 exp), 2 + 4 LDS reads per 8 products"),
          "fwd64": (4, "forward, d_k 64: 54 VALU (16 exp), 4 + 8 LDS reads per 8 products"),
-         "fwd128": (5, "forward, d_k 128: 30 VALU (8 exp), 4 + 8 LDS reads per 8 products")}
+         "fwd128": (5, "forward, d_k 128: 26 VALU (8 exp), 4 + 8 LDS reads per 8 products")}
 
 _lib = None
 

@@ -473,9 +473,15 @@ struct SpRing {
   unsigned char* s[4];
 };
 
-// RAGGED: N is not a multiple of the 64-query step; rows past N are read as
-// row N - 1 and get probability 0 in the last step.
-template <class E, int NS, int WAVES, bool RAGGED>
+// RAG: 0 when N is a multiple of the 64-query step; otherwise rows past N
+// are read as row N - 1 and get probability 0 in the last step, whose second
+// 32-query unit holds rows (RAG 1: N % 64 above 32) or none (RAG 2: that unit,
+// whose P and dS would all be 0, is not computed). Measured for RAG 2
+// (identical results): B=32, H=12, N=196 combined launch 35.1-38.0 -> 33.6-35.8
+// us, B=16, H=12, N=197 19.7-20.8 -> 18.7-19.9 us.
+inline int dkdv_rag_of(int N) { return N % 64 == 0 ? 0 : (N % 64 <= 32 ? 2 : 1); }
+
+template <class E, int NS, int WAVES, int RAG>
 __device__ __forceinline__ void dkdv_sp_body(const SpRing& ring, int work, const uint16_t* __restrict__ Q,
                                              const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                              const uint16_t* __restrict__ dO, const float* __restrict__ lse2,
@@ -515,7 +521,7 @@ __device__ __forceinline__ void dkdv_sp_body(const SpRing& ring, int work, const
   const Rsrc rL = make_rsrc(lse2 + hrow), rDL = make_rsrc(ndelta + hrow);
   // DMA counts per tile: 2 * QDMA for every wave, one more for waves 0 and 1.
   constexpr int PER = 2 * S::QDMA;
-  // RAGGED: rows past N repeat row N - 1 (finite data, whose probabilities
+  // Ragged: rows past N repeat row N - 1 (finite data, whose probabilities
   // the last step sets to 0).
   auto dma_tile = [&](int i, auto r_) __attribute__((always_inline)) {
     unsigned char* base = slot_base(r_);
@@ -525,11 +531,11 @@ __device__ __forceinline__ void dkdv_sp_body(const SpRing& ring, int work, const
       const int slot0 = (wave * S::QDMA + r) * 64;
       const int p = slot0 + lane;
       const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz<S::ROWB>(row);
-      const int qr = RAGGED ? min(q0 + row, N - 1) : q0 + row;
+      const int qr = RAG ? min(q0 + row, N - 1) : q0 + row;
       dma16(rQ, (uint32_t)(qr * sq.n + chunk * 8) * 2u, base + S::OFF_Q + slot0 * 16);
       dma16(rdO, (uint32_t)(qr * sd.n + chunk * 8) * 2u, base + S::OFF_DO + slot0 * 16);
     }
-    const uint32_t lr = (uint32_t)(RAGGED ? min(q0 + lane, N - 1) : q0 + lane) * 4u;
+    const uint32_t lr = (uint32_t)(RAG ? min(q0 + lane, N - 1) : q0 + lane) * 4u;
     if (wave == 0) dma4(rL, lr, base + S::OFF_L);
     if (wave == 1) dma4(rDL, lr, base + S::OFF_DL);
   };
@@ -714,13 +720,23 @@ __device__ __forceinline__ void dkdv_sp_body(const SpRing& ring, int work, const
     if (i + U < nq - 1) step(i + U, IntC<(1 + U) % NS>{}, BoolC<false>{}, BoolC<false>{}, BoolC<false>{});
   });
   // The last step, nq - 1, in ring slot (nq - 1) % NS, with the row mask when
-  // RAGGED (a template parameter: a second, runtime-selected copy of the step
-  // pushes the kernel over 256 registers).
+  // ragged (a template parameter: a second, runtime-selected copy of the step
+  // pushes the kernel over 256 registers). With RAG 2 its second unit has no
+  // rows: the step is the slot of its first unit without the next unit's
+  // products, then the dV / dK products of that first unit.
   static_for<0, NS>([&](auto r_) __attribute__((always_inline)) {
-    if ((nq - 1) % NS == decltype(r_)::value) {
-      step(nq - 1, r_, BoolC<false>{}, BoolC<true>{}, BoolC<RAGGED>{});
-      slot(BoolC<true>{}, r_, IntC<1>{}, wp_1, wd_1, BoolC<false>{}, r_, IntC<0>{}, s_0, g_0, l_0, BoolC<false>{}, s_1, g_1,
-           l_1, wp_0, wd_0, BoolC<false>{}, 0);
+    constexpr int R = decltype(r_)::value;
+    if ((nq - 1) % NS == R) {
+      if constexpr (RAG == 2) {
+        slot(BoolC<true>{}, IntC<(R + NS - 1) % NS>{}, IntC<1>{}, wp_1, wd_1, BoolC<false>{}, r_, IntC<1>{}, s_1, g_1,
+             l_1, BoolC<true>{}, s_0, g_0, l_0, wp_0, wd_0, BoolC<true>{}, (nq - 1) * S::BRQ);
+        slot(BoolC<true>{}, r_, IntC<0>{}, wp_0, wd_0, BoolC<false>{}, r_, IntC<0>{}, s_0, g_0, l_0, BoolC<false>{},
+             s_1, g_1, l_1, wp_1, wd_1, BoolC<false>{}, 0);
+      } else {
+        step(nq - 1, r_, BoolC<false>{}, BoolC<true>{}, BoolC<(RAG != 0)>{});
+        slot(BoolC<true>{}, r_, IntC<1>{}, wp_1, wd_1, BoolC<false>{}, r_, IntC<0>{}, s_0, g_0, l_0, BoolC<false>{}, s_1,
+             g_1, l_1, wp_0, wd_0, BoolC<false>{}, 0);
+      }
     }
   });
 
@@ -743,7 +759,7 @@ __device__ __forceinline__ void dkdv_sp_body(const SpRing& ring, int work, const
   }
 }
 
-template <class E, int NS, int WAVES, bool RAGGED>
+template <class E, int NS, int WAVES, int RAG>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                         const uint16_t* __restrict__ dO, const float* __restrict__ lse2,
@@ -754,7 +770,7 @@ void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   __shared__ __attribute__((aligned(16))) unsigned char ring1[S::SLOTB];
   __shared__ __attribute__((aligned(16))) unsigned char ring2[S::SLOTB];
   __shared__ __attribute__((aligned(16))) unsigned char ring3[NS == 4 ? S::SLOTB : 16];
-  dkdv_sp_body<E, NS, WAVES, RAGGED>(SpRing{{ring0, ring1, ring2, ring3}}, xcd_remap(blockIdx.x, total), Q, K, V,
+  dkdv_sp_body<E, NS, WAVES, RAG>(SpRing{{ring0, ring1, ring2, ring3}}, xcd_remap(blockIdx.x, total), Q, K, V,
                                      dO, lse2, ndelta, dK, dV, N, n_kblk, c, scale, H, sq, sd, sg);
 }
 
@@ -1315,7 +1331,7 @@ void bwd_dkdv_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
 // results): B=4, H=12, N=2048 173-176 -> 167 us and B=8, H=16, N=1000 123-128
 // -> 119 us with dq_sp_body; at B=32, H=12, N=196 (256 keys in tiles against
 // 224 in steps) it measured 3 % slower than with dq_body.
-template <class E, int NS, bool RAGGED, bool DQSP>
+template <class E, int NS, int RAG, bool DQSP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_sp_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                            const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -1332,10 +1348,10 @@ void bwd_dkdv_sp_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
   __shared__ __attribute__((aligned(16))) unsigned char ring3[NS == 4 ? S::SLOTB : 16];
   const int id = blockIdx.x;
   if (id < total1)
-    dkdv_sp_body<E, NS, kThreads / 64, RAGGED>(SpRing{{ring0, ring1, ring2, ring3}}, xcd_remap(id, total1), Q, K, V,
-                                               dO, lse2, ndelta, dK, dV, N, n_kblk, c, scale, H, sq, sd, sg);
+    dkdv_sp_body<E, NS, kThreads / 64, RAG>(SpRing{{ring0, ring1, ring2, ring3}}, xcd_remap(id, total1), Q, K, V,
+                                            dO, lse2, ndelta, dK, dV, N, n_kblk, c, scale, H, sq, sd, sg);
   else if constexpr (DQSP)
-    dq_sp_body<E, NS, kThreads / 64, RAGGED>(SpRing{{ring0, ring1, ring2, ring3}}, xcd_remap(id - total1, total2), Q,
+    dq_sp_body<E, NS, kThreads / 64, (RAG != 0)>(SpRing{{ring0, ring1, ring2, ring3}}, xcd_remap(id - total1, total2), Q,
                                              K, V, dO, lse2, ndelta, dQ, N, n_qblk, c, scale, H, sq, sd, sg);
   else
     dq_body<E, S::D, 1>(ring0, ring1, xcd_remap(id - total1, total2), Q, K, V, dO, lse2, ndelta, dQ, N, n_qblk, total2,
@@ -1563,14 +1579,16 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
   hipLaunchKernelGGL((bwd_dkdv_sp_dq_kernel<E, BWD_SP_RING, RAG, DQSP>), grid, dim3(kThreads), 0, stream, q, k, v, dO, \
                      lse2, ndelta, dq, dk, dv, N, n_kblk, total1, n_qblk, total2, c, scale, kv_len, H, causal, st[0], \
                      st[2], st[3])
-        const bool dqsp = BWD_DQ_SP && (N % 64 == 0 || N % 64 > 32);
-        if (N % 64) {
-          if (dqsp)
-            ATTN_SP_DQ(true, true);
-          else
-            ATTN_SP_DQ(true, false);
-        } else {
-          ATTN_SP_DQ(false, true);
+        // dq_sp_body where N % 64 is 0 or above 32 (dkdv_rag_of(N) 0 or 1).
+        switch (dkdv_rag_of(N)) {
+#if BWD_DQ_SP
+          case 0: ATTN_SP_DQ(0, true); break;
+          case 1: ATTN_SP_DQ(1, true); break;
+#else
+          case 0: ATTN_SP_DQ(0, false); break;
+          case 1: ATTN_SP_DQ(1, false); break;
+#endif
+          default: ATTN_SP_DQ(2, false); break;
         }
 #undef ATTN_SP_DQ
       } else if (D == 64 && N < BWD_FUSE_MB1_N)  // 32-query steps split evenly over the DMA lanes at d_k = 64 only
@@ -1590,12 +1608,15 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
       if (BWD_SP && !causal && !kv_len && (N + 63) / 64 >= NS) {
         constexpr int W = BWD_SP_WAVES, BCK = DkdvSpShape<W>::BCK;
         const int n_kblk = (N + BCK - 1) / BCK, total = n_kblk * B * H;
-        if (N % 64)
-          hipLaunchKernelGGL((bwd_dkdv_sp_kernel<E, NS, W, true>), dim3(total), dim3(64 * W), 0, stream, q, k, v, dO,
-                             lse2, ndelta, dk, dv, N, n_kblk, total, c, scale, H, st[0], st[2], st[3]);
-        else
-          hipLaunchKernelGGL((bwd_dkdv_sp_kernel<E, NS, W, false>), dim3(total), dim3(64 * W), 0, stream, q, k, v, dO,
-                             lse2, ndelta, dk, dv, N, n_kblk, total, c, scale, H, st[0], st[2], st[3]);
+#define ATTN_SP_DKDV(RAG)                                                                                    \
+  hipLaunchKernelGGL((bwd_dkdv_sp_kernel<E, NS, W, RAG>), dim3(total), dim3(64 * W), 0, stream, q, k, v, dO, lse2, \
+                     ndelta, dk, dv, N, n_kblk, total, c, scale, H, st[0], st[2], st[3])
+        switch (dkdv_rag_of(N)) {
+          case 0: ATTN_SP_DKDV(0); break;
+          case 1: ATTN_SP_DKDV(1); break;
+          default: ATTN_SP_DKDV(2); break;
+        }
+#undef ATTN_SP_DKDV
         return hipGetLastError();
       }
     }

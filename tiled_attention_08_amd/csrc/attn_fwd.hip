@@ -974,11 +974,14 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       if constexpr (VBIAS != 0) __asm__("" : "+v"(voff[hi][db]));
     }
 
-  // One unit's work is issued as 16 chunks, each one matrix product, the
-  // exponentials of one pair of S^T entries and the LDS read of the operand
-  // two products ahead, with scheduling barriers between chunks: the compiler
-  // keeps them in order (left alone, it hoists every operand read of the
-  // iteration and spills). Products: first P V of the previous unit (PV, 8:
+  // One unit's work is issued as 16 chunks at d = 64, each one matrix
+  // product, the exponentials of one pair of S^T entries and the LDS read of
+  // the operand two products ahead, with scheduling barriers between chunks:
+  // the compiler keeps them in order (left alone, it hoists every operand
+  // read of the iteration and spills). At d = 128 a unit has twice the
+  // products and the same exponentials: 32 chunks of one product and one
+  // exponential each (16 chunks of two products with FWD_SP_FINE 0).
+  // Products at d = 64: first P V of the previous unit (PV, 8:
   // key block, 16-key half, 32-dim block; the two 32-dim accumulators
   // alternate), then S^T of the next one (S, 8: the two key blocks' chains
   // alternate, 16-dim chunks in order). The kinds are not interleaved: the

@@ -174,7 +174,7 @@ hipError_t launch_mix(int mix, const u32x4* w, float* out, int iters, hipStream_
     case ATTN_MIX_DKDV: return launch<true, 8, 8, 18, 8, 8>(w, out, iters, s);
     case ATTN_MIX_DQ: return launch<true, 11, 5, 22, 2, 4>(w, out, iters, s);
     case ATTN_MIX_FWD64: return launch<true, 16, 8, 28, 4, 8>(w, out, iters, s);
-    case ATTN_MIX_FWD128: return launch<true, 8, 4, 16, 4, 8>(w, out, iters, s);
+    case ATTN_MIX_FWD128: return launch<true, 8, 4, 14, 4, 8>(w, out, iters, s);
     default: return hipErrorInvalidValue;
   }
 }
