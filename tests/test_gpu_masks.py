@@ -83,6 +83,7 @@ SMALL = [
     (2, 1, 1100, 64, True, None),
     (3, 1, 1100, 64, False, [1100, 1024, 333]),
     (2, 2, 129, 128, True, None),
+    (1, 2, 1088, 128, True, None),  # the pipelined forward's tiles, then its diagonal tiles (partial last block)
     (3, 1, 517, 128, True, [517, 300, 0]),
     (2, 1, 1030, 128, True, [1030, 640]),
     (2, 1, 1030, 128, False, [777, 1]),

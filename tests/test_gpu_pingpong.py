@@ -7,7 +7,8 @@ arithmetic per element as the single-phase forward, in another order. A
 key-padding length equal to N hides no key but routes the same inputs to the
 single-phase kernel, so the results must be identical (O and lse): bf16 and
 fp16, contiguous and packed layouts, and (pipelined forward) inputs whose
-scores are large enough that many tiles take its full rescale path. All are
+scores are large enough that many tiles take its full rescale path; causal
+rows at d_k = 128 (pipelined tiles, then the diagonal) likewise. All are
 also checked against the fp64 oracle by the parity tests.
 """
 from __future__ import annotations
@@ -206,6 +207,37 @@ def test_combined_pipelined_launch_equals_stages(gpu_lib, dtype, B, H, N, layout
     torch.cuda.synchronize()
     assert bool(torch.isfinite(outs[1].float()).all())
     assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("dtype,B,H,N,sigma,layout", [
+    ("bf16", 1, 2, 1024, 1.0, "bhnd"), ("bf16", 2, 2, 2048, 1.0, "bhnd"), ("f16", 2, 1, 1088, 1.0, "bhnd"),
+    ("bf16", 1, 2, 4096, 8.0, "bhnd"), ("bf16", 2, 2, 1152, 1.0, "qkv_packed"),
+])
+def test_pipelined128_causal_equals_single_phase(gpu_lib, dtype, B, H, N, sigma, layout):
+    """Causal rows of whole 64-key tiles (1024 keys or more) at d_k = 128 run the pipelined forward on the tiles a
+    workgroup's queries see in full, then the diagonal tiles with the single-phase kernel's masked tile; a
+    key-padding length of N routes the same inputs to the single-phase kernel: O and lse must be identical
+    (N = 1088 and 1152 end in a partial 256-row block; sigma 8 gives peaked scores)."""
+    import torch
+    d = 128
+    x = make_case(B, H, N, d, dtype, seed=7400 + N, qk_sigma=sigma, with_grad=False)
+    print(f"pipelined causal d=128 {dtype} B={B} H={H} N={N} sigma={sigma} layout={layout}", flush=True)
+    sys.stdout.flush()
+    q, k, v = (to_device(x, n) for n in ("q", "k", "v"))
+    if layout == "qkv_packed":
+        qkv = torch.stack([q.permute(0, 2, 1, 3), k.permute(0, 2, 1, 3), v.permute(0, 2, 1, 3)], dim=2).contiguous()
+        q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+    full = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    outs = []
+    for kv in (None, full):
+        o = torch.empty((B, N, H, d) if layout == "qkv_packed" else (B, H, N, d), dtype=q.dtype, device="cuda")
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        gpu_lib.attn_fwd_ex(q, k, v, o, lse, x.scale, causal=True, kv_len=kv, layout=layout)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(outs[0][1]).all())
+    assert torch.equal(outs[0][0], outs[1][0]), "O"
+    assert torch.equal(outs[0][1], outs[1][1]), "lse"
 
 
 @pytest.mark.parametrize("dtype,B,H,N,sigma,layout", [

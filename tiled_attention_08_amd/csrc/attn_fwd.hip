@@ -115,6 +115,13 @@ constexpr int fwd_waves_per_eu(int D, int QB, int WAVES) {
 #ifndef FWD_SP_KV_SPLIT
 #define FWD_SP_KV_SPLIT 1
 #endif
+// Causal rows at d_k = 128 on the pipelined forward (bit-identical to
+// fwd_kernel): B=2, H=16, N=16384 2011 -> 1905 us, B=4, H=16, N=4096 282-303
+// -> 272-275 us. At d_k = 64 (256-query workgroups against fwd_kernel's 128)
+// it measured the same at N=4096 and 35 % slower at N=2048.
+#ifndef FWD_SP_CAUSAL
+#define FWD_SP_CAUSAL 1
+#endif
 #ifndef FWD_SP128_MIN_N
 #define FWD_SP128_MIN_N 1024
 #endif
@@ -845,7 +852,10 @@ constexpr int kSPRing = 4;
 // can pass unchecked.
 constexpr float kSpecLimit = 128.0f;
 
-template <class E, int D, int QB, int WAVES>
+// CAUSAL: the causal mask. The tiles every query of the workgroup sees in
+// full (keys before its first query) run the pipelined units; the diagonal
+// tiles after them run fwd_kernel's masked tile, one tile at a time.
+template <class E, int D, int QB, int WAVES, bool CAUSAL>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qblk, int total, float c,
@@ -913,7 +923,8 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int g = lane >> 4, gi = lane & 15;
   const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
   const int work = xcd_remap(blockIdx.x, total);
-  const int bh = work / n_qblk, qblk = work - bh * n_qblk;
+  int bh, qblk;  // causal: the last row blocks have the most keys and are handed out first
+  work_order(work, total, n_qblk, CAUSAL, true, bh, qblk);
   const size_t hq = head_off(sq, bh, H);
   const uint16_t* Qh = Q + hq;
   const uint16_t* Kh = K + hq;
@@ -944,7 +955,12 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     for (int db = 0; db < D / 32; ++db) oacc[qb][db] = f32x16{};
   }
 
-  const int nt = N / S::BC;  // tiles (N is a multiple of the tile; the launcher checks nt >= 4)
+  // Pipelined tiles (N is a multiple of the tile; without the mask the
+  // launcher checks nt >= 4) and tiles read: under the causal mask the
+  // workgroup's first query sees the first nt in full (none, or at least 4),
+  // and its rows reach tile nt_dma - 1.
+  const int nt = CAUSAL ? qblk * S::BR / S::BC : N / S::BC;
+  const int nt_dma = CAUSAL ? min(N, (qblk + 1) * S::BR) / S::BC : nt;
 
   auto dma_tile = [&](int j, auto r_) __attribute__((always_inline)) {
     unsigned char* Ks = k_base(r_);
@@ -1171,7 +1187,7 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   auto boundary = [&](int j, auto r_) __attribute__((always_inline)) {
     constexpr int R = decltype(r_)::value;
     if constexpr (QB == 2) {
-      if (j + 2 >= 3 && j + 2 < nt)
+      if (j + 2 >= 3 && j + 2 < nt_dma)
         wait_vmem_below<PER>();
       else
         wait_vmem_below<0>();
@@ -1179,7 +1195,7 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       wait_vmem_below<0>();
     }
     __syncthreads();
-    if (j + 3 < nt) dma_tile(j + 3, IntC<(R + 3) % NS>{});
+    if (j + 3 < nt_dma) dma_tile(j + 3, IntC<(R + 3) % NS>{});
   };
 
   // Two query blocks: S^T of blocks 0 and 1 (one tile apart) in sa / sb, P^T
@@ -1227,37 +1243,160 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       oacc[QB_][m % NDB] = E::mfma(pv_operand(r_, m), p[m / (2 * NDB)][(m / NDB) & 1], oacc[QB_][m % NDB]);
   };
 
+  // A diagonal tile under the causal mask, as fwd_kernel's masked tile: the
+  // same operations in the same order, so the same results. Keys at or past
+  // klim(q) = min(N, q + 1) of the lane's query get probability 0 and stay out
+  // of the row maximum; 32-key blocks no query of the wave sees are skipped
+  // whole.
+  auto diag_tile = [&](int j, auto r_) __attribute__((always_inline)) {
+    const unsigned char* Ks = k_base(r_);
+    const unsigned char* Vs = v_base(r_);
+    auto klim = [&](int q) { return min(N, q + 1); };
+    int kvalid[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) kvalid[qb] = klim(qw0 + qb * 32 + l32) - j * S::BC;
+    const int kbv = min(KB, max(1, (klim(qw0 + 32 * QB - 1) - j * S::BC + 31) >> 5));
+    f32x16 sacc[QB][KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = f32x16{};
+      if (kb >= kbv) continue;
+#pragma unroll
+      for (int cc = 0; cc < NCC; ++cc) {
+        const u32x4 a = lds_read_b128(Ks, kb * 32 * S::ROWB + koff[cc]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[qb][kb] = E::mfma(a, qf[qb][cc], sacc[qb][kb]);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        if (kb >= kbv) continue;
+        const int key = kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          if (key >= kvalid[qb]) sacc[qb][kb][e] = -INFINITY;
+      }
+    float mnew[QB];
+    bool need[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = sacc[qb][0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        if (kb >= kbv) continue;
+#pragma unroll
+        for (int e = (kb == 0 ? 1 : 0); e < 16; e += 2)
+          mx = (e + 1 < 16) ? fmax3(mx, sacc[qb][kb][e], sacc[qb][kb][e + 1]) : fmax2(mx, sacc[qb][kb][e]);
+      }
+      mx = halves_max(mx) * c;
+      mnew[qb] = fmaxf(m_run[qb], mx);
+      need[qb] = mnew[qb] > m_run[qb] + kRescaleSlack;
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (__builtin_amdgcn_ballot_w64(need[qb])) {
+        const float alpha = mnew[qb] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qb] - mnew[qb]);
+        m_run[qb] = mnew[qb];
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[qb][db] *= alpha;
+      }
+    }
+    u32x4 pd[QB][KB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float nm = -m_run[qb];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          if (kb >= kbv) continue;
+          float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][e], c, nm));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[qb][kb][e + 1], c, nm));
+          const int key = kb * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+          if (key >= kvalid[qb]) p0 = 0.f;
+          if (key + 1 >= kvalid[qb]) p1 = 0.f;
+          const uint32_t w = E::pack(p0, p1);
+          pd[qb][kb][e >> 3][(e >> 1) & 3] = w;
+          l_run[qb] = E::sum_pair(w, l_run[qb]);
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          if (kb >= kbv) continue;
+          const int rows = (kb * 32 + c2 * 16) * S::ROWB - VBIAS;
+          const u32x4 a = cat(lds_read_tr16_b64(Vs, rows + voff[0][db]), lds_read_tr16_b64(Vs, rows + voff[1][db]));
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = E::mfma(a, pd[qb][kb][c2], oacc[qb][db]);
+        }
+  };
+
   // Prologue: tiles 0 .. 2 resident, S of unit (0, 0).
-  dma_tile(0, IntC<0>{});
-  dma_tile(1, IntC<1>{});
-  dma_tile(2, IntC<2>{});
+  static_for<0, 3>([&](auto r_) __attribute__((always_inline)) {
+    if (decltype(r_)::value < nt_dma) dma_tile(decltype(r_)::value, r_);
+  });
   wait_vmem_below<0>();
   __syncthreads();
-  s_only(IntC<0>{}, IntC<0>{}, sa);
-  tile(0, IntC<0>{}, BoolC<true>{}, BoolC<false>{});
-  // Tiles 1 .. nt - 1, four per iteration (ring slots 1, 2, 3, 0), then the
-  // rest. The last tile's last unit also computes S^T of a tile nt that does
-  // not exist, from the slot it would occupy (which holds tile nt - 4: finite
-  // data, nt >= 4, no copy in flight); the result is never used. This keeps
-  // one tile body.
-  int j = 1;
-  for (; j + 4 <= nt; j += 4) {
-    tile(j, IntC<1>{}, BoolC<false>{}, BoolC<false>{});
-    tile(j + 1, IntC<2>{}, BoolC<false>{}, BoolC<false>{});
-    tile(j + 2, IntC<3>{}, BoolC<false>{}, BoolC<false>{});
-    tile(j + 3, IntC<0>{}, BoolC<false>{}, BoolC<false>{});
+  if (nt > 0) {
+    s_only(IntC<0>{}, IntC<0>{}, sa);
+    tile(0, IntC<0>{}, BoolC<true>{}, BoolC<false>{});
+    // Tiles 1 .. nt - 1, four per iteration (ring slots 1, 2, 3, 0), then the
+    // rest. The last tile's last unit also computes S^T of tile nt, from the
+    // slot it would occupy (tile nt - 4 without the mask, nt >= 4, no copy in
+    // flight; the first diagonal tile under the causal mask, landed); the
+    // result is never used. This keeps one tile body.
+    int j = 1;
+    for (; j + 4 <= nt; j += 4) {
+      tile(j, IntC<1>{}, BoolC<false>{}, BoolC<false>{});
+      tile(j + 1, IntC<2>{}, BoolC<false>{}, BoolC<false>{});
+      tile(j + 2, IntC<3>{}, BoolC<false>{}, BoolC<false>{});
+      tile(j + 3, IntC<0>{}, BoolC<false>{}, BoolC<false>{});
+    }
+    if (j < nt) tile(j, IntC<1>{}, BoolC<false>{}, BoolC<false>{});
+    if (j + 1 < nt) tile(j + 1, IntC<2>{}, BoolC<false>{}, BoolC<false>{});
+    if (j + 2 < nt) tile(j + 2, IntC<3>{}, BoolC<false>{}, BoolC<false>{});
+    // P V of the last unit (tile nt - 1; query block 1 with two blocks, P^T in
+    // pa; with one block, pa or pb by the tile's parity).
+    constexpr int QL = QB - 1;
+    switch ((nt - 1) % NS) {
+      case 0: pv_only(IntC<0>{}, IntC<QL>{}, pa); break;
+      case 1: pv_only(IntC<1>{}, IntC<QL>{}, QB == 2 ? pa : pb); break;
+      case 2: pv_only(IntC<2>{}, IntC<QL>{}, pa); break;
+      default: pv_only(IntC<3>{}, IntC<QL>{}, QB == 2 ? pa : pb); break;
+    }
   }
-  if (j < nt) tile(j, IntC<1>{}, BoolC<false>{}, BoolC<false>{});
-  if (j + 1 < nt) tile(j + 1, IntC<2>{}, BoolC<false>{}, BoolC<false>{});
-  if (j + 2 < nt) tile(j + 2, IntC<3>{}, BoolC<false>{}, BoolC<false>{});
-  // P V of the last unit (tile nt - 1; query block 1 with two blocks, P^T in
-  // pa; with one block, pa or pb by the tile's parity).
-  constexpr int QL = QB - 1;
-  switch ((nt - 1) % NS) {
-    case 0: pv_only(IntC<0>{}, IntC<QL>{}, pa); break;
-    case 1: pv_only(IntC<1>{}, IntC<QL>{}, QB == 2 ? pa : pb); break;
-    case 2: pv_only(IntC<2>{}, IntC<QL>{}, pa); break;
-    default: pv_only(IntC<3>{}, IntC<QL>{}, QB == 2 ? pa : pb); break;
+
+  if constexpr (CAUSAL) {
+    // The diagonal tiles nt .. nt_dma - 1, one at a time. Copies are issued in
+    // tile order, and before tile j at most tiles j + 1 and j + 2 may still
+    // be in flight; after the barrier every wave is done with tile j - 1,
+    // whose slot takes tile j + 3.
+    const int nvis_w = (qw0 + 32 * QB + S::BC - 1) / S::BC;  // tiles holding a key this wave's last query sees
+    for (int j = nt; j < nt_dma; ++j) {
+      const int ahead = min(2, nt_dma - 1 - j);
+      if (ahead >= 2)
+        wait_vmem_below<2 * PER>();
+      else if (ahead == 1)
+        wait_vmem_below<PER>();
+      else
+        wait_vmem_below<0>();
+      __syncthreads();
+      static_for<0, NS>([&](auto r_) __attribute__((always_inline)) {
+        if (j + 3 < nt_dma && (j + 3) % NS == decltype(r_)::value) dma_tile(j + 3, r_);
+      });
+      if (j < nvis_w) {
+        static_for<0, NS>([&](auto r_) __attribute__((always_inline)) {
+          if (j % NS == decltype(r_)::value) diag_tile(j, r_);
+        });
+      }
+    }
   }
 
 #pragma unroll
@@ -1404,7 +1543,7 @@ static hipError_t launch_fwd_pp(const uint16_t* q, const uint16_t* k, const uint
   return hipGetLastError();
 }
 
-template <class E, int D, int QB, int WAVES>
+template <class E, int D, int QB, int WAVES, bool CAUSAL>
 static hipError_t launch_fwd_sp(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, float* lse,
                                 int B, int H, int N, float scale, Strides sq, Strides so, hipStream_t stream) {
   using S = FwdShape<D, QB, 2, kSPRing, WAVES>;
@@ -1412,7 +1551,7 @@ static hipError_t launch_fwd_sp(const uint16_t* q, const uint16_t* k, const uint
   const int total = n_qblk * B * H;
   const float c = fabsf(scale) * kLog2e;
   const uint32_t qsign = scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_sp_kernel<E, D, QB, WAVES>), dim3(total), dim3(S::THREADS), 0, stream, q, k, v, o, lse, N,
+  hipLaunchKernelGGL((fwd_sp_kernel<E, D, QB, WAVES, CAUSAL>), dim3(total), dim3(S::THREADS), 0, stream, q, k, v, o, lse, N,
                      n_qblk, total, c, qsign, H, sq, so);
   return hipGetLastError();
 }
@@ -1451,10 +1590,13 @@ static hipError_t launch_fwd_e(const uint16_t* q, const uint16_t* k, const uint1
   const bool lng_small_d = N >= FWD_LONG_N_SMALL_D;
   // Rows without masks, whole 64-key tiles, d = 64: the software-pipelined forward.
   if (FWD_SP && d == 64 && !causal && !kv_len && N % 64 == 0 && N >= FWD_SP_MIN_N)
-    return launch_fwd_sp<E, 64, 2, 4>(q, k, v, o, lse, B, H, N, scale, sq, so, stream);
-  // d = 128: one query block per wave, 8 waves sharing the ring (128 KB of LDS, one workgroup per CU).
-  if (FWD_SP128 && d == 128 && !causal && !kv_len && N % 64 == 0 && N >= FWD_SP128_MIN_N)
-    return launch_fwd_sp<E, 128, 1, 8>(q, k, v, o, lse, B, H, N, scale, sq, so, stream);
+    return launch_fwd_sp<E, 64, 2, 4, false>(q, k, v, o, lse, B, H, N, scale, sq, so, stream);
+  // d = 128: one query block per wave, 8 waves sharing the ring (128 KB of LDS, one workgroup per CU). With the
+  // causal mask (FWD_SP_CAUSAL) the kernel takes the tiles a workgroup's queries see in full and finishes with
+  // the diagonal tiles (at d = 64 the single-phase kernel's 128-query workgroups balance the diagonal better).
+  if (FWD_SP128 && d == 128 && !kv_len && (!causal || FWD_SP_CAUSAL) && N % 64 == 0 && N >= FWD_SP128_MIN_N)
+    return causal ? launch_fwd_sp<E, 128, 1, 8, true>(q, k, v, o, lse, B, H, N, scale, sq, so, stream)
+                  : launch_fwd_sp<E, 128, 1, 8, false>(q, k, v, o, lse, B, H, N, scale, sq, so, stream);
   if (FWD_PINGPONG && lng && !causal && !kv_len) {
 #if FWD_PP_D64
     if (d == 64)
