@@ -22,12 +22,15 @@
 // K/V tiles go HBM -> LDS by direct DMA (no staging registers) into a ring
 // of NS slots, so the next NS-1 tiles are in flight while one is computed.
 //
-// Two 16-bit kernels: fwd_kernel (every tile in one order: S, softmax, P V;
-// masks, every head dim, short rows) and fwd_pp_kernel (unmasked rows of 1024
-// keys or more at d = 128: the same tiles and arithmetic per element, with
-// the two halves of the workgroup a phase apart so that the matrix work of
-// one wave of a SIMD overlaps the softmax of the other). Their outputs are
-// equal bit for bit. fwd_f32_kernel is the fp32 forward on the vector ALU.
+// Three 16-bit kernels: fwd_kernel (every tile in one order: S, softmax,
+// P V; masks, every head dim, short rows), fwd_sp_kernel (rows of whole
+// 64-key tiles, unmasked at d = 64 and unmasked or causal at d = 128: the
+// same tiles and arithmetic per element, software-pipelined so that one
+// wave's products overlap its own softmax) and fwd_pp_kernel (other unmasked
+// rows of 1024 keys or more at d = 128: the two halves of the workgroup a
+// phase apart, so that the matrix work of one wave of a SIMD overlaps the
+// softmax of the other). Their outputs are equal bit for bit. fwd_f32_kernel
+// is the fp32 forward on the vector ALU.
 #include "attn_device.h"
 #include "attn_kernels.h"
 
