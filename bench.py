@@ -111,9 +111,12 @@ def fwd_kernel_name(N: int, d: int, causal: bool) -> str:
 
 
 def dkdv_kernel_name(N: int, d: int, causal: bool) -> str:
-    """The stand-alone dK/dV kernel for a shape without key padding: the software-pipelined kernel for unmasked
-    rows of at least three 64-query steps (the last may be partial) at d_k 64, the single-phase kernel otherwise."""
-    return "bwd_dkdv_sp_kernel" if d == 64 and not causal and (N + 63) // 64 >= 3 else "bwd_dkdv_kernel"
+    """The stand-alone dK/dV kernel for a shape without key padding: the software-pipelined kernel at d_k 64 for
+    unmasked rows of at least three 64-query steps (the last may be partial) and for causal rows of whole 128-key
+    blocks (N a multiple of 128, at least 256), the single-phase kernel otherwise."""
+    if d == 64 and (N + 63) // 64 >= 3 and (not causal or N % 128 == 0):
+        return "bwd_dkdv_sp_kernel"
+    return "bwd_dkdv_kernel"
 
 
 def dq_kernel_name(B: int, H: int, N: int, d: int, causal: bool) -> str:

@@ -26,7 +26,8 @@ def test_dkdv_kernel_names():
     assert bench.dkdv_kernel_name(196, 64, False) == "bwd_dkdv_sp_kernel"    # 4 steps, the last partial
     assert bench.dkdv_kernel_name(128, 64, False) == "bwd_dkdv_kernel"       # 2 steps: under the ring of 3
     assert bench.dkdv_kernel_name(129, 64, False) == "bwd_dkdv_sp_kernel"
-    assert bench.dkdv_kernel_name(4096, 64, True) == "bwd_dkdv_kernel"
+    assert bench.dkdv_kernel_name(4096, 64, True) == "bwd_dkdv_sp_kernel"    # causal, whole 128-key blocks
+    assert bench.dkdv_kernel_name(4032, 64, True) == "bwd_dkdv_kernel"       # causal, a partial key block
     assert bench.dkdv_kernel_name(4096, 128, False) == "bwd_dkdv_kernel"
     assert bench.fused_kernel_name(196, 64, False) == "bwd_dkdv_sp_dq_kernel"
     assert bench.fused_kernel_name(197, 64, True) == "bwd_dkdv_dq_kernel"

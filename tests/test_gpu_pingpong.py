@@ -79,6 +79,50 @@ def test_pipelined_equals_single_phase(gpu_lib, dtype, B, H, N, sigma, layout):
 
 
 @pytest.mark.parametrize("dtype,B,H,N,sigma,layout", [
+    ("bf16", 1, 2, 256, 1.0, "bhnd"), ("bf16", 2, 3, 384, 1.0, "bhnd"), ("f16", 1, 2, 1152, 1.0, "bhnd"),
+    ("bf16", 1, 4, 4096, 1.0, "bhnd"), ("bf16", 2, 3, 2048, 8.0, "bhnd"), ("bf16", 2, 2, 640, 1.0, "qkv_packed"),
+])
+def test_pipelined_dkdv_causal_equals_single_phase(gpu_lib, dtype, B, H, N, sigma, layout):
+    """Causal rows of whole 128-key blocks at d_k = 64 run the software-pipelined dK/dV kernel from each block's
+    first visible step, its first two steps masked (the diagonal); a key-padding length equal to N routes the same
+    inputs to the single-phase kernel: dK and dV must be identical. The stage is called on its own."""
+    import torch
+    d = 64
+    x = make_case(B, H, N, d, dtype, seed=7500 + N, qk_sigma=sigma)
+    print(f"pipelined causal dK/dV {dtype} B={B} H={H} N={N} d={d} sigma={sigma} layout={layout}", flush=True)
+    sys.stdout.flush()
+    q, k, v, do = (to_device(x, n) for n in ("q", "k", "v", "do"))
+    if layout == "qkv_packed":
+        qkv = torch.stack([q.permute(0, 2, 1, 3), k.permute(0, 2, 1, 3), v.permute(0, 2, 1, 3)], dim=2).contiguous()
+        q, k, v = qkv[:, :, 0], qkv[:, :, 1], qkv[:, :, 2]
+        do = do.permute(0, 2, 1, 3).contiguous()
+    shape = (B, N, H, d) if layout == "qkv_packed" else (B, H, N, d)
+    o = torch.empty(shape, dtype=q.dtype, device="cuda")
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    gpu_lib.attn_fwd_ex(q, k, v, o, lse, x.scale, causal=True, layout=layout)
+    ws = gpu_lib.workspace_for(q)
+
+    def grads():  # dQ, dK, dV filled with NaN (slices of one packed buffer for the packed layout)
+        if layout == "qkv_packed":
+            g = torch.full((B, N, 3, H, d), float("nan"), dtype=q.dtype, device="cuda")
+            return g[:, :, 0], g[:, :, 1], g[:, :, 2]
+        return tuple(torch.full(shape, float("nan"), dtype=q.dtype, device="cuda") for _ in range(3))
+
+    gpu_lib.attn_bwd_stage(0, q, k, v, o, lse, do, *grads(), x.scale, ws, causal=True, layout=layout)
+    full = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    outs = []
+    for kv in (None, full):
+        dq, dk, dv = grads()
+        gpu_lib.attn_bwd_stage(1, q, k, v, o, lse, do, dq, dk, dv, x.scale, ws, causal=True, kv_len=kv,
+                               layout=layout)
+        outs.append((dk, dv))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(outs[0][0].float()).all()) and bool(torch.isfinite(outs[0][1].float()).all())
+    assert torch.equal(outs[0][0], outs[1][0]), "dK"
+    assert torch.equal(outs[0][1], outs[1][1]), "dV"
+
+
+@pytest.mark.parametrize("dtype,B,H,N,sigma,layout", [
     ("bf16", 1, 2, 256, 1.0, "bhnd"), ("bf16", 2, 3, 320, 1.0, "bhnd"), ("bf16", 1, 2, 576, 1.0, "bhnd"),
     ("f16", 1, 2, 1088, 1.0, "bhnd"), ("bf16", 1, 4, 4096, 1.0, "bhnd"), ("bf16", 2, 3, 2048, 8.0, "bhnd"),
     ("bf16", 2, 2, 704, 1.0, "qkv_packed"),

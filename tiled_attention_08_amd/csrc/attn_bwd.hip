@@ -438,6 +438,13 @@ void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict_
 #ifndef BWD_SP_AHEAD
 #define BWD_SP_AHEAD 2
 #endif
+// Causal rows on the pipelined dK/dV kernel (d_k = 64, N a multiple of 128;
+// bit-identical to the single-phase kernel): B=8, H=16, N=4096 537-547 ->
+// 513-522 us, B=4, H=12, N=2048 67-74 -> 62 us, B=2, H=16, N=8192 509-511 ->
+// 500-501 us.
+#ifndef BWD_SP_CAUSAL
+#define BWD_SP_CAUSAL 1
+#endif
 // BWD_SP_PIN keeps each chunk's exponentials in the chunk (see the slot
 // body). Measured, bit-identical outputs: B=8, H=16, N=4096 977 -> 957-962
 // us, B=2, H=16, N=8192 969 -> 951 us.
@@ -481,13 +488,17 @@ struct SpRing {
 // us, B=16, H=12, N=197 19.7-20.8 -> 18.7-19.9 us.
 inline int dkdv_rag_of(int N) { return N % 64 == 0 ? 0 : (N % 64 <= 32 ? 2 : 1); }
 
-template <class E, int NS, int WAVES, int RAG>
+// CAUSAL (N a multiple of 128): the body starts at the first step whose
+// queries see a key of the block, and masks its first two steps (the
+// diagonal: P and dS are 0 for a key after the query), as dkdv_body does;
+// blocks are handed out heaviest first.
+template <class E, int NS, int WAVES, int RAG, bool CAUSAL>
 __device__ __forceinline__ void dkdv_sp_body(const SpRing& ring, int work, const uint16_t* __restrict__ Q,
                                              const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                              const uint16_t* __restrict__ dO, const float* __restrict__ lse2,
                                              const float* __restrict__ ndelta, uint16_t* __restrict__ dK,
-                                             uint16_t* __restrict__ dV, int N, int n_kblk, float c, float scale,
-                                             int H, Strides sq, Strides sd, Strides sg) {
+                                             uint16_t* __restrict__ dV, int N, int n_kblk, int total, float c,
+                                             float scale, int H, Strides sq, Strides sd, Strides sg) {
   using S = DkdvSpShape<WAVES>;
   constexpr int D = S::D;
   static_assert(NS == 3 || NS == 4, "ring of 3 or 4 step tiles");
@@ -500,10 +511,13 @@ __device__ __forceinline__ void dkdv_sp_body(const SpRing& ring, int work, const
   const int h = lane >> 5, l32 = lane & 31;
   const int g = lane >> 4, gi = lane & 15;
   const int dsub = g & 1, er = gi >> 2, qq = gi & 3;
-  const int bh = work / n_kblk, kblk = work - bh * n_kblk;
+  int bh, kblk;
+  work_order(work, total, n_kblk, CAUSAL, false, bh, kblk);
   const size_t hq = head_off(sq, bh, H), hd = head_off(sd, bh, H), hg = head_off(sg, bh, H);
   const size_t hrow = (size_t)bh * N;
   const int key = kblk * S::BCK + wave * 32 + l32;  // this lane's key (keys past N compute unused gradients)
+  // Steps i of the body are query steps s0 + i (s0 = 0 without the mask).
+  const int s0 = CAUSAL ? kblk * S::BCK / S::BRQ : 0;
 
   u32x4 kf[D / 16], vf[D / 16];
 #pragma unroll
@@ -525,7 +539,7 @@ __device__ __forceinline__ void dkdv_sp_body(const SpRing& ring, int work, const
   // the last step sets to 0).
   auto dma_tile = [&](int i, auto r_) __attribute__((always_inline)) {
     unsigned char* base = slot_base(r_);
-    const int q0 = i * S::BRQ;
+    const int q0 = (s0 + i) * S::BRQ;
 #pragma unroll
     for (int r = 0; r < S::QDMA; ++r) {
       const int slot0 = (wave * S::QDMA + r) * 64;
@@ -641,7 +655,8 @@ __device__ __forceinline__ void dkdv_sp_body(const SpRing& ring, int work, const
       if constexpr (HV) {
         float p = __builtin_amdgcn_exp2f(fmaf(sv[KK], c, -lv[KK]));
         if constexpr (MV) {
-          if (qv0 + 8 * (KK >> 2) + 4 * h + (KK & 3) >= N) p = 0.f;
+          const int qr = qv0 + 8 * (KK >> 2) + 4 * h + (KK & 3);
+          if ((RAG != 0 && qr >= N) || (CAUSAL && qr < key)) p = 0.f;
         }
         const float ds = p * pv[KK];
         if constexpr (KK & 1) {
@@ -663,7 +678,9 @@ __device__ __forceinline__ void dkdv_sp_body(const SpRing& ring, int work, const
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  const int nq = (N + S::BRQ - 1) / S::BRQ;  // steps (the launcher checks nq >= NS)
+  // Steps (the launcher checks that there are at least NS, or under the
+  // causal mask at least 2: N is then a multiple of 128).
+  const int nq = (N + S::BRQ - 1) / S::BRQ - s0;
   // Before the slot of unit (i, 1): tile i + 1 landed and visible to every
   // wave, every wave done with tile i - 1, whose ring slot takes tile
   // i - 1 + NS.
@@ -692,11 +709,11 @@ __device__ __forceinline__ void dkdv_sp_body(const SpRing& ring, int work, const
     constexpr bool FIRST = decltype(first_)::value, LAST = decltype(last_)::value;
     // unit (i, 0): dV / dK of (i - 1, 1), S / dP of (i, 1), P / dS of (i, 0)
     slot(BoolC<!FIRST>{}, IntC<(R + NS - 1) % NS>{}, IntC<1>{}, wp_1, wd_1, BoolC<true>{}, r_, IntC<1>{}, s_1, g_1, l_1,
-         BoolC<true>{}, s_0, g_0, l_0, wp_0, wd_0, mask_, i * S::BRQ);
+         BoolC<true>{}, s_0, g_0, l_0, wp_0, wd_0, mask_, (s0 + i) * S::BRQ);
     boundary(i, r_);
     // unit (i, 1): dV / dK of (i, 0), S / dP of (i + 1, 0), P / dS of (i, 1)
     slot(BoolC<true>{}, r_, IntC<0>{}, wp_0, wd_0, BoolC<!LAST>{}, IntC<(R + 1) % NS>{}, IntC<0>{}, s_0, g_0, l_0,
-         BoolC<true>{}, s_1, g_1, l_1, wp_1, wd_1, mask_, i * S::BRQ + 32);
+         BoolC<true>{}, s_1, g_1, l_1, wp_1, wd_1, mask_, (s0 + i) * S::BRQ + 32);
   };
 
   // Prologue: tiles 0 .. NS - 2 in flight, tile 0 resident, S / dP of unit (0, 0).
@@ -707,17 +724,23 @@ __device__ __forceinline__ void dkdv_sp_body(const SpRing& ring, int work, const
        BoolC<false>{}, s_1, g_1, l_1, wp_0, wd_0, BoolC<false>{}, 0);
   // Steps 0 .. nq - 2, NS per iteration (compile-time ring slots), then the
   // rest and the last step, and the dV / dK of the last unit.
-  step(0, IntC<0>{}, BoolC<true>{}, BoolC<false>{}, BoolC<false>{});
-  int i = 1;
+  // Under the causal mask steps 0 and 1 are the diagonal (masked); step 1
+  // is the last step when there are two.
+  step(0, IntC<0>{}, BoolC<true>{}, BoolC<false>{}, BoolC<CAUSAL>{});
+  constexpr int I0 = CAUSAL ? 2 : 1;  // first step of the loop below
+  if constexpr (CAUSAL) {
+    if (nq > 2) step(1, IntC<1>{}, BoolC<false>{}, BoolC<false>{}, BoolC<true>{});
+  }
+  int i = I0;
   for (; i + NS <= nq - 1; i += NS) {
     static_for<0, NS>([&](auto u_) __attribute__((always_inline)) {
-      step(i + decltype(u_)::value, IntC<(1 + decltype(u_)::value) % NS>{}, BoolC<false>{}, BoolC<false>{},
+      step(i + decltype(u_)::value, IntC<(I0 + decltype(u_)::value) % NS>{}, BoolC<false>{}, BoolC<false>{},
            BoolC<false>{});
     });
   }
   static_for<0, NS - 1>([&](auto u_) __attribute__((always_inline)) {
     constexpr int U = decltype(u_)::value;
-    if (i + U < nq - 1) step(i + U, IntC<(1 + U) % NS>{}, BoolC<false>{}, BoolC<false>{}, BoolC<false>{});
+    if (i + U < nq - 1) step(i + U, IntC<(I0 + U) % NS>{}, BoolC<false>{}, BoolC<false>{}, BoolC<false>{});
   });
   // The last step, nq - 1, in ring slot (nq - 1) % NS, with the row mask when
   // ragged (a template parameter: a second, runtime-selected copy of the step
@@ -729,11 +752,11 @@ __device__ __forceinline__ void dkdv_sp_body(const SpRing& ring, int work, const
     if ((nq - 1) % NS == R) {
       if constexpr (RAG == 2) {
         slot(BoolC<true>{}, IntC<(R + NS - 1) % NS>{}, IntC<1>{}, wp_1, wd_1, BoolC<false>{}, r_, IntC<1>{}, s_1, g_1,
-             l_1, BoolC<true>{}, s_0, g_0, l_0, wp_0, wd_0, BoolC<true>{}, (nq - 1) * S::BRQ);
+             l_1, BoolC<true>{}, s_0, g_0, l_0, wp_0, wd_0, BoolC<true>{}, (s0 + nq - 1) * S::BRQ);
         slot(BoolC<true>{}, r_, IntC<0>{}, wp_0, wd_0, BoolC<false>{}, r_, IntC<0>{}, s_0, g_0, l_0, BoolC<false>{},
              s_1, g_1, l_1, wp_1, wd_1, BoolC<false>{}, 0);
       } else {
-        step(nq - 1, r_, BoolC<false>{}, BoolC<true>{}, BoolC<(RAG != 0)>{});
+        step(nq - 1, r_, BoolC<false>{}, BoolC<true>{}, BoolC<(RAG != 0 || CAUSAL)>{});
         slot(BoolC<true>{}, r_, IntC<1>{}, wp_1, wd_1, BoolC<false>{}, r_, IntC<0>{}, s_0, g_0, l_0, BoolC<false>{}, s_1,
              g_1, l_1, wp_0, wd_0, BoolC<false>{}, 0);
       }
@@ -759,7 +782,7 @@ __device__ __forceinline__ void dkdv_sp_body(const SpRing& ring, int work, const
   }
 }
 
-template <class E, int NS, int WAVES, int RAG>
+template <class E, int NS, int WAVES, int RAG, bool CAUSAL>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                         const uint16_t* __restrict__ dO, const float* __restrict__ lse2,
@@ -770,8 +793,8 @@ void bwd_dkdv_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restri
   __shared__ __attribute__((aligned(16))) unsigned char ring1[S::SLOTB];
   __shared__ __attribute__((aligned(16))) unsigned char ring2[S::SLOTB];
   __shared__ __attribute__((aligned(16))) unsigned char ring3[NS == 4 ? S::SLOTB : 16];
-  dkdv_sp_body<E, NS, WAVES, RAG>(SpRing{{ring0, ring1, ring2, ring3}}, xcd_remap(blockIdx.x, total), Q, K, V,
-                                     dO, lse2, ndelta, dK, dV, N, n_kblk, c, scale, H, sq, sd, sg);
+  dkdv_sp_body<E, NS, WAVES, RAG, CAUSAL>(SpRing{{ring0, ring1, ring2, ring3}}, xcd_remap(blockIdx.x, total), Q, K,
+                                          V, dO, lse2, ndelta, dK, dV, N, n_kblk, total, c, scale, H, sq, sd, sg);
 }
 
 // ---------------------------------------------------------------- stage 2: dQ
@@ -1380,8 +1403,8 @@ void bwd_dkdv_sp_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
   int work;
   fused_order(blockIdx.x, total1, total2, n_kblk, dkdv_part, work);
   if (dkdv_part)
-    dkdv_sp_body<E, NS, kThreads / 64, RAG>(SpRing{{ring0, ring1, ring2, ring3}}, work, Q, K, V, dO, lse2, ndelta, dK,
-                                            dV, N, n_kblk, c, scale, H, sq, sd, sg);
+    dkdv_sp_body<E, NS, kThreads / 64, RAG, false>(SpRing{{ring0, ring1, ring2, ring3}}, work, Q, K, V, dO, lse2,
+                                                   ndelta, dK, dV, N, n_kblk, total1, c, scale, H, sq, sd, sg);
   else if constexpr (DQSP)
     dq_sp_body<E, NS, kThreads / 64, (RAG != 0)>(SpRing{{ring0, ring1, ring2, ring3}}, work, Q, K, V, dO, lse2, ndelta,
                                                  dQ, N, n_qblk, c, scale, H, sq, sd, sg);
@@ -1637,16 +1660,22 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
   } else if (stage == 1) {
     if constexpr (D == 64) {
       constexpr int NS = BWD_SP_RING;
-      if (BWD_SP && !causal && !kv_len && (N + 63) / 64 >= NS) {
+      // Causal rows of whole 128-key blocks (BWD_SP_CAUSAL) too: every block then has at least two steps.
+      const bool sp_causal = causal && BWD_SP_CAUSAL && N % 128 == 0;
+      if (BWD_SP && (!causal || sp_causal) && !kv_len && (N + 63) / 64 >= NS) {
         constexpr int W = BWD_SP_WAVES, BCK = DkdvSpShape<W>::BCK;
         const int n_kblk = (N + BCK - 1) / BCK, total = n_kblk * B * H;
-#define ATTN_SP_DKDV(RAG)                                                                                    \
-  hipLaunchKernelGGL((bwd_dkdv_sp_kernel<E, NS, W, RAG>), dim3(total), dim3(64 * W), 0, stream, q, k, v, dO, lse2, \
-                     ndelta, dk, dv, N, n_kblk, total, c, scale, H, st[0], st[2], st[3])
-        switch (dkdv_rag_of(N)) {
-          case 0: ATTN_SP_DKDV(0); break;
-          case 1: ATTN_SP_DKDV(1); break;
-          default: ATTN_SP_DKDV(2); break;
+#define ATTN_SP_DKDV(RAG, CAUSAL)                                                                            \
+  hipLaunchKernelGGL((bwd_dkdv_sp_kernel<E, NS, W, RAG, CAUSAL>), dim3(total), dim3(64 * W), 0, stream, q, k, v, dO, \
+                     lse2, ndelta, dk, dv, N, n_kblk, total, c, scale, H, st[0], st[2], st[3])
+        if (sp_causal) {
+          ATTN_SP_DKDV(0, true);
+        } else {
+          switch (dkdv_rag_of(N)) {
+            case 0: ATTN_SP_DKDV(0, false); break;
+            case 1: ATTN_SP_DKDV(1, false); break;
+            default: ATTN_SP_DKDV(2, false); break;
+          }
         }
 #undef ATTN_SP_DKDV
         return hipGetLastError();
