@@ -100,10 +100,10 @@ def measured_traffic(workload: str, kernel: str):
 
 def fwd_kernel_name(N: int, d: int, causal: bool) -> str:
     """The forward kernel the library launches for a bf16/fp16 shape without key padding: the software-pipelined
-    kernel for rows of whole 64-key tiles (unmasked with 256 keys or more at d_k 64; unmasked or causal with 1024
-    or more at d_k 128), the ping-pong kernel for other unmasked rows of 1024 keys or more at d_k 128, the
-    single-phase kernel otherwise."""
-    if d == 64 and not causal and N % 64 == 0 and N >= 256:
+    kernel for rows of whole 64-key tiles (at d_k 64 unmasked with 256 keys or more or causal with 1024 or more;
+    unmasked or causal with 1024 or more at d_k 128), the ping-pong kernel for other unmasked rows of 1024 keys or
+    more at d_k 128, the single-phase kernel otherwise."""
+    if d == 64 and N % 64 == 0 and (N >= 1024 if causal else N >= 256):
         return "fwd_sp_kernel"
     if d == 128 and N % 64 == 0 and N >= 1024:
         return "fwd_sp_kernel"

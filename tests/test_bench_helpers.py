@@ -12,7 +12,8 @@ import bench  # noqa: E402
 def test_forward_kernel_names():
     assert bench.fwd_kernel_name(4096, 64, False) == "fwd_sp_kernel"
     assert bench.fwd_kernel_name(196, 64, False) == "fwd_kernel"         # under 256 keys
-    assert bench.fwd_kernel_name(4096, 64, True) == "fwd_kernel"         # causal at d_k 64
+    assert bench.fwd_kernel_name(4096, 64, True) == "fwd_sp_kernel"      # causal at d_k 64, 1024 keys or more
+    assert bench.fwd_kernel_name(512, 64, True) == "fwd_kernel"          # causal at d_k 64, under 1024 keys
     assert bench.fwd_kernel_name(16384, 128, True) == "fwd_sp_kernel"    # causal at d_k 128: pipelined + diagonal
     assert bench.fwd_kernel_name(1100, 128, True) == "fwd_kernel"        # causal, not whole tiles
     assert bench.fwd_kernel_name(16384, 128, False) == "fwd_sp_kernel"   # whole tiles, 1024 keys or more

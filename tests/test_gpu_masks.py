@@ -81,6 +81,7 @@ SMALL = [
     (2, 3, 333, 64, True, None),
     (2, 1, 1000, 64, True, [1000, 517]),
     (2, 1, 1100, 64, True, None),
+    (1, 2, 1088, 64, True, None),  # the pipelined forward's tiles, then its diagonal tiles (partial last block)
     (3, 1, 1100, 64, False, [1100, 1024, 333]),
     (2, 2, 129, 128, True, None),
     (1, 2, 1088, 128, True, None),  # the pipelined forward's tiles, then its diagonal tiles (partial last block)

@@ -8,7 +8,7 @@ key-padding length equal to N hides no key but routes the same inputs to the
 single-phase kernel, so the results must be identical (O and lse): bf16 and
 fp16, contiguous and packed layouts, and (pipelined forward) inputs whose
 scores are large enough that many tiles take its full rescale path; causal
-rows at d_k = 128 (pipelined tiles, then the diagonal) likewise. All are
+rows (pipelined tiles, then the diagonal) likewise. All are
 also checked against the fp64 oracle by the parity tests.
 """
 from __future__ import annotations
@@ -253,19 +253,21 @@ def test_combined_pipelined_launch_equals_stages(gpu_lib, dtype, B, H, N, layout
     assert torch.equal(outs[0], outs[1])
 
 
-@pytest.mark.parametrize("dtype,B,H,N,sigma,layout", [
-    ("bf16", 1, 2, 1024, 1.0, "bhnd"), ("bf16", 2, 2, 2048, 1.0, "bhnd"), ("f16", 2, 1, 1088, 1.0, "bhnd"),
-    ("bf16", 1, 2, 4096, 8.0, "bhnd"), ("bf16", 2, 2, 1152, 1.0, "qkv_packed"),
+@pytest.mark.parametrize("d,dtype,B,H,N,sigma,layout", [
+    (128, "bf16", 1, 2, 1024, 1.0, "bhnd"), (128, "bf16", 2, 2, 2048, 1.0, "bhnd"),
+    (128, "f16", 2, 1, 1088, 1.0, "bhnd"), (128, "bf16", 1, 2, 4096, 8.0, "bhnd"),
+    (128, "bf16", 2, 2, 1152, 1.0, "qkv_packed"),
+    (64, "bf16", 1, 2, 1024, 1.0, "bhnd"), (64, "bf16", 2, 3, 2048, 8.0, "bhnd"), (64, "f16", 2, 2, 1088, 1.0, "bhnd"),
+    (64, "bf16", 1, 2, 4096, 1.0, "bhnd"), (64, "bf16", 2, 2, 1152, 1.0, "qkv_packed"),
 ])
-def test_pipelined128_causal_equals_single_phase(gpu_lib, dtype, B, H, N, sigma, layout):
-    """Causal rows of whole 64-key tiles (1024 keys or more) at d_k = 128 run the pipelined forward on the tiles a
-    workgroup's queries see in full, then the diagonal tiles with the single-phase kernel's masked tile; a
+def test_pipelined_causal_equals_single_phase(gpu_lib, d, dtype, B, H, N, sigma, layout):
+    """Causal rows of whole 64-key tiles (1024 keys or more) at d_k = 64 and 128 run the pipelined forward on the
+    tiles a workgroup's queries see in full, then the diagonal tiles with the single-phase kernel's masked tile; a
     key-padding length of N routes the same inputs to the single-phase kernel: O and lse must be identical
-    (N = 1088 and 1152 end in a partial 256-row block; sigma 8 gives peaked scores)."""
+    (N = 1088 and 1152 end in a partial row block; sigma 8 gives peaked scores)."""
     import torch
-    d = 128
-    x = make_case(B, H, N, d, dtype, seed=7400 + N, qk_sigma=sigma, with_grad=False)
-    print(f"pipelined causal d=128 {dtype} B={B} H={H} N={N} sigma={sigma} layout={layout}", flush=True)
+    x = make_case(B, H, N, d, dtype, seed=7400 + N + d, qk_sigma=sigma, with_grad=False)
+    print(f"pipelined causal d={d} {dtype} B={B} H={H} N={N} sigma={sigma} layout={layout}", flush=True)
     sys.stdout.flush()
     q, k, v = (to_device(x, n) for n in ("q", "k", "v"))
     if layout == "qkv_packed":

@@ -122,6 +122,17 @@ constexpr int fwd_waves_per_eu(int D, int QB, int WAVES) {
 // fwd_kernel): B=2, H=16, N=16384 2011 -> 1905 us, B=4, H=16, N=4096 282-303
 // -> 272-275 us. At d_k = 64 (256-query workgroups against fwd_kernel's 128)
 // it measured the same at N=4096 and 35 % slower at N=2048.
+// Causal rows at d_k = 64 on the pipelined forward with one query block per
+// wave (bit-identical to fwd_kernel): B=2, H=16, N=8192 316 -> 291 us, B=4,
+// H=8, N=1024 17.4 -> 16.5 us, B=4, H=12, N=2048 43.7 -> 42.7 us, B=8, H=16,
+// N=4096 315-318 -> 313 us; at N=256 3 % slower. Two blocks per wave (256-query
+// workgroups) measured 35 % slower at N=2048 (more idle waves on the diagonal).
+#ifndef FWD_SP64_CAUSAL
+#define FWD_SP64_CAUSAL 1
+#endif
+#ifndef FWD_SP64_CAUSAL_MIN_N
+#define FWD_SP64_CAUSAL_MIN_N 1024
+#endif
 #ifndef FWD_SP_CAUSAL
 #define FWD_SP_CAUSAL 1
 #endif
@@ -863,7 +874,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                    uint16_t* __restrict__ O, float* __restrict__ LSE, int N, int n_qblk, int total, float c,
                    uint32_t qsign, int H, Strides sq, Strides so) {
-  static_assert((D == 64 && QB == 2) || (D == 128 && QB == 1), "shapes with a register plan");
+  static_assert((D == 64 && (QB == 1 || QB == 2)) || (D == 128 && QB == 1), "shapes with a register plan");
   constexpr int KB = 2, NS = kSPRing;
   using S = FwdShape<D, QB, KB, NS, WAVES>;
   constexpr int NDB = D / 32, NCC = D / 16;
@@ -1594,6 +1605,10 @@ static hipError_t launch_fwd_e(const uint16_t* q, const uint16_t* k, const uint1
   // Rows without masks, whole 64-key tiles, d = 64: the software-pipelined forward.
   if (FWD_SP && d == 64 && !causal && !kv_len && N % 64 == 0 && N >= FWD_SP_MIN_N)
     return launch_fwd_sp<E, 64, 2, 4, false>(q, k, v, o, lse, B, H, N, scale, sq, so, stream);
+  // Causal rows at d = 64: one query block per wave (128-query workgroups, which balance the diagonal as
+  // fwd_kernel's do), from FWD_SP64_CAUSAL_MIN_N keys.
+  if (FWD_SP && FWD_SP64_CAUSAL && d == 64 && causal && !kv_len && N % 64 == 0 && N >= FWD_SP64_CAUSAL_MIN_N)
+    return launch_fwd_sp<E, 64, 1, 4, true>(q, k, v, o, lse, B, H, N, scale, sq, so, stream);
   // d = 128: one query block per wave, 8 waves sharing the ring (128 KB of LDS, one workgroup per CU). With the
   // causal mask (FWD_SP_CAUSAL) the kernel takes the tiles a workgroup's queries see in full and finishes with
   // the diagonal tiles (at d = 64 the single-phase kernel's 128-query workgroups balance the diagonal better).
