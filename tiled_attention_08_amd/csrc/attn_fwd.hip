@@ -24,7 +24,7 @@
 //
 // Three 16-bit kernels: fwd_kernel (every tile in one order: S, softmax,
 // P V; masks, every head dim, short rows), fwd_sp_kernel (rows of whole
-// 64-key tiles, unmasked at d = 64 and unmasked or causal at d = 128: the
+// 64-key tiles at d = 64 and 128, unmasked or causal: the
 // same tiles and arithmetic per element, software-pipelined so that one
 // wave's products overlap its own softmax) and fwd_pp_kernel (other unmasked
 // rows of 1024 keys or more at d = 128: the two halves of the workgroup a
