@@ -130,8 +130,11 @@ def dq_kernel_name(B: int, H: int, N: int, d: int, causal: bool) -> str:
 
 def fused_kernel_name(N: int, d: int, causal: bool) -> str:
     """The combined dK/dV + dQ launch for a shape without key padding: with the pipelined dK/dV body where the
-    stand-alone pipelined kernel applies, with the single-phase one otherwise."""
-    return "bwd_dkdv_sp_dq_kernel" if dkdv_kernel_name(N, d, causal) == "bwd_dkdv_sp_kernel" else "bwd_dkdv_dq_kernel"
+    stand-alone pipelined kernel applies to unmasked rows, with the single-phase one otherwise (causal rows
+    included)."""
+    if not causal and dkdv_kernel_name(N, d, False) == "bwd_dkdv_sp_kernel":
+        return "bwd_dkdv_sp_dq_kernel"
+    return "bwd_dkdv_dq_kernel"
 
 
 def mix_of_kernel(kernel: str, d: int):

@@ -32,6 +32,7 @@ def test_dkdv_kernel_names():
     assert bench.dkdv_kernel_name(4096, 128, False) == "bwd_dkdv_kernel"
     assert bench.fused_kernel_name(196, 64, False) == "bwd_dkdv_sp_dq_kernel"
     assert bench.fused_kernel_name(197, 64, True) == "bwd_dkdv_dq_kernel"
+    assert bench.fused_kernel_name(256, 64, True) == "bwd_dkdv_dq_kernel"     # causal: single-phase bodies
     assert bench.fused_kernel_name(100, 64, False) == "bwd_dkdv_dq_kernel"
     assert bench.dq_kernel_name(8, 16, 4096, 64, False) == "bwd_dq_kernel"     # 2048 two-block workgroups
     assert bench.dq_kernel_name(4, 12, 2048, 64, False) == "bwd_dq_sp_kernel"  # 384

@@ -1035,6 +1035,14 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #ifndef BWD_DQ_SP
 #define BWD_DQ_SP 1
 #endif
+// The combined launch takes the pipelined dQ body also when N % 64 is at most
+// 32, its empty last unit skipped (RAG 2; identical results): B=16, H=12,
+// N=197 17.5-18.9 -> 17.0-17.6 us, B=16, H=16, N=129 17.6-18.7 -> 16.4-17.1
+// us, B=32, H=12, N=196 unchanged; the stand-alone dQ kernel at N=196 about
+// 5 % faster with the skip.
+#ifndef BWD_DQ_SP_RAG2
+#define BWD_DQ_SP_RAG2 1
+#endif
 #ifndef BWD_DQ_SP_RING
 #define BWD_DQ_SP_RING 3
 #endif
@@ -1052,9 +1060,11 @@ struct DqSpShape {
   static constexpr int OFF_K = 0, OFF_V = TILEB, SLOTB = 2 * TILEB;
 };
 
-// RAGGED: N is not a multiple of the 64-key tile; key rows past N are read
-// as row N - 1 and get probability 0 in the last tile.
-template <class E, int NS, int WAVES, bool RAGGED>
+// RAG (as dkdv_rag_of): 0 when N is a multiple of the 64-key tile;
+// otherwise key rows past N are read as row N - 1 and get probability 0 in
+// the last tile, whose second 32-key unit holds keys (RAG 1) or none (RAG 2:
+// that unit is not computed).
+template <class E, int NS, int WAVES, int RAG>
 __device__ __forceinline__ void dq_sp_body(const SpRing& ring, int work, const uint16_t* __restrict__ Q,
                                            const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                            const uint16_t* __restrict__ dO, const float* __restrict__ lse2_in,
@@ -1103,7 +1113,7 @@ __device__ __forceinline__ void dq_sp_body(const SpRing& ring, int work, const u
       const int slot0 = (wave * S::KDMA + r) * 64;
       const int p = slot0 + lane;
       const int row = p / (D / 8), chunk = (p - row * (D / 8)) ^ swz<S::ROWB>(row);
-      const int kr = RAGGED ? min(j * S::BCK + row, N - 1) : j * S::BCK + row;
+      const int kr = RAG ? min(j * S::BCK + row, N - 1) : j * S::BCK + row;
       const uint32_t off = (uint32_t)(kr * sq.n + chunk * 8) * 2u;
       dma16(rK, off, base + S::OFF_K + slot0 * 16);
       dma16(rV, off, base + S::OFF_V + slot0 * 16);
@@ -1226,7 +1236,7 @@ __device__ __forceinline__ void dq_sp_body(const SpRing& ring, int work, const u
   f32x16 s_0, g_0, s_1, g_1;  // S^T and dP^T - delta of the current units of key blocks 0 and 1
   u32x4 wd_0[2], wd_1[2];     // bf16 dS^T of key blocks 0 and 1
   // Tile j in ring slot R: the slots of units (j, 0) and (j, 1). MASK: the
-  // tile holds keys past N (the last tile when RAGGED).
+  // tile holds keys past N (the last tile when ragged).
   auto tile = [&](int j, auto r_, auto first_, auto last_, auto mask_) __attribute__((always_inline)) {
     constexpr int R = decltype(r_)::value;
     constexpr bool FIRST = decltype(first_)::value, LAST = decltype(last_)::value;
@@ -1258,12 +1268,22 @@ __device__ __forceinline__ void dq_sp_body(const SpRing& ring, int work, const u
     if (j + U < nt - 1) tile(j + U, IntC<(1 + U) % NS>{}, BoolC<false>{}, BoolC<false>{}, BoolC<false>{});
   });
   // The last tile, nt - 1, in ring slot (nt - 1) % NS (with the key mask when
-  // RAGGED), then dQ of its unit (nt - 1, 1).
+  // ragged), then dQ of its unit (nt - 1, 1). With RAG 2 that unit has no
+  // keys: the tile is the slot of its first unit without the next unit's
+  // products, then the dQ products of that first unit.
   static_for<0, NS>([&](auto r_) __attribute__((always_inline)) {
-    if ((nt - 1) % NS == decltype(r_)::value) {
-      tile(nt - 1, r_, BoolC<false>{}, BoolC<true>{}, BoolC<RAGGED>{});
-      slot(BoolC<true>{}, r_, IntC<1>{}, wd_1, BoolC<false>{}, r_, IntC<0>{}, s_0, g_0, BoolC<false>{}, s_1, g_1,
-           wd_0, BoolC<false>{}, 0);
+    constexpr int R = decltype(r_)::value;
+    if ((nt - 1) % NS == R) {
+      if constexpr (RAG == 2) {
+        slot(BoolC<true>{}, IntC<(R + NS - 1) % NS>{}, IntC<1>{}, wd_1, BoolC<false>{}, r_, IntC<1>{}, s_1, g_1,
+             BoolC<true>{}, s_0, g_0, wd_0, BoolC<true>{}, (nt - 1) * S::BCK);
+        slot(BoolC<true>{}, r_, IntC<0>{}, wd_0, BoolC<false>{}, r_, IntC<0>{}, s_0, g_0, BoolC<false>{}, s_1, g_1,
+             wd_1, BoolC<false>{}, 0);
+      } else {
+        tile(nt - 1, r_, BoolC<false>{}, BoolC<true>{}, BoolC<(RAG != 0)>{});
+        slot(BoolC<true>{}, r_, IntC<1>{}, wd_1, BoolC<false>{}, r_, IntC<0>{}, s_0, g_0, BoolC<false>{}, s_1, g_1,
+             wd_0, BoolC<false>{}, 0);
+      }
     }
   });
 
@@ -1282,7 +1302,7 @@ __device__ __forceinline__ void dq_sp_body(const SpRing& ring, int work, const u
   }
 }
 
-template <class E, int NS, int WAVES, bool RAGGED>
+template <class E, int NS, int WAVES, int RAG>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                       const uint16_t* __restrict__ dO, const float* __restrict__ lse2_in,
@@ -1293,7 +1313,7 @@ void bwd_dq_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict
   __shared__ __attribute__((aligned(16))) unsigned char ring1[S::SLOTB];
   __shared__ __attribute__((aligned(16))) unsigned char ring2[S::SLOTB];
   __shared__ __attribute__((aligned(16))) unsigned char ring3[NS == 4 ? S::SLOTB : 16];
-  dq_sp_body<E, NS, WAVES, RAGGED>(SpRing{{ring0, ring1, ring2, ring3}}, xcd_remap(blockIdx.x, total), Q, K, V, dO,
+  dq_sp_body<E, NS, WAVES, RAG>(SpRing{{ring0, ring1, ring2, ring3}}, xcd_remap(blockIdx.x, total), Q, K, V, dO,
                                    lse2_in, ndelta, dQ, N, n_qblk, c, scale, H, sq, sd, sg);
 }
 
@@ -1406,7 +1426,7 @@ void bwd_dkdv_sp_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __res
     dkdv_sp_body<E, NS, kThreads / 64, RAG, false>(SpRing{{ring0, ring1, ring2, ring3}}, work, Q, K, V, dO, lse2,
                                                    ndelta, dK, dV, N, n_kblk, total1, c, scale, H, sq, sd, sg);
   else if constexpr (DQSP)
-    dq_sp_body<E, NS, kThreads / 64, (RAG != 0)>(SpRing{{ring0, ring1, ring2, ring3}}, work, Q, K, V, dO, lse2, ndelta,
+    dq_sp_body<E, NS, kThreads / 64, RAG>(SpRing{{ring0, ring1, ring2, ring3}}, work, Q, K, V, dO, lse2, ndelta,
                                                  dQ, N, n_qblk, c, scale, H, sq, sd, sg);
   else
     dq_body<E, S::D, 1>(ring0, ring1, work, Q, K, V, dO, lse2, ndelta, dQ, N, n_qblk, total2, c, scale, kv_len, H,
@@ -1643,7 +1663,12 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
           case 0: ATTN_SP_DQ(0, false); break;
           case 1: ATTN_SP_DQ(1, false); break;
 #endif
-          default: ATTN_SP_DQ(2, false); break;
+          default:
+            if (BWD_DQ_SP && BWD_DQ_SP_RAG2)
+              ATTN_SP_DQ(2, true);
+            else
+              ATTN_SP_DQ(2, false);
+            break;
         }
 #undef ATTN_SP_DQ
       } else if (D == 64 && N < BWD_FUSE_MB1_N)  // 32-query steps split evenly over the DMA lanes at d_k = 64 only
@@ -1693,12 +1718,15 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
       if (bwd_dq_pipelined(B, H, N, D, causal, kv_len != nullptr)) {
         constexpr int W = 4, BR = DqSpShape<W>::BR;
         const int n_qblk = (N + BR - 1) / BR, total = n_qblk * B * H;
-        if (N % 64)
-          hipLaunchKernelGGL((bwd_dq_sp_kernel<E, NS, W, true>), dim3(total), dim3(64 * W), 0, stream, q, k, v, dO,
-                             lse2, ndelta, dq, N, n_qblk, total, c, scale, H, st[0], st[2], st[3]);
-        else
-          hipLaunchKernelGGL((bwd_dq_sp_kernel<E, NS, W, false>), dim3(total), dim3(64 * W), 0, stream, q, k, v, dO,
-                             lse2, ndelta, dq, N, n_qblk, total, c, scale, H, st[0], st[2], st[3]);
+#define ATTN_SP_DQ1(RAG)                                                                                     \
+  hipLaunchKernelGGL((bwd_dq_sp_kernel<E, NS, W, RAG>), dim3(total), dim3(64 * W), 0, stream, q, k, v, dO, lse2,  \
+                     ndelta, dq, N, n_qblk, total, c, scale, H, st[0], st[2], st[3])
+        switch (dkdv_rag_of(N)) {
+          case 0: ATTN_SP_DQ1(0); break;
+          case 1: ATTN_SP_DQ1(1); break;
+          default: ATTN_SP_DQ1(2); break;
+        }
+#undef ATTN_SP_DQ1
         return hipGetLastError();
       }
     }
