@@ -313,3 +313,55 @@ def test_pipelined128_equals_single_phase(gpu_lib, dtype, B, H, N, sigma, layout
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]), "O"
     assert torch.equal(outs[0][1], outs[1][1]), "lse"
+
+
+# Causal rows on the pipelined kernels over grid shapes: head counts whose work splits evenly over the 8 XCDs or
+# not (the two branches of the heaviest-first order), lengths at and past the thresholds, partial last row blocks.
+CAUSAL_SWEEP = [(d, B, H, N) for d in (64, 128) for (B, H) in ((1, 1), (1, 3), (3, 5), (2, 4))
+                for N in (1024, 1088, 1344, 2112)]
+
+
+@pytest.mark.parametrize("d,B,H,N", CAUSAL_SWEEP)
+def test_causal_pipelined_forward_sweep(gpu_lib, d, B, H, N):
+    """The pipelined causal forward equals the single-phase kernel (key padding of N) bit for bit."""
+    import torch
+    x = make_case(B, H, N, d, "bf16", seed=7600 + N + d + B * H, with_grad=False)
+    print(f"causal sweep fwd d={d} B={B} H={H} N={N}", flush=True)
+    sys.stdout.flush()
+    q, k, v = (to_device(x, n) for n in ("q", "k", "v"))
+    full = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    outs = []
+    for kv in (None, full):
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+        gpu_lib.attn_fwd_ex(q, k, v, o, lse, x.scale, causal=True, kv_len=kv)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(outs[0][1]).all())
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("B,H,N", [(B, H, N) for (B, H) in ((1, 1), (1, 3), (3, 5), (2, 4)) for N in (256, 384, 1152, 2048)])
+def test_causal_pipelined_dkdv_sweep(gpu_lib, B, H, N):
+    """The pipelined causal dK/dV kernel equals the single-phase kernel (key padding of N) bit for bit."""
+    import torch
+    d = 64
+    x = make_case(B, H, N, d, "bf16", seed=7700 + N + B * H)
+    print(f"causal sweep dK/dV B={B} H={H} N={N}", flush=True)
+    sys.stdout.flush()
+    q, k, v, do = (to_device(x, n) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    gpu_lib.attn_fwd_ex(q, k, v, o, lse, x.scale, causal=True)
+    ws = gpu_lib.workspace_for(q)
+    grads = lambda: tuple(torch.full_like(q, float("nan")) for _ in range(3))
+    gpu_lib.attn_bwd_stage(0, q, k, v, o, lse, do, *grads(), x.scale, ws, causal=True)
+    full = torch.full((B,), N, dtype=torch.int32, device="cuda")
+    outs = []
+    for kv in (None, full):
+        dq, dk, dv = grads()
+        gpu_lib.attn_bwd_stage(1, q, k, v, o, lse, do, dq, dk, dv, x.scale, ws, causal=True, kv_len=kv)
+        outs.append((dk, dv))
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(outs[0][0].float()).all())
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
