@@ -1008,8 +1008,13 @@ __device__ __forceinline__ void dq_body(unsigned char* buf0, unsigned char* buf1
   }
 }
 
+// One 32-query block per wave at d_k = 64 (156 registers) runs three waves
+// per SIMD; used for causal rows (BWD_DQ_CAUSAL_QB1).
+constexpr int dq_waves_per_eu(int D, int QB) { return D == 64 && QB == 1 ? 3 : BWD_WAVES_PER_EU; }
+
 template <class E, int D, int QB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(BWD_WAVES_PER_EU, BWD_WAVES_PER_EU)))
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(dq_waves_per_eu(D, QB), dq_waves_per_eu(D, QB))))
 void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                    const uint16_t* __restrict__ dO, const float* __restrict__ lse2_in, const float* __restrict__ ndelta,
                    uint16_t* __restrict__ dQ, int N, int n_qblk, int total, float c, float scale,
@@ -1040,6 +1045,14 @@ void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 // N=197 17.5-18.9 -> 17.0-17.6 us, B=16, H=16, N=129 17.6-18.7 -> 16.4-17.1
 // us, B=32, H=12, N=196 unchanged; the stand-alone dQ kernel at N=196 about
 // 5 % faster with the skip.
+// Causal rows at d_k = 64 run the dQ kernel with one 32-query block per wave
+// (128-query workgroups) at three waves per SIMD: finer blocks balance the
+// triangle. Identical results; per launch B=8, H=16, N=4096 399-406 -> 390-392
+// us, B=4, H=12, N=2048 65-71 -> 48-49 us, B=4, H=8, N=1024 34 -> 20 us,
+// B=16, H=12, N=197 15 -> 10 us.
+#ifndef BWD_DQ_CAUSAL_QB1
+#define BWD_DQ_CAUSAL_QB1 1
+#endif
 #ifndef BWD_DQ_SP_RAG2
 #define BWD_DQ_SP_RAG2 1
 #endif
@@ -1727,6 +1740,16 @@ static hipError_t launch_bwd_stage_t(int stage, const uint16_t* q, const uint16_
           default: ATTN_SP_DQ1(2); break;
         }
 #undef ATTN_SP_DQ1
+        return hipGetLastError();
+      }
+    }
+    if constexpr (D == 64) {
+      if (causal && BWD_DQ_CAUSAL_QB1) {  // 128-query workgroups, three waves per SIMD
+        constexpr int BR = DqShape<D, 1>::BR;
+        const int n_qblk = (N + BR - 1) / BR;
+        const int total = n_qblk * B * H;
+        hipLaunchKernelGGL((bwd_dq_kernel<E, D, 1>), dim3(total), dim3(kThreads), 0, stream, q, k, v, dO, lse2, ndelta,
+                           dq, N, n_qblk, total, c, scale, kv_len, H, causal, st[0], st[2], st[3]);
         return hipGetLastError();
       }
     }

@@ -981,8 +981,8 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
   // Pipelined tiles (N is a multiple of the tile; without the mask the
   // launcher checks nt >= 4) and tiles read: under the causal mask the
-  // workgroup's first query sees the first nt in full (none, or at least 4),
-  // and its rows reach tile nt_dma - 1.
+  // workgroup's first query sees the first nt in full (a multiple of
+  // BR / 64: none, or at least 2), and its rows reach tile nt_dma - 1.
   const int nt = CAUSAL ? qblk * S::BR / S::BC : N / S::BC;
   const int nt_dma = CAUSAL ? min(N, (qblk + 1) * S::BR) / S::BC : nt;
 
