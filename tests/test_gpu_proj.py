@@ -13,6 +13,7 @@ The shapes cover:
   - 256 x 256 tiles with ragged edges, with and without a split (a 4-way split whose last part ends mid-step);
   - ragged token counts and contraction tails (D not a multiple of 64, B N not a multiple of 64);
   - the smallest legal shape;
+  - a 256 x 256-tile product with one contraction step (dw with 40 tokens);
   - the small-product kernels (64 x 64 tiles with the contraction split over the 4 waves).
 """
 from __future__ import annotations
@@ -63,6 +64,7 @@ SHAPES = [
     (5, 7, 136, 3, 64),
     (3, 150, 520, 4, 96),
     (8, 300, 512, 4, 64),
+    (1, 40, 256, 2, 128),
 ]
 
 

@@ -259,20 +259,38 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint16_t* __restrict
 // s then writes its float32 partial C to slice s of the workspace, and a
 // second kernel adds the S slices in split order and rounds once. Results do
 // not depend on the order in which workgroups run.
+#ifndef PROJ_G2_REMAT
+#define PROJ_G2_REMAT 1
+#endif
+#ifndef PROJ_G2_SCHED
+#define PROJ_G2_SCHED 1
+#endif
+#ifndef PROJ_G2_SPLIT
+#define PROJ_G2_SPLIT 1
+#endif
 constexpr int G2_THREADS = 512;
 constexpr int G2_TILE = 256;
 constexpr int G2_STAGEB = 2 * G2_TILE * 64 * 2;  // A and B sub-tiles of one stage
 
-// 16 zero bytes in device memory: the source of every DMA lane whose
-// contraction index lies past the end of its split, so that LDS holds exact
-// zeros there and the products need no masking.
-__device__ __attribute__((aligned(16))) const uint16_t kZeroChunk[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+// Byte offset of a copy lane that must read zeros: at or past the resource's
+// record count (0x7fffffff), so the buffer load returns zeros and touches no
+// memory; LDS then holds exact zeros there and the products need no masking.
+constexpr uint32_t G2_ZERO_OFF = 0x80000000u;
 
-// As dma_tile, for 512 threads; lanes whose global row is at or past rzero,
-// or whose chunk starts at or past column czero, fetch kZeroChunk instead.
+// Largest leading dimension (elements) for which every copy offset of a stage,
+// taken from the stage's origin, stays below 2^31 bytes: at most 255 rows of
+// ld elements plus one row.
+constexpr long G2_MAX_LD = ((1L << 30) - 256) / G2_TILE;
+
+// As dma_tile, for 512 threads, through a buffer resource based at the
+// operand element (ro, co) (row ro, column co of its memory layout); lanes
+// whose global row is at or past rzero, or whose chunk starts at or past
+// column czero, read zeros. The clamped rows and columns are >= (ro, co).
+// Buffer copies count as vector-memory accesses only, so the compiler lets
+// LDS reads of the other stage run while this copy is in flight.
 template <int ROWB, int ROWS>
-__device__ __forceinline__ void dma_tile512(const uint16_t* __restrict__ src, size_t ld, int r0, int rmax, int rzero,
-                                            int c0, int cmax, int czero, unsigned char* dst, int tid) {
+__device__ __forceinline__ void dma_tile512(Rsrc rs, int ld, int ro, int co, int r0, int rmax, int rzero, int c0,
+                                            int cmax, int czero, unsigned char* dst, int tid) {
   constexpr int CPR = ROWB / 16;
   constexpr int ITERS = ROWS * CPR / G2_THREADS;
   static_assert(ITERS >= 1 && ROWS * CPR % G2_THREADS == 0, "whole 512-slot passes");
@@ -283,8 +301,10 @@ __device__ __forceinline__ void dma_tile512(const uint16_t* __restrict__ src, si
     const int p = slot0 + lane;
     const int row = p / CPR, chunk = (p - row * CPR) ^ swz<ROWB>(row);
     const int r = r0 + row, c = c0 + chunk * 8;
-    const uint16_t* a = (r >= rzero || c >= czero) ? kZeroChunk : src + (size_t)min(r, rmax) * ld + min(c, cmax);
-    dma16(a, dst + slot0 * 16);
+    const uint32_t off = (r >= rzero || c >= czero)
+                             ? G2_ZERO_OFF
+                             : 2u * ((uint32_t)(min(r, rmax) - ro) * (uint32_t)ld + (uint32_t)(min(c, cmax) - co));
+    dma16(rs, off, dst + slot0 * 16);
   }
 }
 
@@ -294,15 +314,17 @@ __device__ __forceinline__ void dma_tile512(const uint16_t* __restrict__ src, si
 // with 256-byte rows (half h holds columns 128 h .. 128 h + 127).
 // xlim: rows (k-contiguous) or columns (otherwise) of the operand in memory.
 template <bool KC>
-__device__ __forceinline__ void dma_operand(const uint16_t* __restrict__ src, size_t ld, int x0, int xlim, int k0,
+__device__ __forceinline__ void dma_operand(const uint16_t* __restrict__ src, int ld, int x0, int xlim, int k0,
                                             int kend, unsigned char* dst, int tid) {
   if constexpr (KC) {
-    dma_tile512<128, G2_TILE>(src, ld, x0, xlim - 1, INT32_MAX, k0, kend - 8, kend, dst, tid);
+    const Rsrc rs = make_rsrc(src + (size_t)x0 * ld + k0);
+    dma_tile512<128, G2_TILE>(rs, ld, x0, k0, x0, xlim - 1, INT32_MAX, k0, kend - 8, kend, dst, tid);
   } else {
+    const Rsrc rs = make_rsrc(src + (size_t)k0 * ld + x0);
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
-      dma_tile512<256, 64>(src, ld, k0, kend - 1, kend, x0 + 128 * hf, xlim - 8, INT32_MAX, dst + hf * (64 * 256),
-                           tid);
+      dma_tile512<256, 64>(rs, ld, k0, x0, k0, kend - 1, kend, x0 + 128 * hf, xlim - 8, INT32_MAX,
+                           dst + hf * (64 * 256), tid);
   }
 }
 
@@ -333,7 +355,16 @@ __global__ __launch_bounds__(G2_THREADS) void gemm256_kernel(const uint16_t* __r
                                                              int M, int N, int K, int lda, int ldb, int ldc,
                                                              int tiles_n, int tiles, int S, int kchunk,
                                                              float* __restrict__ part) {
+#if PROJ_G2_SPLIT
+  // One LDS array per stage, selected at compile time: the compiler then
+  // tells the copy into one stage from the reads of the other, and lets the
+  // next stage's copy run during this stage's products (with one array and a
+  // runtime stage index it waited for every copy before the first read).
+  __shared__ __attribute__((aligned(16))) unsigned char smem0[G2_STAGEB];
+  __shared__ __attribute__((aligned(16))) unsigned char smem1[G2_STAGEB];
+#else
   __shared__ __attribute__((aligned(16))) unsigned char smem[2 * G2_STAGEB];
+#endif
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
@@ -345,12 +376,26 @@ __global__ __launch_bounds__(G2_THREADS) void gemm256_kernel(const uint16_t* __r
   const int kbeg = s * kchunk, kend = min(K, kbeg + kchunk);
   const int nsteps = (kend - kbeg + 63) / 64;
 
-  auto dma_step = [&](int st, int buf) {
-    unsigned char* As = smem + buf * G2_STAGEB;
+#if PROJ_G2_SPLIT
+  auto stage = [&](auto b_) __attribute__((always_inline)) -> unsigned char* {
+    if constexpr (decltype(b_)::value == 0) return smem0;
+    else return smem1;
+  };
+#else
+  auto stage = [&](auto b_) __attribute__((always_inline)) -> unsigned char* {
+    return smem + decltype(b_)::value * G2_STAGEB;
+  };
+#endif
+  auto dma_step = [&](int st, auto b_) __attribute__((always_inline)) {
+    unsigned char* As = stage(b_);
     unsigned char* Bs = As + G2_TILE * 64 * 2;
     const int k0 = kbeg + st * 64;
-    dma_operand<AK>(A, lda, m0, M, k0, kend, As, tid);
-    dma_operand<BK>(Bm, ldb, n0, N, k0, kend, Bs, tid);
+    // Per-lane offsets are recomputed at every stage (the empty asm hides that
+    // they repeat): kept live across the loop for both stages they spill.
+    int t = tid;
+    if (PROJ_G2_REMAT) __asm__ volatile("" : "+v"(t));
+    dma_operand<AK>(A, lda, m0, M, k0, kend, As, t);
+    dma_operand<BK>(Bm, ldb, n0, N, k0, kend, Bs, t);
   };
 
   f32x16 acc[2][4];  // [n block][m block] of C^T
@@ -359,35 +404,65 @@ __global__ __launch_bounds__(G2_THREADS) void gemm256_kernel(const uint16_t* __r
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = f32x16{};
 
-  auto compute = [&](int buf) {
-    const unsigned char* As = smem + buf * G2_STAGEB;
+  // Products of one stage. The fragments of an operand that is not
+  // k-contiguous are read with transposing LDS reads, which the compiler
+  // cannot tell apart from the copy into the other stage: all of them are
+  // read before `start` issues that copy. The plain reads of a k-contiguous
+  // operand follow it, one 16-deep sub-step ahead of its products (the
+  // scheduling barriers keep the compiler from reading further ahead).
+  auto compute = [&](auto b_, auto&& start) __attribute__((always_inline)) {
+    const unsigned char* As = stage(b_);
     const unsigned char* Bs = As + G2_TILE * 64 * 2;
+    int ln = lane;
+    if (PROJ_G2_REMAT) __asm__ volatile("" : "+v"(ln));
+    u32x4 af[BK ? 2 : 4][2], bf[AK ? 2 : 4][4];
+    auto read = [&](auto kk_, auto tr_) __attribute__((always_inline)) {
+      constexpr int kk = decltype(kk_)::value;
+      constexpr bool TR = decltype(tr_)::value;
+      if constexpr (BK != TR)
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u32x4 af[2], bf[4];
+        for (int nb = 0; nb < 2; ++nb) af[BK ? kk & 1 : kk][nb] = frag256<BK>(Bs, wn * 64 + nb * 32, kk, ln);
+      if constexpr (AK != TR)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) af[nb] = frag256<BK>(Bs, wn * 64 + nb * 32, kk, lane);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) bf[mb] = frag256<AK>(As, wm * 128 + mb * 32, kk, lane);
+        for (int mb = 0; mb < 4; ++mb) bf[AK ? kk & 1 : kk][mb] = frag256<AK>(As, wm * 128 + mb * 32, kk, ln);
+    };
+    static_for<0, 4>([&](auto kk_) __attribute__((always_inline)) { read(kk_, BoolC<true>{}); });
+    start();
+    read(IntC<0>{}, BoolC<false>{});
+    static_for<0, 4>([&](auto kk_) __attribute__((always_inline)) {
+      constexpr int kk = decltype(kk_)::value;
+      if constexpr (kk + 1 < 4) read(IntC<kk + 1>{}, BoolC<false>{});
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) acc[nb][mb] = E::mfma(af[nb], bf[mb], acc[nb][mb]);
-    }
+        for (int mb = 0; mb < 4; ++mb)
+          acc[nb][mb] = E::mfma(af[BK ? kk & 1 : kk][nb], bf[AK ? kk & 1 : kk][mb], acc[nb][mb]);
+      if (PROJ_G2_SCHED) __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
-  dma_step(0, 0);
+  // Stage st in buffer st % 2 (compile-time: the loop takes two stages per
+  // iteration); the copy of stage st + 1 runs during the products of stage st.
+  // Every stage starts a copy and waits for it on the same path: the last one
+  // copies stage nsteps, whose contraction indices all lie at or past kend,
+  // so every lane takes the zero offset and no memory is read. (A copy and a
+  // wait under separate tests make the compiler assume a copy in flight at
+  // the loop head and wait for it before the first LDS read.)
+  auto one = [&](int st, auto b_) __attribute__((always_inline)) {
+    constexpr int Bf = decltype(b_)::value;
+    compute(b_, [&]() __attribute__((always_inline)) { dma_step(st + 1, IntC<Bf ^ 1>{}); });
+    wait_vmem();
+    __syncthreads();
+  };
+  dma_step(0, IntC<0>{});
   wait_vmem();
   __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nsteps) dma_step(st + 1, buf ^ 1);
-    compute(buf);
-    if (st + 1 < nsteps) {
-      wait_vmem();
-      __syncthreads();
-    }
+  int st = 0;
+  for (; st + 2 <= nsteps; st += 2) {
+    one(st, IntC<0>{});
+    one(st + 1, IntC<1>{});
   }
+  if (st < nsteps) one(st, IntC<0>{});
 
   // acc[nb][mb][4 j + i] = C[m][n], m = m0 + wm 128 + mb 32 + l32,
   // n = n0 + wn 64 + nb 32 + 8 j + 4 h + i.
@@ -509,7 +584,7 @@ template <class E, bool AK, bool BK>
 hipError_t gemm_auto(const uint16_t* A, const uint16_t* Bm, uint16_t* C, int M, int N, int K, int lda, int ldb,
                      int ldc, void* ws, hipStream_t stream) {
   const GemmPlan p = plan_gemm(M, N, K, ws != nullptr);
-  if (p.big) {
+  if (p.big && lda <= G2_MAX_LD && ldb <= G2_MAX_LD) {
     if (p.tiles == 0) return hipErrorInvalidValue;
     float* part = p.S > 1 ? static_cast<float*>(ws) : nullptr;
     hipLaunchKernelGGL((gemm256_kernel<E, AK, BK>), dim3((unsigned)(p.tiles * p.S)), dim3(G2_THREADS), 0, stream, A,
