@@ -14,7 +14,8 @@ The shapes cover:
   - ragged token counts and contraction tails (D not a multiple of 64, B N not a multiple of 64);
   - the smallest legal shape;
   - a 256 x 256-tile product with one contraction step (dw with 40 tokens);
-  - the small-product kernels (64 x 64 tiles with the contraction split over the 4 waves).
+  - the small-product kernels (64 x 64 tiles with the contraction split over the 4 waves);
+  - more than 4 million input features (leading dimensions past 2^22 elements).
 """
 from __future__ import annotations
 
@@ -88,6 +89,38 @@ def test_projection_forward_and_backward(gpu_lib, B, N, D, H, d):
     _check("dx", to_f64(dx), DX, AX, 3 * H * d, "bf16")
     _check("dw", to_f64(dw), DW, AW, T, "bf16")
     assert rel_l2(to_f64(dx), DX) <= TOL_GRAD_RELL2 and rel_l2(to_f64(dw), DW) <= TOL_GRAD_RELL2
+
+
+def test_projection_huge_leading_dimension(gpu_lib):
+    """D = 4,194,312 input features (8 tokens, one head of width 8): rows of x more than 8 MB apart, a forward
+    contraction of 16,384 steps on one workgroup, and a dW product of 32,768 row tiles, all with 64-bit copy
+    addresses. x is zero outside a seeded set of at most 2048 columns (runs at the start, across element 2^22 and
+    at the end), so every float32 sum has at most that many nonzero terms (adding a zero is exact) and the bound
+    uses that count; dW rows of the zero columns must be exactly zero."""
+    import torch
+    B, N, D, H, d = 1, 8, 4194312, 1, 8
+    _say(f"[proj] bf16 B={B} N={N} D={D} H={H} d={d} (global_load_lds copies)")
+    c = make_proj_case(B, N, D, H, d, "bf16", seed=11)
+    keep = np.zeros(D, dtype=bool)
+    keep[np.random.default_rng(11).choice(D, 1792, replace=False)] = True
+    keep[:64] = True
+    keep[(1 << 22) - 64:(1 << 22) + 64] = True
+    keep[-64:] = True
+    nnz = int(keep.sum())
+    assert nnz <= 2048
+    c.raw["x"] = np.where(keep, c.raw["x"], np.uint16(0)).astype(np.uint16)
+    x, w, dy = _up(c, "x"), _up(c, "w"), _up(c, "dqkv")
+    qkv, _, _, _ = gpu_lib.qkv_proj(x, w)
+    dx, dw = gpu_lib.qkv_proj_bwd(x, w, dy)
+    torch.cuda.synchronize()
+    X, W, DY = c.f64("x"), c.f64("w"), c.f64("dqkv")
+    _check("qkv", to_f64(qkv), qkv_projection(X, W), qkv_projection(np.abs(X), np.abs(W)), nnz, "bf16")
+    DX, DW = qkv_projection_bwd(X, W, DY)
+    AX, AW = qkv_projection_bwd(np.abs(X), np.abs(W), np.abs(DY))
+    _check("dx", to_f64(dx), DX, AX, 3 * H * d, "bf16")
+    dw64 = to_f64(dw)
+    _check("dw", dw64, DW, AW, B * N, "bf16")
+    assert not np.any(dw64[~keep]), "dw rows of all-zero x columns must be exactly zero"
 
 
 def test_projection_fp16(gpu_lib):
