@@ -28,9 +28,13 @@ def _say(msg):
 
 # ------------------------------------------------------------------ fp32 forward
 
-@pytest.mark.parametrize("N,d", [(196, 64), (1, 64), (7, 64), (63, 64), (64, 64), (65, 64), (333, 64),
-                                 (1, 128), (129, 128), (200, 128), (77, 32), (260, 32), (1, 96), (150, 96)])
+@pytest.mark.parametrize("N,d", [(196, 64), (1, 64), (7, 64), (63, 64), (64, 64), (65, 64), (256, 64), (257, 64),
+                                 (333, 64), (1, 128), (129, 128), (200, 128), (77, 32), (260, 32), (1, 96),
+                                 (150, 96)])
 def test_fwd_f32_parity(gpu_lib, N, d):
+    """fp32 forward against the oracle. On these small grids, rows of at most 256 keys at d = 32 and 64 take
+    the key-split kernel (the four waves of a workgroup on different key tiles, merged at the end: with
+    N <= 64 three waves see no key); N = 257 and longer rows take the prefetching kernel."""
     import torch
     x = make_case(2 if N < 300 else 1, 2, N, d, "f32", seed=N + d, with_grad=False)
     _say(f"fwd_f32 B={x.B} H={x.H} N={N} d={d}")

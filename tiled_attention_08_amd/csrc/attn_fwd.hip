@@ -1453,6 +1453,9 @@ void fwd_sp_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 // rows per workgroup gave.
 // ------------------------------------------------------------------------
 constexpr int kF32BR = 8;
+#ifndef FWD_F32_SPLIT
+#define FWD_F32_SPLIT 1
+#endif
 constexpr int kBC = 64;  // keys per K/V tile of the fp32 kernel
 
 // PF: the loads of the next K/V tile are issued before the current tile's
@@ -1587,6 +1590,145 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(const float* __restrict__ 
   }
 }
 
+// fp32 forward for grids too small to fill the chip (one head of the ViT
+// shape: 25 workgroups of kF32BR rows): there the time is the chain of key
+// tiles each row walks through. Here the four waves of a workgroup take the
+// same kF32SR rows and every fourth 64-key tile each (wave g: tiles g, g + 4,
+// ...), each keeping its own running maximum, normaliser and partial output
+// (§3, online-softmax bullet, applied per wave); at the end wave 0 merges the
+// four partial states by the same rescaling. For 196 keys every wave walks one
+// tile. All waves run the same number of iterations (a wave whose tile lies
+// past N masks every key), so the workgroup barriers stay uniform. The
+// launcher uses it for rows of at most four tiles.
+constexpr int kF32SR = 2;
+template <int D>
+__global__ __launch_bounds__(256) void fwd_f32_split_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                            const float* __restrict__ V, float* __restrict__ O,
+                                                            float* __restrict__ LSE, int N, int n_qblk, float scale) {
+  static_assert(D == 32 || D == 64, "one wave loads a tile; LDS holds four");
+  constexpr int KG = 4, KS = D + 4, PS = kBC + 4, DC = D / 32;
+  constexpr int PT = kBC * D / 4 / 64;  // float4 of K (and of V) per lane and tile
+  __shared__ __attribute__((aligned(16))) float Ks[KG][kBC * KS];
+  __shared__ __attribute__((aligned(16))) float Vs[KG][kBC * D];
+  __shared__ __attribute__((aligned(16))) float Ps[KG][kF32SR * PS];
+
+  const int tid = threadIdx.x, g = tid >> 6, lane = tid & 63;
+  const int r = lane >> 5, t = lane & 31;
+  const int bh = blockIdx.x / n_qblk, qblk = blockIdx.x - bh * n_qblk;
+  const size_t head = (size_t)bh * N * D;
+  const int q = qblk * kF32SR + r;
+
+  float4 qv[D / 4];
+#pragma unroll
+  for (int i = 0; i < D / 4; ++i)
+    qv[i] = (q < N) ? *reinterpret_cast<const float4*>(Q + head + (size_t)q * D + 4 * i) : make_float4(0.f, 0.f, 0.f, 0.f);
+
+  float acc[DC];
+#pragma unroll
+  for (int i = 0; i < DC; ++i) acc[i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  const int n_tiles = (N + kBC - 1) / kBC, n_iter = (n_tiles + KG - 1) / KG;
+  for (int it = 0; it < n_iter; ++it) {
+    const int j0 = (it * KG + g) * kBC;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int idx = lane + 64 * u, kr = idx / (D / 4), c4 = idx - kr * (D / 4);
+      float4 kk = make_float4(0.f, 0.f, 0.f, 0.f), vv = kk;
+      if (j0 + kr < N) {
+        kk = *reinterpret_cast<const float4*>(K + head + (size_t)(j0 + kr) * D + 4 * c4);
+        vv = *reinterpret_cast<const float4*>(V + head + (size_t)(j0 + kr) * D + 4 * c4);
+      }
+      *reinterpret_cast<float4*>(&Ks[g][kr * KS + 4 * c4]) = kk;
+      *reinterpret_cast<float4*>(&Vs[g][kr * D + 4 * c4]) = vv;
+    }
+    __syncthreads();
+
+    // Scores of keys t and t + 32 of this wave's tile.
+    float s[2] = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const float4 kv = *reinterpret_cast<const float4*>(&Ks[g][(t + 32 * u) * KS + 4 * i]);
+        s[u] = fmaf(qv[i].x, kv.x, s[u]);
+        s[u] = fmaf(qv[i].y, kv.y, s[u]);
+        s[u] = fmaf(qv[i].z, kv.z, s[u]);
+        s[u] = fmaf(qv[i].w, kv.w, s[u]);
+      }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      s[u] = (j0 + t + 32 * u < N) ? s[u] * scale : -INFINITY;
+      mx = fmaxf(mx, s[u]);
+    }
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float mnew = fmaxf(m, mx);
+    // A wave that has seen no key yet keeps m = -inf (and l = 0, acc = 0).
+    const float alpha = mnew == -INFINITY ? 1.f : expf(m - mnew);
+    float rs = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const float p = (j0 + t + 32 * u < N) ? expf(s[u] - mnew) : 0.f;
+      rs += p;
+      Ps[g][r * PS + t + 32 * u] = p;
+    }
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) rs += __shfl_xor(rs, o);
+    l = l * alpha + rs;
+    m = mnew;
+#pragma unroll
+    for (int i = 0; i < DC; ++i) acc[i] *= alpha;
+    __syncthreads();
+    for (int k4 = 0; k4 < kBC; k4 += 4) {
+      const float4 p4 = *reinterpret_cast<const float4*>(&Ps[g][r * PS + k4]);
+      const float pk[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < DC; ++i) acc[i] = fmaf(pk[e], Vs[g][(k4 + e) * D + t * DC + i], acc[i]);
+    }
+  }
+
+  // Merge: waves 1..3 leave (m, l, acc) in LDS (over their K tiles), wave 0
+  // rescales each partial state to the common maximum and adds.
+  __syncthreads();
+  float* part = &Ks[0][0];  // [KG][kF32SR][32][2 + DC]
+  constexpr int PW = 2 + DC;
+  if (g > 0) {
+    float* e = part + ((g * kF32SR + r) * 32 + t) * PW;
+    e[0] = m;
+    e[1] = l;
+#pragma unroll
+    for (int i = 0; i < DC; ++i) e[2 + i] = acc[i];
+  }
+  __syncthreads();
+  if (g > 0) return;
+  float mt = m;
+#pragma unroll
+  for (int o = 1; o < KG; ++o) mt = fmaxf(mt, part[((o * kF32SR + r) * 32 + t) * PW]);
+  const float a0 = m == -INFINITY ? 0.f : expf(m - mt);
+  float lt = l * a0;
+#pragma unroll
+  for (int i = 0; i < DC; ++i) acc[i] *= a0;
+#pragma unroll
+  for (int o = 1; o < KG; ++o) {
+    const float* e = part + ((o * kF32SR + r) * 32 + t) * PW;
+    const float a = e[0] == -INFINITY ? 0.f : expf(e[0] - mt);
+    lt = fmaf(e[1], a, lt);
+#pragma unroll
+    for (int i = 0; i < DC; ++i) acc[i] = fmaf(e[2 + i], a, acc[i]);
+  }
+  if (q < N) {
+    const float inv = 1.0f / lt;
+#pragma unroll
+    for (int i = 0; i < DC; ++i) O[head + (size_t)q * D + t * DC + i] = acc[i] * inv;
+    if (t == 0) LSE[(size_t)bh * N + q] = mt + logf(lt);
+  }
+}
+
 }  // namespace
 
 template <class E, int D, int QB, int KB>
@@ -1698,6 +1840,19 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
   const int n_qblk = (N + kF32BR - 1) / kF32BR;
   const int total = n_qblk * B * H;
   const bool pf = total < 256 && d <= 64;  // under one workgroup per CU: latency-bound
+  // Rows of at most 4 tiles: the key-split kernel, one tile per wave (measured, B=1, H=1, N=196, d=64: 10.8 ->
+  // 6.9 us per call). With more tiles per wave it lost (N = 300: 9.7 -> 15.2 us; N = 700: 26 -> 42 us): it
+  // has no prefetch, and its 2-row workgroups read every K/V tile four times as often.
+  if (pf && FWD_F32_SPLIT && N <= 4 * kBC) {
+    const int n_sblk = (N + kF32SR - 1) / kF32SR;
+    if (d == 32)
+      hipLaunchKernelGGL((fwd_f32_split_kernel<32>), dim3(n_sblk * B * H), dim3(256), 0, stream, q, k, v, o, lse, N,
+                         n_sblk, scale);
+    else
+      hipLaunchKernelGGL((fwd_f32_split_kernel<64>), dim3(n_sblk * B * H), dim3(256), 0, stream, q, k, v, o, lse, N,
+                         n_sblk, scale);
+    return hipGetLastError();
+  }
 #define ATTN_FWD_F32(D)                                                                                           \
   if (pf)                                                                                                         \
     hipLaunchKernelGGL((fwd_f32_kernel<D, D <= 64>), dim3(total), dim3(256), 0, stream, q, k, v, o, lse, N, n_qblk, \
